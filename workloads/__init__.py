@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for the paged-KV attention path.
+
+This module draws lengths, block assignments and N(0,1) tensors, and lays them
+into pools with NaN poison everywhere no valid token lives.  It holds none of
+the attention arithmetic: both the product path and the oracle consume what it
+produces, so it is the only code they share.
+
+Workload shapes (one per named case):
+  tiny_f32      4 sequences, lengths {17, 64, 100, 200}, 8 heads (MHA),
+                head_dim 64, block_size 16, 64 blocks, fp32, scale 1/8
+  mha_7b        64 sequences, lengths uniform in [128, 4096], 32/32 heads,
+                head_dim 128, block_size 16, 200,000-block pool, bf16
+  gqa           128 sequences, lengths round(lognormal(ln 1024, 1.0)) clipped
+                to [16, 8192], 32 query heads over 8 kv heads, head_dim 128,
+                block_size 16, 200,000-block pool, bf16
+  prefix_shared 16 prompts of 2048 + j shared tokens (j = 1 + i mod 15), 8
+                samples each with private tails uniform in [1, 512], 32/32
+                heads, head_dim 128, block_size 16, bf16
+  mixed         8 decode sequences of 32768 tokens (block_size 128,
+                partitions of 512) plus 4 prefill chunks of 512 new tokens over
+                4096 cached ones; 32 query / 8 kv heads, head_dim 128, bf16,
+                8,192-block pool
+
+Seeds: case k uses 0x417 + k.  Lengths, permutations and tails come from
+``numpy.random.default_rng(seed)``; tensors from ``torch.Generator`` seeded
+with the same value on the target device, drawn in fp32 and rounded to bf16
+(round-to-nearest-even) where the case is bf16.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+SEED_BASE = 0x417
+
+
+@dataclasses.dataclass
+class DecodeShape:
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    partition_size: int = 0  # 0: library default
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+TINY_F32 = DecodeShape("tiny_f32", 4, 8, 8, 64, 16, 64, "f32", SEED_BASE + 1)
+MHA_7B = DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "bf16", SEED_BASE + 2)
+GQA = DecodeShape("gqa", 128, 32, 8, 128, 16, 200_000, "bf16", SEED_BASE + 3)
+PREFIX_SHARED = DecodeShape("prefix_shared", 128, 32, 32, 128, 16, 200_000, "bf16",
+                            SEED_BASE + 4)
+MIXED_DECODE = DecodeShape("mixed", 8, 32, 8, 128, 128, 8_192, "bf16", SEED_BASE + 5,
+                           partition_size=512)
+
+SHAPES = {s.name: s for s in (TINY_F32, MHA_7B, GQA, PREFIX_SHARED, MIXED_DECODE)}
+
+
+def draw_lengths(shape: DecodeShape, rng: np.random.Generator) -> np.ndarray:
+    """Context lengths of one decode batch, int32."""
+    if shape.name == "tiny_f32":
+        return np.array([17, 64, 100, 200], dtype=np.int32)
+    if shape.name == "mha_7b":
+        return rng.integers(128, 4096, size=shape.num_seqs, endpoint=True).astype(np.int32)
+    if shape.name == "gqa":
+        raw = np.rint(rng.lognormal(mean=math.log(1024.0), sigma=1.0, size=shape.num_seqs))
+        return np.clip(raw, 16, 8192).astype(np.int32)
+    if shape.name == "mixed":
+        return np.full(shape.num_seqs, 32768, dtype=np.int32)
+    raise ValueError(f"no length recipe for {shape.name}")
+
+
+def blocks_needed(length: int, block_size: int) -> int:
+    return -(-int(length) // int(block_size))
+
+
+def assign_blocks(lengths, block_size: int, num_blocks: int, rng: np.random.Generator,
+                  stride: int | None = None, pad_block: int | None = None):
+    """Give each sequence consecutive entries of one seeded permutation of the pool.
+
+    Sequence 0 takes perm[0:n0], sequence 1 perm[n0:n0+n1], ...  This is the
+    order in which an allocator seeded with ``free_order=perm`` hands blocks
+    out.  The last pool block is kept back as a pad block (never assigned) and
+    fills unused table entries.  Returns (perm, tables[S][stride] int32).
+    """
+    lengths = np.asarray(lengths)
+    counts = [blocks_needed(L, block_size) for L in lengths]
+    pad = num_blocks - 1 if pad_block is None else pad_block
+    pool = np.delete(np.arange(num_blocks, dtype=np.int64), pad)
+    perm = rng.permutation(pool)
+    if sum(counts) > perm.size:
+        raise ValueError("pool too small")
+    width = max(counts + [1]) + 1 if stride is None else stride
+    tables = np.full((len(lengths), width), pad, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(counts):
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    perm = np.concatenate([perm, [pad]])
+    return perm.astype(np.int32), tables
+
+
+def randn(shape, dtype, generator: torch.Generator, device) -> torch.Tensor:
+    """N(0,1) drawn in fp32, rounded to ``dtype``."""
+    x = torch.randn(shape, generator=generator, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def empty_pools(num_blocks, num_kv_heads, block_size, head_dim, dtype, device,
+                k_axes="bhrd", v_axes="bhrd"):
+    """Two NaN-filled pools with the requested axis orders."""
+    dims = {"b": num_blocks, "h": num_kv_heads, "r": block_size, "d": head_dim}
+    k = torch.full([dims[a] for a in k_axes], float("nan"), dtype=dtype, device=device)
+    v = torch.full([dims[a] for a in v_axes], float("nan"), dtype=dtype, device=device)
+    return k, v
+
+
+def _to_axes(t: torch.Tensor, axes: str) -> torch.Tensor:
+    """Permute a [n][h][r][d] tensor to the given axis order."""
+    return t.permute(*["bhrd".index(a) for a in axes])
+
+
+def fill_used_blocks(k_pool, v_pool, tables, lengths, block_size, generator,
+                     k_axes="bhrd", v_axes="bhrd", chunk_blocks: int = 4096):
+    """Write N(0,1) K/V into every valid row of every sequence; rows past a
+    sequence's length in its last block are set to NaN.  Blocks are visited
+    sequence by sequence in table order, so the content depends only on the
+    seed, the lengths and the table order."""
+    h = k_pool.shape[k_axes.index("h")]
+    d = k_pool.shape[k_axes.index("d")]
+    ids, valid_rows = [], []
+    for s, L in enumerate(np.asarray(lengths)):
+        n = blocks_needed(L, block_size)
+        for j in range(n):
+            ids.append(int(tables[s][j]))
+            valid_rows.append(min(block_size, int(L) - j * block_size))
+    ids = np.asarray(ids, dtype=np.int64)
+    valid_rows = np.asarray(valid_rows, dtype=np.int64)
+    dev = k_pool.device
+    for lo in range(0, len(ids), chunk_blocks):
+        hi = min(lo + chunk_blocks, len(ids))
+        idx = torch.as_tensor(ids[lo:hi], device=dev)
+        for pool, axes in ((k_pool, k_axes), (v_pool, v_axes)):
+            data = randn((hi - lo, h, block_size, d), pool.dtype, generator, dev)
+            rows = torch.arange(block_size, device=dev).view(1, 1, block_size, 1)
+            keep = rows < torch.as_tensor(valid_rows[lo:hi], device=dev).view(-1, 1, 1, 1)
+            data = torch.where(keep, data, torch.full_like(data, float("nan")))
+            pool.view(pool.shape)[idx] = _to_axes(data, axes)
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    shape: DecodeShape
+    lengths: np.ndarray
+    perm: np.ndarray
+    tables: np.ndarray
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_axes: str
+    v_axes: str
+
+
+def make_decode_case(shape: DecodeShape, device, k_axes="bhrd", v_axes="bhrd",
+                     seed: int | None = None, lengths=None, num_blocks: int | None = None,
+                     extra_table_slots: int = 0) -> DecodeCase:
+    """A full decode batch for ``shape``: lengths, tables, q and poisoned pools."""
+    seed = shape.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    lens = draw_lengths(shape, rng) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    nb = shape.num_blocks if num_blocks is None else num_blocks
+    stride = max(blocks_needed(L + extra_table_slots, shape.block_size) for L in lens) + 1
+    perm, tables = assign_blocks(lens, shape.block_size, nb, rng, stride=stride)
+    gen = make_generator(seed, device)
+    k_pool, v_pool = empty_pools(nb, shape.num_kv_heads, shape.block_size, shape.head_dim,
+                                 shape.torch_dtype, device, k_axes, v_axes)
+    fill_used_blocks(k_pool, v_pool, tables, lens, shape.block_size, gen, k_axes, v_axes)
+    q = randn((len(lens), shape.num_q_heads, shape.head_dim), shape.torch_dtype, gen, device)
+    return DecodeCase(shape, lens, perm, tables, q, k_pool, v_pool, k_axes, v_axes)
+
+
+# ---------------------------------------------------------------------------
+# prefix-shared parallel sampling
+
+
+@dataclasses.dataclass
+class PrefixPlan:
+    """Per prompt: shared token count; per sample: private tail length."""
+    shared_lens: np.ndarray  # [P]
+    tail_lens: np.ndarray  # [P][samples]
+
+
+def prefix_plan(num_prompts=16, samples=8, prompt_len=2048, seed=SEED_BASE + 4,
+                max_tail=512, fork_offsets=True) -> PrefixPlan:
+    """Prompt i forks after 2048 + j shared tokens, j = 1 + (i mod 15), so the
+    shared last block is partial and the first private append copies it."""
+    rng = np.random.default_rng(seed)
+    if fork_offsets:
+        shared = np.array([prompt_len + 1 + (i % 15) for i in range(num_prompts)], dtype=np.int32)
+    else:
+        shared = np.full(num_prompts, prompt_len, dtype=np.int32)
+    tails = rng.integers(1, max_tail, size=(num_prompts, samples), endpoint=True).astype(np.int32)
+    return PrefixPlan(shared, tails)
+
+
+# ---------------------------------------------------------------------------
+# mixed step: chunked prefill beside decode
+
+
+@dataclasses.dataclass
+class PrefillShape:
+    num_reqs: int = 4
+    new_tokens: int = 512
+    cached_tokens: int = 4096
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 128
+    block_size: int = 128
+    dtype: str = "bf16"
+    seed: int = SEED_BASE + 5
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+MIXED_PREFILL = PrefillShape()
