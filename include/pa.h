@@ -1,0 +1,254 @@
+/*
+ * pa.h — C ABI of libpa: paged-KV attention for MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *   [VE] 《加速 LLM 推理：深入了解 vLLM 引擎》
+ *   [VF] 《大模型推理：vLLM大模型推理框架（附下载）》
+ *   [NV] 《Nano-vLLM 原理：vLLM 风格推理引擎的实现机制》
+ *   [VI] 《vLLM大模型推理引擎：高效解决显存碎片与请求排队难题》
+ *
+ * The KV cache is cut into fixed-size blocks of block_size tokens that live
+ * anywhere in a pre-allocated pool; a per-sequence block table maps logical
+ * block j of a sequence to a physical block ([VE] §3.1; [VI] §2.1).  Token
+ * position pos lives in logical block pos / block_size at offset
+ * pos % block_size ([VF] §1.1).
+ *
+ * Storage layout (the ABI; K and V are separate regions of each block,
+ * [VI] §2.1):
+ *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major)
+ *   Within a block and head, K rows are contiguous per token, V rows are
+ *   contiguous per dimension (tokens innermost).
+ *
+ * Conventions for every device call:
+ *   - All pointers are device pointers owned by the caller, 16-byte aligned.
+ *     The library never allocates or frees device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     Nothing synchronises the host.
+ *   - A non-OK status means nothing was enqueued; pa_last_error() gives text.
+ *     Faults that happen later on the device surface as HIP errors at the
+ *     caller's next synchronisation.
+ *   - Supported: head_dim in {64, 128}; block_size in {16, 32, 64, 128};
+ *     num_q_heads % num_kv_heads == 0 and group size (Hq/Hkv) <= 16;
+ *     dtype bf16 for every call, and fp32 for cache write, block copy and
+ *     decode.  Other shapes return PA_ERR_UNSUPPORTED.
+ *
+ * Host allocator calls touch host memory only and are not thread-safe: one
+ * scheduler thread owns an allocator.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* bad pointer, size or value; nothing done      */
+    PA_ERR_OUT_OF_BLOCKS = 2, /* the pool cannot supply the blocks asked for   */
+    PA_ERR_NOT_FOUND = 3,     /* unknown sequence id                           */
+    PA_ERR_UNSUPPORTED = 4,   /* valid arguments with no kernel for them       */
+    PA_ERR_DEVICE = 5         /* the HIP runtime refused a launch              */
+} pa_status;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char *pa_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device calls                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Cache write: a newly generated token needs only its K/V written into the
+ * slot its block table assigns ([VE] §3.1).
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], dtype.
+ *   slot_mapping   [num_tokens] int64 device: slot = block * block_size + offset.
+ *                  A negative slot, or one >= num_blocks * block_size, is
+ *                  skipped (nothing written for that token).
+ * Bit-exact copy: no conversion, no arithmetic on the values. */
+pa_status pa_cache_write(const void *k_new, const void *v_new,
+                         void *k_cache, void *v_cache,
+                         const int64_t *slot_mapping, int32_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, void *stream);
+
+/* Copy-on-write copy: before a sequence writes into a block it shares, that
+ * whole block (K and V, all heads, all rows) is copied to a private block
+ * ([VI] §2.1, COW for shared prefixes).
+ *   src_dst  [num_pairs][2] int32 device (src, dst).  Pairs with an id
+ *            outside [0, num_blocks) are skipped.  dst blocks must be
+ *            distinct from every src and from each other.
+ * Must be enqueued before the cache write that targets dst. */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache,
+                         const int32_t *src_dst, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, void *stream);
+
+/* Partition size (tokens) pa_decode uses when called with partition_size 0:
+ * sequences longer than one partition are split and their parts processed
+ * independently, then merged ([VF] §1.1: segments of a sequence can be
+ * processed independently).  Always a multiple of 32 and of block_size. */
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t block_size, int32_t max_context_len);
+
+/* Bytes of device workspace pa_decode needs for the split-K partials with
+ * these sizes (partition_size 0 = the default above).  0 when no sequence
+ * can span more than one partition; (size_t)-1 on invalid sizes. */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size);
+
+/* Paged decode attention ([VE] §3.1 block-table walk; [VE] §3.3 scaling,
+ * softmax, weighted sum):
+ *   out[s][h][:] = softmax(scale * q[s][h] . K_s^T) V_s
+ * where K_s, V_s are the first context_lens[s] tokens of sequence s read
+ * through block_tables[s], and query head h reads kv head h / (Hq / Hkv).
+ *   out           [num_seqs][num_q_heads][head_dim] fp32.
+ *   q             [num_seqs][num_q_heads][head_dim], dtype.
+ *   block_tables  [num_seqs][block_table_stride] int32 device.
+ *   context_lens  [num_seqs] int32 device; the count includes the token
+ *                 being decoded (its K/V already written).  0 gives a zero
+ *                 row.  A length < 0, > max_context_len or needing more
+ *                 than block_table_stride blocks, and a table entry outside
+ *                 [0, num_blocks), make that row NaN; nothing is read out of
+ *                 range.
+ *   max_context_len  host-known upper bound of context_lens (sizes the grid).
+ *   partition_size   tokens per split-K partition: 0 = default, else a
+ *                    multiple of 32 and of block_size.
+ *   workspace     device scratch of at least pa_decode_workspace_size(...)
+ *                 bytes (may be NULL when that is 0).  Its contents on entry
+ *                 are irrelevant.  Calls sharing one workspace must be
+ *                 ordered on one stream.
+ * fp32 output; accumulation in fp32. */
+pa_status pa_decode(float *out, const void *q,
+                    const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t block_table_stride,
+                    const int32_t *context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    float scale, int32_t max_context_len,
+                    int32_t partition_size, void *workspace,
+                    size_t workspace_bytes, pa_dtype dtype, void *stream);
+
+/* Chunked prefill: one iteration may carry new prompt chunks beside decode
+ * rows ([VI] §1, continuous batching mixes requests in different phases).
+ * Request r owns query rows cu_q_lens[r] .. cu_q_lens[r+1]-1; its context
+ * holds context_lens[r] tokens whose last qlen_r are the chunk itself (their
+ * K/V already written with pa_cache_write).  Row i of request r sits at
+ * position p = context_lens[r] - qlen_r + i and attends to keys 0..p.
+ *   out         [total_q_tokens][num_q_heads][head_dim] fp32.
+ *   q           [total_q_tokens][num_q_heads][head_dim] bf16.
+ *   cu_q_lens   [num_reqs + 1] int32 device, non-decreasing, cu_q_lens[0]=0,
+ *               cu_q_lens[num_reqs] = total_q_tokens.
+ *   context_lens [num_reqs] int32 device.
+ *   max_q_len, max_context_len  host-known bounds (size the grid).
+ * A request whose qlen exceeds its context, exceeds max_q_len, or whose
+ * context exceeds max_context_len or its table, or a table entry outside
+ * [0, num_blocks), gets NaN rows; nothing is read out of range.  bf16 only. */
+pa_status pa_prefill_chunk(float *out, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables,
+                           int32_t block_table_stride,
+                           const int32_t *cu_q_lens,
+                           const int32_t *context_lens, int32_t num_reqs,
+                           int32_t total_q_tokens, int32_t max_q_len,
+                           int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           float scale, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator                                                       */
+/* ------------------------------------------------------------------------ */
+/* A fixed pool of num_blocks blocks with a per-block reference count
+ * (0 = free, 1 = owned, >1 = shared; the per-block state of [VI] §2.1),
+ * a free list used as a stack ([VI] §2.1 allocation pops the free list),
+ * and one block table per sequence kept in host memory ([VI] §2.1).
+ * A sequence of n tokens holds ceil(n / block_size) blocks ([NV] code
+ * example 1); asking for more than the pool has is an error that changes
+ * nothing ([NV] code example 1). */
+
+typedef struct pa_allocator pa_allocator;
+
+typedef struct {
+    int32_t num_blocks;
+    int32_t num_free;
+    int32_t num_used;
+    int32_t num_shared; /* blocks with refcount > 1 */
+    int64_t cow_copies; /* copy-on-write pairs handed out so far */
+} pa_allocator_stats_t;
+
+/* free_order: NULL, or a permutation of 0..num_blocks-1 giving the order in
+ * which blocks are first handed out (free_order[0] first).  Without it,
+ * block 0 first.  *out receives the handle (host memory only). */
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t *free_order, pa_allocator **out);
+void pa_allocator_destroy(pa_allocator *a);
+
+/* New empty sequence.  INVALID_ARG if the id exists. */
+pa_status pa_seq_create(pa_allocator *a, int64_t seq_id);
+
+/* Child shares every block of parent (refcount + 1 each) and its length
+ * ([VE] §3.1: parallel and speculative sampling share a prefix's blocks). */
+pa_status pa_seq_fork(pa_allocator *a, int64_t parent, int64_t child);
+
+/* Append n_tokens positions to a sequence; blocks are taken on demand, one
+ * when a position starts a new block ([VE] §3.1).  slots_out[i] receives the
+ * slot of position len+i.  If the last block is partly filled and shared, it
+ * is first replaced by a fresh private block and (old, new) written to
+ * cow_pairs_out (copy-on-write, [VI] §2.1); *n_cow gets the number of pairs
+ * (0 or 1).  The caller copies those pairs (pa_copy_blocks) before writing
+ * the new slots.  All or nothing: OUT_OF_BLOCKS, or INVALID_ARG when
+ * cow_cap is too small, leave every table and count unchanged.
+ *   slots_out     [n_tokens] host; cow_pairs_out [cow_cap][2] host. */
+pa_status pa_seq_append(pa_allocator *a, int64_t seq_id, int32_t n_tokens,
+                        int64_t *slots_out, int32_t *cow_pairs_out,
+                        int32_t cow_cap, int32_t *n_cow);
+
+/* Release a finished sequence: each block loses a reference; blocks that
+ * reach zero go back on the free list at once ([VE] §3.1), last table entry
+ * first, so the sequence's first block is handed out next. */
+pa_status pa_seq_free(pa_allocator *a, int64_t seq_id);
+
+pa_status pa_seq_length(const pa_allocator *a, int64_t seq_id, int32_t *len);
+
+/* Copy the sequence's block table (physical ids, logical order) to out
+ * [cap]; *n_out gets its length.  INVALID_ARG if cap is too small. */
+pa_status pa_seq_block_table(const pa_allocator *a, int64_t seq_id,
+                             int32_t *out, int32_t cap, int32_t *n_out);
+
+pa_status pa_allocator_stats(const pa_allocator *a, pa_allocator_stats_t *out);
+pa_status pa_block_refcount(const pa_allocator *a, int32_t block,
+                            int32_t *refcount);
+
+/* One scheduling step for many sequences at once: append n_tokens[i]
+ * positions to seq_ids[i] for every i, writing the slots back to back into
+ * slots_out (sum of n_tokens entries) and every copy-on-write pair into
+ * cow_pairs_out.  All or nothing across the whole batch.  Ids must be
+ * distinct. */
+pa_status pa_batch_append(pa_allocator *a, int32_t num_seqs,
+                          const int64_t *seq_ids, const int32_t *n_tokens,
+                          int64_t *slots_out, int32_t *cow_pairs_out,
+                          int32_t cow_cap, int32_t *n_cow);
+
+/* Dense block tables and lengths of a batch, ready to copy to the device:
+ * tables_out [num_seqs][stride] (entries past a sequence's blocks set to
+ * pad_value), context_lens_out [num_seqs].  INVALID_ARG if a table does not
+ * fit in stride. */
+pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs,
+                          const int64_t *seq_ids, int32_t *tables_out,
+                          int32_t stride, int32_t pad_value,
+                          int32_t *context_lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

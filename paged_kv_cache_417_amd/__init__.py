@@ -1,0 +1,307 @@
+"""Python binding of libpa (paged-KV attention for MI355X / gfx950).
+
+A thin ctypes layer: every function here marshals torch tensors into the raw
+pointers and sizes of the C ABI declared in ``include/pa.h`` and raises
+:class:`PAError` on a non-OK status.  All computation happens in the HIP
+kernels of ``libpa.so``; if the library is missing, importing this package
+fails.  PyTorch provides device memory and the current stream only.
+
+Storage layout (the ABI): ``k_cache [NB][Hkv][BS][D]``, ``v_cache
+[NB][Hkv][D][BS]``; see :func:`kv_cache_shapes`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = 1
+PA_ERR_OUT_OF_BLOCKS = 2
+PA_ERR_NOT_FOUND = 3
+PA_ERR_UNSUPPORTED = 4
+PA_ERR_DEVICE = 5
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+
+# Axis order of the two pools, in the letters b (block), h (kv head),
+# r (row = token within block), d (head dim).
+K_AXES = "bhrd"
+V_AXES = "bhdr"
+
+# Every symbol the header declares; the CPU tests check the library exports them.
+EXPORTED = (
+    "pa_last_error", "pa_cache_write", "pa_copy_blocks", "pa_decode_default_partition",
+    "pa_decode_workspace_size", "pa_decode", "pa_prefill_chunk", "pa_allocator_create",
+    "pa_allocator_destroy", "pa_seq_create", "pa_seq_fork", "pa_seq_append", "pa_seq_free",
+    "pa_seq_length", "pa_seq_block_table", "pa_allocator_stats", "pa_block_refcount",
+    "pa_batch_append", "pa_batch_tables",
+)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libpa status {status}: {message}")
+        self.status = status
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+class AllocatorStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_free", ctypes.c_int32),
+                ("num_used", ctypes.c_int32), ("num_shared", ctypes.c_int32),
+                ("cow_copies", ctypes.c_int64)]
+
+
+def _declare(lib):
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    st = ctypes.c_int
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "pa_last_error": (ctypes.c_char_p, []),
+        "pa_cache_write": (st, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]),
+        "pa_copy_blocks": (st, [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]),
+        "pa_decode_default_partition": (i32, [i32, i32, i32, i32]),
+        "pa_decode_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "pa_decode": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                           i32, vp, sz, ctypes.c_int, vp]),
+        "pa_prefill_chunk": (st, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, f32, ctypes.c_int, vp]),
+        "pa_allocator_create": (st, [i32, i32, pi32, ctypes.POINTER(vp)]),
+        "pa_allocator_destroy": (None, [vp]),
+        "pa_seq_create": (st, [vp, i64]),
+        "pa_seq_fork": (st, [vp, i64, i64]),
+        "pa_seq_append": (st, [vp, i64, i32, pi64, pi32, i32, pi32]),
+        "pa_seq_free": (st, [vp, i64]),
+        "pa_seq_length": (st, [vp, i64, pi32]),
+        "pa_seq_block_table": (st, [vp, i64, pi32, i32, pi32]),
+        "pa_allocator_stats": (st, [vp, ctypes.POINTER(AllocatorStats)]),
+        "pa_block_refcount": (st, [vp, i32, pi32]),
+        "pa_batch_append": (st, [vp, i32, pi64, pi32, pi64, pi32, i32, pi32]),
+        "pa_batch_tables": (st, [vp, i32, pi64, pi32, i32, i32, pi32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python paged_kv_cache_417_amd/build.py` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+_declare(_lib)
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int):
+    if status != PA_OK:
+        msg = _lib.pa_last_error().decode(errors="replace")
+        if status == PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(status, msg)
+        raise PAError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    return 99  # rejected by the library as an invalid dtype
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def kv_cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int):
+    """Shapes of (k_cache, v_cache) in the library's layout."""
+    return ((num_blocks, num_kv_heads, block_size, head_dim),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def _geometry(k_cache: torch.Tensor):
+    nb, hkv, bs, d = k_cache.shape
+    return nb, hkv, bs, d
+
+
+# ---------------------------------------------------------------------------
+# device calls
+
+
+def pa_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    nb, hkv, bs, d = _geometry(k_cache)
+    _check(_lib.pa_cache_write(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping),
+                               k_new.shape[0], hkv, d, bs, nb, _dtype_code(k_cache),
+                               ctypes.c_void_p(_stream(stream))))
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
+    nb, hkv, bs, d = _geometry(k_cache)
+    n = src_dst.numel() // 2
+    _check(_lib.pa_copy_blocks(_p(k_cache), _p(v_cache), _p(src_dst), n, hkv, d, bs, nb,
+                               _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
+
+
+def pa_decode_default_partition(num_seqs, num_kv_heads, block_size, max_context_len) -> int:
+    return int(_lib.pa_decode_default_partition(num_seqs, num_kv_heads, block_size,
+                                                max_context_len))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, partition_size=0) -> int:
+    n = _lib.pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_context_len, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: invalid sizes")
+    return int(n)
+
+
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                     partition_size=0, device="cuda"):
+    """A device buffer large enough for pa_decode's split-K partials (or None)."""
+    n = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 max_context_len, partition_size)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+              partition_size=0, workspace=None, stream=None) -> None:
+    nb, hkv, bs, d = _geometry(k_cache)
+    s, hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                          block_tables.shape[1], _p(context_lens), s, hq, hkv, d, bs, nb,
+                          float(scale), int(max_context_len), int(partition_size), _p(workspace),
+                          ws_bytes, _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
+
+
+def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,
+                     max_q_len, max_context_len, stream=None) -> None:
+    nb, hkv, bs, d = _geometry(k_cache)
+    tq, hq, _ = q.shape
+    _check(_lib.pa_prefill_chunk(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                 block_tables.shape[1], _p(cu_q_lens), _p(context_lens),
+                                 context_lens.shape[0], tq, int(max_q_len), int(max_context_len),
+                                 hq, hkv, d, bs, nb, float(scale), _dtype_code(k_cache),
+                                 ctypes.c_void_p(_stream(stream))))
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+
+
+def _i64p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class Allocator:
+    """Owner of one ``pa_allocator`` handle (host memory only)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        import numpy as np
+        self._np = np
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            self._free_order = np.ascontiguousarray(free_order, dtype=np.int32)
+            fo = _i32p(self._free_order)
+        _check(_lib.pa_allocator_create(self.num_blocks, self.block_size, fo, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pa_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def create(self, seq_id: int):
+        _check(_lib.pa_seq_create(self._h, seq_id))
+
+    def fork(self, parent: int, child: int):
+        _check(_lib.pa_seq_fork(self._h, parent, child))
+
+    def append(self, seq_id: int, n_tokens: int):
+        """Returns (slots int64 [n], cow_pairs int32 [k][2])."""
+        np = self._np
+        slots = np.zeros(max(n_tokens, 1), dtype=np.int64)
+        pairs = np.zeros((1, 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pa_seq_append(self._h, seq_id, n_tokens, _i64p(slots), _i32p(pairs), 1,
+                                  ctypes.byref(ncow)))
+        return slots[:n_tokens], pairs[:ncow.value]
+
+    def batch_append(self, seq_ids, n_tokens, slots_out=None, pairs_out=None):
+        """Append n_tokens[i] to seq_ids[i] for all i at once (all or nothing).
+        Returns (slots, cow_pairs)."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        total = int(nt.sum())
+        slots = slots_out if slots_out is not None else np.zeros(max(total, 1), dtype=np.int64)
+        cap = len(ids)
+        pairs = pairs_out if pairs_out is not None else np.zeros((max(cap, 1), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pa_batch_append(self._h, len(ids), _i64p(ids), _i32p(nt), _i64p(slots),
+                                    _i32p(pairs), pairs.shape[0], ctypes.byref(ncow)))
+        return slots[:total], pairs[:ncow.value]
+
+    def batch_tables(self, seq_ids, stride: int, pad_value: int = 0, tables_out=None,
+                     lens_out=None):
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = tables_out if tables_out is not None else np.zeros((len(ids), stride), np.int32)
+        lens = lens_out if lens_out is not None else np.zeros(len(ids), np.int32)
+        _check(_lib.pa_batch_tables(self._h, len(ids), _i64p(ids), _i32p(tables), stride,
+                                    pad_value, _i32p(lens)))
+        return tables, lens
+
+    def free(self, seq_id: int):
+        _check(_lib.pa_seq_free(self._h, seq_id))
+
+    def length(self, seq_id: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_seq_length(self._h, seq_id, ctypes.byref(n)))
+        return n.value
+
+    def block_table(self, seq_id: int):
+        np = self._np
+        n = ctypes.c_int32(0)
+        cap = self.length(seq_id) // self.block_size + 2
+        out = np.zeros(cap, dtype=np.int32)
+        _check(_lib.pa_seq_block_table(self._h, seq_id, _i32p(out), cap, ctypes.byref(n)))
+        return out[:n.value]
+
+    def stats(self) -> dict:
+        st = AllocatorStats()
+        _check(_lib.pa_allocator_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in AllocatorStats._fields_}
+
+    def refcount(self, block: int) -> int:
+        r = ctypes.c_int32(0)
+        _check(_lib.pa_block_refcount(self._h, block, ctypes.byref(r)))
+        return r.value

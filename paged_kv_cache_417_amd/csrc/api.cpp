@@ -1,0 +1,237 @@
+// api.cpp — C-ABI device entry points: argument validation, then launch.
+//
+// Every check runs before anything is enqueued, so a non-OK status means the
+// stream is untouched.  Shapes and layouts are documented in pa.h.
+#include <cinttypes>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+bool supported_block_size(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+bool valid_dtype(pa_dtype t) { return t == PA_DTYPE_F32 || t == PA_DTYPE_BF16; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMaxGroup = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Common checks of the cache geometry.
+pa_status check_geometry(const char *fn, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks) {
+    if (num_kv_heads <= 0 || num_blocks <= 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: num_kv_heads=%d num_blocks=%d", fn, num_kv_heads,
+                        num_blocks);
+    if (!supported_head_dim(head_dim))
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, head_dim);
+    if (!supported_block_size(block_size))
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32, 64, 128)", fn,
+                        block_size);
+    return PA_OK;
+}
+
+// Partition size in tokens: a multiple of 32 (the decode step) and of the
+// block size.  Start at 512 and halve while the grid would leave the 256
+// compute units short of work (about 8 waves each).
+int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                          int32_t max_context_len) {
+    const int32_t unit = block_size > 32 ? block_size : 32;
+    int32_t ps = 512;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    while (ps / 2 >= unit && (ps / 2) % unit == 0 &&
+           pairs * ceil_div(max_context_len > 0 ? max_context_len : 1, ps) < 2048)
+        ps /= 2;
+    return ps;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                         const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         void *stream) {
+    const char *fn = "pa_cache_write";
+    if (num_tokens < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_tokens %d", fn, num_tokens);
+    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
+    if (!k_cache || !v_cache || (num_tokens > 0 && (!k_new || !v_new || !slot_mapping)))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    int rc = pa::launch_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
+                                    num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, pa_dtype dtype, void *stream) {
+    const char *fn = "pa_copy_blocks";
+    if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_pairs %d", fn, num_pairs);
+    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
+    if (!k_cache || !v_cache || (num_pairs > 0 && !src_dst))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src_dst, 4))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    int rc = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, num_kv_heads, head_dim,
+                                    block_size, num_blocks, dtype, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                    int32_t max_context_len) {
+    return default_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_context_len < 0 || partition_size < 0)
+        return (size_t)-1;
+    const int32_t ps = partition_size ? partition_size
+                                      : default_partition(num_seqs, num_kv_heads, block_size,
+                                                          max_context_len);
+    const int64_t np_max = ceil_div(max_context_len > 0 ? max_context_len : 1, ps);
+    return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_max);
+}
+
+pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t block_table_stride,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    float scale, int32_t max_context_len, int32_t partition_size, void *workspace,
+                    size_t workspace_bytes, pa_dtype dtype, void *stream) {
+    const char *fn = "pa_decode";
+    if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
+    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
+    if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %d not a multiple of num_kv_heads %d",
+                        fn, num_q_heads, num_kv_heads);
+    if (num_q_heads / num_kv_heads > kMaxGroup)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: group size %d > %d", fn,
+                        num_q_heads / num_kv_heads, kMaxGroup);
+    if (block_table_stride <= 0 || max_context_len < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: block_table_stride %d max_context_len %d", fn,
+                        block_table_stride, max_context_len);
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale not finite", fn);
+    if (partition_size < 0 ||
+        (partition_size > 0 && (partition_size % 32 != 0 || partition_size % block_size != 0)))
+        return pa::fail(PA_ERR_INVALID_ARG,
+                        "%s: partition_size %d must be 0 or a multiple of 32 and of block_size %d",
+                        fn, partition_size, block_size);
+    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    const int32_t ps = partition_size ? partition_size
+                                      : default_partition(num_seqs, num_kv_heads, block_size,
+                                                          max_context_len);
+    const int64_t np_max = ceil_div(max_context_len > 0 ? max_context_len : 1, ps);
+    if (np_max > 65535 * 1024LL)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many partitions", fn);
+    const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_max);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: workspace %zu bytes, need %zu", fn,
+                        workspace ? workspace_bytes : (size_t)0, need);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: num_seqs/num_kv_heads above 65535", fn);
+    if (num_seqs == 0) return pa::ok();
+
+    pa::DecodeParams p{};
+    p.out = out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.table_stride = block_table_stride;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.num_blocks = num_blocks;
+    p.max_context_len = max_context_len;
+    p.partition_size = ps;
+    p.np_max = (int32_t)np_max;
+    p.scale_log2 = scale * kLog2e;
+    if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_max, &p.ws_ml,
+                                             &p.ws_o);
+    int rc = dtype == PA_DTYPE_BF16 ? pa::launch_decode_mfma(p, stream)
+                                    : pa::launch_decode_valu(p, dtype, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    rc = pa::launch_decode_reduce(p, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: reduce launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
+pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, int32_t block_table_stride,
+                           const int32_t *cu_q_lens, const int32_t *context_lens, int32_t num_reqs,
+                           int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale, pa_dtype dtype,
+                           void *stream) {
+    const char *fn = "pa_prefill_chunk";
+    if (num_reqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (dtype != PA_DTYPE_BF16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
+    if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %d not a multiple of num_kv_heads %d",
+                        fn, num_q_heads, num_kv_heads);
+    if (num_q_heads / num_kv_heads > kMaxGroup)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: group size %d > %d", fn,
+                        num_q_heads / num_kv_heads, kMaxGroup);
+    if (block_table_stride <= 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: block_table_stride %d", fn, block_table_stride);
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARG, "%s: scale not finite", fn);
+    if (num_reqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !cu_q_lens ||
+                         !context_lens))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(cu_q_lens, 4) || !aligned(context_lens, 4))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (num_reqs > 65535 || num_kv_heads > 65535)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: num_reqs/num_kv_heads above 65535", fn);
+    if (num_reqs == 0 || total_q_tokens == 0 || max_q_len == 0) return pa::ok();
+    pa::PrefillParams p{};
+    p.out = out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.cu_q_lens = cu_q_lens;
+    p.context_lens = context_lens;
+    p.table_stride = block_table_stride;
+    p.num_reqs = num_reqs;
+    p.total_q_tokens = total_q_tokens;
+    p.max_q_len = max_q_len;
+    p.max_context_len = max_context_len;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size = block_size;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = scale * kLog2e;
+    int rc = pa::launch_prefill(p, stream);
+    if (rc == -1) return pa::fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", fn);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
+}  // extern "C"

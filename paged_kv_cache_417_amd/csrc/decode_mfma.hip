@@ -1,0 +1,291 @@
+// decode_mfma.hip — paged decode attention for bf16 KV on the gfx950 matrix
+// cores, one wave per (sequence, kv head, partition).
+//
+// Sources (page title, section):
+//   [VE] 《加速 LLM 推理：深入了解 vLLM 引擎》 §3.1 — the kernel finds every
+//        physical block of a sequence through its block table and reads K/V
+//        from those scattered blocks; §3.3 — scaling, softmax and weighted sum
+//        fused in one kernel, access pattern built for memory bandwidth.
+//   [VF] 《大模型推理：vLLM大模型推理框架（附下载）》 §1.1 — segments of one
+//        sequence can be processed independently (split-K partitions).
+//
+// Work split.  The wave walks its partition in steps of 32 tokens.  All G
+// query heads of the kv head ride in the 16 columns of one MFMA tile, so K
+// and V are read once per group; for MHA only column 0 is live.  The tile is
+// wasteful in flops (G/16 of it is used) but decode moves one byte per flop
+// or so: the bound is HBM, and the matrix core removes the per-token
+// cross-lane dot-product reductions the vector ALU would need.
+//
+// Per step (lane = 16*g + n, g in 0..3, n in 0..15):
+//   S = K q^T : two v_mfma_f32_16x16x32_bf16 chains (tiles a and b), A = K
+//       rows, B = q columns.  Tile a's A row n is token 8*(n/4) + n%4, tile
+//       b's is that + 4, so afterwards lane (g, n) holds the scores of tokens
+//       8g .. 8g+7 of head n -- exactly the B operand layout PV needs.  Head
+//       dims are assigned to MFMA k-slots as d = 64*(ks/2) + 16*g + 8*(ks%2)
+//       + i for A and B alike, so each lane reads 32 contiguous bytes per
+//       64-dim slab.
+//   online softmax : running max shared by the four lanes of a head (two
+//       butterfly exchanges), per-lane running sum; exp2 with log2(e) folded
+//       into the scale.
+//   O += P V : A = V^T rows (dimension-major V layout gives 8 consecutive
+//       tokens per lane in one 16-byte load), B = P.  P is fed as a bf16 hi
+//       part plus a bf16 remainder (two MFMAs), which keeps P's error near
+//       2^-16 instead of bf16's 2^-9.
+// Tokens at or past the context length are excluded by selecting -inf
+// scores and zero V elements (NaN-poisoned rows cannot leak), and their
+// addresses are clamped onto the last valid token so no unallocated block is
+// touched.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+template <int D>
+struct StepRegs {
+    u32x4 ka[D / 32];  // K rows for tile a, one 16-byte k-slot per MFMA k-step
+    u32x4 kb[D / 32];
+    u32x4 vt[D / 16];  // V^T rows d = 16*j + n, 8 tokens each
+};
+
+// Element offset of k-step ks's 8 dims for lane group g.
+__device__ __forceinline__ int kslot_dim(int ks, int g) {
+    return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+}
+
+template <int D, int BS, bool TAIL>
+__device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__restrict__ kc,
+                                          const uint16_t *__restrict__ vc, int32_t t0, int32_t L,
+                                          int32_t bidA, int32_t bidB, int32_t hkv, int32_t kvh,
+                                          int lane) {
+    const int n = lane & 15, g = lane >> 4;
+    int ta = t0 + 8 * (n >> 2) + (n & 3);
+    int tb = ta + 4;
+    int tv = t0 + 8 * g;
+    if (TAIL) {
+        ta = min(ta, L - 1);
+        tb = min(tb, L - 1);
+        tv = min(tv, (L - 1) & ~7);
+    }
+    // Within a 32-token step the tokens span one block (BS >= 32) or two
+    // consecutive ones (BS == 16): the second holds step tokens 16..31.
+    const int32_t ba = (BS == 16 && ta - t0 >= 16) ? bidB : bidA;
+    const int32_t bb = (BS == 16 && tb - t0 >= 16) ? bidB : bidA;
+    const int32_t bv = (BS == 16 && tv - t0 >= 16) ? bidB : bidA;
+    const uint16_t *ka = kc + (((int64_t)ba * hkv + kvh) * BS + (ta % BS)) * D;
+    const uint16_t *kb = kc + (((int64_t)bb * hkv + kvh) * BS + (tb % BS)) * D;
+    const uint16_t *vp = vc + (((int64_t)bv * hkv + kvh) * D + n) * BS + (tv % BS);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        r.ka[ks] = ld16(ka + kslot_dim(ks, g));
+        r.kb[ks] = ld16(kb + kslot_dim(ks, g));
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) r.vt[j] = ld16(vp + (int64_t)j * 16 * BS);
+}
+
+template <int D, bool TAIL>
+__device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 *qb, int32_t t0,
+                                             int32_t L, float scale_log2, float &m, float &l,
+                                             floatx4 *acc, int lane) {
+    const int g = lane >> 4;
+    floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.ka[ks]), qb[ks], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.kb[ks]), qb[ks], sb, 0, 0, 0);
+    }
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[i] = sa[i] * scale_log2;
+        z[4 + i] = sb[i] * scale_log2;
+    }
+    const int tbase = t0 + 8 * g;
+    if (TAIL) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (tbase + i >= L) z[i] = kNegInf;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = fmaxf(mx, xor_shuffle(mx, 16));
+    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float f = exp2f(m - m_new);
+    float p[8], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = exp2f(z[i] - m_new);
+        sum += p[i];
+    }
+    l = l * f + sum;
+    m = m_new;
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 hi = (__bf16)p[i];
+        ph[i] = hi;
+        pl[i] = (__bf16)(p[i] - (float)hi);
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        acc[j] *= f;
+        u32x4 v = r.vt[j];
+        if (TAIL) {
+            // zero the bf16 elements of tokens >= L (pairs packed per dword)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int t = tbase + 2 * w;
+                uint32_t keep = (t < L ? 0x0000ffffu : 0u) | (t + 1 < L ? 0xffff0000u : 0u);
+                v[w] &= keep;
+            }
+        }
+        const bf16x8 vb = as_bf16x8(v);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, ph, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pl, acc[j], 0, 0, 0);
+    }
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
+    const int part = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g = lane >> 4;
+
+    const int32_t L = p.context_lens[s];
+    const int32_t nb = (L + BS - 1) / BS;
+    const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
+    const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
+    if (part >= np) return;
+
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int h = kvh * G + n;  // this lane's query head (live when n < G)
+    const bool live = n < G;
+    float *out_row = p.out + ((int64_t)s * p.num_q_heads + h) * D;
+
+    if (bad_len) {
+        if (live) {
+            const floatx4 nan4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                  __builtin_nanf("")};
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j)
+                *reinterpret_cast<floatx4 *>(out_row + 16 * j + 4 * g) = nan4;
+        }
+        return;
+    }
+
+    // q as the B operand: column n = head, k-slot dims per kslot_dim().
+    bf16x8 qb[D / 32];
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
+                           ((int64_t)s * p.num_q_heads + (live ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        u32x4 v = ld16(qrow + kslot_dim(ks, g));
+        if (!live) v = u32x4{0u, 0u, 0u, 0u};
+        qb[ks] = as_bf16x8(v);
+    }
+
+    const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
+    const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+    const int32_t *table = p.block_tables + (int64_t)s * p.table_stride;
+    const int32_t t_begin = part * p.partition_size;
+    const int32_t t_end = min(L, t_begin + p.partition_size);
+    const int32_t nsteps = (t_end - t_begin + 31) / 32;
+    const bool has_tail = ((t_end - t_begin) & 31) != 0;
+    const int32_t nfull = has_tail ? nsteps - 1 : nsteps;
+
+    float m = kNegInf, lsum = 0.f;
+    floatx4 acc[D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    bool bad_block = false;
+    auto block_ids = [&](int32_t t0, int32_t &bidA, int32_t &bidB) {
+        const int32_t ja = min(t0 / BS, nb - 1);
+        const int32_t jb = min((t0 + 16) / BS, nb - 1);
+        bidA = table[ja];
+        bidB = table[jb];
+        if ((uint32_t)bidA >= (uint32_t)p.num_blocks) { bad_block = true; bidA = 0; }
+        if ((uint32_t)bidB >= (uint32_t)p.num_blocks) { bad_block = true; bidB = 0; }
+    };
+
+    if (nfull > 0) {
+        StepRegs<D> cur, nxt;
+        int32_t bA, bB;
+        block_ids(t_begin, bA, bB);
+        load_step<D, BS, false>(cur, kc, vc, t_begin, L, bA, bB, p.num_kv_heads, kvh, lane);
+        for (int32_t i = 0; i < nfull; ++i) {
+            const int32_t t0 = t_begin + 32 * i;
+            if (i + 1 < nfull) {
+                block_ids(t0 + 32, bA, bB);
+                load_step<D, BS, false>(nxt, kc, vc, t0 + 32, L, bA, bB, p.num_kv_heads, kvh,
+                                        lane);
+            }
+            compute_step<D, false>(cur, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+            cur = nxt;
+        }
+    }
+    if (has_tail) {
+        StepRegs<D> r;
+        int32_t bA, bB;
+        const int32_t t0 = t_begin + 32 * nfull;
+        block_ids(t0, bA, bB);
+        load_step<D, BS, true>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
+        compute_step<D, true>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+    }
+
+    lsum += xor_shuffle(lsum, 16);
+    lsum += xor_shuffle(lsum, 32);
+    if (!live) return;
+    const float qnan = __builtin_nanf("");
+    if (np == 1) {
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            floatx4 o = acc[j] * inv;
+            if (bad_block) o = floatx4{qnan, qnan, qnan, qnan};
+            *reinterpret_cast<floatx4 *>(out_row + 16 * j + 4 * g) = o;
+        }
+    } else {
+        const int64_t slot = ((int64_t)s * p.num_q_heads + h) * p.np_max + part;
+        float *o_part = p.ws_o + slot * D;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            floatx4 o = acc[j];
+            if (bad_block) o = floatx4{qnan, qnan, qnan, qnan};
+            *reinterpret_cast<floatx4 *>(o_part + 16 * j + 4 * g) = o;
+        }
+        if (g == 0) {
+            p.ws_ml[2 * slot] = bad_block ? qnan : m;
+            p.ws_ml[2 * slot + 1] = bad_block ? qnan : lsum;
+        }
+    }
+}
+
+template <int D, int BS>
+void launch_one(const DecodeParams &p, hipStream_t s) {
+    dim3 grid(p.np_max, p.num_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS>), grid, dim3(64), 0, s, p);
+}
+
+}  // namespace
+
+int launch_decode_mfma(const DecodeParams &p, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.num_seqs == 0) return 0;
+#define PA_CASE(Dv, BSv)                                        \
+    if (p.head_dim == Dv && p.block_size == BSv) {              \
+        launch_one<Dv, BSv>(p, s);                              \
+        return (int)hipGetLastError();                          \
+    }
+    PA_CASE(128, 16) PA_CASE(128, 32) PA_CASE(128, 64) PA_CASE(128, 128)
+    PA_CASE(64, 16) PA_CASE(64, 32) PA_CASE(64, 64) PA_CASE(64, 128)
+#undef PA_CASE
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,50 @@
+// device_common.h — vector types and small device helpers for gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load/store through a vector type (one dwordx4 per lane).
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Wave64 butterfly exchange (ds_bpermute under the hood for cross-row masks).
+__device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// DPP moves within a 16-lane row.  Controls: quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of N adjacent lanes (N in 2, 4, 8, 16); every lane of the
+// group ends with the group total.  Pairing: xor 1, xor 2 inside a quad,
+// then mirrors, which pair each lane with a lane of the other half.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group size");
+    v += dpp<0xB1>(v);
+    if constexpr (N >= 4) v += dpp<0x4E>(v);
+    if constexpr (N >= 8) v += dpp<0x141>(v);
+    if constexpr (N >= 16) v += dpp<0x140>(v);
+    return v;
+}
+
+constexpr float kNegInf = -__builtin_inff();
+
+}  // namespace pa

@@ -1,0 +1,82 @@
+// launch.h — internal launchers behind the C ABI (host side, no HIP types).
+//
+// Each launcher enqueues its kernel(s) on `stream` and returns the
+// hipError_t of the launch as an int (0 = success).  Arguments have already
+// been validated by the C-ABI layer.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+struct DecodeParams {
+    float *out;
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    float *ws_ml;      // [S][Hq][np_max][2] (running max in log2 units, sum)
+    float *ws_o;       // [S][Hq][np_max][D] unnormalised partial outputs
+    int32_t table_stride;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t max_context_len;
+    int32_t partition_size;
+    int32_t np_max;    // ceil(max_context_len / partition_size), >= 1
+    float scale_log2;  // scale * log2(e)
+};
+
+struct PrefillParams {
+    float *out;
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *cu_q_lens;
+    const int32_t *context_lens;
+    int32_t table_stride;
+    int32_t num_reqs;
+    int32_t total_q_tokens;
+    int32_t max_q_len;
+    int32_t max_context_len;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t num_blocks;
+    float scale_log2;
+};
+
+// Workspace layout shared by the decode kernels and the split-K reduce.
+size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                              int64_t np_max);
+void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int64_t np_max,
+                            float **ml, float **o);
+
+int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                       void *stream);
+
+int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, pa_dtype dtype, void *stream);
+
+// bf16 decode on the matrix cores (any group size up to 16).
+int launch_decode_mfma(const DecodeParams &p, void *stream);
+// Vector-ALU decode (fp32 or bf16, any group size up to 16).
+int launch_decode_valu(const DecodeParams &p, pa_dtype dtype, void *stream);
+// Merge split-K partials; a no-op for sequences with one partition.
+int launch_decode_reduce(const DecodeParams &p, void *stream);
+
+int launch_prefill(const PrefillParams &p, void *stream);
+
+}  // namespace pa

@@ -1,0 +1,16 @@
+// pa_internal.h — shared helpers of libpa's host code (not part of the ABI).
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+// Record a message for pa_last_error() on this thread and return `st`.
+pa_status fail(pa_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear this thread's message and return PA_OK.
+pa_status ok();
+
+}  // namespace pa

@@ -1,0 +1,154 @@
+"""The C++ host allocator (behind the C ABI) against the Python reference
+model: identical slots, tables, refcounts, copy-on-write pairs and failures
+on randomised operation sequences, plus all-or-nothing failure checks."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_417_amd as pa
+from oracle.allocator_model import AllocatorModel, OutOfBlocks
+
+
+def same_state(a: pa.Allocator, m: AllocatorModel):
+    assert a.stats() == m.stats()
+    for b in range(m.num_blocks):
+        assert a.refcount(b) == m.refcount[b]
+    for sid, table in m.tables.items():
+        assert list(a.block_table(sid)) == table
+        assert a.length(sid) == m.lengths[sid]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_operations_match_model(seed):
+    rng = np.random.default_rng(seed)
+    nb, bs = int(rng.choice([8, 32, 64])), int(rng.choice([1, 4, 16]))
+    order = rng.permutation(nb)
+    a = pa.Allocator(nb, bs, free_order=order)
+    m = AllocatorModel(nb, bs, free_order=order)
+    live, next_id = [], 100
+    for step in range(600):
+        op = int(rng.integers(5))
+        if op == 0 or not live:
+            a.create(next_id)
+            m.create(next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op in (1, 2):
+            sid = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 3 * bs + 2))
+            try:
+                ms, mp = m.append(sid, n)
+                model_oom = False
+            except OutOfBlocks:
+                model_oom = True
+            if model_oom:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append(sid, n)
+            else:
+                s, p = a.append(sid, n)
+                assert list(s) == ms
+                assert [tuple(x) for x in p] == mp
+        elif op == 3:
+            parent = live[int(rng.integers(len(live)))]
+            a.fork(parent, next_id)
+            m.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        else:
+            sid = live.pop(int(rng.integers(len(live))))
+            a.free(sid)
+            m.free(sid)
+        if step % 50 == 0:
+            same_state(a, m)
+    same_state(a, m)
+
+
+def test_batch_append_equals_sequential_appends():
+    rng = np.random.default_rng(3)
+    order = rng.permutation(256)
+    a = pa.Allocator(256, 4, free_order=order)
+    m = AllocatorModel(256, 4, free_order=order)
+    for sid in range(6):
+        a.create(sid)
+        m.create(sid)
+    a.append(0, 6)
+    m.append(0, 6)
+    for child in (1, 2):  # 0, 1, 2 share a half-full block
+        a.fork(0, child + 10)
+        m.fork(0, child + 10)
+    ids = [0, 11, 12, 3, 4]
+    ns = [1, 1, 1, 5, 0]
+    slots, pairs = a.batch_append(ids, ns)
+    want_s, want_p = [], []
+    for sid, n in zip(ids, ns):
+        s, p = m.append(sid, n)
+        want_s += s
+        want_p += p
+    assert list(slots) == want_s
+    assert [tuple(x) for x in pairs] == want_p
+    # the last of the three sharers wrote in place: two copies, not three
+    assert len(want_p) == 2
+    tables, lens = a.batch_tables([0, 11, 12, 3], stride=4, pad_value=-7)
+    for row, sid in zip(tables, [0, 11, 12, 3]):
+        t = m.tables[sid]
+        assert list(row[:len(t)]) == t and (row[len(t):] == -7).all()
+    assert list(lens) == [m.lengths[s] for s in (0, 11, 12, 3)]
+
+
+def test_out_of_blocks_leaves_state_unchanged():
+    a = pa.Allocator(5, 4)
+    a.create(1)
+    a.create(2)
+    a.append(1, 9)  # 3 blocks
+    before = (a.stats(), list(a.block_table(1)), [a.refcount(b) for b in range(5)])
+    with pytest.raises(pa.OutOfBlocks):
+        a.append(1, 12)  # needs 3 more, 2 free
+    with pytest.raises(pa.OutOfBlocks):
+        a.batch_append([1, 2], [4, 8])  # 1 + 2 blocks > 2 free
+    assert (a.stats(), list(a.block_table(1)), [a.refcount(b) for b in range(5)]) == before
+    assert a.length(1) == 9 and a.length(2) == 0
+
+
+def test_errors():
+    a = pa.Allocator(8, 4)
+    with pytest.raises(pa.PAError) as e:
+        a.append(42, 1)
+    assert e.value.status == pa.PA_ERR_NOT_FOUND
+    with pytest.raises(pa.PAError) as e:
+        a.free(42)
+    assert e.value.status == pa.PA_ERR_NOT_FOUND
+    a.create(1)
+    with pytest.raises(pa.PAError) as e:
+        a.create(1)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    with pytest.raises(pa.PAError):
+        a.fork(1, 1)
+    with pytest.raises(pa.PAError):
+        a.batch_append([1, 1], [1, 1])  # repeated id
+    with pytest.raises(pa.PAError):
+        pa.Allocator(4, 4, free_order=[0, 1, 1, 2])
+    with pytest.raises(pa.PAError):
+        a.refcount(8)
+    # cow_cap too small: nothing changes
+    a.append(1, 2)
+    a.fork(1, 2)
+    lib = pa.lib()
+    import ctypes
+    slots = np.zeros(1, np.int64)
+    n = ctypes.c_int32(0)
+    st = lib.pa_seq_append(a._h, 2, 1, slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                           None, 0, ctypes.byref(n))
+    assert st == pa.PA_ERR_INVALID_ARG and a.length(2) == 2 and a.refcount(a.block_table(1)[0]) == 2
+
+
+def test_tiny_batch_blocks_and_append():
+    """The tiny fp32 batch: lengths {17, 64, 100, 200} take {2, 4, 7, 13}
+    blocks; one appended token each moves that to {2, 5, 7, 13} = 27."""
+    order = np.random.default_rng(0x418).permutation(64)
+    a = pa.Allocator(64, 16, free_order=order)
+    for s, L in enumerate([17, 64, 100, 200]):
+        a.create(s)
+        a.append(s, L)
+    assert [len(a.block_table(s)) for s in range(4)] == [2, 4, 7, 13]
+    a.batch_append([0, 1, 2, 3], [1, 1, 1, 1])
+    assert [len(a.block_table(s)) for s in range(4)] == [2, 5, 7, 13]
+    assert a.stats()["num_used"] == 27
