@@ -19,6 +19,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kMaxGroup = 16;
 constexpr float kLog2e = 1.4426950408889634f;
+// Decode workgroups per launch: a 1-D grid of 64-lane workgroups must stay
+// below 2^32 threads.
+constexpr int64_t kMaxDecodeItems = (1LL << 26) - 1;
 
 // Common checks of the cache geometry.
 pa_status check_geometry(const char *fn, int32_t num_kv_heads, int32_t head_dim,
@@ -140,14 +143,14 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                                       : default_partition(num_seqs, num_kv_heads, block_size,
                                                           max_context_len);
     const int64_t np_max = ceil_div(max_context_len > 0 ? max_context_len : 1, ps);
-    if (np_max > 65535 * 1024LL)
-        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many partitions", fn);
     const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_max);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: workspace %zu bytes, need %zu", fn,
                         workspace ? workspace_bytes : (size_t)0, need);
-    if (num_seqs > 65535 || num_kv_heads > 65535)
-        return pa::fail(PA_ERR_UNSUPPORTED, "%s: num_seqs/num_kv_heads above 65535", fn);
+    if (np_max * num_kv_heads * (int64_t)num_seqs > kMaxDecodeItems)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions x kv heads x sequences > %lld",
+                        fn, (long long)(np_max * num_kv_heads * (int64_t)num_seqs),
+                        (long long)kMaxDecodeItems);
     if (num_seqs == 0) return pa::ok();
 
     pa::DecodeParams p{};

@@ -150,9 +150,10 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
 
 template <int D, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
+    const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
+    const int part = item.part;
+    const int kvh = item.kvh;
+    const int s = item.seq;
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;
 
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
 
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
-    dim3 grid(p.np_max, p.num_kv_heads, p.num_seqs);
+    const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
     hipLaunchKernelGGL((decode_mfma_kernel<D, BS>), grid, dim3(64), 0, s, p);
 }
 

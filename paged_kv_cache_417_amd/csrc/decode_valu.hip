@@ -52,9 +52,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     constexpr int QD = D / 4;            // dims per lane in q.k
     constexpr int DPL = D / 64;          // dims per lane in P V
     const int BS = p.block_size;
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
+    const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
+    const int part = item.part;
+    const int kvh = item.kvh;
+    const int s = item.seq;
     const int lane = threadIdx.x;
     const int r = lane >> 2, c = lane & 3;
 
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 int launch_decode_valu(const DecodeParams &p, pa_dtype dtype, void *stream) {
     if (p.num_seqs == 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    dim3 grid(p.np_max, p.num_kv_heads, p.num_seqs);
+    const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
     if (dtype == PA_DTYPE_F32) {
         if (p.head_dim == 64)
             hipLaunchKernelGGL((decode_valu_kernel<uint32_t, 64>), grid, dim3(64), 0, s, p);

@@ -47,4 +47,20 @@ __device__ __forceinline__ float group_sum(float v) {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Work item of one decode workgroup.  The grid is 1-D over
+// kv_head (fastest) x sequence x partition (slowest).  Consecutive
+// workgroups go to the eight XCDs in turn, so with the kv head fastest each
+// XCD receives the same share of heads of every sequence and partition --
+// equal work per XCD whatever the length mix -- and the first partitions of
+// all sequences are dispatched before the later, partly empty ones.
+struct DecodeItem {
+    int kvh, seq, part;
+};
+__device__ __forceinline__ DecodeItem decode_item(int num_kv_heads, int num_seqs) {
+    const uint32_t i = blockIdx.x;
+    const uint32_t rest = i / (uint32_t)num_kv_heads;
+    return DecodeItem{(int)(i - rest * (uint32_t)num_kv_heads),
+                      (int)(rest % (uint32_t)num_seqs), (int)(rest / (uint32_t)num_seqs)};
+}
+
 }  // namespace pa
