@@ -209,8 +209,6 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(cu_q_lens, 4) || !aligned(context_lens, 4))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-    if (num_reqs > 65535 || num_kv_heads > 65535)
-        return pa::fail(PA_ERR_UNSUPPORTED, "%s: num_reqs/num_kv_heads above 65535", fn);
     if (num_reqs == 0 || total_q_tokens == 0 || max_q_len == 0) return pa::ok();
     pa::PrefillParams p{};
     p.out = out;

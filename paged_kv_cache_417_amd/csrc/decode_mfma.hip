@@ -48,11 +48,6 @@ struct StepRegs {
     u32x4 vt[D / 16];  // V^T rows d = 16*j + n, 8 tokens each
 };
 
-// Element offset of k-step ks's 8 dims for lane group g.
-__device__ __forceinline__ int kslot_dim(int ks, int g) {
-    return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
-}
-
 template <int D, int BS, bool TAIL>
 __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__restrict__ kc,
                                           const uint16_t *__restrict__ vc, int32_t t0, int32_t L,

@@ -47,6 +47,15 @@ __device__ __forceinline__ float group_sum(float v) {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// MFMA k-slot -> head-dim map shared by the A and B operands of a
+// v_mfma_f32_16x16x32_bf16 contraction over head dims: k-step ks, lane group
+// g (= lane / 16) covers the 8 dims starting at the returned offset, so each
+// lane reads 32 contiguous bytes per 64-dim slab.  Any map works as long as
+// both operands use the same one.
+__device__ __forceinline__ int kslot_dim(int ks, int g) {
+    return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+}
+
 // Work item of one decode workgroup.  The grid is 1-D over
 // kv_head (fastest) x sequence x partition (slowest).  Consecutive
 // workgroups go to the eight XCDs in turn, so with the kv head fastest each

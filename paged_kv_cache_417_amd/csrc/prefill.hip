@@ -1,9 +1,336 @@
-// prefill.hip — chunked causal prefill over paged K/V (placeholder: no kernel yet).
+// prefill.hip — chunked causal prefill over paged K/V on the gfx950 matrix
+// cores (bf16 in, fp32 accumulate, fp32 out).
+//
+// Sources (page title, section):
+//   [VI] 《vLLM大模型推理引擎：高效解决显存碎片与请求排队难题》 §1 — one
+//        iteration carries requests in different phases (prompt chunks beside
+//        decode rows).
+//   [VE] 《加速 LLM 推理：深入了解 vLLM 引擎》 §3.1 — K/V found through the
+//        block table in scattered blocks; §3.3 — scaling, softmax, weighted
+//        sum fused, matrix products on the matrix units.
+//
+// Work split.  One workgroup of four waves per (request, kv head, chunk of
+// query positions).  The workgroup serves 128 (position, head) pairs: all G
+// query heads of the kv head for 128 / G consecutive positions, so each K/V
+// tile is fetched from HBM once for the whole group.  Pair c of wave w is
+// w * 32 + c; head = pair % G, position = pair / G.  Each wave holds its 32
+// pairs as the 16 columns of two MFMA tiles.
+//
+// Per 32-key step:
+//   staging : the workgroup copies K [32 keys][D] and V^T [D][32 keys] of the
+//       step from the paged pools into LDS (double-buffered; the next step's
+//       global loads are in flight while the current step computes).  K rows
+//       are stored in MFMA row order and both tiles are padded by 16 bytes
+//       per row so the 16 lanes of a read phase hit distinct LDS banks.
+//   S^T = K Q^T : v_mfma_f32_16x16x32_bf16, A = K rows (tile a: keys
+//       8*(n/4) + n%4, tile b: those + 4), B = the wave's q columns; lane
+//       (g, n) ends with the scores of keys 8g .. 8g+7 of column n.
+//   causal mask + online softmax : keys past a column's position get -inf
+//       (a select, so no value of a masked key reaches the result); the
+//       running max is shared by the four lanes of a column.
+//   O^T += V^T P^T : A = V^T rows from LDS, B = P as a bf16 high part plus a
+//       bf16 remainder (two MFMAs), keeping P's error near 2^-16.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pa {
+namespace {
 
-int launch_prefill(const PrefillParams &, void *) { return -1; }
+constexpr int kWaves = 4;
+constexpr int kPairs = kWaves * 32;  // (position, head) pairs per workgroup
+constexpr int kTile = 32;            // keys per step
+
+template <int D>
+struct PrefillSmem {
+    uint16_t k[2][kTile][D + 8];   // K rows in MFMA row order, 16 B pad per row
+    uint16_t v[2][D][kTile + 8];   // V^T: one row of 32 keys per dim, 16 B pad
+};
+
+// LDS row of key kk (0..31) of a step: tile a's row n is key 8*(n/4) + n%4,
+// tile b's row n (stored at 16 + n) is that key + 4.
+__device__ __forceinline__ int k_row(int kk) {
+    return ((kk >> 2) & 1) * 16 + 4 * (kk >> 3) + (kk & 3);
+}
+
+template <int D, int BS>
+struct Stage {
+    static constexpr int kPasses = D / 64;  // 16-byte loads per thread for K (and for V)
+    u32x4 k[kPasses];
+    u32x4 v[kPasses];
+};
+
+// Global -> registers for keys t0 .. t0+31.  Keys at or past nkeys are not
+// read (their table entries may not exist): K gets zeros, V gets zeros, so
+// a masked key contributes exactly nothing.
+template <int D, int BS>
+__device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p,
+                                           const int32_t *__restrict__ table, int kvh,
+                                           int32_t t0, int32_t nkeys, int tid, bool &bad) {
+    const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
+    const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
+        const int idx = ps * 256 + tid;
+        // K: D/8 chunks of 16 bytes per key
+        {
+            const int kk = idx / (D / 8), ch = idx % (D / 8);
+            const int32_t t = t0 + kk;
+            u32x4 val = zero;
+            if (t < nkeys) {
+                int32_t blk = table[t / BS];
+                if ((uint32_t)blk >= (uint32_t)p.num_blocks) {
+                    bad = true;
+                    blk = 0;
+                }
+                val = ld16(kc + (((int64_t)blk * p.num_kv_heads + kvh) * BS + t % BS) * D + ch * 8);
+            }
+            st.k[ps] = val;
+        }
+        // V^T: 4 chunks of 8 keys per dim
+        {
+            const int dim = idx >> 2, ch = idx & 3;
+            const int32_t t = t0 + 8 * ch;
+            u32x4 val = zero;
+            if (t < nkeys) {
+                int32_t blk = table[t / BS];
+                if ((uint32_t)blk >= (uint32_t)p.num_blocks) {
+                    bad = true;
+                    blk = 0;
+                }
+                val = ld16(vc + (((int64_t)blk * p.num_kv_heads + kvh) * D + dim) * BS + t % BS);
+                if (t + 8 > nkeys) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
+                                              (t + 2 * w + 1 < nkeys ? 0xffff0000u : 0u);
+                        val[w] &= keep;
+                    }
+                }
+            }
+            st.v[ps] = val;
+        }
+    }
+}
+
+template <int D, int BS>
+__device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, const Stage<D, BS> &st,
+                                            int tid) {
+#pragma unroll
+    for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
+        const int idx = ps * 256 + tid;
+        const int kk = idx / (D / 8), ch = idx % (D / 8);
+        *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = st.k[ps];
+        const int dim = idx >> 2, chv = idx & 3;
+        *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = st.v[ps];
+    }
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+    __shared__ PrefillSmem<D> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int ppw = kPairs / G;  // positions per workgroup
+
+    // workgroup -> (kv head fastest, request, chunk slowest): each XCD gets
+    // an equal share of kv heads.
+    const uint32_t item = blockIdx.x;
+    const uint32_t rest = item / (uint32_t)p.num_kv_heads;
+    const int kvh = (int)(item - rest * (uint32_t)p.num_kv_heads);
+    const int r = (int)(rest % (uint32_t)p.num_reqs);
+    const int chunk = (int)(rest / (uint32_t)p.num_reqs);
+
+    const int32_t q0 = p.cu_q_lens[r], q1 = p.cu_q_lens[r + 1];
+    if (q0 < 0 || q1 < q0 || q1 > p.total_q_tokens) return;  // no row can be named safely
+    const int32_t qlen = q1 - q0;
+    const int32_t ctx = p.context_lens[r];
+    const int32_t i_begin = chunk * ppw;
+    if (i_begin >= qlen) return;
+
+    const bool bad_req = qlen > ctx || qlen > p.max_q_len || ctx > p.max_context_len ||
+                         (int64_t)(ctx + BS - 1) / BS > p.table_stride;
+    if (bad_req) {
+        // NaN for every row this workgroup would own (grid-stride over chunks
+        // in case qlen exceeds the bound the grid was sized for).
+        const int nchunks = (p.max_q_len + ppw - 1) / ppw;
+        const float qnan = __builtin_nanf("");
+        for (int32_t rb = i_begin; rb < qlen; rb += nchunks * ppw) {
+            const int32_t re = min(qlen, rb + ppw);
+            const int64_t elems = (int64_t)(re - rb) * G * D;
+            for (int64_t e = tid; e < elems; e += 256) {
+                const int32_t row = rb + (int32_t)(e / (G * D));
+                const int hg = (int)((e / D) % G), d = (int)(e % D);
+                p.out[((int64_t)(q0 + row) * p.num_q_heads + kvh * G + hg) * D + d] = qnan;
+            }
+        }
+        return;
+    }
+
+    const int32_t i_end = min(qlen, i_begin + ppw);
+    const int32_t base_pos = ctx - qlen;   // absolute position of row 0 of the chunk
+    const int32_t nkeys = base_pos + i_end;  // keys 0 .. nkeys-1 are visible to some row
+
+    // This lane's two columns.
+    int32_t pos[2];
+    int64_t qoff[2];
+    bf16x8 qb[2][D / 32];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int pair = w * 32 + ct * 16 + n;
+        const int hg = pair % G;
+        const int32_t ii = i_begin + pair / G;
+        const bool valid = pair < ppw * G && ii < i_end;
+        pos[ct] = valid ? base_pos + ii : -1;
+        qoff[ct] = ((int64_t)(q0 + (valid ? ii : 0)) * p.num_q_heads + kvh * G + hg) * D;
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + qoff[ct];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            u32x4 v = ld16(qrow + kslot_dim(ks, g));
+            if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+            qb[ct][ks] = as_bf16x8(v);
+        }
+    }
+    // Largest position among this wave's valid columns (-1: none).
+    int32_t wave_maxpos = -1;
+    {
+        const int first = w * 32, last = min(w * 32 + 31, ppw * G - 1);
+        if (first <= last && i_begin + first / G < i_end)
+            wave_maxpos = base_pos + min(i_begin + last / G, i_end - 1);
+    }
+
+    const int32_t *table = p.block_tables + (int64_t)r * p.table_stride;
+    float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+    floatx4 acc[2][D / 16];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    bool bad = false;
+    Stage<D, BS> st;
+    stage_load<D, BS>(st, p, table, kvh, 0, nkeys, tid, bad);
+    stage_store<D, BS>(sm, 0, st, tid);
+    __syncthreads();
+
+    const int32_t ntiles = (nkeys + kTile - 1) / kTile;
+    for (int32_t it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        const int32_t t0 = it * kTile;
+        const bool more = it + 1 < ntiles;
+        if (more) stage_load<D, BS>(st, p, table, kvh, t0 + kTile, nkeys, tid, bad);
+
+        if (wave_maxpos >= t0) {
+            u32x4 ka[D / 32], kb[D / 32];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                ka[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][n][kslot_dim(ks, g)]);
+                kb[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 + n][kslot_dim(ks, g)]);
+            }
+            bf16x8 ph[2], pl[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qb[ct][ks], sa,
+                                                                 0, 0, 0);
+                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qb[ct][ks], sb,
+                                                                 0, 0, 0);
+                }
+                float z[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    z[i] = sa[i] * p.scale_log2;
+                    z[4 + i] = sb[i] * p.scale_log2;
+                }
+                const int32_t tb = t0 + 8 * g;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (tb + i > pos[ct]) z[i] = kNegInf;
+                float mx = z[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+                mx = fmaxf(mx, xor_shuffle(mx, 16));
+                mx = fmaxf(mx, xor_shuffle(mx, 32));
+                const float m_new = fmaxf(m[ct], mx);
+                // A column with no visible key yet keeps m = -inf; subtract 0
+                // then so every weight is exp2(-inf) = 0 rather than NaN.
+                const float msub = m_new == kNegInf ? 0.f : m_new;
+                const float f = exp2f(m[ct] - msub);
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float pv = exp2f(z[i] - msub);
+                    sum += pv;
+                    const __bf16 hi = (__bf16)pv;
+                    ph[ct][i] = hi;
+                    pl[ct][i] = (__bf16)(pv - (float)hi);
+                }
+                l[ct] = l[ct] * f + sum;
+                m[ct] = m_new;
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
+            }
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) {
+                const bf16x8 vv =
+                    as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.v[buf][16 * j + n][8 * g]));
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, ph[ct], acc[ct][j], 0,
+                                                                         0, 0);
+                    acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pl[ct], acc[ct][j], 0,
+                                                                         0, 0);
+                }
+            }
+        }
+        if (more) stage_store<D, BS>(sm, buf ^ 1, st, tid);
+        __syncthreads();
+    }
+
+    const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        float lt = l[ct];
+        lt += xor_shuffle(lt, 16);
+        lt += xor_shuffle(lt, 32);
+        if (pos[ct] < 0) continue;
+        const float inv = 1.f / lt;
+        float *orow = p.out + qoff[ct];
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            floatx4 o = acc[ct][j] * inv;
+            if (any_bad) o = floatx4{qnan, qnan, qnan, qnan};
+            *reinterpret_cast<floatx4 *>(orow + 16 * j + 4 * g) = o;
+        }
+    }
+}
+
+template <int D, int BS>
+int launch_one(const PrefillParams &p, hipStream_t s) {
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int ppw = kPairs / G;
+    const int64_t nchunks = (p.max_q_len + ppw - 1) / ppw;
+    const int64_t wgs = nchunks * p.num_reqs * p.num_kv_heads;
+    if (wgs > (1LL << 24) - 1) return -1;
+    hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillParams &p, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+#define PA_CASE(Dv, BSv) \
+    if (p.head_dim == Dv && p.block_size == BSv) return launch_one<Dv, BSv>(p, s);
+    PA_CASE(128, 16) PA_CASE(128, 32) PA_CASE(128, 64) PA_CASE(128, 128)
+    PA_CASE(64, 16) PA_CASE(64, 32) PA_CASE(64, 64) PA_CASE(64, 128)
+#undef PA_CASE
+    return -1;
+}
 
 }  // namespace pa

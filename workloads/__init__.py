@@ -249,3 +249,46 @@ class PrefillShape:
 
 
 MIXED_PREFILL = PrefillShape()
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    shape: PrefillShape
+    context_lens: np.ndarray  # [R] cached + new tokens
+    q_lens: np.ndarray  # [R] new tokens (query rows) per request
+    cu_q_lens: np.ndarray  # [R+1]
+    perm: np.ndarray
+    tables: np.ndarray
+    q: torch.Tensor  # [sum q_lens][Hq][D]
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_axes: str
+    v_axes: str
+
+
+def make_prefill_case(shape: PrefillShape, device, k_axes="bhrd", v_axes="bhrd",
+                      context_lens=None, q_lens=None, num_blocks: int | None = None,
+                      seed: int | None = None) -> PrefillCase:
+    """Prefill chunks whose K/V (cached part and the chunk itself) already sit
+    in the pools.  Default: ``num_reqs`` requests of ``new_tokens`` rows over
+    ``cached_tokens`` cached ones."""
+    seed = shape.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if q_lens is None:
+        q_lens = np.full(shape.num_reqs, shape.new_tokens, dtype=np.int32)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    if context_lens is None:
+        context_lens = q_lens + shape.cached_tokens
+    context_lens = np.asarray(context_lens, dtype=np.int32)
+    assert (q_lens <= context_lens).all()
+    need = sum(blocks_needed(c, shape.block_size) for c in context_lens)
+    nb = need + 2 if num_blocks is None else num_blocks
+    perm, tables = assign_blocks(context_lens, shape.block_size, nb, rng)
+    gen = make_generator(seed, device)
+    k_pool, v_pool = empty_pools(nb, shape.num_kv_heads, shape.block_size, shape.head_dim,
+                                 shape.torch_dtype, device, k_axes, v_axes)
+    fill_used_blocks(k_pool, v_pool, tables, context_lens, shape.block_size, gen, k_axes, v_axes)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = randn((int(cu[-1]), shape.num_q_heads, shape.head_dim), shape.torch_dtype, gen, device)
+    return PrefillCase(shape, context_lens, q_lens, cu, perm, tables, q, k_pool, v_pool, k_axes,
+                       v_axes)
