@@ -1,27 +1,37 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the paged-KV attention path on one MI355X.
 
-One step = one decode iteration of the whole batch through the C ABI:
-  host allocator appends one token per sequence (slots, on-demand blocks) ->
-  block tables / lengths / slots copied to the device ->
-  pa_cache_write of the new tokens' K/V -> pa_decode (partition + split-K
-  reduce kernels).
-Workload (7B-shaped batch): 64 sequences with context lengths uniform in
-[128, 4096], 32 query heads = 32 kv heads, head_dim 128, block_size 16,
-blocks shuffled across a 200,000-block pool, bf16 K/V, fp32 accumulation.
-Inputs are synthetic (seeded N(0,1)), resident in HBM before timing starts.
+Headline step (the 7B-shaped batch): 64 sequences with context lengths
+uniform in [128, 4096], 32 query heads = 32 kv heads, head_dim 128,
+block_size 16, blocks shuffled across a 200,000-block pool, bf16 K/V, fp32
+accumulation.  One step appends one token to every sequence: pa_cache_write
+of the new K/V rows into the slots the host allocator assigned, then
+pa_decode (partition kernel + split-K reduce) over the grown contexts.
+Inputs are synthetic (seeded N(0,1)) and resident in HBM: the allocator runs
+ahead of the timed region for every step, and its slots, block tables and
+lengths are uploaded before timing starts.  The allocator's own host cost and
+the rate with per-step host work and PCIe uploads in the loop are reported
+beside `value`, never as it.
 
-Prints one JSON line.  `value` = decoded tokens per second (sequences per
-step / step time).  `roofline` covers pa_decode (both of its kernels), timed
-with HIP events on the launch stream inside the timed region; `cpu_baseline`
-is the fp64 oracle on a bounded sample of the same batch.
+Prints one JSON line.  `value` = decoded tokens per second.  `roofline`
+covers pa_decode, timed with HIP events on its launch stream inside the
+timed region.  `rows` measures the other steps of the path on their own
+workloads (grouped-query decode, prefix-shared decode with copy-on-write,
+long-context split-K decode, chunked prefill, the mixed step, cache write,
+block copy, allocator).  `cpu_baseline` is the fp64 oracle on the same batch.
+
+Counter runs: `--calibrate` adds one plain block copy of known size (1 GiB
+read + 1 GiB written) after the timed loop; `--pmc-summary FETCH_DIR
+WRITE_DIR` turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) into
+the per-launch HBM traffic file the `traffic` field reads.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -31,8 +41,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode tokens/s and achieved KV HBM GB/s (% of MI355X peak), 1 GPU"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mha_7b_traffic.json")
-KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip")
+DECODE_KERNEL = "decode_mfma_kernel"
+KERNEL_SOURCES = ("decode_mfma.hip", "device_common.h", "launch.h")
+CALIB_PAIRS = 4096
 
 
 def log(*a):
@@ -47,16 +60,27 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes(lengths, hq, hkv, d, bs, e_kv=2, e_q=2):
-    """K/V bytes of valid tokens + q + fp32 output + block-table entries + lengths."""
+def decode_bytes(lengths, hq, hkv, d, bs, e_kv=2, e_q=2):
+    """Algorithmic bytes of one decode call: K and V of every valid token,
+    q, the fp32 output, the block-table entries read and the lengths."""
     kv = sum(int(L) for L in lengths) * hkv * d * 2 * e_kv
     s = len(lengths)
     tables = sum(-(-int(L) // bs) for L in lengths) * 4
     return kv + s * hq * d * e_q + s * hq * d * 4 + tables + s * 4
 
 
-def measured_traffic(src_hash: str, n_launch_bytes: float):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+def prefill_flops(ctx, qlens, hq, d):
+    """QK^T and PV flops of causal chunks: row i of a chunk sees ctx-qlen+i+1 keys."""
+    total = 0
+    for c, q in zip(ctx, qlens):
+        c, q = int(c), int(q)
+        keys = q * (c - q) + q * (q + 1) // 2
+        total += 4 * hq * d * keys
+    return total
+
+
+def measured_traffic(src_hash: str):
+    """HBM bytes per decode launch from the committed counter runs, if they
     were taken on this exact kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -68,20 +92,34 @@ def measured_traffic(src_hash: str, n_launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
+def events_time(torch, fn, reps, stream):
+    """Per-call milliseconds of fn() from HIP events on `stream`."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ts)
+    return ms[len(ms) // 2], ms
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline
+
+
 def cpu_baseline(case, budget_s: float):
     """The fp64 oracle, single-threaded, on whole sequences of the batch until
-    the time budget is spent (at least one)."""
-    import numpy as np
-    import torch
-
+    the time budget is spent or the batch is done."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from paged_helpers import gather_blocks, host_bits
 
     sh = case.shape
-    order = list(range(len(case.lengths)))
     done, elapsed, tokens = 0, 0.0, 0
-    for s in order:
+    for s in range(len(case.lengths)):
         k_sub, v_sub, t_sub, l_sub = gather_blocks(case.k_pool, case.v_pool, case.tables,
                                                    case.lengths, [s], sh.block_size)
         q_sub = host_bits(case.q[s:s + 1])
@@ -93,36 +131,23 @@ def cpu_baseline(case, budget_s: float):
         if elapsed >= budget_s:
             break
     return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(order)} sequences of the batch ({tokens} context tokens), "
-                      f"all {sh.num_q_heads} heads, fp64, one thread, {elapsed:.1f} s"}
+            "sample": f"{done} of {len(case.lengths)} sequences of the batch ({tokens} context "
+                      f"tokens), all {sh.num_q_heads} heads, fp64, one thread, {elapsed:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle time for the CPU baseline (0 = skip)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence or kv head with no exchange)", file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# headline: 7B-shaped decode step
 
-    import numpy as np
-    import torch
 
-    import paged_kv_cache_417_amd as pa
-    import workloads as wl
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
+def headline(args, pa, wl, torch, np):
     dev = "cuda"
     sh = wl.MHA_7B
     K, W = args.steps, args.warmup
+    nsteps = K + W
     log(f"bench: building {sh.name} batch (S={sh.num_seqs}, NB={sh.num_blocks})")
-    case = wl.make_decode_case(sh, dev, pa.K_AXES, pa.V_AXES, extra_table_slots=K + W + 1)
+    host_steps = min(K, 20)
+    case = wl.make_decode_case(sh, dev, pa.K_AXES, pa.V_AXES,
+                               extra_table_slots=nsteps + host_steps + 1)
     S = sh.num_seqs
     stride = case.tables.shape[1]
     pad = sh.num_blocks - 1
@@ -137,19 +162,89 @@ def main():
     t_chk, l_chk = alloc.batch_tables(ids, stride, pad)
     assert (t_chk == case.tables).all() and (l_chk == case.lengths).all()
 
+    # Every step's slots, tables and lengths, ahead of time (host cost timed).
+    ones = np.ones(S, dtype=np.int32)
+    h_slots = np.zeros((nsteps, S), dtype=np.int64)
+    h_tabs = np.zeros((nsteps, S, stride), dtype=np.int32)
+    h_lens = np.zeros((nsteps, S), dtype=np.int32)
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        alloc.batch_append(ids, ones, slots_out=h_slots[i])
+        alloc.batch_tables(ids, stride, pad, tables_out=h_tabs[i], lens_out=h_lens[i])
+    alloc_us = (time.perf_counter() - t0) * 1e6 / nsteps
+    d_slots = torch.as_tensor(h_slots, device=dev)
+    d_tabs = torch.as_tensor(h_tabs, device=dev)
+    d_lens = torch.as_tensor(h_lens, device=dev)
+
     gen = wl.make_generator(sh.seed + 1000, dev)
-    nsteps = K + W
     k_new = wl.randn((nsteps, S, sh.num_kv_heads, sh.head_dim), torch.bfloat16, gen, dev)
     v_new = wl.randn((nsteps, S, sh.num_kv_heads, sh.head_dim), torch.bfloat16, gen, dev)
     q_all = wl.randn((nsteps, S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
-    max_len = int(case.lengths.max()) + nsteps
+    max_len = int(h_lens.max())
     ps = args.partition_size
     ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
                              max_len, ps, dev)
     ps_used = ps or pa.pa_decode_default_partition(S, sh.num_kv_heads, sh.block_size, max_len)
+    stream = torch.cuda.current_stream()
+    dec_events = []
 
-    # double-buffered pinned host staging and device copies
+    def step(i, timed):
+        pa.pa_cache_write(k_new[i], v_new[i], case.k_pool, case.v_pool, d_slots[i])
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        pa.pa_decode(out, q_all[i], case.k_pool, case.v_pool, d_tabs[i], d_lens[i], sh.scale,
+                     max_len, ps, ws)
+        if timed:
+            e1.record(stream)
+            dec_events.append((e0, e1))
+
+    log(f"bench: warmup {W} steps, partition {ps_used}")
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"bench: timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(W, nsteps):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    dec_ms = [a.elapsed_time(b) for a, b in dec_events]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    bytes_avg = sum(decode_bytes(h_lens[i], sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
+                                 sh.block_size) for i in range(W, nsteps)) / K
+    achieved = bytes_avg / (dec_avg_ms * 1e-3) / 1e9
+    assert torch.isfinite(out).all()
+    log(f"bench: step {ms_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us "
+        f"(min {min(dec_ms) * 1e3:.1f}, max {max(dec_ms) * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s algorithmic, allocator {alloc_us:.1f} us/step on the host")
+
+    # The same step with the host allocator and PCIe uploads inside the loop
+    # (pinned staging, double-buffered); reported, never `value`.
+    host_max = max_len + host_steps
+    host_ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                                  host_max, ps, dev)
+    host_rate = host_inclusive_rate(pa, wl, torch, np, case, alloc, ids, stride, pad, k_new,
+                                    v_new, q_all, out, host_ws, ps, host_max, host_steps)
+
+    if args.calibrate:
+        calibrate_copy(pa, torch, np, case, alloc)
+
+    res = {
+        "S": S, "ms_step": ms_step, "dec_avg_ms": dec_avg_ms, "dec_ms": dec_ms,
+        "bytes_avg": bytes_avg, "achieved": achieved, "ps": ps_used,
+        "seq_len": float(h_lens[-1].mean()), "alloc_us": alloc_us, "host_rate": host_rate,
+    }
+    return case, res
+
+
+def host_inclusive_rate(pa, wl, torch, np, case, alloc, ids, stride, pad, k_new, v_new, q_all,
+                        out, ws, ps, max_len, steps):
+    sh = case.shape
+    S = len(ids)
+    dev = "cuda"
     h_slots = [torch.zeros(S, dtype=torch.int64).pin_memory() for _ in range(2)]
     h_tabs = [torch.zeros((S, stride), dtype=torch.int32).pin_memory() for _ in range(2)]
     h_lens = [torch.zeros(S, dtype=torch.int32).pin_memory() for _ in range(2)]
@@ -159,98 +254,405 @@ def main():
     copied = [None, None]
     ones = np.ones(S, dtype=np.int32)
     stream = torch.cuda.current_stream()
-    dec_events = []
-    step_lengths = []
-
-    def step(i, timed):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
         b = i % 2
         if copied[b] is not None:
-            copied[b].synchronize()  # staging buffer b free again
-        slots_np = h_slots[b].numpy()
-        alloc.batch_append(ids, ones, slots_out=slots_np)
-        tabs_np, lens_np = h_tabs[b].numpy(), h_lens[b].numpy()
-        alloc.batch_tables(ids, stride, pad, tables_out=tabs_np, lens_out=lens_np)
+            copied[b].synchronize()
+        alloc.batch_append(ids, ones, slots_out=h_slots[b].numpy())
+        alloc.batch_tables(ids, stride, pad, tables_out=h_tabs[b].numpy(),
+                           lens_out=h_lens[b].numpy())
         d_slots[b].copy_(h_slots[b], non_blocking=True)
         d_tabs[b].copy_(h_tabs[b], non_blocking=True)
         d_lens[b].copy_(h_lens[b], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(stream)
         copied[b] = ev
-        pa.pa_cache_write(k_new[i], v_new[i], case.k_pool, case.v_pool, d_slots[b])
-        if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        pa.pa_decode(out, q_all[i], case.k_pool, case.v_pool, d_tabs[b], d_lens[b], sh.scale,
+        j = i % k_new.shape[0]
+        pa.pa_cache_write(k_new[j], v_new[j], case.k_pool, case.v_pool, d_slots[b])
+        pa.pa_decode(out, q_all[j], case.k_pool, case.v_pool, d_tabs[b], d_lens[b], sh.scale,
                      max_len, ps, ws)
-        if timed:
-            e1.record(stream)
-            dec_events.append((e0, e1))
-            step_lengths.append(lens_np.copy())
-
-    log(f"bench: warmup {W} steps, partition {ps_used}")
-    for i in range(W):
-        step(i, False)
     torch.cuda.synchronize()
-    log(f"bench: timing {K} steps")
+    return S * steps / (time.perf_counter() - t0)
+
+
+def calibrate_copy(pa, torch, np, case, alloc):
+    """One pa_copy_blocks launch over CALIB_PAIRS blocks nobody uses: reads
+    and writes exactly CALIB_PAIRS * 2 * block_bytes each.  The counter runs
+    divide the decode kernel's counters by this kernel's to calibrate."""
+    st = alloc.stats()
+    free = case.perm[st["num_used"]:-1]  # never handed out (the last entry is the pad block)
+    assert len(free) >= 2 * CALIB_PAIRS
+    pairs = np.stack([free[:CALIB_PAIRS], free[CALIB_PAIRS:2 * CALIB_PAIRS]], axis=1)
+    d = torch.as_tensor(pairs.astype(np.int32), device="cuda")
+    torch.cuda.synchronize()
+    pa.pa_copy_blocks(case.k_pool, case.v_pool, d)
+    torch.cuda.synchronize()
+    log(f"bench: calibration copy of {CALIB_PAIRS} blocks done")
+
+
+# ---------------------------------------------------------------------------
+# the other rows of the path, each on its own workload
+
+
+def row_gqa(pa, wl, torch, np, reps):
+    sh = wl.GQA
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
+    r = decode_row(pa, torch, case, reps)
+    r["workload"] = ("gqa decode: 128 seqs, ctx round(lognormal(ln 1024, 1)) clipped "
+                     "[16, 8192], 32 q / 8 kv heads, head_dim 128, block 16, bf16")
+    return r
+
+
+def row_long(pa, wl, torch, np, reps):
+    sh = wl.MIXED_DECODE
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
+    r = decode_row(pa, torch, case, reps, ps=sh.partition_size)
+    r["workload"] = ("long-context split-K decode: 8 seqs x 32768 tokens, block 128, "
+                     "partitions of 512, 32 q / 8 kv heads, head_dim 128, bf16")
+    return r
+
+
+def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, logical_only=False):
+    sh = case.shape
+    dev = "cuda"
+    lens = case.lengths if lengths is None else lengths
+    tabs = case.tables if tables is None else tables
+    S = len(lens)
+    maxlen = int(max(lens))
+    t_dev = torch.as_tensor(tabs, device=dev)
+    l_dev = torch.as_tensor(lens, device=dev)
+    out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, ps, dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, ps,
+                     ws)
+
+    for _ in range(3):
+        call()
+    med, _ = events_time(torch, call, reps, stream)
+    b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size)
+    gbps = b / (med * 1e-3) / 1e9
+    return {"us": med * 1e3, "algorithmic_bytes": b, "GBps": gbps,
+            "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "tokens_per_s": S / (med * 1e-3),
+            "bound": "hbm"}
+
+
+def row_prefix_shared(pa, wl, torch, np, reps):
+    """16 prompts x 8 samples sharing the prompt's blocks; 112 copy-on-writes
+    of the partial shared block before the tails are written."""
+    sh = wl.PREFIX_SHARED
+    dev = "cuda"
+    plan = wl.prefix_plan()
+    rng = np.random.default_rng(sh.seed)
+    order = rng.permutation(sh.num_blocks)
+    alloc = pa.Allocator(sh.num_blocks, sh.block_size, free_order=order)
+    kshape, vshape = pa.kv_cache_shapes(sh.num_blocks, sh.num_kv_heads, sh.block_size,
+                                        sh.head_dim)
+    k_pool = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    gen = wl.make_generator(sh.seed, dev)
+    n_prompts, samples = plan.tail_lens.shape
+    pids = [1000 * i for i in range(n_prompts)]
+    for p in pids:
+        alloc.create(p)
+    slots, _ = alloc.batch_append(pids, plan.shared_lens)
+    shape = (len(slots), sh.num_kv_heads, sh.head_dim)
+    pa.pa_cache_write(wl.randn(shape, torch.bfloat16, gen, dev),
+                      wl.randn(shape, torch.bfloat16, gen, dev), k_pool, v_pool,
+                      torch.as_tensor(slots, device=dev))
+    ids = []
+    for p in pids:
+        ids.append(p)
+        for k in range(1, samples):
+            alloc.fork(p, p + k)
+            ids.append(p + k)
     t0 = time.perf_counter()
-    for i in range(W, W + K):
-        step(i, True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    dec_ms = [a.elapsed_time(b) for a, b in dec_events]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    bytes_avg = sum(algorithmic_bytes(L, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
-                                      sh.block_size) for L in step_lengths) / len(step_lengths)
-    achieved = bytes_avg / (dec_avg_ms * 1e-3) / 1e9
-    assert torch.isfinite(out).all()
-    log(f"bench: step {ms_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us "
-        f"(min {min(dec_ms) * 1e3:.1f}, max {max(dec_ms) * 1e3:.1f}), "
-        f"{achieved:.0f} GB/s algorithmic")
+    slots, pairs = alloc.batch_append(ids, plan.tail_lens.reshape(-1))
+    append_us = (time.perf_counter() - t0) * 1e6
+    d_pairs = torch.as_tensor(pairs, device=dev)
+    stream = torch.cuda.current_stream()
 
+    def copy():
+        pa.pa_copy_blocks(k_pool, v_pool, d_pairs)
+
+    copy_med, _ = events_time(torch, copy, reps, stream)  # idempotent: sources are unchanged
+    block_bytes = sh.num_kv_heads * sh.block_size * sh.head_dim * 2
+    copy_bytes = len(pairs) * 2 * block_bytes * 2  # K and V regions, read + write
+    shape = (len(slots), sh.num_kv_heads, sh.head_dim)
+    pa.pa_cache_write(wl.randn(shape, torch.bfloat16, gen, dev),
+                      wl.randn(shape, torch.bfloat16, gen, dev), k_pool, v_pool,
+                      torch.as_tensor(slots, device=dev))
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    q = wl.randn((len(ids), sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    case = wl.DecodeCase(sh, lens, order, tables, q, k_pool, v_pool, pa.K_AXES, pa.V_AXES)
+    r = decode_row(pa, torch, case, reps)
+    # unique bytes: each physical block's valid rows once
+    unique_tokens = 0
+    seen = set()
+    for s in range(len(ids)):
+        for j in range(wl.blocks_needed(int(lens[s]), sh.block_size)):
+            b = int(tables[s, j])
+            if b not in seen:
+                seen.add(b)
+                unique_tokens += min(sh.block_size, int(lens[s]) - j * sh.block_size)
+    kv_unique = unique_tokens * sh.num_kv_heads * sh.head_dim * 2 * 2
+    kv_logical = int(lens.sum()) * sh.num_kv_heads * sh.head_dim * 2 * 2
+    other = r["algorithmic_bytes"] - kv_logical
+    r["unique_bytes"] = kv_unique + other
+    r["GBps_unique"] = r["unique_bytes"] / (r["us"] * 1e-6) / 1e9
+    r["frac_unique_of_8TBps"] = r["GBps_unique"] / PEAK_HBM_GBPS
+    r["workload"] = ("prefix-shared decode: 16 prompts of 2048+j tokens x 8 samples sharing "
+                     "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16")
+    cow = {"us": copy_med * 1e3, "pairs": int(len(pairs)), "bytes_moved": copy_bytes,
+           "GBps": copy_bytes / (copy_med * 1e-3) / 1e9, "bound": "latency (256 KiB per pair)",
+           "host_append_us": append_us,
+           "workload": "copy-on-write of the 112 shared partial blocks (K+V, 32 heads)"}
+    return r, cow
+
+
+def row_mixed(pa, wl, torch, np, reps):
+    """Mixed step: 8 decode sequences at 32768 tokens and 4 prompt chunks of
+    512 new tokens over 4096 cached, one cache write for all 2056 new rows."""
+    dev = "cuda"
+    dsh, psh = wl.MIXED_DECODE, wl.MIXED_PREFILL
+    hkv, d, bs = dsh.num_kv_heads, dsh.head_dim, dsh.block_size
+    nb = dsh.num_blocks
+    rng = np.random.default_rng(dsh.seed)
+    alloc = pa.Allocator(nb, bs, free_order=rng.permutation(nb))
+    dec_ids, pre_ids = list(range(8)), list(range(100, 104))
+    for s in dec_ids + pre_ids:
+        alloc.create(s)
+    kshape, vshape = pa.kv_cache_shapes(nb, hkv, bs, d)
+    k_pool = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    gen = wl.make_generator(dsh.seed, dev)
+    slots, _ = alloc.batch_append(dec_ids + pre_ids, [32767] * 8 + [4096] * 4)
+    for lo in range(0, len(slots), 65536):
+        hi = min(len(slots), lo + 65536)
+        shape = (hi - lo, hkv, d)
+        pa.pa_cache_write(wl.randn(shape, torch.bfloat16, gen, dev),
+                          wl.randn(shape, torch.bfloat16, gen, dev), k_pool, v_pool,
+                          torch.as_tensor(slots[lo:hi], device=dev))
+    slots, _ = alloc.batch_append(dec_ids + pre_ids, [1] * 8 + [512] * 4)
+    d_slots = torch.as_tensor(slots, device=dev)
+    kn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    vn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    dt, dl = alloc.batch_tables(dec_ids, 257)
+    pt, pl = alloc.batch_tables(pre_ids, 40)
+    dt, dl, pt, pl = (torch.as_tensor(x, device=dev) for x in (dt, dl, pt, pl))
+    cu = torch.as_tensor(np.arange(0, 2049, 512, dtype=np.int32), device=dev)
+    qd = wl.randn((8, dsh.num_q_heads, d), torch.bfloat16, gen, dev)
+    qp = wl.randn((2048, psh.num_q_heads, d), torch.bfloat16, gen, dev)
+    out_d = torch.empty((8, dsh.num_q_heads, d), device=dev)
+    out_p = torch.empty((2048, psh.num_q_heads, d), device=dev)
+    ws = pa.decode_workspace(8, dsh.num_q_heads, hkv, d, bs, 32768, 512, dev)
+    stream = torch.cuda.current_stream()
+
+    def cw():
+        pa.pa_cache_write(kn, vn, k_pool, v_pool, d_slots)
+
+    def dec():
+        pa.pa_decode(out_d, qd, k_pool, v_pool, dt, dl, dsh.scale, 32768, 512, ws)
+
+    def pre():
+        pa.pa_prefill_chunk(out_p, qp, k_pool, v_pool, pt, cu, pl, psh.scale, 512, 4608)
+
+    def step():
+        cw()
+        dec()
+        pre()
+
+    for f in (cw, dec, pre, step):
+        f()
+    cw_med, _ = events_time(torch, cw, reps, stream)
+    pre_med, _ = events_time(torch, pre, reps, stream)
+    step_med, _ = events_time(torch, step, reps, stream)
+    flops = prefill_flops([4608] * 4, [512] * 4, psh.num_q_heads, d)
+    cw_bytes = len(slots) * hkv * d * 2 * 2 * 2  # K and V rows, read + write
+    prefill = {"us": pre_med * 1e3, "flops": flops,
+               "TFLOPs": flops / (pre_med * 1e-3) / 1e12,
+               "frac_of_2.5PF_bf16": flops / (pre_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "bound": "mfma",
+               "workload": "chunked prefill: 4 requests x 512 new tokens over 4096 cached "
+                           "(causal), 32 q / 8 kv heads, head_dim 128, block 128, bf16"}
+    cache_write = {"us": cw_med * 1e3, "tokens": len(slots), "bytes_moved": cw_bytes,
+                   "GBps": cw_bytes / (cw_med * 1e-3) / 1e9, "bound": "latency",
+                   "workload": "cache write of 8 decode + 2048 prompt-chunk tokens, 8 kv heads, "
+                               "head_dim 128, block 128, bf16"}
+    mixed = {"us": step_med * 1e3,
+             "workload": "cache write (2056 tokens) + decode 8 x 32768 (split-K 512) + "
+                         "prefill 4 x 512 over 4096, one stream"}
+    return prefill, cache_write, mixed
+
+
+# ---------------------------------------------------------------------------
+# counter summaries
+
+
+def _read_counters(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, kernel_substr):
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or kernel_substr not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def pmc_summary(fetch_dir, write_dir, block_bytes):
+    """Per-launch HBM bytes of the decode kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the same counter's reading for the
+    calibration copy (CALIB_PAIRS blocks of block_bytes per K and V region,
+    read once and written once)."""
+    expect = CALIB_PAIRS * 2 * block_bytes
+    out = {"kernel": DECODE_KERNEL, "kernel_source_sha256": kernel_source_hash(),
+           "calibration": f"pa_copy_blocks over {CALIB_PAIRS} blocks: {expect} B read, "
+                          f"{expect} B written"}
+    total = 0.0
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counters(d)
+        dec = _per_dispatch(rows, name, DECODE_KERNEL)
+        cal = _per_dispatch(rows, name, "copy_blocks_kernel")
+        cal = [c for c in cal if c * 1024 > expect / 4]  # the calibration launch, not COW copies
+        if not dec or not cal:
+            raise SystemExit(f"{name}: decode dispatches {len(dec)}, calibration {len(cal)}")
+        factor = expect / (sum(cal) / len(cal) * 1024)
+        per_launch = sum(dec) / len(dec) * 1024 * factor
+        out[name] = {"decode_kib_per_dispatch_raw": sum(dec) / len(dec),
+                     "calibration_kib_raw": sum(cal) / len(cal), "scale": factor,
+                     "decode_bytes_per_launch": per_launch, "dispatches": len(dec)}
+        total += per_launch
+    out["hbm_bytes_per_launch"] = total
+    return out
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--rows", type=int, default=1, help="1: also measure the other rows")
+    ap.add_argument("--reps", type=int, default=20, help="timed repetitions per row")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="add one block copy of known size for the counter runs")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        import workloads as wl
+        sh = wl.MHA_7B
+        block_bytes = sh.num_kv_heads * sh.block_size * sh.head_dim * 2
+        s = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], block_bytes)
+        print(json.dumps(s, indent=1))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path "
+              "shards by sequence or kv head with no exchange, and this build runs on one GPU",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_417_amd as pa
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    case, h = headline(args, pa, wl, torch, np)
+    K, W = args.steps, args.warmup
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(src_hash, bytes_avg)
     result = {
         "metric": METRIC,
-        "value": S / (ms_step * 1e-3),
+        "value": h["S"] / (h["ms_step"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": ms_step,
+        "ms_per_step": h["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) K/V/q, lengths uniform [128, 4096])",
         "config": {
-            "workload": "mha_7b decode step: 64 seqs, ctx U[128,4096] (+1 per step), 32 q / "
-                        "32 kv heads, head_dim 128, block 16, 200000-block pool, bf16 KV, "
-                        "fp32 accumulate",
-            "global_batch": S,
-            "seq_len": int(np.mean(step_lengths[-1])),
-            "partition_size": ps_used,
+            "workload": "7B-shaped decode step: 64 seqs, ctx U[128,4096] (+1 per step), 32 q / "
+                        "32 kv heads, head_dim 128, block 16, 200000-block pool shuffled, bf16 "
+                        "KV, fp32 accumulate; cache write + decode per step",
+            "global_batch": h["S"],
+            "seq_len": h["seq_len"],
+            "partition_size": h["ps"],
             "parallelism": "none (1 GPU)",
         },
-        "kv_gbps": achieved,
-        "hbm_frac": achieved / PEAK_HBM_GBPS,
-        "decode_us": dec_avg_ms * 1e3,
+        "kv_gbps": h["achieved"],
+        "hbm_frac": h["achieved"] / PEAK_HBM_GBPS,
+        "decode_us": h["dec_avg_ms"] * 1e3,
         "roofline": {
             "kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
             "bound": "hbm",
-            "achieved": achieved,
+            "achieved": h["achieved"],
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
-            "algorithmic_bytes": bytes_avg,
+            "frac": h["achieved"] / PEAK_HBM_GBPS,
+            "traffic": measured_traffic(src_hash),
+            "algorithmic_bytes": h["bytes_avg"],
         },
+        "host_allocator_us_per_step": h["alloc_us"],
+        "host_inclusive_tokens_per_s": h["host_rate"],
     }
     if args.cpu_budget > 0:
         log("bench: CPU baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
+    del case
+    torch.cuda.empty_cache()
+
+    if args.rows:
+        rows = {}
+        log("bench: row gqa")
+        rows["decode_gqa"] = row_gqa(pa, wl, torch, np, args.reps)
+        torch.cuda.empty_cache()
+        log("bench: row prefix-shared")
+        rows["decode_prefix_shared"], rows["copy_blocks_cow"] = row_prefix_shared(
+            pa, wl, torch, np, args.reps)
+        torch.cuda.empty_cache()
+        log("bench: row long-context split-K")
+        rows["decode_long_splitk"] = row_long(pa, wl, torch, np, args.reps)
+        torch.cuda.empty_cache()
+        log("bench: row mixed step")
+        rows["prefill_chunk"], rows["cache_write"], rows["mixed_step"] = row_mixed(
+            pa, wl, torch, np, args.reps)
+        rows["allocator"] = {"host_us_per_step": h["alloc_us"],
+                             "workload": "batch append of one token to 64 sequences + dense "
+                                         "tables [64][stride] (host, C ABI)"}
+        result["rows"] = rows
+        for k, v in rows.items():
+            log(f"bench: {k}: " + ", ".join(f"{a}={b:.4g}" if isinstance(b, float) else
+                                            f"{a}={b}" for a, b in v.items()
+                                            if a != "workload"))
     print(json.dumps(result), flush=True)
 
 

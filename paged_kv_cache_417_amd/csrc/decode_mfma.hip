@@ -192,46 +192,61 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
     const int32_t t_end = min(L, t_begin + p.partition_size);
     const int32_t nsteps = (t_end - t_begin + 31) / 32;
     const bool has_tail = ((t_end - t_begin) & 31) != 0;
-    const int32_t nfull = has_tail ? nsteps - 1 : nsteps;
 
     float m = kNegInf, lsum = 0.f;
     floatx4 acc[D / 16];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // The partition's block-table slice lives in one VGPR (lane j holds the
+    // entry of logical block win + j); block ids are read with readlane, so
+    // no table load sits between a step's issue and the previous step's data.
+    const int32_t b_last = (t_end - 1) / BS;  // last logical block of the partition
+    int32_t win = t_begin / BS;
+    int32_t tbl = (nsteps > 0 && win + lane <= b_last) ? table[win + lane] : 0;
     bool bad_block = false;
-    auto block_ids = [&](int32_t t0, int32_t &bidA, int32_t &bidB) {
-        const int32_t ja = min(t0 / BS, nb - 1);
-        const int32_t jb = min((t0 + 16) / BS, nb - 1);
-        bidA = table[ja];
-        bidB = table[jb];
-        if ((uint32_t)bidA >= (uint32_t)p.num_blocks) { bad_block = true; bidA = 0; }
-        if ((uint32_t)bidB >= (uint32_t)p.num_blocks) { bad_block = true; bidB = 0; }
+    auto block_id = [&](int32_t j) -> int32_t {
+        if (j - win >= 64) {  // next 64 entries (partitions longer than 64 blocks)
+            win = j;
+            tbl = (win + lane <= b_last) ? table[win + lane] : 0;
+        }
+        int32_t b = __builtin_amdgcn_readlane(tbl, j - win);
+        if ((uint32_t)b >= (uint32_t)p.num_blocks) {
+            bad_block = true;
+            b = 0;
+        }
+        return b;
+    };
+    // Step s covers tokens t_begin + 32 s .. +31.  Loads clamp past the end
+    // of the context (a no-op except in the tail step), compute masks there.
+    auto issue = [&](StepRegs<D> &r, int32_t st) {
+        const int32_t t0 = t_begin + 32 * st;
+        const int32_t bA = block_id(t0 / BS);
+        const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, b_last)) : bA;
+        load_step<D, BS, true>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
+    };
+    auto consume = [&](const StepRegs<D> &r, int32_t st) {
+        const int32_t t0 = t_begin + 32 * st;
+        if (has_tail && st == nsteps - 1)
+            compute_step<D, true>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        else
+            compute_step<D, false>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
     };
 
-    if (nfull > 0) {
-        StepRegs<D> cur, nxt;
-        int32_t bA, bB;
-        block_ids(t_begin, bA, bB);
-        load_step<D, BS, false>(cur, kc, vc, t_begin, L, bA, bB, p.num_kv_heads, kvh, lane);
-        for (int32_t i = 0; i < nfull; ++i) {
-            const int32_t t0 = t_begin + 32 * i;
-            if (i + 1 < nfull) {
-                block_ids(t0 + 32, bA, bB);
-                load_step<D, BS, false>(nxt, kc, vc, t0 + 32, L, bA, bB, p.num_kv_heads, kvh,
-                                        lane);
-            }
-            compute_step<D, false>(cur, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
-            cur = nxt;
+    // Two register buffers in ping-pong: while one step is consumed the next
+    // one's loads are in flight.  No buffer is ever copied into the other, so
+    // the wait before a step's math covers that step's loads only.
+    if (nsteps > 0) {
+        StepRegs<D> ra, rb;
+        issue(ra, 0);
+        int32_t st = 0;
+        for (; st + 1 < nsteps; st += 2) {
+            issue(rb, st + 1);
+            consume(ra, st);
+            if (st + 2 < nsteps) issue(ra, st + 2);
+            consume(rb, st + 1);
         }
-    }
-    if (has_tail) {
-        StepRegs<D> r;
-        int32_t bA, bB;
-        const int32_t t0 = t_begin + 32 * nfull;
-        block_ids(t0, bA, bB);
-        load_step<D, BS, true>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
-        compute_step<D, true>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        if (st < nsteps) consume(ra, st);
     }
 
     lsum += xor_shuffle(lsum, 16);

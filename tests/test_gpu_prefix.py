@@ -1,0 +1,216 @@
+"""Prefix-shared parallel sampling on the GPU: 16 prompts, each forked into 8
+samples that share the prompt's blocks through refcounted block tables, then
+given private tails of 1..512 tokens.  The prompt's last block is partly
+filled and shared, so every sample but the last holder copies it first
+(copy-on-write through pa_copy_blocks) before its cache write.
+
+Checks: the copies and writes are bit-exact and leave the shared source
+intact; decode over shared tables is bit-identical to decode over private
+duplicates of the same content; sampled rows match the fp64 oracle within
+2e-3; forking exactly at a block boundary needs no copy.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from paged_helpers import host_bits, oracle_decode_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_417_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def build_shared_batch(pa, sh, plan, dev, pool_blocks):
+    """Run the allocator through prompts, forks and tails; write every token's
+    K/V.  Returns (alloc, ids, k_pool, v_pool, free_order, cow_pairs)."""
+    rng = np.random.default_rng(sh.seed)
+    order = rng.permutation(pool_blocks)
+    alloc = pa.Allocator(pool_blocks, sh.block_size, free_order=order)
+    hkv, d = sh.num_kv_heads, sh.head_dim
+    kshape, vshape = pa.kv_cache_shapes(pool_blocks, hkv, sh.block_size, d)
+    k_pool = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    gen = wl.make_generator(sh.seed, dev)
+    n_prompts, samples = plan.tail_lens.shape
+    prompt_ids = [1000 * i for i in range(n_prompts)]
+    for pid in prompt_ids:
+        alloc.create(pid)
+    slots, pairs = alloc.batch_append(prompt_ids, plan.shared_lens)
+    assert len(pairs) == 0
+    kn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    vn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    pa.pa_cache_write(kn, vn, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    ids = []
+    for pid in prompt_ids:
+        ids.append(pid)
+        for k in range(1, samples):
+            alloc.fork(pid, pid + k)
+            ids.append(pid + k)
+    tails = plan.tail_lens.reshape(-1)
+    slots, pairs = alloc.batch_append(ids, tails)
+    if len(pairs):
+        pa.pa_copy_blocks(k_pool, v_pool, torch.as_tensor(pairs, device=dev))
+    kn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    vn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    pa.pa_cache_write(kn, vn, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    torch.cuda.synchronize()
+    return alloc, ids, k_pool, v_pool, order, pairs
+
+
+def test_prefix_shared_sampling(pa):
+    sh = wl.PREFIX_SHARED
+    dev = "cuda"
+    plan = wl.prefix_plan()
+    say(f"case prefix-shared: {plan.tail_lens.shape} samples, shared {list(plan.shared_lens[:4])}..")
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    n_prompts, samples = plan.tail_lens.shape
+    # one copy per sample except the last holder of each prompt's partial block
+    assert len(pairs) == n_prompts * (samples - 1)
+    st = alloc.stats()
+    assert st["cow_copies"] == n_prompts * (samples - 1)
+    full_shared = sum(int(L) // sh.block_size for L in plan.shared_lens)
+    assert st["num_shared"] == full_shared
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    # every sample reads the same physical blocks for its full shared blocks
+    for i in range(n_prompts):
+        nfull = int(plan.shared_lens[i]) // sh.block_size
+        grp = tables[i * samples:(i + 1) * samples, :nfull]
+        assert (grp == grp[0]).all()
+    # copy sources hold the prompt's partial block unchanged: each copy's
+    # first rows equal its source's rows bit for bit
+    src = torch.as_tensor(pairs[:, 0].astype(np.int64), device=dev)
+    dst = torch.as_tensor(pairs[:, 1].astype(np.int64), device=dev)
+    for p, (s_b, d_b) in enumerate(pairs):
+        j = int(plan.shared_lens[p // (samples - 1)]) % sh.block_size
+        assert torch.equal(k_pool[d_b, :, :j].view(torch.int16), k_pool[s_b, :, :j].view(torch.int16))
+        assert torch.equal(v_pool[d_b, :, :, :j].view(torch.int16),
+                           v_pool[s_b, :, :, :j].view(torch.int16))
+    del src, dst
+
+    gen = wl.make_generator(sh.seed + 7, dev)
+    S = len(ids)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    maxlen = int(lens.max())
+    t_dev = torch.as_tensor(tables, device=dev)
+    l_dev = torch.as_tensor(lens, device=dev)
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, 0, dev)
+    out_shared = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
+    pa.pa_decode(out_shared, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, 0, ws)
+
+    # private duplicates: every table entry of every sequence gets its own
+    # fresh block holding a bit copy of the original
+    used = st["num_used"]
+    fresh = iter(order[used:].tolist())
+    dup_tables = np.full_like(tables, sh.num_blocks - 1)
+    copy_pairs = []
+    for s in range(S):
+        for j in range(wl.blocks_needed(int(lens[s]), sh.block_size)):
+            b = next(fresh)
+            dup_tables[s, j] = b
+            copy_pairs.append((int(tables[s, j]), b))
+    pa.pa_copy_blocks(k_pool, v_pool, torch.as_tensor(np.asarray(copy_pairs, np.int32), device=dev))
+    out_dup = torch.empty_like(out_shared)
+    pa.pa_decode(out_dup, q, k_pool, v_pool, torch.as_tensor(dup_tables, device=dev), l_dev,
+                 sh.scale, maxlen, 0, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_shared).all()
+    assert torch.equal(out_shared, out_dup)
+    say(f"  shared == duplicated bit for bit over {S} sequences, {len(copy_pairs)} blocks")
+
+    # oracle on sampled sequences: first and last sample of a few prompts,
+    # the longest and the shortest tail
+    rows = sorted({0, samples - 1, 5 * samples, 5 * samples + samples - 1, S - 1,
+                   int(np.argmax(lens)), int(np.argmin(lens))})
+    ref = oracle_decode_rows(q, k_pool, v_pool, tables, lens, rows, sh.block_size, sh.scale,
+                             pa.K_AXES, pa.V_AXES)
+    got = out_shared[torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+    err = float(np.abs(got - ref).max())
+    say(f"  rows {rows} max err {err:.3e}")
+    assert err <= TOL
+
+
+def test_fork_at_block_boundary_needs_no_copy(pa):
+    """Forking right after a 2048-token prompt (128 full blocks) leaves no
+    partial shared block: the samples' first appends take fresh blocks."""
+    sh = wl.PREFIX_SHARED
+    plan = wl.prefix_plan(num_prompts=2, samples=8, fork_offsets=False)
+    alloc = pa.Allocator(4096, sh.block_size)
+    for i in range(2):
+        alloc.create(i * 100)
+    alloc.batch_append([0, 100], plan.shared_lens)
+    ids = []
+    for pid in (0, 100):
+        ids.append(pid)
+        for k in range(1, 8):
+            alloc.fork(pid, pid + k)
+            ids.append(pid + k)
+    slots, pairs = alloc.batch_append(ids, plan.tail_lens.reshape(-1))
+    assert len(pairs) == 0
+    assert alloc.stats()["cow_copies"] == 0
+    assert alloc.stats()["num_shared"] == 2 * 128
+
+
+def test_cow_then_write_leaves_other_sharers_intact(pa):
+    """Small case with the whole pools on the host: after a fork, copy and
+    tail writes, every sequence un-pages (oracle) to its prompt followed by
+    its own tail, bit for bit."""
+    sh = wl.DecodeShape("cow_small", 4, 4, 2, 64, 16, 64, "bf16", 31)
+    dev = "cuda"
+    alloc = pa.Allocator(sh.num_blocks, sh.block_size,
+                         free_order=np.random.default_rng(3).permutation(sh.num_blocks))
+    kshape, vshape = pa.kv_cache_shapes(sh.num_blocks, 2, 16, 64)
+    k_pool = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    gen = wl.make_generator(5, dev)
+    alloc.create(0)
+    prompt_len = 37
+    slots, _ = alloc.append(0, prompt_len)
+    kp = wl.randn((prompt_len, 2, 64), torch.bfloat16, gen, dev)
+    vp = wl.randn((prompt_len, 2, 64), torch.bfloat16, gen, dev)
+    pa.pa_cache_write(kp, vp, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    for c in (1, 2, 3):
+        alloc.fork(0, c)
+    tails = {0: 5, 1: 20, 2: 1, 3: 11}
+    tail_k, tail_v = {}, {}
+    for s in (1, 2, 0, 3):  # the parent is not last: it copies too
+        slots, pairs = alloc.append(s, tails[s])
+        if len(pairs):
+            pa.pa_copy_blocks(k_pool, v_pool, torch.as_tensor(pairs, device=dev))
+        tail_k[s] = wl.randn((tails[s], 2, 64), torch.bfloat16, gen, dev)
+        tail_v[s] = wl.randn((tails[s], 2, 64), torch.bfloat16, gen, dev)
+        pa.pa_cache_write(tail_k[s], tail_v[s], k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    torch.cuda.synchronize()
+    assert alloc.stats()["cow_copies"] == 3
+    kh, vh = host_bits(k_pool), host_bits(v_pool)
+    for s in range(4):
+        table = alloc.block_table(s)
+        L = prompt_len + tails[s]
+        assert alloc.length(s) == L
+        for h in range(2):
+            k = oracle.unpage(kh, pa.K_AXES, table, L, h)
+            v = oracle.unpage(vh, pa.V_AXES, table, L, h)
+            want_k = np.concatenate([oracle.widen(host_bits(kp[:, h])),
+                                     oracle.widen(host_bits(tail_k[s][:, h]))])
+            want_v = np.concatenate([oracle.widen(host_bits(vp[:, h])),
+                                     oracle.widen(host_bits(tail_v[s][:, h]))])
+            assert (k == want_k).all() and (v == want_v).all()
