@@ -543,6 +543,50 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
     return out
 
 
+PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
+          "long-context split-K decode", "mixed step (cache write + decode + prefill)")
+
+
+def mark_phase(torch):
+    """A tiny spin kernel (a few hundred cycles) that separates the workloads
+    in a kernel trace; trace_summary() splits dispatches on it."""
+    torch.cuda._sleep(200)
+
+
+def trace_summary(d):
+    """Markdown table of a rocprofv3 --kernel-trace run: libpa kernels grouped
+    by workload (the spin-kernel markers), name and grid size; durations in us."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    groups = {}
+    phase = -1
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "spin_kernel" in name:
+            phase += 1
+            continue
+        if "pa::" not in name:
+            continue
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0].replace("pa::", "")
+        label = PHASES[phase] if 0 <= phase < len(PHASES) else "-"
+        key = (label, short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault(key, []).append(dur)
+    lines = ["| workload | kernel | workgroups | threads/wg | calls | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (ph, k, grid, wg), v in groups.items():
+        lines.append(f"| {ph} | {k} | {grid // wg} | {wg} | {len(v)} | {sum(v) / len(v):.1f} | "
+                     f"{min(v):.1f} | {max(v):.1f} |")
+    return "\n".join(lines)
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -560,7 +604,12 @@ def main():
                     help="add one block copy of known size for the counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print a per-kernel table of a rocprofv3 --kernel-trace run and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.pmc_summary:
         import workloads as wl
         sh = wl.MHA_7B
@@ -581,6 +630,7 @@ def main():
     import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mark_phase(torch)
     case, h = headline(args, pa, wl, torch, np)
     K, W = args.steps, args.warmup
     src_hash = kernel_source_hash()
@@ -633,16 +683,20 @@ def main():
     if args.rows:
         rows = {}
         log("bench: row gqa")
+        mark_phase(torch)
         rows["decode_gqa"] = row_gqa(pa, wl, torch, np, args.reps)
         torch.cuda.empty_cache()
         log("bench: row prefix-shared")
+        mark_phase(torch)
         rows["decode_prefix_shared"], rows["copy_blocks_cow"] = row_prefix_shared(
             pa, wl, torch, np, args.reps)
         torch.cuda.empty_cache()
         log("bench: row long-context split-K")
+        mark_phase(torch)
         rows["decode_long_splitk"] = row_long(pa, wl, torch, np, args.reps)
         torch.cuda.empty_cache()
         log("bench: row mixed step")
+        mark_phase(torch)
         rows["prefill_chunk"], rows["cache_write"], rows["mixed_step"] = row_mixed(
             pa, wl, torch, np, args.reps)
         rows["allocator"] = {"host_us_per_step": h["alloc_us"],

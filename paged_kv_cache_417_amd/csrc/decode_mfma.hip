@@ -72,11 +72,15 @@ __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__rest
     const uint16_t *vp = vc + (((int64_t)bv * hkv + kvh) * D + n) * BS + (tv % BS);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-        r.ka[ks] = ld16(ka + kslot_dim(ks, g));
-        r.kb[ks] = ld16(kb + kslot_dim(ks, g));
+        r.ka[ks] = ld16_nt(ka + kslot_dim(ks, g));
+        r.kb[ks] = ld16_nt(kb + kslot_dim(ks, g));
     }
+    // A step reads whole V^T rows of a block when BS <= 32; with larger
+    // blocks it reads 64 of each row's 2*BS bytes and the following steps
+    // read the rest of those cache lines, so the lines must stay cached.
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) r.vt[j] = ld16(vp + (int64_t)j * 16 * BS);
+    for (int j = 0; j < D / 16; ++j)
+        r.vt[j] = BS <= 32 ? ld16_nt(vp + (int64_t)j * 16 * BS) : ld16(vp + (int64_t)j * 16 * BS);
 }
 
 template <int D, bool TAIL>
@@ -143,8 +147,11 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
     }
 }
 
+// Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
+// in 256 registers without spills.
 template <int D, int BS>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
+    DecodeParams p) {
     const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
     const int part = item.part;
     const int kvh = item.kvh;

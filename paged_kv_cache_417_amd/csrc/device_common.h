@@ -14,6 +14,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 16-byte global load/store through a vector type (one dwordx4 per lane).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// 16-byte load marked nontemporal: the K/V stream of a decode call is read
+// once, and the hint keeps it from displacing cache lines that are reused.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
