@@ -109,8 +109,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
     float mx = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = fmaxf(mx, xor_shuffle(mx, 16));
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    mx = rows4_max(mx);
     const float m_new = fmaxf(m, mx);
     const float f = exp2f(m - m_new);
     float p[8], sum = 0.f;
@@ -256,8 +255,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         if (st < nsteps) consume(ra, st);
     }
 
-    lsum += xor_shuffle(lsum, 16);
-    lsum += xor_shuffle(lsum, 32);
+    lsum = rows4_sum(lsum);
     if (!live) return;
     const float qnan = __builtin_nanf("");
     if (np == 1) {

@@ -29,6 +29,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Wave64 butterfly exchange (ds_bpermute under the hood for cross-row masks).
 __device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float rows4_max(float v) {
+    v = fmaxf(v, xor_shuffle(v, 16));
+    return fmaxf(v, xor_shuffle(v, 32));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    v += xor_shuffle(v, 16);
+    return v + xor_shuffle(v, 32);
+}
+
 // DPP moves within a 16-lane row.  Controls: quad_perm [1,0,3,2] = 0xB1,
 // quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
 template <int CTRL>

@@ -39,6 +39,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kPairs = kWaves * 32;  // (position, head) pairs per workgroup
 constexpr int kTile = 32;            // keys per step
+constexpr float kRescaleMargin = 8.f;  // log2 units; weights stay below 2^8
 
 template <int D>
 struct PrefillSmem {
@@ -126,8 +127,11 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, const S
     }
 }
 
+// Two waves per SIMD (two workgroups per CU): one workgroup's MFMAs run
+// while the other waits at its barrier or on LDS.
 template <int D, int BS>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void prefill_kernel(
+    PrefillParams p) {
     __shared__ PrefillSmem<D> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -253,13 +257,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                 float mx = z[0];
 #pragma unroll
                 for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-                mx = fmaxf(mx, xor_shuffle(mx, 16));
-                mx = fmaxf(mx, xor_shuffle(mx, 32));
+                mx = rows4_max(mx);
+                // Lazy rescaling: the exponent base m[ct] moves only when the
+                // column's max grows by more than kRescaleMargin (log2
+                // units), so weights stay below 2^kRescaleMargin and the
+                // accumulators are rescaled on few steps.  The test is
+                // wave-uniform.
                 const float m_new = fmaxf(m[ct], mx);
+                if (__any(m_new > m[ct] + kRescaleMargin)) {
+                    const float f = m_new == kNegInf ? 1.f : exp2f(m[ct] - m_new);
+                    l[ct] *= f;
+#pragma unroll
+                    for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
+                    m[ct] = m_new;
+                }
                 // A column with no visible key yet keeps m = -inf; subtract 0
                 // then so every weight is exp2(-inf) = 0 rather than NaN.
-                const float msub = m_new == kNegInf ? 0.f : m_new;
-                const float f = exp2f(m[ct] - msub);
+                const float msub = m[ct] == kNegInf ? 0.f : m[ct];
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -269,10 +283,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                     ph[ct][i] = hi;
                     pl[ct][i] = (__bf16)(pv - (float)hi);
                 }
-                l[ct] = l[ct] * f + sum;
-                m[ct] = m_new;
-#pragma unroll
-                for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
+                l[ct] += sum;
             }
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) {
@@ -295,9 +306,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const float qnan = __builtin_nanf("");
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        float lt = l[ct];
-        lt += xor_shuffle(lt, 16);
-        lt += xor_shuffle(lt, 32);
+        const float lt = rows4_sum(l[ct]);
         if (pos[ct] < 0) continue;
         const float inv = 1.f / lt;
         float *orow = p.out + qoff[ct];
