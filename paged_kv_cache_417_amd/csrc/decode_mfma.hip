@@ -111,11 +111,11 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = rows4_max(mx);
     const float m_new = fmaxf(m, mx);
-    const float f = exp2f(m - m_new);
+    const float f = fast_exp2(m - m_new);
     float p[8], sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(z[i] - m_new);
+        p[i] = fast_exp2(z[i] - m_new);
         sum += p[i];
     }
     l = l * f + sum;

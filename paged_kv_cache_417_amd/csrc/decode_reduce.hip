@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     for (int32_t c0 = 0; c0 < np; c0 += kReduceChunk) {
         const int32_t cn = min(kReduceChunk, np - c0);
         for (int32_t i = tid; i < cn; i += kReduceThreads) {
-            const float w = exp2f(ml[2 * (c0 + i)] - M);
+            const float w = fast_exp2(ml[2 * (c0 + i)] - M);
             w_s[i] = w;
             lpart += w * ml[2 * (c0 + i) + 1];
         }

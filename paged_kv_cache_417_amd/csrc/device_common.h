@@ -62,6 +62,12 @@ __device__ __forceinline__ float group_sum(float v) {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// 2^x on the transcendental unit (v_exp_f32), without the library's
+// rescaling for subnormal results: those flush to zero.  Softmax weights
+// below 2^-126 of the running maximum change nothing.  2^0 = 1 and
+// 2^-inf = 0 exactly.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // MFMA k-slot -> head-dim map shared by the A and B operands of a
 // v_mfma_f32_16x16x32_bf16 contraction over head dims: k-step ks, lane group
 // g (= lane / 16) covers the 8 dims starting at the returned offset, so each

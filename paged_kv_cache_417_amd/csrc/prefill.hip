@@ -197,12 +197,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             qb[ct][ks] = as_bf16x8(v);
         }
     }
-    // Largest position among this wave's valid columns (-1: none).
-    int32_t wave_maxpos = -1;
+    // Largest and smallest position among this wave's valid columns
+    // (wave_maxpos = -1: none).  Keys up to wave_minpos are visible to every
+    // valid column, so steps that end there need no causal mask.
+    int32_t wave_maxpos = -1, wave_minpos = -1;
     {
         const int first = w * 32, last = min(w * 32 + 31, ppw * G - 1);
-        if (first <= last && i_begin + first / G < i_end)
+        if (first <= last && i_begin + first / G < i_end) {
             wave_maxpos = base_pos + min(i_begin + last / G, i_end - 1);
+            wave_minpos = base_pos + i_begin + first / G;
+        }
     }
 
     const int32_t *table = p.block_tables + (int64_t)r * p.table_stride;
@@ -250,10 +254,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                     z[i] = sa[i] * p.scale_log2;
                     z[4 + i] = sb[i] * p.scale_log2;
                 }
-                const int32_t tb = t0 + 8 * g;
+                if (t0 + kTile - 1 > wave_minpos) {  // the step crosses a column's position
+                    const int32_t tb = t0 + 8 * g;
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (tb + i > pos[ct]) z[i] = kNegInf;
+                    for (int i = 0; i < 8; ++i)
+                        if (tb + i > pos[ct]) z[i] = kNegInf;
+                }
                 float mx = z[0];
 #pragma unroll
                 for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 // wave-uniform.
                 const float m_new = fmaxf(m[ct], mx);
                 if (__any(m_new > m[ct] + kRescaleMargin)) {
-                    const float f = m_new == kNegInf ? 1.f : exp2f(m[ct] - m_new);
+                    const float f = m_new == kNegInf ? 1.f : fast_exp2(m[ct] - m_new);
                     l[ct] *= f;
 #pragma unroll
                     for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float pv = exp2f(z[i] - msub);
+                    const float pv = fast_exp2(z[i] - msub);
                     sum += pv;
                     const __bf16 hi = (__bf16)pv;
                     ph[ct][i] = hi;
