@@ -138,6 +138,30 @@ pa_status pa_decode(float *out, const void *q,
                     int32_t partition_size, void *workspace,
                     size_t workspace_bytes, pa_dtype dtype, void *stream);
 
+/* Flags of pa_decode_ex. */
+enum {
+    /* K/V blocks of this batch are read by more than one sequence (shared
+     * prompt prefixes, parallel sampling: [VE] §3.1 KV sharing).  The
+     * kernel then loads K/V with the normal cache policy so that sharers
+     * running at the same time hit in cache; without the flag K/V are
+     * streamed with nontemporal loads, which is faster when every block is
+     * read once.  Results are bit-identical either way. */
+    PA_DECODE_KV_REUSE = 1
+};
+
+/* pa_decode with flags (a bitwise OR of the PA_DECODE_* values; 0 gives
+ * pa_decode).  Unknown flag bits are INVALID_ARG. */
+pa_status pa_decode_ex(float *out, const void *q,
+                       const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, int32_t block_table_stride,
+                       const int32_t *context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       float scale, int32_t max_context_len,
+                       int32_t partition_size, void *workspace,
+                       size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
+                       void *stream);
+
 /* Chunked prefill: one iteration may carry new prompt chunks beside decode
  * rows ([VI] §1, continuous batching mixes requests in different phases).
  * Request r owns query rows cu_q_lens[r] .. cu_q_lens[r+1]-1; its context

@@ -27,6 +27,7 @@ PA_ERR_UNSUPPORTED = 4
 PA_ERR_DEVICE = 5
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
+PA_DECODE_KV_REUSE = 1
 
 # Axis order of the two pools, in the letters b (block), h (kv head),
 # r (row = token within block), d (head dim).
@@ -36,7 +37,8 @@ V_AXES = "bhdr"
 # Every symbol the header declares; the CPU tests check the library exports them.
 EXPORTED = (
     "pa_last_error", "pa_cache_write", "pa_copy_blocks", "pa_decode_default_partition",
-    "pa_decode_workspace_size", "pa_decode", "pa_prefill_chunk", "pa_allocator_create",
+    "pa_decode_workspace_size", "pa_decode", "pa_decode_ex", "pa_prefill_chunk",
+    "pa_allocator_create",
     "pa_allocator_destroy", "pa_seq_create", "pa_seq_fork", "pa_seq_append", "pa_seq_free",
     "pa_seq_length", "pa_seq_block_table", "pa_allocator_stats", "pa_block_refcount",
     "pa_batch_append", "pa_batch_tables",
@@ -72,6 +74,8 @@ def _declare(lib):
         "pa_decode_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                            i32, vp, sz, ctypes.c_int, vp]),
+        "pa_decode_ex": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                              i32, vp, sz, ctypes.c_int, ctypes.c_uint32, vp]),
         "pa_prefill_chunk": (st, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                   i32, i32, i32, f32, ctypes.c_int, vp]),
         "pa_allocator_create": (st, [i32, i32, pi32, ctypes.POINTER(vp)]),
@@ -182,14 +186,19 @@ def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, 
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None) -> None:
+              partition_size=0, workspace=None, stream=None, kv_reuse=False) -> None:
+    """Paged decode; kv_reuse=True (pa_decode_ex with PA_DECODE_KV_REUSE) for
+    batches whose sequences share blocks."""
     nb, hkv, bs, d = _geometry(k_cache)
     s, hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.pa_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
-                          block_tables.shape[1], _p(context_lens), s, hq, hkv, d, bs, nb,
-                          float(scale), int(max_context_len), int(partition_size), _p(workspace),
-                          ws_bytes, _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
+    args = (_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
+            _p(context_lens), s, hq, hkv, d, bs, nb, float(scale), int(max_context_len),
+            int(partition_size), _p(workspace), ws_bytes, _dtype_code(k_cache))
+    if kv_reuse:
+        _check(_lib.pa_decode_ex(*args, PA_DECODE_KV_REUSE, ctypes.c_void_p(_stream(stream))))
+    else:
+        _check(_lib.pa_decode(*args, ctypes.c_void_p(_stream(stream))))
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,

@@ -115,7 +115,22 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                     float scale, int32_t max_context_len, int32_t partition_size, void *workspace,
                     size_t workspace_bytes, pa_dtype dtype, void *stream) {
+    return pa_decode_ex(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        scale, max_context_len, partition_size, workspace, workspace_bytes,
+                        dtype, 0u, stream);
+}
+
+pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, int32_t block_table_stride,
+                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t max_context_len,
+                       int32_t partition_size, void *workspace, size_t workspace_bytes,
+                       pa_dtype dtype, uint32_t flags, void *stream) {
     const char *fn = "pa_decode";
+    if (flags & ~(uint32_t)PA_DECODE_KV_REUSE)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
     if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
     if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
     if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
@@ -171,6 +186,7 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     p.partition_size = ps;
     p.np_max = (int32_t)np_max;
     p.scale_log2 = scale * kLog2e;
+    p.kv_reuse = (flags & PA_DECODE_KV_REUSE) != 0;
     if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_max, &p.ws_ml,
                                              &p.ws_o);
     int rc = dtype == PA_DTYPE_BF16 ? pa::launch_decode_mfma(p, stream)

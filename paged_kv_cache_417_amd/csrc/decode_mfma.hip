@@ -48,7 +48,7 @@ struct StepRegs {
     u32x4 vt[D / 16];  // V^T rows d = 16*j + n, 8 tokens each
 };
 
-template <int D, int BS, bool TAIL>
+template <int D, int BS, bool TAIL, bool NT>
 __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__restrict__ kc,
                                           const uint16_t *__restrict__ vc, int32_t t0, int32_t L,
                                           int32_t bidA, int32_t bidB, int32_t hkv, int32_t kvh,
@@ -72,15 +72,16 @@ __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__rest
     const uint16_t *vp = vc + (((int64_t)bv * hkv + kvh) * D + n) * BS + (tv % BS);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-        r.ka[ks] = ld16_nt(ka + kslot_dim(ks, g));
-        r.kb[ks] = ld16_nt(kb + kslot_dim(ks, g));
+        r.ka[ks] = NT ? ld16_nt(ka + kslot_dim(ks, g)) : ld16(ka + kslot_dim(ks, g));
+        r.kb[ks] = NT ? ld16_nt(kb + kslot_dim(ks, g)) : ld16(kb + kslot_dim(ks, g));
     }
     // A step reads whole V^T rows of a block when BS <= 32; with larger
     // blocks it reads 64 of each row's 2*BS bytes and the following steps
     // read the rest of those cache lines, so the lines must stay cached.
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
-        r.vt[j] = BS <= 32 ? ld16_nt(vp + (int64_t)j * 16 * BS) : ld16(vp + (int64_t)j * 16 * BS);
+        r.vt[j] = NT && BS <= 32 ? ld16_nt(vp + (int64_t)j * 16 * BS)
+                                 : ld16(vp + (int64_t)j * 16 * BS);
 }
 
 template <int D, bool TAIL>
@@ -148,7 +149,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
 
 // Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
 // in 256 registers without spills.
-template <int D, int BS>
+template <int D, int BS, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
     DecodeParams p) {
     const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         const int32_t t0 = t_begin + 32 * st;
         const int32_t bA = block_id(t0 / BS);
         const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, b_last)) : bA;
-        load_step<D, BS, true>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
+        load_step<D, BS, true, NT>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
     };
     auto consume = [&](const StepRegs<D> &r, int32_t st) {
         const int32_t t0 = t_begin + 32 * st;
@@ -285,7 +286,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS>), grid, dim3(64), 0, s, p);
+    if (p.kv_reuse)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false>), grid, dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, true>), grid, dim3(64), 0, s, p);
 }
 
 }  // namespace

@@ -32,6 +32,7 @@ struct DecodeParams {
     int32_t partition_size;
     int32_t np_max;    // ceil(max_context_len / partition_size), >= 1
     float scale_log2;  // scale * log2(e)
+    bool kv_reuse;     // keep K/V cached (shared blocks) instead of streaming them
 };
 
 struct PrefillParams {

@@ -63,6 +63,14 @@ def test_decode_rejects(over, status):
     assert lib.pa_last_error()
 
 
+def test_decode_ex_flags():
+    args = list(decode_args(S=0, out=NULL, q=NULL, tables=NULL, lens=NULL))
+    assert lib.pa_decode_ex(*args[:-1], pa.PA_DECODE_KV_REUSE, STREAM) == pa.PA_OK
+    assert lib.pa_decode_ex(*args[:-1], 0, STREAM) == pa.PA_OK
+    assert lib.pa_decode_ex(*args[:-1], 6, STREAM) == pa.PA_ERR_INVALID_ARG
+    assert b"flags" in lib.pa_last_error()
+
+
 def test_decode_workspace_too_small_and_sizes():
     need = pa.pa_decode_workspace_size(2, 8, 8, 128, 16, 5000, 512)
     assert need > 0

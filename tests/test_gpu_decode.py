@@ -201,6 +201,29 @@ def test_block_permutation_is_bit_identical(pa):
     assert torch.equal(out1, out3)  # run to run
 
 
+def test_kv_reuse_flag_is_bit_identical(pa):
+    """The cache policy changes how K/V are loaded, never the result."""
+    say("case kv reuse flag")
+    for bs in (16, 128):
+        case = small_case(pa, "bf16", 8, 2, 128, bs, [37, 500, 1024, 3, 2049], seed=6 + bs)
+        sh = case.shape
+        dev = "cuda"
+        lens = case.lengths
+        maxlen = int(max(lens))
+        t_dev = torch.as_tensor(case.tables, device=dev)
+        l_dev = torch.as_tensor(lens, device=dev)
+        ws = pa.decode_workspace(len(lens), 8, 2, 128, bs, maxlen, 0, dev)
+        outs = []
+        for reuse in (False, True):
+            out = torch.empty((len(lens), 8, 128), device=dev)
+            pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, 0,
+                         ws, kv_reuse=reuse)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        check_rows(pa, case, outs[1], range(len(lens)))
+
+
 def test_context_one_returns_v_exactly(pa):
     say("case len1")
     for dtype in ("bf16", "f32"):
