@@ -29,14 +29,33 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Wave64 butterfly exchange (ds_bpermute under the hood for cross-row masks).
 __device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Max / sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48).
+// Max / sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48),
+// on the VALU.  v_permlane16_swap(a, b) leaves rows (a0, b0, a2, b2) in a and
+// (a1, b1, a3, b3) in b; v_permlane32_swap(a, b) leaves (a_lo, b_lo) and
+// (a_hi, b_hi).  With a = b = v, combining a and b pairs every lane with its
+// partner row; two swaps cover all four rows.  Written as inline assembly on
+// two explicit registers: the compiler's builtin for these instructions
+// keeps only one of the two results when both operands hold the same value.
+// The s_nop pairs give the VALU-write -> permlane-read wait states.
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float rows4_max(float v) {
-    v = fmaxf(v, xor_shuffle(v, 16));
-    return fmaxf(v, xor_shuffle(v, 32));
+    float a = v, b = v;
+    swap16(a, b);
+    float c = fmaxf(a, b), d = c;
+    swap32(c, d);
+    return fmaxf(c, d);
 }
 __device__ __forceinline__ float rows4_sum(float v) {
-    v += xor_shuffle(v, 16);
-    return v + xor_shuffle(v, 32);
+    float a = v, b = v;
+    swap16(a, b);
+    float c = a + b, d = c;
+    swap32(c, d);
+    return c + d;
 }
 
 // DPP moves within a 16-lane row.  Controls: quad_perm [1,0,3,2] = 0xB1,
