@@ -33,35 +33,14 @@ void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int
 namespace {
 
 constexpr int kReduceThreads = 256;
-constexpr int kReduceChunk = 1024;  // partitions whose weights sit in LDS at once
 
-// Max (or sum) over the 256 threads of the workgroup; every thread gets it.
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float v, float *scratch) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const float o = xor_shuffle(v, m);
-        v = MAX ? fmaxf(v, o) : v + o;
-    }
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();  // scratch free from any earlier use
-    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
-    __syncthreads();
-    float r = scratch[0];
-#pragma unroll
-    for (int i = 1; i < kReduceThreads / 64; ++i) r = MAX ? fmaxf(r, scratch[i]) : r + scratch[i];
-    return r;
-}
-
-// One workgroup of 256 threads per (sequence, query head).  The partitions'
-// maxima are read in parallel and reduced; each thread then owns one dim d
-// and one slice of the partitions (256 / D slices), summing its weighted
-// partial outputs with independent loads; the slices are added in LDS.  The
-// order of every sum depends only on partition indices: deterministic.
+// One workgroup of 256 threads per (sequence, query head).  Thread (slice
+// sl, dim d) merges partitions sl, sl + slices, ... (slices = 256 / D) with
+// the same online rescaling the partition kernel uses, so its loads do not
+// wait on any reduction; the slices are then merged by the first D threads.
+// Every merge runs in partition-index order: the result is deterministic.
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
-    __shared__ float w_s[kReduceChunk];
-    __shared__ float o_s[kReduceThreads];
-    __shared__ float scratch[kReduceThreads / 64];
+    __shared__ float part_m[kReduceThreads], part_l[kReduceThreads], part_o[kReduceThreads];
     const int s = blockIdx.x / p.num_q_heads;
     const int h = blockIdx.x % p.num_q_heads;
     const int tid = threadIdx.x;
@@ -72,35 +51,35 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     if (np <= 1) return;  // written directly by the partition kernel
     const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.np_max;
     const float *ml = p.ws_ml + 2 * base;
-
-    float mx = kNegInf;
-    for (int32_t i = tid; i < np; i += kReduceThreads) mx = fmaxf(mx, ml[2 * i]);
-    const float M = block_reduce<true>(mx, scratch);
-
     const int D = p.head_dim;
     const int slices = kReduceThreads / D;
     const int d = tid % D, sl = tid / D;
-    float lpart = 0.f, o = 0.f;
-    for (int32_t c0 = 0; c0 < np; c0 += kReduceChunk) {
-        const int32_t cn = min(kReduceChunk, np - c0);
-        for (int32_t i = tid; i < cn; i += kReduceThreads) {
-            const float w = fast_exp2(ml[2 * (c0 + i)] - M);
-            w_s[i] = w;
-            lpart += w * ml[2 * (c0 + i) + 1];
-        }
-        __syncthreads();
-        const float *op = p.ws_o + (base + c0) * D + d;
-#pragma unroll 8
-        for (int32_t i = sl; i < cn; i += slices) o += w_s[i] * op[(int64_t)i * D];
-        __syncthreads();
+    const float *op = p.ws_o + base * D + d;
+
+    float m = kNegInf, l = 0.f, o = 0.f;
+#pragma unroll 4
+    for (int32_t i = sl; i < np; i += slices) {
+        const float mi = ml[2 * i], li = ml[2 * i + 1], oi = op[(int64_t)i * D];
+        const float mn = fmaxf(m, mi);
+        const float a = fast_exp2(m - mn), b = fast_exp2(mi - mn);
+        l = l * a + li * b;
+        o = o * a + oi * b;
+        m = mn;
     }
-    const float lsum = block_reduce<false>(lpart, scratch);
-    o_s[tid] = o;
+    part_m[tid] = m;
+    part_l[tid] = l;
+    part_o[tid] = o;
     __syncthreads();
     if (tid < D) {
-        float t = o_s[tid];
-        for (int k = 1; k < slices; ++k) t += o_s[k * D + tid];
-        p.out[((int64_t)s * p.num_q_heads + h) * D + tid] = t / lsum;
+        float M = part_m[tid];
+        for (int k = 1; k < slices; ++k) M = fmaxf(M, part_m[k * D + tid]);
+        float lt = 0.f, ot = 0.f;
+        for (int k = 0; k < slices; ++k) {
+            const float w = fast_exp2(part_m[k * D + tid] - M);
+            lt += w * part_l[k * D + tid];
+            ot += w * part_o[k * D + tid];
+        }
+        p.out[((int64_t)s * p.num_q_heads + h) * D + tid] = ot / lt;
     }
 }
 
