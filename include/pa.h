@@ -69,7 +69,9 @@ const char *pa_last_error(void);
  *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], dtype.
  *   slot_mapping   [num_tokens] int64 device: slot = block * block_size + offset.
  *                  A negative slot, or one >= num_blocks * block_size, is
- *                  skipped (nothing written for that token).
+ *                  skipped (nothing written for that token).  Slots must be
+ *                  distinct: if two tokens name one slot, which of them
+ *                  lands is unspecified.
  * Bit-exact copy: no conversion, no arithmetic on the values. */
 pa_status pa_cache_write(const void *k_new, const void *v_new,
                          void *k_cache, void *v_cache,

@@ -16,40 +16,94 @@
 namespace pa {
 namespace {
 
-// One thread per (token, kv head, 16-byte chunk of the head's row).  The K
-// chunk is a single 16-byte store; the V chunk's elements go to VEC different
-// dimension rows at the token's column.
+// K: one thread per (token, kv head, 16-byte chunk of the head's row): one
+// 16-byte store into the token's row of its block.
 template <typename T>
-__global__ __launch_bounds__(256) void cache_write_kernel(
-    const T *__restrict__ k_new, const T *__restrict__ v_new, T *__restrict__ k_cache,
-    T *__restrict__ v_cache, const int64_t *__restrict__ slots, int32_t num_tokens,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks) {
+__device__ __forceinline__ void write_k(const T *__restrict__ k_new, T *__restrict__ k_cache,
+                                        const int64_t *__restrict__ slots, int64_t idx,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks) {
     constexpr int VEC = 16 / sizeof(T);
     const int32_t chunks = head_dim / VEC;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
-    if (idx >= total) return;
+    if (idx >= (int64_t)num_tokens * num_kv_heads * chunks) return;
     const int32_t c = (int32_t)(idx % chunks);
     const int64_t th = idx / chunks;  // token * Hkv + head
     const int32_t h = (int32_t)(th % num_kv_heads);
-    const int64_t t = th / num_kv_heads;
-    const int64_t slot = slots[t];
+    const int64_t slot = slots[th / num_kv_heads];
     if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
     const int64_t b = slot / block_size;
     const int32_t o = (int32_t)(slot % block_size);
-    const int64_t src = th * head_dim + (int64_t)c * VEC;
-    const int64_t bh = b * num_kv_heads + h;
+    st16(k_cache + ((b * num_kv_heads + h) * block_size + o) * head_dim + (int64_t)c * VEC,
+         ld16(k_new + th * head_dim + (int64_t)c * VEC));
+}
 
-    st16(k_cache + (bh * block_size + o) * head_dim + (int64_t)c * VEC, ld16(k_new + src));
-
+// V (dimension rows of a block): one thread per (run of VEC consecutive
+// tokens, kv head, dim).  Lanes walk the dims, so the reads of each token's
+// row are coalesced.  When the run's slots are consecutive and start at a
+// multiple of VEC -- the usual case for a prompt chunk, whose tokens fill
+// blocks in order -- the run lands as one 16-byte store into the dim row;
+// otherwise (decode steps: one token per sequence) each token's element is
+// stored on its own.
+template <typename T>
+__device__ __forceinline__ void write_v(const T *__restrict__ v_new, T *__restrict__ v_cache,
+                                        const int64_t *__restrict__ slots, int64_t idx,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int64_t runs = ((int64_t)num_tokens + VEC - 1) / VEC;
+    if (idx >= runs * num_kv_heads * head_dim) return;
+    const int32_t d = (int32_t)(idx % head_dim);
+    const int64_t rh = idx / head_dim;
+    const int32_t h = (int32_t)(rh % num_kv_heads);
+    const int64_t t0 = (rh / num_kv_heads) * VEC;
+    const int64_t limit = (int64_t)num_blocks * block_size;
+    const int32_t n = (int32_t)min((int64_t)VEC, (int64_t)num_tokens - t0);
+    const int64_t s0 = slots[t0];
+    bool packed = n == VEC && s0 >= 0 && s0 + VEC <= limit && s0 % VEC == 0;
     union {
         u32x4 v;
         T e[VEC];
     } u;
-    u.v = ld16(v_new + src);
-    T *vcol = v_cache + (bh * head_dim + (int64_t)c * VEC) * block_size + o;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) vcol[(int64_t)e * block_size] = u.e[e];
+    for (int i = 0; i < VEC; ++i) {
+        if (i < n) {
+            u.e[i] = v_new[((t0 + i) * num_kv_heads + h) * head_dim + d];
+            if (i > 0) packed = packed && slots[t0 + i] == s0 + i;
+        }
+    }
+    if (packed) {
+        const int64_t b = s0 / block_size;
+        const int32_t o = (int32_t)(s0 % block_size);
+        st16(v_cache + ((b * num_kv_heads + h) * head_dim + d) * block_size + o, u.v);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        if (i >= n) break;
+        const int64_t slot = slots[t0 + i];
+        if (slot < 0 || slot >= limit) continue;
+        const int64_t b = slot / block_size;
+        const int32_t o = (int32_t)(slot % block_size);
+        v_cache[((b * num_kv_heads + h) * head_dim + d) * block_size + o] = u.e[i];
+    }
+}
+
+// Workgroups [0, k_groups) write K, the rest write V.
+template <typename T>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const T *__restrict__ k_new, const T *__restrict__ v_new, T *__restrict__ k_cache,
+    T *__restrict__ v_cache, const int64_t *__restrict__ slots, int32_t num_tokens,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    uint32_t k_groups) {
+    if (blockIdx.x < k_groups) {
+        write_k<T>(k_new, k_cache, slots, (int64_t)blockIdx.x * 256 + threadIdx.x, num_tokens,
+                   num_kv_heads, head_dim, block_size, num_blocks);
+    } else {
+        write_v<T>(v_new, v_cache, slots, (int64_t)(blockIdx.x - k_groups) * 256 + threadIdx.x,
+                   num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+    }
 }
 
 // One thread per 16 bytes of one pair's K or V block region (both regions are
@@ -78,19 +132,23 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                        void *stream) {
     if (num_tokens == 0) return 0;
     const int vec = dtype == PA_DTYPE_BF16 ? 8 : 4;
-    const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / vec);
-    const dim3 grid((unsigned)((total + 255) / 256));
+    const int64_t k_threads = (int64_t)num_tokens * num_kv_heads * (head_dim / vec);
+    const int64_t v_threads = ((int64_t)num_tokens + vec - 1) / vec * num_kv_heads * head_dim;
+    const int64_t k_groups = (k_threads + 255) / 256;
+    const int64_t groups = k_groups + (v_threads + 255) / 256;
+    if (groups > 0xffffffffLL / 256) return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)groups);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (dtype == PA_DTYPE_BF16) {
         hipLaunchKernelGGL(cache_write_kernel<uint16_t>, grid, dim3(256), 0, s,
                            (const uint16_t *)k_new, (const uint16_t *)v_new, (uint16_t *)k_cache,
                            (uint16_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           block_size, num_blocks);
+                           block_size, num_blocks, (uint32_t)k_groups);
     } else {
         hipLaunchKernelGGL(cache_write_kernel<uint32_t>, grid, dim3(256), 0, s,
                            (const uint32_t *)k_new, (const uint32_t *)v_new, (uint32_t *)k_cache,
                            (uint32_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           block_size, num_blocks);
+                           block_size, num_blocks, (uint32_t)k_groups);
     }
     return (int)hipGetLastError();
 }

@@ -353,6 +353,47 @@ def test_cache_write_full_pool_bit_exact(pa):
     assert (chunked_checksum(k_pool), chunked_checksum(v_pool)) == before
 
 
+@pytest.mark.parametrize("dtype,d,bs", [("bf16", 128, 16), ("bf16", 64, 128), ("f32", 64, 16),
+                                         ("f32", 128, 32)])
+def test_cache_write_runs_bit_exact(pa, dtype, d, bs):
+    """Slot patterns of prompt chunks and decode steps mixed in one call:
+    aligned runs of consecutive slots, unaligned runs, a run crossing into
+    the next block, random slots and skipped (-1) slots.  Whole pools are
+    compared with the oracle bit for bit."""
+    say(f"case cache write runs {dtype} d={d} bs={bs}")
+    dev = "cuda"
+    nb, hkv = 48, 4
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kshape, vshape = pa.kv_cache_shapes(nb, hkv, bs, d)
+    k_pool = torch.full(kshape, float("nan"), dtype=tdt, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=tdt, device=dev)
+    k_host, v_host = host_bits(k_pool).copy(), host_bits(v_pool).copy()
+    rng = np.random.default_rng(d + bs)
+    blocks = rng.permutation(nb)
+    slots = []
+    slots += list(range(blocks[0] * bs, blocks[0] * bs + 3 * bs // 2 if bs > 16 else bs))  # aligned run
+    slots += list(range(blocks[1] * bs + 3, blocks[1] * bs + bs))  # unaligned start
+    slots += list(range(blocks[2] * bs + bs - 5, blocks[2] * bs + bs + 6))  # crosses a block end
+    slots += [int(x) for x in rng.choice(np.arange(blocks[5] * bs, blocks[5] * bs + bs), 7,
+                                         replace=False)]  # scattered, no run
+    slots += [-1, -1, blocks[6] * bs + 1, -1]
+    slots = np.array([sl for sl in slots if sl < nb * bs], dtype=np.int64)
+    # keep slots distinct (a slot written twice has no defined winner)
+    _, first = np.unique(np.where(slots < 0, -np.arange(len(slots)) - 1, slots), return_index=True)
+    slots = slots[np.sort(first)]
+    T = len(slots)
+    gen = wl.make_generator(d * 7 + bs, dev)
+    k_new = wl.randn((T, hkv, d), tdt, gen, dev)
+    v_new = wl.randn((T, hkv, d), tdt, gen, dev)
+    pa.pa_cache_write(k_new, v_new, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    torch.cuda.synchronize()
+    oracle.cache_write(host_bits(k_new), host_bits(v_new), k_host, v_host, slots, pa.K_AXES,
+                       pa.V_AXES)
+    bits = np.uint16 if dtype == "bf16" else np.uint32
+    assert (host_bits(k_pool).view(bits) == k_host.view(bits)).all()
+    assert (host_bits(v_pool).view(bits) == v_host.view(bits)).all()
+
+
 def test_copy_blocks_bit_exact(pa):
     say("case copy blocks")
     case = small_case(pa, "bf16", 8, 8, 128, 16, [300, 200], seed=44)
