@@ -16,6 +16,8 @@
 namespace pa {
 namespace {
 
+constexpr int32_t kRunBatch = 256;  // tokens per call from which V is written by runs
+
 // K: one thread per (token, kv head, 16-byte chunk of the head's row): one
 // 16-byte store into the token's row of its block.
 template <typename T>
@@ -90,8 +92,38 @@ __device__ __forceinline__ void write_v(const T *__restrict__ v_new, T *__restri
     }
 }
 
-// Workgroups [0, k_groups) write K, the rest write V.
+// V, one thread per (token, kv head, 16-byte chunk): one 16-byte load of
+// the token's row and VEC element stores into VEC dim rows.  Cheapest when
+// no two tokens of the batch share a block row (decode steps).
 template <typename T>
+__device__ __forceinline__ void write_v_tokens(const T *__restrict__ v_new,
+                                               T *__restrict__ v_cache,
+                                               const int64_t *__restrict__ slots, int64_t idx,
+                                               int32_t num_tokens, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int32_t chunks = head_dim / VEC;
+    if (idx >= (int64_t)num_tokens * num_kv_heads * chunks) return;
+    const int32_t c = (int32_t)(idx % chunks);
+    const int64_t th = idx / chunks;
+    const int32_t h = (int32_t)(th % num_kv_heads);
+    const int64_t slot = slots[th / num_kv_heads];
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const int64_t b = slot / block_size;
+    const int32_t o = (int32_t)(slot % block_size);
+    union {
+        u32x4 v;
+        T e[VEC];
+    } u;
+    u.v = ld16(v_new + th * head_dim + (int64_t)c * VEC);
+    T *col = v_cache + ((b * num_kv_heads + h) * head_dim + (int64_t)c * VEC) * block_size + o;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) col[(int64_t)e * block_size] = u.e[e];
+}
+
+// Workgroups [0, k_groups) write K, the rest write V, by runs or by tokens.
+template <typename T, bool RUNS>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const T *__restrict__ k_new, const T *__restrict__ v_new, T *__restrict__ k_cache,
     T *__restrict__ v_cache, const int64_t *__restrict__ slots, int32_t num_tokens,
@@ -100,9 +132,13 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     if (blockIdx.x < k_groups) {
         write_k<T>(k_new, k_cache, slots, (int64_t)blockIdx.x * 256 + threadIdx.x, num_tokens,
                    num_kv_heads, head_dim, block_size, num_blocks);
-    } else {
+    } else if (RUNS) {
         write_v<T>(v_new, v_cache, slots, (int64_t)(blockIdx.x - k_groups) * 256 + threadIdx.x,
                    num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+    } else {
+        write_v_tokens<T>(v_new, v_cache, slots,
+                          (int64_t)(blockIdx.x - k_groups) * 256 + threadIdx.x, num_tokens,
+                          num_kv_heads, head_dim, block_size, num_blocks);
     }
 }
 
@@ -132,24 +168,28 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                        void *stream) {
     if (num_tokens == 0) return 0;
     const int vec = dtype == PA_DTYPE_BF16 ? 8 : 4;
+    // Batches of many tokens are mostly prompt chunks whose slots run in
+    // order; small ones are decode steps (one token per sequence).  Both V
+    // paths are exact for any slots: the choice only affects speed.
+    const bool runs = num_tokens >= kRunBatch;
     const int64_t k_threads = (int64_t)num_tokens * num_kv_heads * (head_dim / vec);
-    const int64_t v_threads = ((int64_t)num_tokens + vec - 1) / vec * num_kv_heads * head_dim;
+    const int64_t v_threads = runs ? ((int64_t)num_tokens + vec - 1) / vec * num_kv_heads * head_dim
+                                   : k_threads;
     const int64_t k_groups = (k_threads + 255) / 256;
     const int64_t groups = k_groups + (v_threads + 255) / 256;
     if (groups > 0xffffffffLL / 256) return (int)hipErrorInvalidValue;
     const dim3 grid((unsigned)groups);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+#define PA_LAUNCH(T, R)                                                                         \
+    hipLaunchKernelGGL((cache_write_kernel<T, R>), grid, dim3(256), 0, s, (const T *)k_new,     \
+                       (const T *)v_new, (T *)k_cache, (T *)v_cache, slot_mapping, num_tokens, \
+                       num_kv_heads, head_dim, block_size, num_blocks, (uint32_t)k_groups)
     if (dtype == PA_DTYPE_BF16) {
-        hipLaunchKernelGGL(cache_write_kernel<uint16_t>, grid, dim3(256), 0, s,
-                           (const uint16_t *)k_new, (const uint16_t *)v_new, (uint16_t *)k_cache,
-                           (uint16_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           block_size, num_blocks, (uint32_t)k_groups);
+        if (runs) PA_LAUNCH(uint16_t, true); else PA_LAUNCH(uint16_t, false);
     } else {
-        hipLaunchKernelGGL(cache_write_kernel<uint32_t>, grid, dim3(256), 0, s,
-                           (const uint32_t *)k_new, (const uint32_t *)v_new, (uint32_t *)k_cache,
-                           (uint32_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           block_size, num_blocks, (uint32_t)k_groups);
+        if (runs) PA_LAUNCH(uint32_t, true); else PA_LAUNCH(uint32_t, false);
     }
+#undef PA_LAUNCH
     return (int)hipGetLastError();
 }
 

@@ -353,14 +353,17 @@ def test_cache_write_full_pool_bit_exact(pa):
     assert (chunked_checksum(k_pool), chunked_checksum(v_pool)) == before
 
 
+@pytest.mark.parametrize("big", [False, True])
 @pytest.mark.parametrize("dtype,d,bs", [("bf16", 128, 16), ("bf16", 64, 128), ("f32", 64, 16),
                                          ("f32", 128, 32)])
-def test_cache_write_runs_bit_exact(pa, dtype, d, bs):
+def test_cache_write_runs_bit_exact(pa, dtype, d, bs, big):
     """Slot patterns of prompt chunks and decode steps mixed in one call:
     aligned runs of consecutive slots, unaligned runs, a run crossing into
-    the next block, random slots and skipped (-1) slots.  Whole pools are
-    compared with the oracle bit for bit."""
-    say(f"case cache write runs {dtype} d={d} bs={bs}")
+    the next block, random slots and skipped (-1) slots.  Small batches and
+    batches of hundreds of tokens take different V paths in the library;
+    both are checked.  Whole pools are compared with the oracle bit for
+    bit."""
+    say(f"case cache write runs {dtype} d={d} bs={bs} big={big}")
     dev = "cuda"
     nb, hkv = 48, 4
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -377,6 +380,11 @@ def test_cache_write_runs_bit_exact(pa, dtype, d, bs):
     slots += [int(x) for x in rng.choice(np.arange(blocks[5] * bs, blocks[5] * bs + bs), 7,
                                          replace=False)]  # scattered, no run
     slots += [-1, -1, blocks[6] * bs + 1, -1]
+    if big:  # whole blocks filled in order, as a prompt chunk does, to past 256 tokens
+        j = 7
+        while len(slots) < 320:
+            slots += list(range(blocks[j] * bs, blocks[j] * bs + bs))
+            j += 1
     slots = np.array([sl for sl in slots if sl < nb * bs], dtype=np.int64)
     # keep slots distinct (a slot written twice has no defined winner)
     _, first = np.unique(np.where(slots < 0, -np.arange(len(slots)) - 1, slots), return_index=True)
