@@ -60,13 +60,14 @@ struct Stage {
     u32x4 v[kPasses];
 };
 
-// Global -> registers for keys t0 .. t0+31.  Keys at or past nkeys are not
-// read (their table entries may not exist): K gets zeros, V gets zeros, so
-// a masked key contributes exactly nothing.
+// Global -> registers for keys t0 .. t0+31, whose blocks are bidA (keys
+// t0 .. t0+15) and bidB (keys t0+16 .. t0+31; the same block unless
+// BS == 16).  Keys at or past nkeys are not read: K gets zeros, V gets
+// zeros, so a masked key contributes exactly nothing.
 template <int D, int BS>
-__device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p,
-                                           const int32_t *__restrict__ table, int kvh,
-                                           int32_t t0, int32_t nkeys, int tid, bool &bad) {
+__device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p, int kvh,
+                                           int32_t t0, int32_t nkeys, int32_t bidA,
+                                           int32_t bidB, int tid) {
     const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
     const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -79,12 +80,8 @@ __device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams
             const int32_t t = t0 + kk;
             u32x4 val = zero;
             if (t < nkeys) {
-                int32_t blk = table[t / BS];
-                if ((uint32_t)blk >= (uint32_t)p.num_blocks) {
-                    bad = true;
-                    blk = 0;
-                }
-                val = ld16(kc + (((int64_t)blk * p.num_kv_heads + kvh) * BS + t % BS) * D + ch * 8);
+                const int64_t blk = (BS == 16 && kk >= 16) ? bidB : bidA;
+                val = ld16(kc + ((blk * p.num_kv_heads + kvh) * BS + t % BS) * D + ch * 8);
             }
             st.k[ps] = val;
         }
@@ -94,35 +91,35 @@ __device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams
             const int32_t t = t0 + 8 * ch;
             u32x4 val = zero;
             if (t < nkeys) {
-                int32_t blk = table[t / BS];
-                if ((uint32_t)blk >= (uint32_t)p.num_blocks) {
-                    bad = true;
-                    blk = 0;
-                }
-                val = ld16(vc + (((int64_t)blk * p.num_kv_heads + kvh) * D + dim) * BS + t % BS);
-                if (t + 8 > nkeys) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
-                                              (t + 2 * w + 1 < nkeys ? 0xffff0000u : 0u);
-                        val[w] &= keep;
-                    }
-                }
+                const int64_t blk = (BS == 16 && ch >= 2) ? bidB : bidA;
+                val = ld16(vc + ((blk * p.num_kv_heads + kvh) * D + dim) * BS + t % BS);
             }
-            st.v[ps] = val;
+            st.v[ps] = val;  // keys past nkeys in a partial chunk are cleared by stage_store
         }
     }
 }
 
+// Registers -> LDS.  A V chunk that straddles nkeys has its keys from nkeys
+// on cleared here rather than right after its load, so that the loads of a
+// step never wait before the previous step's math.
 template <int D, int BS>
-__device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, const Stage<D, BS> &st,
-                                            int tid) {
+__device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D, BS> &st,
+                                            int tid, int32_t t0, int32_t nkeys) {
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         const int kk = idx / (D / 8), ch = idx % (D / 8);
         *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = st.k[ps];
         const int dim = idx >> 2, chv = idx & 3;
+        const int32_t t = t0 + 8 * chv;
+        if (t + 8 > nkeys) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
+                                      (t + 2 * w + 1 < nkeys ? 0xffff0000u : 0u);
+                st.v[ps][w] &= keep;
+            }
+        }
         *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = st.v[ps];
     }
 }
@@ -217,10 +214,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // The request's block-table entries live in one VGPR per wave, 64 at a
+    // time (lane j holds the entry of logical block win + j); block ids are
+    // read with readlane, so no table load stands between a step and its
+    // K/V loads.  Entries past the last block of visible keys are not read.
+    const int32_t nblk = (nkeys + BS - 1) / BS;
+    int32_t win = 0;
+    int32_t tbl = lane < nblk ? table[lane] : 0;
     bool bad = false;
+    auto block_id = [&](int32_t j) -> int32_t {
+        if (j - win >= 64) {
+            win = j;
+            tbl = win + lane < nblk ? table[win + lane] : 0;
+        }
+        int32_t b = __builtin_amdgcn_readlane(tbl, j - win);
+        if ((uint32_t)b >= (uint32_t)p.num_blocks) {
+            bad = true;
+            b = 0;
+        }
+        return b;
+    };
+    auto stage = [&](Stage<D, BS> &st, int32_t t0) {
+        const int32_t bA = block_id(t0 / BS);
+        const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, nblk - 1)) : bA;
+        stage_load<D, BS>(st, p, kvh, t0, nkeys, bA, bB, tid);
+    };
+
     Stage<D, BS> st;
-    stage_load<D, BS>(st, p, table, kvh, 0, nkeys, tid, bad);
-    stage_store<D, BS>(sm, 0, st, tid);
+    stage(st, 0);
+    stage_store<D, BS>(sm, 0, st, tid, 0, nkeys);
     __syncthreads();
 
     const int32_t ntiles = (nkeys + kTile - 1) / kTile;
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         const int buf = it & 1;
         const int32_t t0 = it * kTile;
         const bool more = it + 1 < ntiles;
-        if (more) stage_load<D, BS>(st, p, table, kvh, t0 + kTile, nkeys, tid, bad);
+        if (more) stage(st, t0 + kTile);
 
         if (wave_maxpos >= t0) {
             u32x4 ka[D / 32], kb[D / 32];
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 }
             }
         }
-        if (more) stage_store<D, BS>(sm, buf ^ 1, st, tid);
+        if (more) stage_store<D, BS>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
         __syncthreads();
     }
 
