@@ -30,6 +30,8 @@
 //       running max is shared by the four lanes of a column.
 //   O^T += V^T P^T : A = V^T rows from LDS, B = P as a bf16 high part plus a
 //       bf16 remainder (two MFMAs), keeping P's error near 2^-16.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -62,47 +64,49 @@ struct Stage {
 
 // Global -> registers for keys t0 .. t0+31, whose blocks are bidA (keys
 // t0 .. t0+15) and bidB (keys t0+16 .. t0+31; the same block unless
-// BS == 16).  Keys at or past nkeys are not read: K gets zeros, V gets
-// zeros, so a masked key contributes exactly nothing.
+// BS == 16).  The step's base addresses are wave-uniform; each thread adds a
+// fixed offset.  Keys at or past nkeys are not read (K and V get zeros), so
+// a masked key contributes exactly nothing; only the last step of a
+// workgroup checks this.
 template <int D, int BS>
 __device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p, int kvh,
                                            int32_t t0, int32_t nkeys, int32_t bidA,
                                            int32_t bidB, int tid) {
     const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
     const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+    const int64_t hkv = p.num_kv_heads;
+    const int32_t rowA = t0 % BS, rowB = (t0 + 16) % BS;
+    const uint16_t *kA = kc + ((bidA * hkv + kvh) * BS + rowA) * D;
+    const uint16_t *kB = kc + ((bidB * hkv + kvh) * BS + rowB) * D;
+    const uint16_t *vA = vc + (bidA * hkv + kvh) * (int64_t)D * BS + rowA;
+    const uint16_t *vB = vc + (bidB * hkv + kvh) * (int64_t)D * BS + rowB;
+    const bool full = t0 + kTile <= nkeys;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         // K: D/8 chunks of 16 bytes per key
-        {
-            const int kk = idx / (D / 8), ch = idx % (D / 8);
-            const int32_t t = t0 + kk;
-            u32x4 val = zero;
-            if (t < nkeys) {
-                const int64_t blk = (BS == 16 && kk >= 16) ? bidB : bidA;
-                val = ld16(kc + ((blk * p.num_kv_heads + kvh) * BS + t % BS) * D + ch * 8);
-            }
-            st.k[ps] = val;
-        }
+        const int kk = idx / (D / 8), ch = idx % (D / 8);
+        const bool k_in_b = BS == 16 && kk >= 16;
+        const uint16_t *kp = (k_in_b ? kB : kA) + (k_in_b ? kk - 16 : kk) * D + ch * 8;
         // V^T: 4 chunks of 8 keys per dim
-        {
-            const int dim = idx >> 2, ch = idx & 3;
-            const int32_t t = t0 + 8 * ch;
-            u32x4 val = zero;
-            if (t < nkeys) {
-                const int64_t blk = (BS == 16 && ch >= 2) ? bidB : bidA;
-                val = ld16(vc + ((blk * p.num_kv_heads + kvh) * D + dim) * BS + t % BS);
-            }
-            st.v[ps] = val;  // keys past nkeys in a partial chunk are cleared by stage_store
+        const int dim = idx >> 2, cv = idx & 3;
+        const bool v_in_b = BS == 16 && cv >= 2;
+        const uint16_t *vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cv - 2 : cv);
+        if (full) {
+            st.k[ps] = ld16(kp);
+            st.v[ps] = ld16(vp);
+        } else {
+            st.k[ps] = t0 + kk < nkeys ? ld16(kp) : zero;
+            st.v[ps] = t0 + 8 * cv < nkeys ? ld16(vp) : zero;  // partial chunk: stage_store
         }
     }
 }
 
-// Registers -> LDS.  A V chunk that straddles nkeys has its keys from nkeys
-// on cleared here rather than right after its load, so that the loads of a
-// step never wait before the previous step's math.
-template <int D, int BS>
+// Registers -> LDS.  On the last step (TAIL) a V chunk that straddles nkeys
+// has its keys from nkeys on cleared here rather than right after its load,
+// so the loads of a step never wait before the previous step's math.
+template <int D, int BS, bool TAIL>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D, BS> &st,
                                             int tid, int32_t t0, int32_t nkeys) {
 #pragma unroll
@@ -111,8 +115,8 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D
         const int kk = idx / (D / 8), ch = idx % (D / 8);
         *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = st.k[ps];
         const int dim = idx >> 2, chv = idx & 3;
-        const int32_t t = t0 + 8 * chv;
-        if (t + 8 > nkeys) {
+        if constexpr (TAIL) {
+            const int32_t t = t0 + 8 * chv;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
@@ -131,7 +135,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     PrefillParams p) {
     __shared__ PrefillSmem<D> sm;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int n = lane & 15, g = lane >> 4;
     const int G = p.num_q_heads / p.num_kv_heads;
     const int ppw = kPairs / G;  // positions per workgroup
@@ -194,16 +199,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             qb[ct][ks] = as_bf16x8(v);
         }
     }
-    // Largest and smallest position among this wave's valid columns
-    // (wave_maxpos = -1: none).  Keys up to wave_minpos are visible to every
-    // valid column, so steps that end there need no causal mask.
-    int32_t wave_maxpos = -1, wave_minpos = -1;
+    // Largest position among this wave's valid columns (-1: none): steps
+    // past it hold no key any column of the wave sees.
+    int32_t wave_maxpos = -1;
     {
         const int first = w * 32, last = min(w * 32 + 31, ppw * G - 1);
-        if (first <= last && i_begin + first / G < i_end) {
+        if (first <= last && i_begin + first / G < i_end)
             wave_maxpos = base_pos + min(i_begin + last / G, i_end - 1);
-            wave_minpos = base_pos + i_begin + first / G;
-        }
     }
 
     const int32_t *table = p.block_tables + (int64_t)r * p.table_stride;
@@ -242,11 +244,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 
     Stage<D, BS> st;
     stage(st, 0);
-    stage_store<D, BS>(sm, 0, st, tid, 0, nkeys);
+    if (kTile <= nkeys)
+        stage_store<D, BS, false>(sm, 0, st, tid, 0, nkeys);
+    else
+        stage_store<D, BS, true>(sm, 0, st, tid, 0, nkeys);
     __syncthreads();
 
+    // One 32-key step.  MASK: some column of the workgroup may sit before
+    // a key of the step (causal mask needed).  Steps ending at or before the
+    // workgroup's first position need no mask for any column; they run a
+    // body compiled without it.
     const int32_t ntiles = (nkeys + kTile - 1) / kTile;
-    for (int32_t it = 0; it < ntiles; ++it) {
+    auto step = [&](int32_t it, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = it & 1;
         const int32_t t0 = it * kTile;
         const bool more = it + 1 < ntiles;
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                     z[i] = sa[i] * p.scale_log2;
                     z[4 + i] = sb[i] * p.scale_log2;
                 }
-                if (t0 + kTile - 1 > wave_minpos) {  // the step crosses a column's position
+                if constexpr (MASK) {
                     const int32_t tb = t0 + 8 * g;
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
@@ -326,9 +336,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 }
             }
         }
-        if (more) stage_store<D, BS>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
+        if (more) {
+            if (t0 + 2 * kTile <= nkeys)
+                stage_store<D, BS, false>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
+            else
+                stage_store<D, BS, true>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
+        }
         __syncthreads();
-    }
+    };
+    const int32_t wg_minpos = base_pos + i_begin;  // first position of the workgroup's rows
+    const int32_t nomask = min(ntiles, (wg_minpos + 1) / kTile);
+    int32_t it = 0;
+    for (; it < nomask; ++it) step(it, std::false_type{});
+    for (; it < ntiles; ++it) step(it, std::true_type{});
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     const float qnan = __builtin_nanf("");
