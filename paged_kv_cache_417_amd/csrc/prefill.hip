@@ -182,6 +182,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // This lane's two columns.
     int32_t pos[2];
     int64_t qoff[2];
+    // Scores are scaled by |scale| * log2(e) inside the exponent (one fma
+    // per weight); a negative scale flips q's sign bits instead, which is
+    // exact, so the maximum can be taken on unscaled scores.
+    const float sc = fabsf(p.scale_log2);
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     bf16x8 qb[2][D / 32];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) + qoff[ct];
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-            u32x4 v = ld16(qrow + kslot_dim(ks, g));
+            u32x4 v = ld16(qrow + kslot_dim(ks, g)) ^ qsign;
             if (!valid) v = u32x4{0u, 0u, 0u, 0u};
             qb[ct][ks] = as_bf16x8(v);
         }
@@ -280,22 +285,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                     sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qb[ct][ks], sb,
                                                                  0, 0, 0);
                 }
-                float z[8];
+                float sr[8];  // unscaled scores of keys t0 + 8g + i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    z[i] = sa[i] * p.scale_log2;
-                    z[4 + i] = sb[i] * p.scale_log2;
+                    sr[i] = sa[i];
+                    sr[4 + i] = sb[i];
                 }
-                if constexpr (MASK) {
-                    const int32_t tb = t0 + 8 * g;
+                bool vis[8];
+                float mr = kNegInf;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (tb + i > pos[ct]) z[i] = kNegInf;
+                for (int i = 0; i < 8; ++i) {
+                    vis[i] = !MASK || t0 + 8 * g + i <= pos[ct];
+                    mr = fmaxf(mr, vis[i] ? sr[i] : kNegInf);
                 }
-                float mx = z[0];
-#pragma unroll
-                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-                mx = rows4_max(mx);
+                mr = rows4_max(mr);
+                const float mx = mr == kNegInf ? kNegInf : mr * sc;
                 // Lazy rescaling: the exponent base m[ct] moves only when the
                 // column's max grows by more than kRescaleMargin (log2
                 // units), so weights stay below 2^kRescaleMargin and the
@@ -312,15 +316,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 // A column with no visible key yet keeps m = -inf; subtract 0
                 // then so every weight is exp2(-inf) = 0 rather than NaN.
                 const float msub = m[ct] == kNegInf ? 0.f : m[ct];
+                // P = hi + lo: hi keeps the top 16 bits of each fp32 weight
+                // (a bf16 value), lo = P - hi is exact in fp32 and rounded to
+                // bf16, so P enters the bf16 products with ~16 bits.
                 float sum = 0.f;
+                uint32_t hb[8];
+                float lo[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float pv = fast_exp2(z[i] - msub);
+                    const float arg = fmaf(sr[i], sc, -msub);
+                    const float pv = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
                     sum += pv;
-                    const __bf16 hi = (__bf16)pv;
-                    ph[ct][i] = hi;
-                    pl[ct][i] = (__bf16)(pv - (float)hi);
+                    hb[i] = __float_as_uint(pv);
+                    lo[i] = pv - __uint_as_float(hb[i] & 0xffff0000u);
                 }
+                u32x4 hw, lw;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    hw[k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
+                    lw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                             f32x2{lo[2 * k], lo[2 * k + 1]}, bf16x2));
+                }
+                ph[ct] = as_bf16x8(hw);
+                pl[ct] = as_bf16x8(lw);
                 l[ct] += sum;
             }
 #pragma unroll

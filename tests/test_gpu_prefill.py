@@ -110,6 +110,32 @@ def test_prefill_group_sizes(pa, hq, hkv):
     say(f"  max err {check_all(case, out):.3e}")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.7])
+def test_prefill_any_scale(pa, scale):
+    """The scale may be negative or zero (scale 0 gives the mean of the
+    visible V rows)."""
+    ctx, ql = [90, 40, 257], [90, 7, 33]
+    sh = wl.PrefillShape(num_reqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=16, seed=61)
+    say(f"case prefill scale {scale}")
+    case = wl.make_prefill_case(sh, "cuda", pa.K_AXES, pa.V_AXES, context_lens=ctx, q_lens=ql)
+    dev = "cuda"
+    out = torch.full((case.q.shape[0], 8, 128), 7.0, device=dev)
+    pa.pa_prefill_chunk(out, case.q, case.k_pool, case.v_pool,
+                        torch.as_tensor(case.tables, device=dev),
+                        torch.as_tensor(case.cu_q_lens, device=dev),
+                        torch.as_tensor(case.context_lens, device=dev), scale, max(ql), max(ctx))
+    torch.cuda.synchronize()
+    rows = list(range(3))
+    k_sub, v_sub, t_sub, l_sub = gather_blocks(case.k_pool, case.v_pool, case.tables,
+                                               case.context_lens, rows, sh.block_size)
+    ref = oracle.prefill(host_bits(case.q), k_sub, v_sub, t_sub, case.cu_q_lens, l_sub, scale,
+                         case.k_axes, case.v_axes)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    say(f"  max err {err:.3e}")
+    assert err <= TOL
+
+
 def test_prefill_last_row_matches_decode(pa):
     """The last row of a chunk is a decode step over the whole context."""
     sh = wl.PrefillShape(num_reqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
