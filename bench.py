@@ -110,18 +110,25 @@ def events_time(torch, fn, reps, stream):
 # CPU baseline
 
 
-def cpu_baseline(case, budget_s: float):
-    """The fp64 oracle, single-threaded, on whole sequences of the batch until
-    the time budget is spent or the batch is done."""
+def _oracle_helpers():
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from paged_helpers import gather_blocks, host_bits
+    return oracle, gather_blocks, host_bits
 
+
+def oracle_decode_sample(case, budget_s: float, tables=None, lengths=None):
+    """The fp64 oracle, single-threaded, on whole sequences of a decode batch
+    (all heads) until the time budget is spent or the batch is done.
+    Returns (sequences done, context tokens, seconds)."""
+    oracle, gather_blocks, host_bits = _oracle_helpers()
     sh = case.shape
+    tabs = case.tables if tables is None else tables
+    lens = case.lengths if lengths is None else lengths
     done, elapsed, tokens = 0, 0.0, 0
-    for s in range(len(case.lengths)):
-        k_sub, v_sub, t_sub, l_sub = gather_blocks(case.k_pool, case.v_pool, case.tables,
-                                                   case.lengths, [s], sh.block_size)
+    for s in range(len(lens)):
+        k_sub, v_sub, t_sub, l_sub = gather_blocks(case.k_pool, case.v_pool, tabs, lens, [s],
+                                                   sh.block_size)
         q_sub = host_bits(case.q[s:s + 1])
         t0 = time.perf_counter()
         oracle.decode(q_sub, k_sub, v_sub, t_sub, l_sub, sh.scale, case.k_axes, case.v_axes)
@@ -130,9 +137,112 @@ def cpu_baseline(case, budget_s: float):
         tokens += int(l_sub[0])
         if elapsed >= budget_s:
             break
+    return done, tokens, elapsed
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle on the headline batch (whole sequences, all heads)."""
+    done, tokens, elapsed = oracle_decode_sample(case, budget_s)
+    sh = case.shape
     return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {len(case.lengths)} sequences of the batch ({tokens} context "
                       f"tokens), all {sh.num_q_heads} heads, fp64, one thread, {elapsed:.1f} s"}
+
+
+def cpu_decode_row(case, budget_s, tables=None, lengths=None):
+    done, tokens, elapsed = oracle_decode_sample(case, budget_s, tables, lengths)
+    n = len(case.lengths if lengths is None else lengths)
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {n} sequences ({tokens} context tokens), all heads, fp64, "
+                      f"one thread, {elapsed:.1f} s"}
+
+
+def cpu_prefill_row(q, k_pool, v_pool, tables, cu, ctx, scale, block_size, budget_s):
+    """Oracle prefill on single rows of request 0 (each a 1-row chunk at its
+    position, over all keys up to it) until the budget is spent."""
+    oracle, gather_blocks, host_bits = _oracle_helpers()
+    import numpy as np
+    qlen0 = int(cu[1] - cu[0])
+    done, elapsed = 0, 0.0
+    for i in range(qlen0):
+        pos = int(ctx[0]) - qlen0 + i
+        k_sub, v_sub, t_sub, _ = gather_blocks(k_pool, v_pool, tables[:1], [pos + 1], [0],
+                                               block_size)
+        qrow = host_bits(q[int(cu[0]) + i:int(cu[0]) + i + 1])
+        t0 = time.perf_counter()
+        oracle.prefill(qrow, k_sub, v_sub, t_sub, np.array([0, 1], np.int32),
+                       np.array([pos + 1], np.int32), scale, "bhrd", "bhdr")
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": done / elapsed, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} query rows of request 0 (each over its >= {int(ctx[0]) - qlen0 + 1} "
+                      f"visible keys), all heads, fp64, one thread, {elapsed:.1f} s"}
+
+
+def cpu_cache_write_row(k_new, v_new, slots, hkv, d, bs, budget_s):
+    """Oracle cache write of the same tokens into a host pool holding just
+    the blocks they touch, repeated until the budget is spent."""
+    oracle, _, host_bits = _oracle_helpers()
+    import numpy as np
+    slots = np.asarray(slots, dtype=np.int64)
+    blocks = np.unique(slots[slots >= 0] // bs)
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    sub = np.array([remap[int(x) // bs] * bs + int(x) % bs if x >= 0 else -1 for x in slots],
+                   dtype=np.int64)
+    kh, vh = host_bits(k_new), host_bits(v_new)
+    kp = np.zeros((len(blocks), hkv, bs, d), dtype=kh.dtype)
+    vp = np.zeros((len(blocks), hkv, d, bs), dtype=vh.dtype)
+    reps, elapsed = 0, 0.0
+    while elapsed < budget_s:
+        t0 = time.perf_counter()
+        oracle.cache_write(kh, vh, kp, vp, sub, "bhrd", "bhdr")
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * len(slots) / elapsed, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle", "sample": f"{reps} writes of the {len(slots)} tokens into a host "
+                                        f"pool of their {len(blocks)} blocks, {elapsed:.1f} s"}
+
+
+def cpu_allocator_row(case, steps):
+    """The plain-Python reference model of the allocator replaying the
+    headline batch's prompts and then `steps` decode appends of one token to
+    every sequence, with the dense table built each step."""
+    from oracle.allocator_model import AllocatorModel
+    sh = case.shape
+    m = AllocatorModel(sh.num_blocks, sh.block_size, free_order=case.perm)
+    ids = list(range(len(case.lengths)))
+    for s, L in zip(ids, case.lengths):
+        m.create(s)
+        m.append(s, int(L))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for s in ids:
+            m.append(s, 1)
+        [list(m.tables[s]) for s in ids]
+    elapsed = time.perf_counter() - t0
+    return {"value": elapsed * 1e6 / steps, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} steps of 64 appends + tables on the Python reference model"}
+
+
+def cpu_copy_row(pairs, hkv, d, bs, budget_s):
+    """Oracle whole-block copies of the same number of pairs on host pools."""
+    oracle, _, _ = _oracle_helpers()
+    import numpy as np
+    n = len(pairs)
+    kp = np.zeros((2 * n, hkv, bs, d), dtype=np.uint16)
+    vp = np.zeros((2 * n, hkv, d, bs), dtype=np.uint16)
+    local = np.stack([np.arange(n), np.arange(n, 2 * n)], axis=1).astype(np.int32)
+    reps, elapsed = 0, 0.0
+    while elapsed < budget_s:
+        t0 = time.perf_counter()
+        oracle.copy_blocks(kp, vp, local, "bhrd", "bhdr")
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * n / elapsed, "unit": "block pairs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} copies of {n} block pairs (K and V, {hkv} heads) on host pools, "
+                      f"{elapsed:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -296,19 +406,23 @@ def calibrate_copy(pa, torch, np, case, alloc):
 # the other rows of the path, each on its own workload
 
 
-def row_gqa(pa, wl, torch, np, reps):
+def row_gqa(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.GQA
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
     r = decode_row(pa, torch, case, reps)
+    if cpu_budget > 0:
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     r["workload"] = ("gqa decode: 128 seqs, ctx round(lognormal(ln 1024, 1)) clipped "
                      "[16, 8192], 32 q / 8 kv heads, head_dim 128, block 16, bf16")
     return r
 
 
-def row_long(pa, wl, torch, np, reps):
+def row_long(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.MIXED_DECODE
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
     r = decode_row(pa, torch, case, reps, ps=sh.partition_size)
+    if cpu_budget > 0:
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     r["workload"] = ("long-context split-K decode: 8 seqs x 32768 tokens, block 128, "
                      "partitions of 512, 32 q / 8 kv heads, head_dim 128, bf16")
     return r
@@ -342,7 +456,7 @@ def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=
             "bound": "hbm"}
 
 
-def row_prefix_shared(pa, wl, torch, np, reps):
+def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     """16 prompts x 8 samples sharing the prompt's blocks; 112 copy-on-writes
     of the partial shared block before the tails are written."""
     sh = wl.PREFIX_SHARED
@@ -413,14 +527,20 @@ def row_prefix_shared(pa, wl, torch, np, reps):
     r["frac_unique_of_8TBps"] = r["GBps_unique"] / PEAK_HBM_GBPS
     r["workload"] = ("prefix-shared decode: 16 prompts of 2048+j tokens x 8 samples sharing "
                      "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16")
+    if cpu_budget > 0:
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     cow = {"us": copy_med * 1e3, "pairs": int(len(pairs)), "bytes_moved": copy_bytes,
            "GBps": copy_bytes / (copy_med * 1e-3) / 1e9, "bound": "latency (256 KiB per pair)",
            "host_append_us": append_us,
            "workload": "copy-on-write of the 112 shared partial blocks (K+V, 32 heads)"}
+    cow["gpu_block_pairs_per_s"] = len(pairs) / (copy_med * 1e-3)
+    if cpu_budget > 0:
+        cow["cpu_oracle"] = cpu_copy_row(pairs, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                                         cpu_budget)
     return r, cow
 
 
-def row_mixed(pa, wl, torch, np, reps):
+def row_mixed(pa, wl, torch, np, reps, cpu_budget):
     """Mixed step: 8 decode sequences at 32768 tokens and 4 prompt chunks of
     512 new tokens over 4096 cached, one cache write for all 2056 new rows."""
     dev = "cuda"
@@ -489,6 +609,14 @@ def row_mixed(pa, wl, torch, np, reps):
                    "GBps": cw_bytes / (cw_med * 1e-3) / 1e9, "bound": "latency",
                    "workload": "cache write of 8 decode + 2048 prompt-chunk tokens, 8 kv heads, "
                                "head_dim 128, block 128, bf16"}
+    prefill["gpu_query_rows_per_s"] = 2048 / (pre_med * 1e-3)
+    cache_write["gpu_tokens_per_s"] = len(slots) / (cw_med * 1e-3)
+    if cpu_budget > 0:
+        torch.cuda.synchronize()
+        prefill["cpu_oracle"] = cpu_prefill_row(qp, k_pool, v_pool, pt.cpu().numpy(),
+                                                cu.cpu().numpy(), pl.cpu().numpy(), psh.scale,
+                                                bs, cpu_budget)
+        cache_write["cpu_oracle"] = cpu_cache_write_row(kn, vn, slots, hkv, d, bs, cpu_budget)
     mixed = {"us": step_med * 1e3,
              "workload": "cache write (2056 tokens) + decode 8 x 32768 (split-K 512) + "
                          "prefill 4 x 512 over 4096, one stream"}
@@ -604,6 +732,8 @@ def main():
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--rows", type=int, default=1, help="1: also measure the other rows")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per row")
+    ap.add_argument("--row-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle time per row beside its GPU time (0 = skip)")
     ap.add_argument("--calibrate", action="store_true",
                     help="add one block copy of known size for the counter runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -681,6 +811,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
+    alloc_case = wl.DecodeCase(case.shape, case.lengths, case.perm, None, None, None, None,
+                               case.k_axes, case.v_axes)
     del case
     torch.cuda.empty_cache()
 
@@ -688,29 +820,32 @@ def main():
         rows = {}
         log("bench: row gqa")
         mark_phase(torch)
-        rows["decode_gqa"] = row_gqa(pa, wl, torch, np, args.reps)
+        rows["decode_gqa"] = row_gqa(pa, wl, torch, np, args.reps, args.row_cpu_budget)
         torch.cuda.empty_cache()
         log("bench: row prefix-shared")
         mark_phase(torch)
         rows["decode_prefix_shared"], rows["copy_blocks_cow"] = row_prefix_shared(
-            pa, wl, torch, np, args.reps)
+            pa, wl, torch, np, args.reps, args.row_cpu_budget)
         torch.cuda.empty_cache()
         log("bench: row long-context split-K")
         mark_phase(torch)
-        rows["decode_long_splitk"] = row_long(pa, wl, torch, np, args.reps)
+        rows["decode_long_splitk"] = row_long(pa, wl, torch, np, args.reps, args.row_cpu_budget)
         torch.cuda.empty_cache()
         log("bench: row mixed step")
         mark_phase(torch)
         rows["prefill_chunk"], rows["cache_write"], rows["mixed_step"] = row_mixed(
-            pa, wl, torch, np, args.reps)
+            pa, wl, torch, np, args.reps, args.row_cpu_budget)
         rows["allocator"] = {"host_us_per_step": h["alloc_us"],
                              "workload": "batch append of one token to 64 sequences + dense "
                                          "tables [64][stride] (host, C ABI)"}
+        if args.row_cpu_budget > 0:
+            rows["allocator"]["cpu_oracle"] = cpu_allocator_row(alloc_case, 20)
         result["rows"] = rows
         for k, v in rows.items():
-            log(f"bench: {k}: " + ", ".join(f"{a}={b:.4g}" if isinstance(b, float) else
-                                            f"{a}={b}" for a, b in v.items()
-                                            if a != "workload"))
+            log(f"bench: {k}: " + ", ".join(
+                f"{a}={b:.4g}" if isinstance(b, float) else
+                (f"{a}={b['value']:.4g} {b['unit']}" if isinstance(b, dict) else f"{a}={b}")
+                for a, b in v.items() if a != "workload"))
     print(json.dumps(result), flush=True)
 
 
