@@ -153,7 +153,6 @@ template <int D, int BS, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
     DecodeParams p) {
     const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
-    const int part = item.part;
     const int kvh = item.kvh;
     const int s = item.seq;
     const int lane = threadIdx.x;
@@ -163,7 +162,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int32_t nb = (L + BS - 1) / BS;
     const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
     const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-    if (part >= np) return;
+    const int part = decode_partition(item.slot, np, p.np_max);
+    if (part < 0) return;
 
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h = kvh * G + n;  // this lane's query head (live when n < G)

@@ -53,7 +53,6 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     constexpr int DPL = D / 64;          // dims per lane in P V
     const int BS = p.block_size;
     const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
-    const int part = item.part;
     const int kvh = item.kvh;
     const int s = item.seq;
     const int lane = threadIdx.x;
@@ -63,7 +62,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     const int32_t nb = (L + BS - 1) / BS;
     const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
     const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-    if (part >= np) return;
+    const int part = decode_partition(item.slot, np, p.np_max);
+    if (part < 0) return;
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h0 = kvh * G;
     const float qnan = __builtin_nanf("");

@@ -99,19 +99,26 @@ __device__ __forceinline__ int kslot_dim(int ks, int g) {
 }
 
 // Work item of one decode workgroup.  The grid is 1-D over
-// kv_head (fastest) x sequence x partition (slowest).  Consecutive
-// workgroups go to the eight XCDs in turn, so with the kv head fastest each
-// XCD receives the same share of heads of every sequence and partition --
-// equal work per XCD whatever the length mix -- and the first partitions of
-// all sequences are dispatched before the later, partly empty ones.
+// kv_head (fastest) x sequence x slot (slowest).  Consecutive workgroups go
+// to the eight XCDs in turn, so with the kv head fastest each XCD receives
+// the same share of heads of every sequence and slot -- equal work per XCD
+// whatever the length mix.  Slots count partitions back from the end of a
+// sequence: the last slot holds every sequence's final, usually partial,
+// partition, so the shortest work is dispatched last and the kernel drains
+// with short waves (decode_partition() turns a slot into a partition).
 struct DecodeItem {
-    int kvh, seq, part;
+    int kvh, seq, slot;
 };
 __device__ __forceinline__ DecodeItem decode_item(int num_kv_heads, int num_seqs) {
     const uint32_t i = blockIdx.x;
     const uint32_t rest = i / (uint32_t)num_kv_heads;
     return DecodeItem{(int)(i - rest * (uint32_t)num_kv_heads),
                       (int)(rest % (uint32_t)num_seqs), (int)(rest / (uint32_t)num_seqs)};
+}
+// Partition of a slot for a sequence with np of at most np_max partitions;
+// negative when the sequence has no partition in that slot.
+__device__ __forceinline__ int decode_partition(int slot, int np, int np_max) {
+    return np - np_max + slot;
 }
 
 }  // namespace pa
