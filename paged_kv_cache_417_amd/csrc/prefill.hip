@@ -65,9 +65,12 @@ struct Stage {
 // Global -> registers for keys t0 .. t0+31, whose blocks are bidA (keys
 // t0 .. t0+15) and bidB (keys t0+16 .. t0+31; the same block unless
 // BS == 16).  The step's base addresses are wave-uniform; each thread adds a
-// fixed offset.  Keys at or past nkeys are not read (K and V get zeros), so
-// a masked key contributes exactly nothing; only the last step of a
-// workgroup checks this.
+// fixed offset.  Every call issues the same loads with no branch, so the
+// compiler can wait for one stage while the next is in flight: a K row or V
+// chunk that lies wholly at or past nkeys is read from the tile's first key
+// instead (t0 < nkeys always).  Such keys sit past every position of the
+// workgroup, so the causal mask drops their scores and stage_store zeroes
+// their V elements: they contribute exactly nothing.
 template <int D, int BS>
 __device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p, int kvh,
                                            int32_t t0, int32_t nkeys, int32_t bidA,
@@ -80,32 +83,30 @@ __device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams
     const uint16_t *kB = kc + ((bidB * hkv + kvh) * BS + rowB) * D;
     const uint16_t *vA = vc + (bidA * hkv + kvh) * (int64_t)D * BS + rowA;
     const uint16_t *vB = vc + (bidB * hkv + kvh) * (int64_t)D * BS + rowB;
-    const bool full = t0 + kTile <= nkeys;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int32_t nvalid = nkeys - t0;  // keys of the tile that exist, >= 1
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         // K: D/8 chunks of 16 bytes per key
-        const int kk = idx / (D / 8), ch = idx % (D / 8);
+        int kk = idx / (D / 8);
+        const int ch = idx % (D / 8);
+        if (kk >= nvalid) kk = 0;
         const bool k_in_b = BS == 16 && kk >= 16;
         const uint16_t *kp = (k_in_b ? kB : kA) + (k_in_b ? kk - 16 : kk) * D + ch * 8;
         // V^T: 4 chunks of 8 keys per dim
-        const int dim = idx >> 2, cv = idx & 3;
+        const int dim = idx >> 2;
+        int cv = idx & 3;
+        if (8 * cv >= nvalid) cv = 0;
         const bool v_in_b = BS == 16 && cv >= 2;
         const uint16_t *vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cv - 2 : cv);
-        if (full) {
-            st.k[ps] = ld16(kp);
-            st.v[ps] = ld16(vp);
-        } else {
-            st.k[ps] = t0 + kk < nkeys ? ld16(kp) : zero;
-            st.v[ps] = t0 + 8 * cv < nkeys ? ld16(vp) : zero;  // partial chunk: stage_store
-        }
+        st.k[ps] = ld16(kp);
+        st.v[ps] = ld16(vp);
     }
 }
 
-// Registers -> LDS.  On the last step (TAIL) a V chunk that straddles nkeys
-// has its keys from nkeys on cleared here rather than right after its load,
-// so the loads of a step never wait before the previous step's math.
+// Registers -> LDS.  On the last step (TAIL) the V elements of keys at or
+// past nkeys are cleared here rather than right after their load, so the
+// loads of a step never wait before the previous step's math.
 template <int D, int BS, bool TAIL>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D, BS> &st,
                                             int tid, int32_t t0, int32_t nkeys) {
@@ -233,6 +234,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         if (j - win >= 64) {
             win = j;
             tbl = win + lane < nblk ? table[win + lane] : 0;
+            // Wait on this path only (vmcnt(0)): the window is then never
+            // pending where the paths join, so the steps in between keep
+            // their loads in flight across the readlanes below.
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         int32_t b = __builtin_amdgcn_readlane(tbl, j - win);
         if ((uint32_t)b >= (uint32_t)p.num_blocks) {
@@ -247,25 +252,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         stage_load<D, BS>(st, p, kvh, t0, nkeys, bA, bB, tid);
     };
 
-    Stage<D, BS> st;
-    stage(st, 0);
+    // Two register stages: while step it computes from LDS, the loads of
+    // step it + 2 are in flight and those of step it + 1 (issued one step
+    // earlier) are stored to the other LDS buffer at the end of the step, so
+    // a load has two steps of math to arrive.
+    const int32_t ntiles = (nkeys + kTile - 1) / kTile;
+    const int32_t last_t0 = (ntiles - 1) * kTile;
+    Stage<D, BS> stA, stB;
+    stage(stA, 0);
+    stage(stB, min(kTile, last_t0));  // a tile past the end re-reads the last one, unused
     if (kTile <= nkeys)
-        stage_store<D, BS, false>(sm, 0, st, tid, 0, nkeys);
+        stage_store<D, BS, false>(sm, 0, stA, tid, 0, nkeys);
     else
-        stage_store<D, BS, true>(sm, 0, st, tid, 0, nkeys);
+        stage_store<D, BS, true>(sm, 0, stA, tid, 0, nkeys);
     __syncthreads();
 
     // One 32-key step.  MASK: some column of the workgroup may sit before
     // a key of the step (causal mask needed).  Steps ending at or before the
     // workgroup's first position need no mask for any column; they run a
     // body compiled without it.
-    const int32_t ntiles = (nkeys + kTile - 1) / kTile;
-    auto step = [&](int32_t it, auto mask_tag) {
+    // cur holds step it + 1's loads, nxt receives step it + 2's.
+    auto step = [&](int32_t it, auto mask_tag, Stage<D, BS> &cur, Stage<D, BS> &nxt) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = it & 1;
         const int32_t t0 = it * kTile;
         const bool more = it + 1 < ntiles;
-        if (more) stage(st, t0 + kTile);
+        stage(nxt, min(t0 + 2 * kTile, last_t0));  // past the end: re-read, never stored
 
         if (wave_maxpos >= t0) {
             u32x4 ka[D / 32], kb[D / 32];
@@ -292,21 +304,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                     sr[4 + i] = sb[i];
                 }
                 bool vis[8];
-                float mr = kNegInf;
+                float mr = kNegInf;  // this lane's largest visible score
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     vis[i] = !MASK || t0 + 8 * g + i <= pos[ct];
                     mr = fmaxf(mr, vis[i] ? sr[i] : kNegInf);
                 }
-                mr = rows4_max(mr);
-                const float mx = mr == kNegInf ? kNegInf : mr * sc;
-                // Lazy rescaling: the exponent base m[ct] moves only when the
-                // column's max grows by more than kRescaleMargin (log2
-                // units), so weights stay below 2^kRescaleMargin and the
-                // accumulators are rescaled on few steps.  The test is
-                // wave-uniform.
-                const float m_new = fmaxf(m[ct], mx);
-                if (__any(m_new > m[ct] + kRescaleMargin)) {
+                // Lazy rescaling: the exponent base m[ct] moves only when a
+                // weight of the step would reach 2^kRescaleMargin, so the
+                // accumulators are rescaled on few steps.  The test needs no
+                // cross-lane max: if no lane's own max passes the bound,
+                // every weight of the column stays below it.  When some
+                // lane's does (a wave-uniform branch), the exact column max
+                // becomes the new base of every column.
+                if (__any(mr * sc > m[ct] + kRescaleMargin)) {
+                    const float cm = rows4_max(mr);
+                    const float mx = cm == kNegInf ? kNegInf : cm * sc;
+                    const float m_new = fmaxf(m[ct], mx);
                     const float f = m_new == kNegInf ? 1.f : fast_exp2(m[ct] - m_new);
                     l[ct] *= f;
 #pragma unroll
@@ -319,17 +333,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 // P = hi + lo: hi keeps the top 16 bits of each fp32 weight
                 // (a bf16 value), lo = P - hi is exact in fp32 and rounded to
                 // bf16, so P enters the bf16 products with ~16 bits.
-                float sum = 0.f;
+                float pv[8];
                 uint32_t hb[8];
                 float lo[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float arg = fmaf(sr[i], sc, -msub);
-                    const float pv = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
-                    sum += pv;
-                    hb[i] = __float_as_uint(pv);
-                    lo[i] = pv - __uint_as_float(hb[i] & 0xffff0000u);
+                    pv[i] = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
+                    hb[i] = __float_as_uint(pv[i]);
+                    lo[i] = pv[i] - __uint_as_float(hb[i] & 0xffff0000u);
                 }
+                const float sum =
+                    ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
                 u32x4 hw, lw;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -356,17 +371,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         if (more) {
             if (t0 + 2 * kTile <= nkeys)
-                stage_store<D, BS, false>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
+                stage_store<D, BS, false>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
             else
-                stage_store<D, BS, true>(sm, buf ^ 1, st, tid, t0 + kTile, nkeys);
+                stage_store<D, BS, true>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
         }
         __syncthreads();
     };
+    // Even steps find step it + 1 in stB, odd steps in stA.  The loop runs
+    // steps in pairs so each body names its stages at compile time: the two
+    // are never copied into each other or selected at run time, and each
+    // wait covers one stage's loads.  The unmasked run is cut to an even
+    // length; a step it leaves over runs with the mask, which is exact.
     const int32_t wg_minpos = base_pos + i_begin;  // first position of the workgroup's rows
-    const int32_t nomask = min(ntiles, (wg_minpos + 1) / kTile);
+    const int32_t nomask = min(ntiles, (wg_minpos + 1) / kTile) & ~1;
     int32_t it = 0;
-    for (; it < nomask; ++it) step(it, std::false_type{});
-    for (; it < ntiles; ++it) step(it, std::true_type{});
+    for (; it < nomask; it += 2) {
+        step(it, std::false_type{}, stB, stA);
+        step(it + 1, std::false_type{}, stA, stB);
+    }
+    for (; it < ntiles; it += 2) {
+        step(it, std::true_type{}, stB, stA);
+        if (it + 1 < ntiles) step(it + 1, std::true_type{}, stA, stB);
+    }
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     const float qnan = __builtin_nanf("");
