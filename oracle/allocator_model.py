@@ -31,6 +31,33 @@ Semantics (identical in the C++ allocator):
   * ``free(seq)``: every block of the sequence loses one reference; blocks that
     reach zero are pushed back, last table entry first, so the sequence's first
     block is the next one handed out.
+
+Prefix cache (the pages: [VI] §2.1 allocation first reuses blocks that can be
+shared with the request's prefix before taking free ones, keeps per-block
+state free / allocated / shareable, and moves cold blocks out under an LRU
+policy; [VI] §3 a switch that turns prompt sharing on; [NV] practical advice,
+the prefix-cache hit rate as a serving metric).  The pages fix no key or
+eviction rule; the reading taken here:
+  * A block is registered once all its positions were appended with token
+    ids (``append_tokens``) along an unbroken chain from position 0.  Its key
+    is ``(parent, tokens of the block)``, where ``parent`` is the physical
+    block of the previous logical block (-1 for the first).  Since the
+    parent's own key names everything before it, a key names the whole prefix
+    exactly.  A key that is already registered is not registered again; the
+    sequence's chain stops there.  ``append`` (no token ids) stops the chain.
+  * ``create_prefix(seq, tokens, max_cached)``: looks up the full blocks of
+    ``tokens`` in order, at most ``max_cached // BS`` of them, and stops at the
+    first miss.  Every hit joins the new sequence's table with one more
+    reference; the length becomes ``hits * BS``.  Counters: every full block
+    of ``tokens`` is queried, hits are counted.
+  * Released blocks whose key is registered are not pushed on the free stack
+    but appended to an LRU queue (they keep their contents for later hits);
+    a hit on a queued block takes it out of the queue.
+  * Taking a block pops the free stack; when it is empty, the oldest queued
+    block is taken.  If that block is registered it is evicted: its key and
+    the keys of all its registered descendants are dropped (their holders all
+    hold it, so they are queued too; they stay in the queue, unregistered).
+    Free blocks = stack + queue.
 """
 from __future__ import annotations
 
@@ -53,13 +80,39 @@ class AllocatorModel:
         self.tables: dict[int, list[int]] = {}
         self.lengths: dict[int, int] = {}
         self.cow_copies = 0
+        # prefix cache
+        self.keys: dict[tuple, int] = {}          # (parent, tokens) -> block
+        self.key_of: dict[int, tuple] = {}        # block -> its key
+        self.children: dict[int, list[int]] = {}  # block -> registered children
+        self.lru: list[int] = []                  # released cached blocks, oldest first
+        self.chain: dict[int, bool] = {}          # seq -> every position has token ids
+        self.pending: dict[int, list[int]] = {}   # seq -> tokens of its partial block
+        self.parent: dict[int, int] = {}          # seq -> block of its last full block
+        self.queried_blocks = 0
+        self.hit_blocks = 0
 
     # -- helpers -----------------------------------------------------------
     def _take(self) -> int:
-        b = self.stack.pop()
+        if self.stack:
+            b = self.stack.pop()
+        else:
+            b = self.lru.pop(0)
+            if b in self.key_of:
+                self._unregister(b)
         assert self.refcount[b] == 0
         self.refcount[b] = 1
         return b
+
+    def _unregister(self, b: int, parent_going: bool = False) -> None:
+        for c in self.children.pop(b, []):
+            self._unregister(c, parent_going=True)
+        key = self.key_of.pop(b)
+        del self.keys[key]
+        if key[0] >= 0 and not parent_going:
+            self.children[key[0]].remove(b)
+
+    def _num_free(self) -> int:
+        return len(self.stack) + len(self.lru)
 
     @staticmethod
     def blocks_for(num_tokens: int, block_size: int) -> int:
@@ -71,6 +124,35 @@ class AllocatorModel:
             raise KeyError(f"sequence {seq} exists")
         self.tables[seq] = []
         self.lengths[seq] = 0
+        self.chain[seq] = True
+        self.pending[seq] = []
+        self.parent[seq] = -1
+
+    def create_prefix(self, seq: int, tokens, max_cached: int) -> int:
+        """New sequence starting with the cached blocks of ``tokens``;
+        returns the number of cached positions."""
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} exists")
+        bs = self.block_size
+        tokens = [int(t) for t in tokens]
+        self.queried_blocks += len(tokens) // bs
+        table, parent = [], -1
+        for j in range(min(len(tokens), max(max_cached, 0)) // bs):
+            b = self.keys.get((parent, tuple(tokens[j * bs:(j + 1) * bs])))
+            if b is None:
+                break
+            if self.refcount[b] == 0:
+                self.lru.remove(b)
+            self.refcount[b] += 1
+            table.append(b)
+            parent = b
+        self.hit_blocks += len(table)
+        self.tables[seq] = table
+        self.lengths[seq] = len(table) * bs
+        self.chain[seq] = True
+        self.pending[seq] = []
+        self.parent[seq] = parent
+        return len(table) * bs
 
     def fork(self, parent: int, child: int) -> None:
         if parent not in self.tables:
@@ -79,6 +161,9 @@ class AllocatorModel:
             raise KeyError(child)
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
+        self.chain[child] = self.chain[parent]
+        self.pending[child] = list(self.pending[parent])
+        self.parent[child] = self.parent[parent]
         for b in self.tables[child]:
             self.refcount[b] += 1
 
@@ -89,14 +174,18 @@ class AllocatorModel:
         cow = n > 0 and length % bs != 0 and self.refcount[table[-1]] > 1
         return fresh + (1 if cow else 0), cow
 
-    def append(self, seq: int, n: int):
+    def append(self, seq: int, n: int, tokens=None):
+        """Append n positions (with their token ids when ``tokens`` is given:
+        see the prefix cache above)."""
         if seq not in self.tables:
             raise LookupError(seq)
         if n < 0:
             raise ValueError(n)
+        if tokens is not None and len(tokens) != n:
+            raise ValueError("len(tokens) != n")
         need, cow = self.needed_blocks(seq, n)
-        if need > len(self.stack):
-            raise OutOfBlocks(f"need {need} blocks, {len(self.stack)} free")
+        if need > self._num_free():
+            raise OutOfBlocks(f"need {need} blocks, {self._num_free()} free")
         table = self.tables[seq]
         bs = self.block_size
         pairs = []
@@ -109,13 +198,32 @@ class AllocatorModel:
             self.cow_copies += 1
         slots = []
         length = self.lengths[seq]
+        if tokens is None and n > 0:
+            self.chain[seq] = False
+            self.pending[seq] = []
         for i in range(n):
             pos = length + i
             if pos % bs == 0:
                 table.append(self._take())
             slots.append(table[pos // bs] * bs + pos % bs)
+            if tokens is not None and self.chain[seq]:
+                self.pending[seq].append(int(tokens[i]))
+                if pos % bs == bs - 1:
+                    self._register(seq, table[pos // bs])
         self.lengths[seq] = length + n
         return slots, pairs
+
+    def _register(self, seq: int, b: int) -> None:
+        key = (self.parent[seq], tuple(self.pending[seq]))
+        self.pending[seq] = []
+        if key in self.keys:
+            self.chain[seq] = False
+            return
+        self.keys[key] = b
+        self.key_of[b] = key
+        if key[0] >= 0:
+            self.children.setdefault(key[0], []).append(b)
+        self.parent[seq] = b
 
     def free(self, seq: int) -> None:
         if seq not in self.tables:
@@ -123,16 +231,27 @@ class AllocatorModel:
         for b in reversed(self.tables[seq]):
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
-                self.stack.append(b)
-        del self.tables[seq]
-        del self.lengths[seq]
+                if b in self.key_of:
+                    self.lru.append(b)
+                else:
+                    self.stack.append(b)
+        for d in (self.tables, self.lengths, self.chain, self.pending, self.parent):
+            del d[seq]
 
     # -- queries -------------------------------------------------------------
     def stats(self) -> dict:
         return {
             "num_blocks": self.num_blocks,
-            "num_free": len(self.stack),
-            "num_used": self.num_blocks - len(self.stack),
+            "num_free": self._num_free(),
+            "num_used": self.num_blocks - self._num_free(),
             "num_shared": sum(1 for r in self.refcount if r > 1),
             "cow_copies": self.cow_copies,
+        }
+
+    def prefix_stats(self) -> dict:
+        return {
+            "queried_blocks": self.queried_blocks,
+            "hit_blocks": self.hit_blocks,
+            "cached_blocks": len(self.keys),
+            "cached_free_blocks": sum(1 for b in self.lru if b in self.key_of),
         }

@@ -144,3 +144,142 @@ def test_random_ops_conserve_references():
         st = a.stats()
         assert st["num_free"] + st["num_used"] == 64
         assert st["num_free"] == sum(1 for r in a.refcount if r == 0)
+
+
+# -- prefix cache -------------------------------------------------------------
+# [VI] §2.1: allocation first reuses blocks shareable with the request's prefix,
+# then takes free ones; cold blocks leave under an LRU policy.  [NV] practical
+# advice: the prefix-cache hit rate is the metric to watch.  The expected tables
+# below are worked out by hand from that reading (keys = (parent block, tokens)).
+
+def _prompt(a, seq, tokens, max_cached=None):
+    """Serve a prompt the way a scheduler would: reuse, then append the rest."""
+    n = a.create_prefix(seq, tokens, len(tokens) if max_cached is None else max_cached)
+    slots, pairs = a.append(seq, len(tokens) - n, tokens=tokens[n:])
+    return n, slots, pairs
+
+
+def test_prefix_hit_shares_full_blocks_only():
+    a = AllocatorModel(16, 4)  # blocks handed out 0, 1, 2, ...
+    n, slots, _ = _prompt(a, 1, list(range(10)))       # blocks 0, 1 full, 2 partial
+    assert n == 0 and a.tables[1] == [0, 1, 2]
+    n, slots, _ = _prompt(a, 2, list(range(9)) + [99])  # same first 8 tokens
+    assert n == 8 and a.tables[2] == [0, 1, 3]
+    assert slots == [12, 13]                          # positions 8, 9 in block 3
+    assert a.refcount[:4] == [2, 2, 1, 1]
+    assert a.prefix_stats() == {"queried_blocks": 4, "hit_blocks": 2, "cached_blocks": 2,
+                                "cached_free_blocks": 0}
+
+
+def test_prefix_key_covers_the_whole_prefix():
+    a = AllocatorModel(16, 4)
+    _prompt(a, 1, [1, 2, 3, 4, 5, 6, 7, 8])
+    # same second block, different first block: no hit at all
+    n, _, _ = _prompt(a, 2, [9, 9, 9, 9, 5, 6, 7, 8])
+    assert n == 0 and a.tables[2] == [2, 3]
+
+
+def test_max_cached_leaves_positions_to_compute():
+    a = AllocatorModel(16, 4)
+    _prompt(a, 1, list(range(8)))
+    n, slots, _ = _prompt(a, 2, list(range(8)), max_cached=7)
+    assert n == 4 and a.tables[2] == [0, 2]  # block 1's twin not re-registered
+    assert slots == [8, 9, 10, 11]
+    assert a.key_of.get(2) is None
+
+
+def test_released_blocks_stay_cached_and_are_revived():
+    a = AllocatorModel(8, 4)
+    _prompt(a, 1, list(range(12)))  # blocks 0, 1, 2 registered
+    a.free(1)
+    assert a.stack == [7, 6, 5, 4, 3] and a.lru == [2, 1, 0]
+    assert a.stats()["num_free"] == 8
+    n, _, _ = _prompt(a, 2, list(range(8)) + [50, 51])
+    assert n == 8 and a.tables[2] == [0, 1, 3]  # revived 0, 1; new block from the stack
+    assert a.lru == [2] and a.refcount[:4] == [1, 1, 0, 1]
+
+
+def test_eviction_takes_oldest_and_drops_descendants():
+    a = AllocatorModel(4, 2)
+    _prompt(a, 1, [1, 2, 3, 4])   # blocks 0 <- 1 (1's parent is 0)
+    _prompt(a, 2, [7, 7])         # block 2
+    a.free(2)                     # lru: [2]
+    a.free(1)                     # lru: [2, 1, 0]
+    assert a.lru == [2, 1, 0]
+    _prompt(a, 3, [5, 5, 6, 6])   # needs 2 blocks: 3 from the stack, then evicts 2
+    assert a.tables[3] == [3, 2] and a.lru == [1, 0]
+    _prompt(a, 4, [8, 8])         # evicts 1 (child of 0): 0 keeps its key
+    assert a.tables[4] == [1]
+    assert (-1, (1, 2)) in a.keys and (0, (3, 4)) not in a.keys
+    a.free(4)                     # block 1 ([8, 8]) queued
+    n, _, _ = _prompt(a, 5, [1, 2, 3, 4])  # only the first block hits now
+    assert n == 2 and a.tables[5] == [0, 1]  # 1 evicted again for the second block
+    assert a.keys[(0, (3, 4))] == 1 and (-1, (8, 8)) not in a.keys
+
+
+def test_evicting_a_parent_drops_its_queued_children():
+    a = AllocatorModel(3, 2)
+    _prompt(a, 1, [1, 1, 2, 2])   # 0 <- 1
+    a.free(1)                     # pushed last entry first: lru [1, 0]
+    a.lru = [0, 1]                # reorder by hand: the parent is now the oldest
+    _prompt(a, 2, [9, 9])         # takes 2 from the stack
+    _prompt(a, 3, [8, 8])         # evicts 0, which drops child 1's key too
+    assert a.tables[3] == [0] and a.keys == {(-1, (9, 9)): 2, (-1, (8, 8)): 0}
+    assert a.lru == [1] and 1 not in a.key_of
+
+
+def test_plain_append_stops_the_chain():
+    a = AllocatorModel(16, 4)
+    a.create(1)
+    a.append(1, 2)                           # no token ids
+    a.append(1, 6, tokens=[1, 2, 3, 4, 5, 6])
+    assert a.keys == {}
+    assert _prompt(a, 2, [1, 2, 3, 4])[0] == 0
+
+
+def test_fork_continues_the_chain_and_duplicates_are_not_registered():
+    a = AllocatorModel(16, 4)
+    _prompt(a, 1, [1, 2, 3, 4, 5, 6])        # block 0 registered, 1 partial
+    a.fork(1, 2)
+    a.append(1, 2, tokens=[7, 8])            # 1 fills block 1: COW? no, 2 shares it
+    a.append(2, 2, tokens=[7, 8])            # the twin fills its own copy
+    k = (0, (5, 6, 7, 8))
+    assert a.keys[k] in a.tables[1] and a.key_of.get(a.tables[2][1]) is None
+    assert not a.chain[2] and a.chain[1]
+
+
+def test_random_prefix_ops_keep_invariants():
+    rng = np.random.default_rng(11)
+    a = AllocatorModel(24, 2)
+    live, nxt = [], 0
+    vocab = [[1, 2, 3, 4, 5, 6], [1, 2, 3, 4, 7, 7], [9, 9, 1, 2], [1, 2]]
+    for _ in range(400):
+        op = int(rng.integers(4))
+        try:
+            if op == 0 or not live:
+                toks = list(vocab[int(rng.integers(len(vocab)))]) + [int(rng.integers(3))]
+                live.append(nxt)
+                nxt += 1
+                _prompt(a, live[-1], toks, max_cached=len(toks) - 1)
+            elif op == 1:
+                sid = live[int(rng.integers(len(live)))]
+                k = int(rng.integers(1, 4))
+                a.append(sid, k, tokens=[int(x) for x in rng.integers(0, 3, k)])
+            elif op == 2:
+                a.fork(live[int(rng.integers(len(live)))], nxt)
+                live.append(nxt)
+                nxt += 1
+            else:
+                a.free(live.pop(int(rng.integers(len(live)))))
+        except OutOfBlocks:
+            pass
+        held = [b for t in a.tables.values() for b in t]
+        assert sum(a.refcount) == len(held)
+        assert sorted(a.stack + a.lru + sorted(set(held))) == list(range(24))
+        for key, b in a.keys.items():
+            assert a.key_of[b] == key
+            assert a.refcount[b] > 0 or b in a.lru
+            if key[0] >= 0:
+                assert key[0] in a.key_of and b in a.children[key[0]]
+                # every holder of a block holds its parent
+                assert a.refcount[key[0]] >= a.refcount[b]
