@@ -226,6 +226,53 @@ def cpu_allocator_row(case, steps):
             "sample": f"{steps} steps of 64 appends + tables on the Python reference model"}
 
 
+def row_prefix_cache(pa, wl, np, cpu_budget):
+    """Prefix cache on the chat workload: 128 requests opening with one of 16
+    shared system prompts (2049..2063 tokens) plus 16..512 user tokens, block
+    16, a 200,000-block shuffled pool.  Each request is admitted the way a
+    scheduler would: reuse the cached full blocks of its prompt (leaving the
+    last position to compute), then append the rest with token ids.  Host
+    only: the kernels see ordinary block tables."""
+    plan = wl.chat_plan()
+    bs, nb = 16, 200_000
+    order = np.random.default_rng(wl.SEED_BASE + 6).permutation(nb)
+    prompts = [plan.prompt(r) for r in range(len(plan.user_tokens))]
+    a = pa.Allocator(nb, bs, free_order=order)
+    cached = 0
+    t0 = time.perf_counter()
+    for r, toks in enumerate(prompts):
+        n = a.create_prefix(r, toks, len(toks) - 1)
+        a.append_tokens(r, toks[n:])
+        cached += n
+    dt = time.perf_counter() - t0
+    st = a.prefix_stats()
+    total = sum(len(t) for t in prompts)
+    out = {"host_us_per_request": dt * 1e6 / len(prompts),
+           "hit_rate": st["hit_blocks"] / max(st["queried_blocks"], 1),
+           "cached_token_frac": cached / total,
+           "prefill_tokens_saved": cached, "prompt_tokens": total,
+           "cached_blocks": st["cached_blocks"],
+           "workload": "prefix cache: 128 requests over 16 shared system prompts of 2049..2063 "
+                       "tokens + 16..512 user tokens, block 16, 200000-block pool (host, C ABI)"}
+    if cpu_budget > 0:
+        from oracle.allocator_model import AllocatorModel
+        m = AllocatorModel(nb, bs, free_order=order)
+        done, t0 = 0, time.perf_counter()
+        for r, toks in enumerate(prompts):
+            toks = toks.tolist()
+            n = m.create_prefix(r, toks, len(toks) - 1)
+            m.append(r, len(toks) - n, tokens=toks[n:])
+            done += 1
+            if time.perf_counter() - t0 > cpu_budget:
+                break
+        el = time.perf_counter() - t0
+        out["cpu_oracle"] = {"value": el * 1e6 / done, "unit": "us/request", "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"first {done} of {len(prompts)} requests on the Python "
+                                       "reference model"}
+    return out
+
+
 def cpu_copy_row(pairs, hkv, d, bs, budget_s):
     """Oracle whole-block copies of the same number of pairs on host pools."""
     oracle, _, _ = _oracle_helpers()
@@ -840,6 +887,8 @@ def main():
                                          "tables [64][stride] (host, C ABI)"}
         if args.row_cpu_budget > 0:
             rows["allocator"]["cpu_oracle"] = cpu_allocator_row(alloc_case, 20)
+        log("bench: row prefix cache")
+        rows["prefix_cache"] = row_prefix_cache(pa, wl, np, args.row_cpu_budget)
         result["rows"] = rows
         for k, v in rows.items():
             log(f"bench: {k}: " + ", ".join(

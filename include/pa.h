@@ -241,7 +241,8 @@ pa_status pa_seq_append(pa_allocator *a, int64_t seq_id, int32_t n_tokens,
 
 /* Release a finished sequence: each block loses a reference; blocks that
  * reach zero go back on the free list at once ([VE] §3.1), last table entry
- * first, so the sequence's first block is handed out next. */
+ * first, so the sequence's first block is handed out next (registered
+ * prefix-cache blocks are queued instead: see the prefix cache below). */
 pa_status pa_seq_free(pa_allocator *a, int64_t seq_id);
 
 pa_status pa_seq_length(const pa_allocator *a, int64_t seq_id, int32_t *len);
@@ -273,6 +274,70 @@ pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs,
                           const int64_t *seq_ids, int32_t *tables_out,
                           int32_t stride, int32_t pad_value,
                           int32_t *context_lens_out);
+
+/* ------------------------------------------------------------------------ */
+/* Prefix cache                                                               */
+/* ------------------------------------------------------------------------ */
+/* Allocation first reuses blocks that can be shared with a request's prefix,
+ * then takes free ones; cold blocks leave under an LRU policy ([VI] §2.1,
+ * and §3's switch for prompt sharing).  The hit rate is the metric to watch
+ * ([NV] practical advice).  The pages fix no key or eviction rule; this
+ * library's:
+ *  - A block is registered once every position in it was appended with its
+ *    token id (pa_seq_append_tokens / pa_batch_append_tokens), along an
+ *    unbroken chain from position 0.  Its key is (parent, token ids), parent
+ *    being the physical block of the previous logical block (-1 for the
+ *    first); since the parent's key names everything before it, a key names
+ *    the whole prefix exactly (lookups compare the stored ids, not only a
+ *    hash).  A key already registered is not registered again, and that
+ *    ends the sequence's chain; so does any append without token ids.
+ *  - A registered block whose last reference goes is queued (oldest first)
+ *    instead of returning to the free stack, and keeps its contents.
+ *  - Taking a block pops the free stack; when it is empty, the oldest queued
+ *    block is taken, and its key and its registered descendants' keys are
+ *    dropped.  pa_allocator_stats counts stack and queue as free.
+ *  - A cached block's contents are those written by the work the caller
+ *    enqueued after the append that filled it: reuse it on the same stream,
+ *    or after that work. */
+
+typedef struct {
+    int64_t queried_blocks;     /* full prompt blocks looked up so far */
+    int64_t hit_blocks;         /* of them, found in the cache */
+    int32_t cached_blocks;      /* blocks registered now */
+    int32_t cached_free_blocks; /* of them, queued with no holder */
+} pa_prefix_stats_t;
+
+/* New sequence seq_id for a prompt of n_tokens token ids: its table starts
+ * with the cached blocks of the longest registered chain of the prompt's
+ * full blocks, at most max_cached_tokens / block_size of them (pass
+ * n_tokens - 1 to leave the last position to compute).  Each reused block
+ * gains a reference; *n_cached gets the positions covered (a multiple of
+ * block_size), which is the new sequence's length.  The caller appends the
+ * rest of the prompt with pa_seq_append_tokens.  Counts n_tokens /
+ * block_size queried blocks.  INVALID_ARG if the id exists; nothing changes
+ * on failure.
+ *   tokens [n_tokens] host. */
+pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id,
+                               const int32_t *tokens, int32_t n_tokens,
+                               int32_t max_cached_tokens, int32_t *n_cached);
+
+/* pa_seq_append with the token ids of the new positions: blocks that become
+ * full are registered (see above).  tokens [n_tokens] host. */
+pa_status pa_seq_append_tokens(pa_allocator *a, int64_t seq_id,
+                               const int32_t *tokens, int32_t n_tokens,
+                               int64_t *slots_out, int32_t *cow_pairs_out,
+                               int32_t cow_cap, int32_t *n_cow);
+
+/* pa_batch_append with token ids: tokens holds sum(n_tokens) ids, the
+ * sequences' ids back to back in batch order. */
+pa_status pa_batch_append_tokens(pa_allocator *a, int32_t num_seqs,
+                                 const int64_t *seq_ids,
+                                 const int32_t *n_tokens,
+                                 const int32_t *tokens, int64_t *slots_out,
+                                 int32_t *cow_pairs_out, int32_t cow_cap,
+                                 int32_t *n_cow);
+
+pa_status pa_prefix_cache_stats(const pa_allocator *a, pa_prefix_stats_t *out);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,8 @@ EXPORTED = (
     "pa_allocator_create",
     "pa_allocator_destroy", "pa_seq_create", "pa_seq_fork", "pa_seq_append", "pa_seq_free",
     "pa_seq_length", "pa_seq_block_table", "pa_allocator_stats", "pa_block_refcount",
-    "pa_batch_append", "pa_batch_tables",
+    "pa_batch_append", "pa_batch_tables", "pa_seq_create_prefix", "pa_seq_append_tokens",
+    "pa_batch_append_tokens", "pa_prefix_cache_stats",
 )
 
 
@@ -59,6 +60,11 @@ class AllocatorStats(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_free", ctypes.c_int32),
                 ("num_used", ctypes.c_int32), ("num_shared", ctypes.c_int32),
                 ("cow_copies", ctypes.c_int64)]
+
+
+class PrefixStats(ctypes.Structure):
+    _fields_ = [("queried_blocks", ctypes.c_int64), ("hit_blocks", ctypes.c_int64),
+                ("cached_blocks", ctypes.c_int32), ("cached_free_blocks", ctypes.c_int32)]
 
 
 def _declare(lib):
@@ -90,6 +96,10 @@ def _declare(lib):
         "pa_block_refcount": (st, [vp, i32, pi32]),
         "pa_batch_append": (st, [vp, i32, pi64, pi32, pi64, pi32, i32, pi32]),
         "pa_batch_tables": (st, [vp, i32, pi64, pi32, i32, i32, pi32]),
+        "pa_seq_create_prefix": (st, [vp, i64, pi32, i32, i32, pi32]),
+        "pa_seq_append_tokens": (st, [vp, i64, pi32, i32, pi64, pi32, i32, pi32]),
+        "pa_batch_append_tokens": (st, [vp, i32, pi64, pi32, pi32, pi64, pi32, i32, pi32]),
+        "pa_prefix_cache_stats": (st, [vp, ctypes.POINTER(PrefixStats)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -241,7 +251,7 @@ class Allocator:
         self._h = h
 
     def close(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and _lib is not None:  # _lib is None at interpreter exit
             _lib.pa_allocator_destroy(self._h)
             self._h = None
 
@@ -278,6 +288,52 @@ class Allocator:
         _check(_lib.pa_batch_append(self._h, len(ids), _i64p(ids), _i32p(nt), _i64p(slots),
                                     _i32p(pairs), pairs.shape[0], ctypes.byref(ncow)))
         return slots[:total], pairs[:ncow.value]
+
+    def create_prefix(self, seq_id: int, tokens, max_cached_tokens=None) -> int:
+        """New sequence reusing the cached blocks of the prompt ``tokens``;
+        returns the positions covered (its length)."""
+        np = self._np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        mc = len(t) if max_cached_tokens is None else int(max_cached_tokens)
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_seq_create_prefix(self._h, seq_id, _i32p(t) if len(t) else None, len(t),
+                                         mc, ctypes.byref(n)))
+        return n.value
+
+    def append_tokens(self, seq_id: int, tokens):
+        """Append positions with their token ids (full blocks get registered).
+        Returns (slots, cow_pairs)."""
+        np = self._np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.zeros(max(len(t), 1), dtype=np.int64)
+        pairs = np.zeros((1, 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pa_seq_append_tokens(self._h, seq_id, _i32p(t) if len(t) else None, len(t),
+                                         _i64p(slots), _i32p(pairs), 1, ctypes.byref(ncow)))
+        return slots[:len(t)], pairs[:ncow.value]
+
+    def batch_append_tokens(self, seq_ids, tokens_per_seq):
+        """``tokens_per_seq[i]`` is appended to ``seq_ids[i]``, all at once."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        nt = np.array([len(t) for t in tokens_per_seq], dtype=np.int32)
+        flat = np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int32)
+                                                    for t in tokens_per_seq] or
+                                                   [np.zeros(0, np.int32)]), dtype=np.int32)
+        flat = flat if len(flat) else np.zeros(1, dtype=np.int32)
+        total = int(nt.sum())
+        slots = np.zeros(max(total, 1), dtype=np.int64)
+        pairs = np.zeros((max(len(ids), 1), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_lib.pa_batch_append_tokens(self._h, len(ids), _i64p(ids), _i32p(nt),
+                                           _i32p(flat), _i64p(slots), _i32p(pairs),
+                                           pairs.shape[0], ctypes.byref(ncow)))
+        return slots[:total], pairs[:ncow.value]
+
+    def prefix_stats(self) -> dict:
+        st = PrefixStats()
+        _check(_lib.pa_prefix_cache_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in PrefixStats._fields_}
 
     def batch_tables(self, seq_ids, stride: int, pad_value: int = 0, tables_out=None,
                      lens_out=None):

@@ -8,12 +8,25 @@
 //        ceil(n / block_size) blocks per sequence; running out is an error.
 //   [VI] 《vLLM大模型推理引擎：高效解决显存碎片与请求排队难题》 §2.1 — a
 //        pre-allocated pool, per-block state, host-side block tables,
-//        copy-on-write for shared prefixes, a free list popped at its end.
+//        copy-on-write for shared prefixes, a free list popped at its end;
+//        allocation first reuses blocks shareable with the request's prefix,
+//        and cold blocks leave under an LRU policy.
+//   [NV] practical advice — the prefix-cache hit rate as a serving metric.
 //
 // State: refcount[b] per block (0 free, 1 owned, >1 shared), a free stack
 // (top = back of the vector), and per sequence its table and length.  Every
 // mutating call first works out everything it needs, checks it can be
 // satisfied, and only then commits, so a failed call changes nothing.
+//
+// Prefix cache.  A block all of whose positions were appended with token ids,
+// along an unbroken chain from position 0, is registered under the key
+// (parent, tokens): parent is the physical block of the previous logical
+// block (-1 for the first), whose own key names everything before it, so a
+// key names the whole prefix exactly.  Keys live in a hash map from a 64-bit
+// hash to blocks, and every hit is checked against the stored parent and
+// tokens.  Released registered blocks wait in an LRU queue instead of the
+// free stack; taking a block pops the stack first, then the oldest queued
+// block, whose key (and its registered descendants' keys) it drops.
 #include <algorithm>
 #include <new>
 #include <unordered_map>
@@ -27,7 +40,24 @@ namespace {
 struct Sequence {
     std::vector<int32_t> table;
     int32_t length = 0;
+    bool chain = true;             // every position so far came with a token id
+    std::vector<int32_t> pending;  // token ids of the partial last block
+    int32_t parent = -1;           // block of the last registered full block
 };
+
+// 64-bit FNV-1a over the parent id and the block's token ids.
+inline uint64_t key_hash(int32_t parent, const int32_t *tokens, int32_t n) {
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&h](uint32_t v) {
+        for (int i = 0; i < 4; ++i) {
+            h ^= (v >> (8 * i)) & 0xffu;
+            h *= 1099511628211ull;
+        }
+    };
+    mix((uint32_t)parent);
+    for (int32_t i = 0; i < n; ++i) mix((uint32_t)tokens[i]);
+    return h;
+}
 
 // Blocks needed for n tokens: ceil(n / bs).
 inline int64_t blocks_for(int64_t n, int64_t bs) { return (n + bs - 1) / bs; }
@@ -39,13 +69,135 @@ struct pa_allocator {
     int32_t block_size = 0;
     std::vector<int32_t> refcount;
     std::vector<int32_t> free_stack;
-    std::unordered_map<int64_t, Sequence> seqs;
+    std::unordered_map<int64_t, Sequence> seqs;  // pending reserved to block_size
     int64_t cow_copies = 0;
     int32_t num_shared = 0;
 
+    // prefix cache
+    std::vector<char> registered;        // per block
+    std::vector<int32_t> key_parent;     // per registered block
+    std::vector<int32_t> key_tokens;     // [num_blocks][block_size], registered blocks
+    std::vector<uint64_t> key_hashes;    // per registered block
+    std::vector<std::vector<int32_t>> children;  // registered children per block
+    std::unordered_multimap<uint64_t, int32_t> key_map;
+    // Released registered blocks, oldest first: an intrusive list over the
+    // block ids (no allocation once the arrays exist).
+    std::vector<int32_t> lru_prev, lru_next;
+    std::vector<char> in_lru;
+    int32_t lru_head = -1, lru_tail = -1;
+    size_t lru_size = 0;
+    int64_t queried_blocks = 0, hit_blocks = 0;
+    int32_t num_registered = 0;
+
+    bool cache_ready() const { return !registered.empty(); }
+    // Per-block prefix-cache arrays, sized on first use.
+    void init_cache() {
+        if (cache_ready()) return;
+        registered.assign(num_blocks, 0);
+        key_parent.assign(num_blocks, -1);
+        key_tokens.assign((size_t)num_blocks * block_size, 0);
+        key_hashes.assign(num_blocks, 0);
+        children.resize(num_blocks);
+        lru_prev.assign(num_blocks, -1);
+        lru_next.assign(num_blocks, -1);
+        in_lru.assign(num_blocks, 0);
+    }
+    size_t num_free() const { return free_stack.size() + lru_size; }
+    void lru_push_back(int32_t b) {
+        lru_prev[b] = lru_tail;
+        lru_next[b] = -1;
+        if (lru_tail >= 0) lru_next[lru_tail] = b; else lru_head = b;
+        lru_tail = b;
+        in_lru[b] = 1;
+        ++lru_size;
+    }
+    void lru_remove(int32_t b) {
+        const int32_t pv = lru_prev[b], nx = lru_next[b];
+        if (pv >= 0) lru_next[pv] = nx; else lru_head = nx;
+        if (nx >= 0) lru_prev[nx] = pv; else lru_tail = pv;
+        in_lru[b] = 0;
+        --lru_size;
+    }
+
+    int32_t lookup(int32_t parent, const int32_t *tokens) const {
+        if (!cache_ready()) return -1;
+        auto range = key_map.equal_range(key_hash(parent, tokens, block_size));
+        for (auto it = range.first; it != range.second; ++it) {
+            const int32_t b = it->second;
+            if (key_parent[b] == parent &&
+                std::equal(tokens, tokens + block_size,
+                           key_tokens.begin() + (size_t)b * block_size))
+                return b;
+        }
+        return -1;
+    }
+    // Drops the key of b and of every registered descendant (all of them are
+    // queued: whoever holds a block holds its parent).
+    void unregister_tree(int32_t top) {
+        const int32_t p = key_parent[top];
+        if (p >= 0) {
+            auto &sib = children[p];
+            sib.erase(std::find(sib.begin(), sib.end(), top));
+        }
+        std::vector<int32_t> todo{top};
+        while (!todo.empty()) {
+            const int32_t b = todo.back();
+            todo.pop_back();
+            for (int32_t c : children[b]) todo.push_back(c);
+            children[b].clear();
+            auto range = key_map.equal_range(key_hashes[b]);
+            for (auto it = range.first; it != range.second; ++it)
+                if (it->second == b) {
+                    key_map.erase(it);
+                    break;
+                }
+            registered[b] = 0;
+            key_parent[b] = -1;
+            --num_registered;
+        }
+    }
+    // Registers the just-filled block b of s under (s.parent, s.pending);
+    // a key already present, or no memory, ends the sequence's chain.
+    void register_block(Sequence &s, int32_t b) {
+        const uint64_t h = key_hash(s.parent, s.pending.data(), block_size);
+        bool ok = lookup(s.parent, s.pending.data()) < 0;
+        if (ok) {
+            try {
+                if (s.parent >= 0) children[s.parent].push_back(b);
+                try {
+                    key_map.emplace(h, b);
+                } catch (...) {
+                    if (s.parent >= 0) children[s.parent].pop_back();
+                    throw;
+                }
+            } catch (...) {
+                ok = false;
+            }
+        }
+        if (ok) {
+            registered[b] = 1;
+            key_parent[b] = s.parent;
+            key_hashes[b] = h;
+            std::copy(s.pending.begin(), s.pending.end(),
+                      key_tokens.begin() + (size_t)b * block_size);
+            ++num_registered;
+            s.parent = b;
+        } else {
+            s.chain = false;
+        }
+        s.pending.clear();
+    }
+
     int32_t take() {
-        int32_t b = free_stack.back();
-        free_stack.pop_back();
+        int32_t b;
+        if (!free_stack.empty()) {
+            b = free_stack.back();
+            free_stack.pop_back();
+        } else {
+            b = lru_head;
+            lru_remove(b);
+            if (registered[b]) unregister_tree(b);
+        }
         refcount[b] = 1;
         return b;
     }
@@ -56,6 +208,14 @@ struct pa_allocator {
     bool drop_ref(int32_t b) {
         if (refcount[b]-- == 2) --num_shared;
         return refcount[b] == 0;
+    }
+    // A block whose last reference went: queued if registered, else stacked.
+    void release(int32_t b) {
+        if (cache_ready() && registered[b]) {
+            lru_push_back(b);
+        } else {
+            free_stack.push_back(b);  // capacity is num_blocks
+        }
     }
 
     // Blocks an append of n tokens needs, and whether it starts with a COW.
@@ -70,8 +230,8 @@ struct pa_allocator {
     // decision is taken again here: an earlier append in the same batch may
     // have copied away from a block this sequence shared, leaving it the sole
     // holder, so the check-time count is an upper bound.
-    void commit_append(Sequence &s, int32_t n, int64_t *slots, int32_t *pairs,
-                       int32_t *n_pairs) {
+    void commit_append(Sequence &s, int32_t n, const int32_t *tokens, int64_t *slots,
+                       int32_t *pairs, int32_t *n_pairs) {
         int64_t unused;
         bool cow;
         needs(s, n, &unused, &cow);
@@ -87,10 +247,19 @@ struct pa_allocator {
         } else {
             *n_pairs = 0;
         }
+        if (!tokens && n > 0) {
+            s.chain = false;
+            s.pending.clear();
+        }
         for (int32_t i = 0; i < n; ++i) {
             int64_t pos = (int64_t)s.length + i;
             if (pos % block_size == 0) s.table.push_back(take());
             slots[i] = (int64_t)s.table[pos / block_size] * block_size + pos % block_size;
+            if (tokens && s.chain) {
+                s.pending.push_back(tokens[i]);  // capacity reserved by the caller
+                if (pos % block_size == block_size - 1)
+                    register_block(s, s.table[pos / block_size]);
+            }
         }
         s.length += n;
     }
@@ -169,15 +338,15 @@ pa_status pa_seq_fork(pa_allocator *a, int64_t parent, int64_t child) {
     return pa::ok();
 }
 
-pa_status pa_seq_append(pa_allocator *a, int64_t seq_id, int32_t n_tokens,
-                        int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
-                        int32_t *n_cow) {
-    return pa_batch_append(a, 1, &seq_id, &n_tokens, slots_out, cow_pairs_out, cow_cap, n_cow);
-}
+}  // extern "C"
 
-pa_status pa_batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids,
-                          const int32_t *n_tokens, int64_t *slots_out, int32_t *cow_pairs_out,
-                          int32_t cow_cap, int32_t *n_cow) {
+namespace {
+
+// Shared body of the append calls; tokens (the concatenated token ids of the
+// batch) may be NULL.
+pa_status batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids,
+                       const int32_t *n_tokens, const int32_t *tokens, int64_t *slots_out,
+                       int32_t *cow_pairs_out, int32_t cow_cap, int32_t *n_cow) {
     if (!a) return pa::fail(PA_ERR_INVALID_ARG, "append: NULL allocator");
     if (num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !n_tokens)) || !n_cow || cow_cap < 0)
         return pa::fail(PA_ERR_INVALID_ARG, "append: bad arguments");
@@ -209,15 +378,18 @@ pa_status pa_batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_
     if (total_cow > cow_cap || (total_cow > 0 && !cow_pairs_out))
         return pa::fail(PA_ERR_INVALID_ARG, "append: %lld copy-on-write pairs, cow_cap %d",
                         (long long)total_cow, cow_cap);
-    if (total_blocks > (int64_t)a->free_stack.size())
+    if (total_blocks > (int64_t)a->num_free())
         return pa::fail(PA_ERR_OUT_OF_BLOCKS, "append: need %lld blocks, %zu free",
-                        (long long)total_blocks, a->free_stack.size());
-    // Reserve table capacity before committing anything: the commit loop
-    // below then cannot fail part-way.
+                        (long long)total_blocks, a->num_free());
+    // Reserve table (and pending-token) capacity before committing anything:
+    // the commit loop below then cannot fail part-way.
     try {
-        for (int32_t i = 0; i < num_seqs; ++i)
+        if (tokens) a->init_cache();
+        for (int32_t i = 0; i < num_seqs; ++i) {
             seqs[i]->table.reserve(blocks_for((int64_t)seqs[i]->length + n_tokens[i],
                                               a->block_size));
+            if (tokens) seqs[i]->pending.reserve(a->block_size);
+        }
     } catch (...) {
         return pa::fail(PA_ERR_INVALID_ARG, "append: out of host memory");
     }
@@ -225,12 +397,105 @@ pa_status pa_batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_
     int32_t pairs = 0;
     for (int32_t i = 0; i < num_seqs; ++i) {
         int32_t np = 0;
-        a->commit_append(*seqs[i], n_tokens[i], slots_out + slot_off,
-                         cow_pairs_out ? cow_pairs_out + 2 * pairs : nullptr, &np);
+        a->commit_append(*seqs[i], n_tokens[i], tokens ? tokens + slot_off : nullptr,
+                         slots_out + slot_off, cow_pairs_out ? cow_pairs_out + 2 * pairs : nullptr,
+                         &np);
         slot_off += n_tokens[i];
         pairs += np;
     }
     *n_cow = pairs;
+    return pa::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_seq_append(pa_allocator *a, int64_t seq_id, int32_t n_tokens,
+                        int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
+                        int32_t *n_cow) {
+    return batch_append(a, 1, &seq_id, &n_tokens, nullptr, slots_out, cow_pairs_out, cow_cap,
+                        n_cow);
+}
+
+pa_status pa_batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids,
+                          const int32_t *n_tokens, int64_t *slots_out, int32_t *cow_pairs_out,
+                          int32_t cow_cap, int32_t *n_cow) {
+    return batch_append(a, num_seqs, seq_ids, n_tokens, nullptr, slots_out, cow_pairs_out,
+                        cow_cap, n_cow);
+}
+
+pa_status pa_seq_append_tokens(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                               int32_t n_tokens, int64_t *slots_out, int32_t *cow_pairs_out,
+                               int32_t cow_cap, int32_t *n_cow) {
+    if (n_tokens > 0 && !tokens)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_tokens: tokens is NULL");
+    static const int32_t kNone = 0;
+    return batch_append(a, 1, &seq_id, &n_tokens, tokens ? tokens : &kNone, slots_out,
+                        cow_pairs_out, cow_cap, n_cow);
+}
+
+pa_status pa_batch_append_tokens(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids,
+                                 const int32_t *n_tokens, const int32_t *tokens,
+                                 int64_t *slots_out, int32_t *cow_pairs_out, int32_t cow_cap,
+                                 int32_t *n_cow) {
+    if (!tokens)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_append_tokens: tokens is NULL");
+    return batch_append(a, num_seqs, seq_ids, n_tokens, tokens, slots_out, cow_pairs_out,
+                        cow_cap, n_cow);
+}
+
+pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                               int32_t n_tokens, int32_t max_cached_tokens, int32_t *n_cached) {
+    const char *fn = "pa_seq_create_prefix";
+    if (!a || !n_cached || n_tokens < 0 || (n_tokens > 0 && !tokens))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    if (a->seqs.count(seq_id))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: sequence %lld exists", fn, (long long)seq_id);
+    const int32_t bs = a->block_size;
+    const int32_t full = n_tokens / bs;
+    const int32_t limit = std::min(n_tokens, std::max(max_cached_tokens, 0)) / bs;
+    std::vector<int32_t> hits;
+    try {
+        a->init_cache();
+        int32_t parent = -1;
+        for (int32_t j = 0; j < limit; ++j) {
+            const int32_t b = a->lookup(parent, tokens + (int64_t)j * bs);
+            if (b < 0) break;
+            hits.push_back(b);
+            parent = b;
+        }
+        Sequence s;
+        s.table = hits;
+        s.length = (int32_t)hits.size() * bs;
+        s.parent = parent;
+        s.pending.reserve(bs);
+        a->seqs.emplace(seq_id, std::move(s));
+    } catch (...) {
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: out of host memory", fn);
+    }
+    for (int32_t b : hits) {
+        if (a->refcount[b] == 0) {
+            a->lru_remove(b);
+            a->refcount[b] = 1;
+        } else {
+            a->add_ref(b);
+        }
+    }
+    a->queried_blocks += full;
+    a->hit_blocks += (int64_t)hits.size();
+    *n_cached = (int32_t)hits.size() * bs;
+    return pa::ok();
+}
+
+pa_status pa_prefix_cache_stats(const pa_allocator *a, pa_prefix_stats_t *out) {
+    if (!a || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_prefix_cache_stats: NULL argument");
+    out->queried_blocks = a->queried_blocks;
+    out->hit_blocks = a->hit_blocks;
+    out->cached_blocks = a->num_registered;
+    int32_t queued = 0;
+    for (int32_t b = a->lru_head; b >= 0; b = a->lru_next[b]) queued += a->registered[b] ? 1 : 0;
+    out->cached_free_blocks = queued;
     return pa::ok();
 }
 
@@ -241,7 +506,7 @@ pa_status pa_seq_free(pa_allocator *a, int64_t seq_id) {
         return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_free: no sequence %lld", (long long)seq_id);
     const std::vector<int32_t> &t = it->second.table;
     for (auto r = t.rbegin(); r != t.rend(); ++r)
-        if (a->drop_ref(*r)) a->free_stack.push_back(*r);  // capacity is num_blocks
+        if (a->drop_ref(*r)) a->release(*r);
     a->seqs.erase(it);
     return pa::ok();
 }
@@ -299,7 +564,7 @@ pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs, const int64_t
 pa_status pa_allocator_stats(const pa_allocator *a, pa_allocator_stats_t *out) {
     if (!a || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_allocator_stats: NULL argument");
     out->num_blocks = a->num_blocks;
-    out->num_free = (int32_t)a->free_stack.size();
+    out->num_free = (int32_t)a->num_free();
     out->num_used = a->num_blocks - out->num_free;
     out->num_shared = a->num_shared;
     out->cow_copies = a->cow_copies;

@@ -152,3 +152,108 @@ def test_tiny_batch_blocks_and_append():
     a.batch_append([0, 1, 2, 3], [1, 1, 1, 1])
     assert [len(a.block_table(s)) for s in range(4)] == [2, 5, 7, 13]
     assert a.stats()["num_used"] == 27
+
+
+# -- prefix cache: the C++ allocator against the model ---------------------------
+
+def same_prefix_state(a: pa.Allocator, m: AllocatorModel):
+    same_state(a, m)
+    assert a.prefix_stats() == m.prefix_stats()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_prefix_operations_match_model(seed):
+    """Prompts drawn from a few shared prefixes, token appends, plain appends,
+    forks and frees on a small pool (so eviction runs often): slots, COW pairs,
+    tables, refcounts, free counts and cache counters must agree exactly."""
+    rng = np.random.default_rng(100 + seed)
+    nb, bs = int(rng.choice([12, 24, 48])), int(rng.choice([1, 2, 4]))
+    order = rng.permutation(nb)
+    a = pa.Allocator(nb, bs, free_order=order)
+    m = AllocatorModel(nb, bs, free_order=order)
+    stems = [list(rng.integers(0, 4, int(rng.integers(1, 4 * bs + 3)))) for _ in range(4)]
+    live, next_id = [], 1000
+    for step in range(500):
+        op = int(rng.integers(6))
+        if op <= 1 or not live:
+            toks = [int(x) for x in stems[int(rng.integers(4))]]
+            toks += [int(x) for x in rng.integers(0, 4, int(rng.integers(0, 2 * bs + 1)))]
+            mc = int(rng.integers(0, len(toks) + 1))
+            na = a.create_prefix(next_id, toks, mc)
+            nm = m.create_prefix(next_id, toks, mc)
+            assert na == nm
+            live.append(next_id)
+            rest = toks[nm:]
+            try:
+                ms, mp = m.append(next_id, len(rest), tokens=rest)
+                oom = False
+            except OutOfBlocks:
+                oom = True
+            if oom:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append_tokens(next_id, rest)
+            else:
+                s, p = a.append_tokens(next_id, rest)
+                assert list(s) == ms and [tuple(x) for x in p] == mp
+            next_id += 1
+        elif op == 2:
+            sid = live[int(rng.integers(len(live)))]
+            k = int(rng.integers(0, 2 * bs + 1))
+            toks = [int(x) for x in rng.integers(0, 4, k)]
+            plain = rng.random() < 0.15
+            try:
+                ms, mp = m.append(sid, k, tokens=None if plain else toks)
+                oom = False
+            except OutOfBlocks:
+                oom = True
+            if oom:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append(sid, k) if plain else a.append_tokens(sid, toks)
+            else:
+                s, p = a.append(sid, k) if plain else a.append_tokens(sid, toks)
+                assert list(s) == ms and [tuple(x) for x in p] == mp
+        elif op == 3:
+            parent = live[int(rng.integers(len(live)))]
+            a.fork(parent, next_id)
+            m.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        else:
+            sid = live.pop(int(rng.integers(len(live))))
+            a.free(sid)
+            m.free(sid)
+        if step % 25 == 0:
+            same_prefix_state(a, m)
+    same_prefix_state(a, m)
+    assert m.hit_blocks > 0  # the workload did exercise the cache
+
+
+def test_batch_append_tokens_equals_sequential():
+    a = pa.Allocator(64, 4)
+    m = AllocatorModel(64, 4)
+    for sid in (1, 2, 3):
+        a.create(sid)
+        m.create(sid)
+    batch = {1: [1, 2, 3, 4, 5], 2: [1, 2, 3, 4, 6, 6, 6, 6], 3: []}
+    s, p = a.batch_append_tokens(list(batch), list(batch.values()))
+    want = []
+    for sid, t in batch.items():
+        want += m.append(sid, len(t), tokens=t)[0]
+    assert list(s) == want
+    same_prefix_state(a, m)
+    # sequence 2's first block is a duplicate of 1's: only 1's is registered
+    assert a.create_prefix(9, [1, 2, 3, 4, 6, 6, 6, 6]) == 4
+    assert m.create_prefix(9, [1, 2, 3, 4, 6, 6, 6, 6], 8) == 4
+    same_prefix_state(a, m)
+
+
+def test_prefix_errors_change_nothing():
+    a = pa.Allocator(4, 2)
+    a.create_prefix(1, [1, 2, 3, 4, 5])
+    a.append_tokens(1, [1, 2, 3, 4, 5])
+    before = (a.stats(), a.prefix_stats(), list(a.block_table(1)))
+    with pytest.raises(pa.PAError):
+        a.create_prefix(1, [1, 2])  # id exists
+    with pytest.raises(pa.OutOfBlocks):
+        a.append_tokens(1, [0] * 9)
+    assert (a.stats(), a.prefix_stats(), list(a.block_table(1))) == before

@@ -214,3 +214,93 @@ def test_cow_then_write_leaves_other_sharers_intact(pa):
             want_v = np.concatenate([oracle.widen(host_bits(vp[:, h])),
                                      oracle.widen(host_bits(tail_v[s][:, h]))])
             assert (k == want_k).all() and (v == want_v).all()
+
+
+def test_prefix_cache_hits_decode_like_fresh_prompts(pa):
+    """Requests open with one of four shared system prompts.  A first wave
+    (one request per system prompt) is written and released, so its full
+    blocks wait in the cache queue; a second wave finds them there
+    (pa_seq_create_prefix), writes only its uncached positions, and decodes.
+    K/V rows are a function of (system prompt, position) inside the system
+    prompt, so reuse is exact.  Decode over the cached tables must equal, bit
+    for bit, decode over the same prompts written in full into private blocks
+    by an allocator without the cache; sampled rows match the fp64 oracle."""
+    sh = wl.DecodeShape("prefix_cache", 12, 8, 4, 64, 16, 1024, "bf16", 77)
+    dev = "cuda"
+    plan = wl.chat_plan(num_system=4, requests=12, system_len=300, max_user=200)
+    hkv, d, bs = sh.num_kv_heads, sh.head_dim, sh.block_size
+    gen = wl.make_generator(sh.seed, dev)
+    sys_k = [wl.randn((len(t), hkv, d), torch.bfloat16, gen, dev) for t in plan.system_tokens]
+    sys_v = [wl.randn((len(t), hkv, d), torch.bfloat16, gen, dev) for t in plan.system_tokens]
+    usr_k = [wl.randn((len(t), hkv, d), torch.bfloat16, gen, dev) for t in plan.user_tokens]
+    usr_v = [wl.randn((len(t), hkv, d), torch.bfloat16, gen, dev) for t in plan.user_tokens]
+
+    def rows(r, lo):
+        """K/V rows of request r's positions lo.. (system rows, then user rows)."""
+        s, n_sys = int(plan.system_of[r]), len(plan.system_tokens[int(plan.system_of[r])])
+        ks = torch.cat([sys_k[s], usr_k[r]])[lo:]
+        vs = torch.cat([sys_v[s], usr_v[r]])[lo:]
+        assert ks.shape[0] == n_sys + len(plan.user_tokens[r]) - lo
+        return ks.contiguous(), vs.contiguous()
+
+    def pools():
+        kshape, vshape = pa.kv_cache_shapes(sh.num_blocks, hkv, bs, d)
+        return (torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev),
+                torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev))
+
+    order = np.random.default_rng(sh.seed).permutation(sh.num_blocks)
+    cached = pa.Allocator(sh.num_blocks, bs, free_order=order)
+    kc, vc = pools()
+    cached_tokens = {}
+    for wave in (range(4), range(4, 12)):
+        for r in wave:
+            toks = plan.prompt(r)
+            n = cached.create_prefix(r, toks, len(toks) - 1)
+            cached_tokens[r] = n
+            slots, pairs = cached.append_tokens(r, toks[n:])
+            assert len(pairs) == 0
+            k, v = rows(r, n)
+            pa.pa_cache_write(k, v, kc, vc, torch.as_tensor(slots, device=dev))
+        if wave.start == 0:
+            for r in wave:
+                cached.free(r)
+            # every full block of the first wave's prompts stays cached
+            assert cached.prefix_stats()["cached_free_blocks"] == sum(
+                len(plan.prompt(r)) // bs for r in wave)
+    ids = list(range(4, 12))
+    st = cached.prefix_stats()
+    say(f"case prefix cache: hits {st['hit_blocks']} of {st['queried_blocks']} blocks, "
+        f"cached tokens {[cached_tokens[r] for r in ids]}")
+    for r in ids:  # every second-wave request reused its system prompt's full blocks
+        assert cached_tokens[r] == len(plan.system_tokens[int(plan.system_of[r])]) // bs * bs
+
+    fresh = pa.Allocator(sh.num_blocks, bs, free_order=order)
+    kf, vf = pools()
+    for r in ids:
+        fresh.create(r)
+        slots, _ = fresh.append(r, len(plan.prompt(r)))
+        k, v = rows(r, 0)
+        pa.pa_cache_write(k, v, kf, vf, torch.as_tensor(slots, device=dev))
+
+    stride = max(wl.blocks_needed(len(plan.prompt(r)), bs) for r in ids) + 1
+    tc, lc = cached.batch_tables(ids, stride, sh.num_blocks - 1)
+    tf, lf = fresh.batch_tables(ids, stride, sh.num_blocks - 1)
+    assert (lc == lf).all()
+    S = len(ids)
+    q = wl.randn((S, sh.num_q_heads, d), torch.bfloat16, wl.make_generator(sh.seed + 1, dev), dev)
+    maxlen = int(lc.max())
+    ws = pa.decode_workspace(S, sh.num_q_heads, hkv, d, bs, maxlen, 64, dev)
+    l_dev = torch.as_tensor(lc, device=dev)
+    out_c = torch.empty((S, sh.num_q_heads, d), device=dev)
+    out_f = torch.empty_like(out_c)
+    pa.pa_decode(out_c, q, kc, vc, torch.as_tensor(tc, device=dev), l_dev, sh.scale, maxlen, 64, ws)
+    pa.pa_decode(out_f, q, kf, vf, torch.as_tensor(tf, device=dev), l_dev, sh.scale, maxlen, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_c).all()
+    assert torch.equal(out_c, out_f)
+    sample = [0, 3, S - 1]
+    ref = oracle_decode_rows(q, kc, vc, tc, lc, sample, bs, sh.scale, pa.K_AXES, pa.V_AXES)
+    got = out_c[torch.as_tensor(sample, device=dev)].double().cpu().numpy()
+    err = float(np.abs(got - ref).max())
+    say(f"  cached == fresh bit for bit over {S} requests; oracle rows {sample} err {err:.3e}")
+    assert err <= TOL

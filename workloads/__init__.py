@@ -20,6 +20,9 @@ Workload shapes (one per named case):
                 partitions of 512) plus 4 prefill chunks of 512 new tokens over
                 4096 cached ones; 32 query / 8 kv heads, head_dim 128, bf16,
                 8,192-block pool
+  chat          (prefix cache) 128 requests, each opening with one of 16
+                system prompts of 2048 + j tokens (j = 1 + i mod 15) and going
+                on with 16..512 user tokens; token ids uniform over 32,000
 
 Seeds: case k uses 0x417 + k.  Lengths, permutations and tails come from
 ``numpy.random.default_rng(seed)``; tensors from ``torch.Generator`` seeded
@@ -221,6 +224,32 @@ def prefix_plan(num_prompts=16, samples=8, prompt_len=2048, seed=SEED_BASE + 4,
         shared = np.full(num_prompts, prompt_len, dtype=np.int32)
     tails = rng.integers(1, max_tail, size=(num_prompts, samples), endpoint=True).astype(np.int32)
     return PrefixPlan(shared, tails)
+
+
+@dataclasses.dataclass
+class ChatPlan:
+    """Requests that open with one of a few shared system prompts."""
+    system_tokens: list  # [num_system] int32 arrays (token ids)
+    system_of: np.ndarray  # [requests] which system prompt each request opens with
+    user_tokens: list  # [requests] int32 arrays
+
+    def prompt(self, r: int) -> np.ndarray:
+        return np.concatenate([self.system_tokens[int(self.system_of[r])], self.user_tokens[r]])
+
+
+def chat_plan(num_system=16, requests=128, system_len=2048, max_user=512, vocab=32000,
+              seed=SEED_BASE + 6) -> ChatPlan:
+    """System prompt i has system_len + 1 + (i mod 15) tokens (its last block
+    partial, as in the prefix-shared batch); request r opens with system
+    prompt r mod num_system and goes on with U{16..max_user} user tokens.
+    Token ids are uniform over the vocabulary."""
+    rng = np.random.default_rng(seed)
+    sys_tok = [rng.integers(0, vocab, system_len + 1 + (i % 15)).astype(np.int32)
+               for i in range(num_system)]
+    which = (np.arange(requests) % num_system).astype(np.int32)
+    user = [rng.integers(0, vocab, int(rng.integers(16, max_user, endpoint=True))).astype(np.int32)
+            for _ in range(requests)]
+    return ChatPlan(sys_tok, which, user)
 
 
 # ---------------------------------------------------------------------------
