@@ -58,6 +58,25 @@ eviction rule; the reading taken here:
     the keys of all its registered descendants are dropped (their holders all
     hold it, so they are queued too; they stay in the queue, unregistered).
     Free blocks = stack + queue.
+
+Swap (the pages: [NV] best practice 5, preemption moves a low-priority
+request's KV cache out to CPU memory and back in when room returns; [VI] §2.1,
+cold blocks migrate to CPU memory; [VI] §5, a CPU swap space).  Reading taken:
+  * ``set_swap_space(n)`` gives a host pool of n blocks with its own free
+    stack (host block 0 handed out first).
+  * ``swap_out(seq)``: every table entry j in order gets a host block; the
+    pairs (device block, host block) are returned for the copy; then the
+    device blocks lose one reference each, last entry first, exactly as in
+    ``free``.  The table now holds host blocks and the sequence is swapped.
+    Sharing is not kept: a shared device block stays with its other holders
+    and the swapped sequence owns a private host copy.
+  * ``swap_in(seq)``: every entry j in order gets a device block (``_take``);
+    pairs (host block, device block) are returned; the host blocks go back on
+    the host stack, last entry first.  The new blocks are private and
+    unregistered, so the sequence's prefix chain ends.
+  * All or nothing: not enough host (or device) blocks raises OutOfBlocks
+    with no change.  A swapped sequence cannot be appended to, forked or put
+    in a batch table; freeing it returns its host blocks.
 """
 from __future__ import annotations
 
@@ -90,6 +109,12 @@ class AllocatorModel:
         self.parent: dict[int, int] = {}          # seq -> block of its last full block
         self.queried_blocks = 0
         self.hit_blocks = 0
+        # swap space
+        self.host_stack: list[int] = []
+        self.num_host_blocks = 0
+        self.swapped: set[int] = set()
+        self.swap_out_blocks = 0
+        self.swap_in_blocks = 0
 
     # -- helpers -----------------------------------------------------------
     def _take(self) -> int:
@@ -154,9 +179,58 @@ class AllocatorModel:
         self.parent[seq] = parent
         return len(table) * bs
 
+    def set_swap_space(self, num_host_blocks: int) -> None:
+        if self.swapped:
+            raise ValueError("sequences are swapped out")
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_stack = list(range(self.num_host_blocks - 1, -1, -1))
+
+    def swap_out(self, seq: int):
+        if seq not in self.tables:
+            raise LookupError(seq)
+        if seq in self.swapped:
+            raise ValueError("already swapped out")
+        table = self.tables[seq]
+        if len(table) > len(self.host_stack):
+            raise OutOfBlocks(f"need {len(table)} host blocks, {len(self.host_stack)} free")
+        host = [self.host_stack.pop() for _ in table]
+        pairs = list(zip(table, host))
+        for b in reversed(table):
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                if b in self.key_of:
+                    self.lru.append(b)
+                else:
+                    self.stack.append(b)
+        self.tables[seq] = host
+        self.swapped.add(seq)
+        self.swap_out_blocks += len(host)
+        return pairs
+
+    def swap_in(self, seq: int):
+        if seq not in self.tables:
+            raise LookupError(seq)
+        if seq not in self.swapped:
+            raise ValueError("not swapped out")
+        host = self.tables[seq]
+        if len(host) > self._num_free():
+            raise OutOfBlocks(f"need {len(host)} blocks, {self._num_free()} free")
+        dev = [self._take() for _ in host]
+        pairs = list(zip(host, dev))
+        for h in reversed(host):
+            self.host_stack.append(h)
+        self.tables[seq] = dev
+        self.swapped.discard(seq)
+        self.chain[seq] = False
+        self.pending[seq] = []
+        self.swap_in_blocks += len(dev)
+        return pairs
+
     def fork(self, parent: int, child: int) -> None:
         if parent not in self.tables:
             raise LookupError(parent)
+        if parent in self.swapped:
+            raise ValueError("swapped out")
         if child in self.tables:
             raise KeyError(child)
         self.tables[child] = list(self.tables[parent])
@@ -183,6 +257,8 @@ class AllocatorModel:
             raise ValueError(n)
         if tokens is not None and len(tokens) != n:
             raise ValueError("len(tokens) != n")
+        if seq in self.swapped:
+            raise ValueError("swapped out")
         need, cow = self.needed_blocks(seq, n)
         if need > self._num_free():
             raise OutOfBlocks(f"need {need} blocks, {self._num_free()} free")
@@ -228,6 +304,11 @@ class AllocatorModel:
     def free(self, seq: int) -> None:
         if seq not in self.tables:
             raise LookupError(seq)
+        if seq in self.swapped:
+            for h in reversed(self.tables[seq]):
+                self.host_stack.append(h)
+            self.swapped.discard(seq)
+            self.tables[seq] = []
         for b in reversed(self.tables[seq]):
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
@@ -254,4 +335,13 @@ class AllocatorModel:
             "hit_blocks": self.hit_blocks,
             "cached_blocks": len(self.keys),
             "cached_free_blocks": sum(1 for b in self.lru if b in self.key_of),
+        }
+
+    def swap_stats(self) -> dict:
+        return {
+            "num_host_blocks": self.num_host_blocks,
+            "num_host_free": len(self.host_stack),
+            "swapped_seqs": len(self.swapped),
+            "swap_out_blocks": self.swap_out_blocks,
+            "swap_in_blocks": self.swap_in_blocks,
         }

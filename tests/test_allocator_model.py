@@ -283,3 +283,95 @@ def test_random_prefix_ops_keep_invariants():
                 assert key[0] in a.key_of and b in a.children[key[0]]
                 # every holder of a block holds its parent
                 assert a.refcount[key[0]] >= a.refcount[b]
+
+
+# -- swap space ---------------------------------------------------------------
+# [NV] best practice 5: preemption swaps a request's KV cache out to CPU memory
+# and back in when room returns.  [VI] §2.1: cold blocks migrate to CPU memory.
+# Expected tables below are worked out by hand from that reading.
+
+def test_swap_out_and_in_round_trip():
+    a = AllocatorModel(8, 4)
+    a.set_swap_space(6)
+    a.create(1)
+    a.append(1, 10)                       # device blocks 0, 1, 2
+    a.create(2)
+    a.append(2, 4)                        # device block 3
+    pairs = a.swap_out(1)
+    assert pairs == [(0, 0), (1, 1), (2, 2)]
+    assert a.tables[1] == [0, 1, 2] and 1 in a.swapped
+    assert a.stack[-3:] == [2, 1, 0]      # released last entry first
+    assert a.stats()["num_free"] == 7 and a.swap_stats()["num_host_free"] == 3
+    a.create(3)
+    a.append(3, 5)                        # takes device 0, 1 (the swapped ones)
+    assert a.tables[3] == [0, 1]
+    pairs = a.swap_in(1)                  # needs 3: takes 2, then 4, 5
+    assert pairs == [(0, 2), (1, 4), (2, 5)]
+    assert a.tables[1] == [2, 4, 5] and a.lengths[1] == 10
+    assert a.host_stack == [5, 4, 3, 2, 1, 0]
+    assert a.swap_stats() == {"num_host_blocks": 6, "num_host_free": 6, "swapped_seqs": 0,
+                              "swap_out_blocks": 3, "swap_in_blocks": 3}
+
+
+def test_swap_out_of_a_sharer_keeps_the_others():
+    a = AllocatorModel(8, 4)
+    a.set_swap_space(4)
+    a.create(1)
+    a.append(1, 6)                        # blocks 0 (full), 1 (partial)
+    a.fork(1, 2)
+    assert a.refcount[:2] == [2, 2]
+    pairs = a.swap_out(2)
+    assert pairs == [(0, 0), (1, 1)] and a.refcount[:2] == [1, 1]
+    assert a.tables[1] == [0, 1]
+    a.swap_in(2)
+    assert a.tables[2] == [2, 3] and a.refcount[:4] == [1, 1, 1, 1]
+
+
+def test_swap_failures_change_nothing():
+    a = AllocatorModel(4, 2)
+    a.set_swap_space(2)
+    a.create(1)
+    a.append(1, 6)                        # 3 blocks
+    before = (list(a.stack), list(a.host_stack), dict(a.tables), set(a.swapped))
+    with pytest.raises(OutOfBlocks):
+        a.swap_out(1)                     # 3 host blocks needed, 2 exist
+    assert (list(a.stack), list(a.host_stack), dict(a.tables), set(a.swapped)) == before
+    b = AllocatorModel(4, 2)
+    b.set_swap_space(4)
+    b.create(1)
+    b.append(1, 6)                        # 0, 1, 2
+    b.swap_out(1)
+    b.create(2)
+    b.append(2, 4)                        # takes 0, 1
+    b.create(3)
+    b.append(3, 3)                        # takes 2, 3
+    with pytest.raises(OutOfBlocks):
+        b.swap_in(1)                      # no device block left
+    assert 1 in b.swapped and b.tables[1] == [0, 1, 2]
+
+
+def test_swapped_sequence_rejects_use_and_frees_host_blocks():
+    a = AllocatorModel(8, 4)
+    a.set_swap_space(4)
+    a.create(1)
+    a.append(1, 5)
+    a.swap_out(1)
+    with pytest.raises(ValueError):
+        a.append(1, 1)
+    with pytest.raises(ValueError):
+        a.fork(1, 2)
+    a.free(1)
+    assert a.host_stack == [3, 2, 1, 0] and a.stats()["num_free"] == 8
+
+
+def test_swap_out_of_cached_blocks_keeps_them_cached():
+    a = AllocatorModel(8, 2)
+    a.set_swap_space(4)
+    a.create_prefix(1, [5, 6, 7, 8], 4)
+    a.append(1, 4, tokens=[5, 6, 7, 8])   # blocks 0, 1 registered
+    a.swap_out(1)
+    assert a.lru == [1, 0]                # cached, queued
+    assert a.create_prefix(2, [5, 6, 7, 8, 9], 4) == 4
+    assert a.tables[2] == [0, 1]
+    a.swap_in(1)                          # fresh private blocks
+    assert a.tables[1] == [2, 3] and not a.chain[1]
