@@ -273,6 +273,87 @@ def row_prefix_cache(pa, wl, np, cpu_budget):
     return out
 
 
+PCIE_GBPS = 64.0  # PCIe 5.0 x16, per direction, nominal
+
+
+def row_swap(pa, wl, torch, np, reps, cpu_budget):
+    """Swap space: 8 sequences of 4096 tokens (7B-shaped blocks: 32 kv heads,
+    head_dim 128, block 16, bf16; 256 KiB per block pair of K and V regions)
+    move to a pinned host pool and back.  Each repetition is one swap-out of
+    all eight (allocator + one pa_swap_blocks launch, device -> host) and one
+    swap-in (host -> device); the copies are timed with HIP events."""
+    dev = "cuda"
+    hkv, d, bs, nb, nh = 32, 128, 16, 4096, 2048
+    kshape, vshape = pa.kv_cache_shapes(nb, hkv, bs, d)
+    k_dev = torch.empty(kshape, dtype=torch.bfloat16, device=dev)
+    v_dev = torch.empty(vshape, dtype=torch.bfloat16, device=dev)
+    gen = wl.make_generator(wl.SEED_BASE + 7, dev)
+    for t in (k_dev, v_dev):  # content does not matter to the copy; fill it anyway
+        for i in range(0, nb, 512):
+            t[i:i + 512] = wl.randn(tuple(t[i:i + 512].shape), torch.bfloat16, gen, dev)
+    hk, hv = pa.kv_cache_shapes(nh, hkv, bs, d)
+    k_host = torch.empty(hk, dtype=torch.bfloat16, pin_memory=True)
+    v_host = torch.empty(hv, dtype=torch.bfloat16, pin_memory=True)
+    alloc = pa.Allocator(nb, bs, free_order=np.random.default_rng(wl.SEED_BASE + 7).permutation(nb))
+    alloc.set_swap_space(nh)
+    seqs = list(range(8))
+    for sid in seqs:
+        alloc.create(sid)
+        alloc.append(sid, 4096)
+    stream = torch.cuda.current_stream()
+    t_out, t_in, host_us = [], [], []
+    for rep in range(reps + 2):
+        h0 = time.perf_counter()
+        pairs = np.concatenate([alloc.swap_out(s) for s in seqs])
+        h1 = time.perf_counter()
+        dp = torch.as_tensor(pairs, device=dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pa.pa_swap_blocks(k_dev, v_dev, k_host, v_host, dp)
+        e[1].record(stream)
+        h2 = time.perf_counter()
+        pairs = np.concatenate([alloc.swap_in(s) for s in seqs])
+        h3 = time.perf_counter()
+        dp = torch.as_tensor(pairs, device=dev)
+        e[2].record(stream)
+        pa.pa_swap_blocks(k_host, v_host, k_dev, v_dev, dp)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if rep >= 2:  # two warm-ups
+            t_out.append(e[0].elapsed_time(e[1]))
+            t_in.append(e[2].elapsed_time(e[3]))
+            host_us.append(((h1 - h0) + (h3 - h2)) * 1e6 / 2)
+    n_pairs = len(pairs)
+    moved = n_pairs * 2 * hkv * bs * d * 2
+    mo, mi = sorted(t_out)[len(t_out) // 2], sorted(t_in)[len(t_in) // 2]
+    out = {"us_out": mo * 1e3, "us_in": mi * 1e3, "bytes_each_way": moved,
+           "GBps_out": moved / (mo * 1e-3) / 1e9, "GBps_in": moved / (mi * 1e-3) / 1e9,
+           "frac_out_of_pcie5x16": moved / (mo * 1e-3) / 1e9 / PCIE_GBPS,
+           "frac_in_of_pcie5x16": moved / (mi * 1e-3) / 1e9 / PCIE_GBPS,
+           "host_us_per_swap_of_8": sorted(host_us)[len(host_us) // 2],
+           "bound": "pcie",
+           "workload": "swap 8 seqs x 4096 tokens (2048 blocks of 32 kv heads x 16 x 128 bf16, "
+                       "K and V) to a pinned host pool and back"}
+    if cpu_budget > 0:
+        oracle, _, _ = _oracle_helpers()
+        m = 64
+        src_k = np.zeros((m, hkv, bs, d), np.uint16)
+        src_v = np.zeros((m, hkv, d, bs), np.uint16)
+        dst_k, dst_v = np.zeros_like(src_k), np.zeros_like(src_v)
+        local = np.stack([np.arange(m), np.arange(m)[::-1]], axis=1).astype(np.int32)
+        done, el = 0, 0.0
+        while el < cpu_budget:
+            t0 = time.perf_counter()
+            oracle.swap_blocks(src_k, src_v, dst_k, dst_v, local, "bhrd", "bhdr")
+            el += time.perf_counter() - t0
+            done += m
+        out["cpu_oracle"] = {"value": done * 2 * hkv * bs * d * 2 / el / 1e9, "unit": "GB/s",
+                             "cores": 1, "kind": "oracle",
+                             "sample": f"{done} block pairs copied host to host by the oracle"}
+    del k_dev, v_dev, k_host, v_host
+    return out
+
+
 def cpu_copy_row(pairs, hkv, d, bs, budget_s):
     """Oracle whole-block copies of the same number of pairs on host pools."""
     oracle, _, _ = _oracle_helpers()
@@ -723,7 +804,8 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
 
 
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
-          "long-context split-K decode", "mixed step (cache write + decode + prefill)")
+          "long-context split-K decode", "mixed step (cache write + decode + prefill)",
+          "swap out / in (pinned host pool)")
 
 
 def mark_phase(torch):
@@ -889,6 +971,10 @@ def main():
             rows["allocator"]["cpu_oracle"] = cpu_allocator_row(alloc_case, 20)
         log("bench: row prefix cache")
         rows["prefix_cache"] = row_prefix_cache(pa, wl, np, args.row_cpu_budget)
+        log("bench: row swap")
+        mark_phase(torch)
+        rows["swap"] = row_swap(pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
         result["rows"] = rows
         for k, v in rows.items():
             log(f"bench: {k}: " + ", ".join(

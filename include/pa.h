@@ -339,6 +339,68 @@ pa_status pa_batch_append_tokens(pa_allocator *a, int32_t num_seqs,
 
 pa_status pa_prefix_cache_stats(const pa_allocator *a, pa_prefix_stats_t *out);
 
+/* ------------------------------------------------------------------------ */
+/* Swap space                                                                 */
+/* ------------------------------------------------------------------------ */
+/* Preemption moves a request's KV cache out to CPU memory and back in when
+ * room returns ([NV] best practice 5); cold blocks migrate to CPU memory
+ * ([VI] §2.1); a CPU swap space extends the cache ([VI] §5).  Here a caller-
+ * owned host pool (pinned, same block layout as the device pools) holds
+ * num_host_blocks blocks; the allocator keeps its own free stack for it
+ * (host block 0 handed out first). */
+
+typedef struct {
+    int32_t num_host_blocks;
+    int32_t num_host_free;
+    int32_t swapped_seqs;
+    int64_t swap_out_blocks; /* blocks moved out so far */
+    int64_t swap_in_blocks;  /* blocks moved in so far */
+} pa_swap_stats_t;
+
+/* Size the host pool.  INVALID_ARG while any sequence is swapped out. */
+pa_status pa_allocator_set_swap_space(pa_allocator *a, int32_t num_host_blocks);
+
+/* Swap a resident sequence out.  Every table entry j, in order, gets a host
+ * block; pairs_out[j] = (device block, host block) [cap][2] host, *n_pairs
+ * entries.  Then the device blocks lose one reference each, last entry
+ * first, as in pa_seq_free (a block shared with other sequences stays theirs;
+ * the swapped sequence owns a private host copy).  The caller copies the
+ * pairs device -> host (pa_swap_blocks) before any work that may write the
+ * released blocks.  The sequence's table then holds host block ids; it
+ * cannot be appended to, forked or put in a batch table until swapped in.
+ * OUT_OF_BLOCKS (host pool short) or INVALID_ARG (cap too small) change
+ * nothing. */
+pa_status pa_seq_swap_out(pa_allocator *a, int64_t seq_id, int32_t *pairs_out,
+                          int32_t cap, int32_t *n_pairs);
+
+/* Swap a sequence back in: every entry j, in order, gets a fresh device
+ * block; pairs_out[j] = (host block, device block); the host blocks return to
+ * the host stack, last entry first.  The new blocks are private and not in
+ * the prefix cache.  The caller copies the pairs host -> device before the
+ * sequence's next use.  OUT_OF_BLOCKS or INVALID_ARG change nothing.
+ * pa_seq_free of a swapped sequence returns its host blocks. */
+pa_status pa_seq_swap_in(pa_allocator *a, int64_t seq_id, int32_t *pairs_out,
+                         int32_t cap, int32_t *n_pairs);
+
+pa_status pa_seq_is_swapped(const pa_allocator *a, int64_t seq_id,
+                            int32_t *swapped);
+pa_status pa_swap_stats(const pa_allocator *a, pa_swap_stats_t *out);
+
+/* Copy whole blocks between two pools of the same geometry, on the GPU:
+ * for each pair i, block src_dst[2i] of (src_k, src_v) goes to block
+ * src_dst[2i + 1] of (dst_k, dst_v), K and V regions, all heads.  One pool is
+ * normally device memory and the other the pinned host pool (the copy then
+ * runs over PCIe); both may be device memory.  Each pool pointer must be
+ * device memory or pinned host memory mapped for the device (checked:
+ * pageable memory is INVALID_ARG); src_dst [num_pairs][2] int32 must be
+ * device-accessible too.  Pairs naming a block outside its pool are skipped.
+ * Pools must not overlap. */
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks,
+                         void *dst_k, void *dst_v, int32_t dst_blocks,
+                         const int32_t *src_dst, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

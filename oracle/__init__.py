@@ -74,6 +74,9 @@ def _load():
                                         i32, i32]
         lib.orc_copy_blocks.restype = None
         lib.orc_copy_blocks.argtypes = [vp, _Strides, vp, _Strides, vp, i32, i32, i32, i32, i32]
+        lib.orc_swap_blocks.restype = None
+        lib.orc_swap_blocks.argtypes = [vp, _Strides, vp, _Strides, vp, _Strides, vp, _Strides,
+                                        vp, i32, i32, i32, i32, i32]
         lib.orc_unpage.restype = None
         lib.orc_unpage.argtypes = [vp, _Strides, ctypes.c_int, vp, i32, i32, i32, i32, vp]
         _lib = lib
@@ -194,6 +197,19 @@ def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping,
     lib.orc_cache_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _strides(k_cache, k_axes),
                         _ptr(v_cache), _strides(v_cache, v_axes), _ptr(slot_mapping), t, hkv, d,
                         bs, k_cache.itemsize)
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst, k_axes="bhrd", v_axes="bhrd") -> None:
+    """Copy whole blocks src_dst[i][0] of the source pools to src_dst[i][1] of
+    the destination pools, K and V ([NV] best practice 5, [VI] §2.1 swap)."""
+    lib = _load()
+    src_dst = _c(src_dst, np.int32).reshape(-1, 2)
+    _, hkv, bs, d = pool_dims(src_k, k_axes)
+    assert pool_dims(dst_k, k_axes)[1:] == (hkv, bs, d) and src_k.itemsize == dst_k.itemsize
+    lib.orc_swap_blocks(_ptr(src_k), _strides(src_k, k_axes), _ptr(src_v),
+                        _strides(src_v, v_axes), _ptr(dst_k), _strides(dst_k, k_axes),
+                        _ptr(dst_v), _strides(dst_v, v_axes), _ptr(src_dst), src_dst.shape[0],
+                        hkv, d, bs, src_k.itemsize)
 
 
 def copy_blocks(k_cache, v_cache, src_dst, k_axes="bhrd", v_axes="bhrd") -> None:

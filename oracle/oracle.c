@@ -196,6 +196,36 @@ void orc_cache_write(const void *k_new, const void *v_new,
     }
 }
 
+/* Swap space: whole blocks move between the device pool and a host pool
+ * ([NV] best practice 5, preemption to CPU memory; [VI] §2.1 cold blocks to
+ * CPU memory).  Block src of the source pools is copied, K and V, every
+ * head and row, to block dst of the destination pools. */
+void orc_swap_blocks(const void *src_k, orc_strides sks, const void *src_v, orc_strides svs,
+                     void *dst_k, orc_strides dks, void *dst_v, orc_strides dvs,
+                     const int32_t *src_dst, int32_t num_pairs,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t elem_size)
+{
+    for (int32_t p = 0; p < num_pairs; ++p) {
+        int64_t src = src_dst[2 * p];
+        int64_t dst = src_dst[2 * p + 1];
+        for (int32_t h = 0; h < num_kv_heads; ++h)
+            for (int32_t r = 0; r < block_size; ++r)
+                for (int32_t d = 0; d < head_dim; ++d) {
+                    memcpy((char *)dst_k + (dst * dks.block + h * dks.head + r * dks.row +
+                                            d * dks.dim) * elem_size,
+                           (const char *)src_k + (src * sks.block + h * sks.head + r * sks.row +
+                                                  d * sks.dim) * elem_size,
+                           (size_t)elem_size);
+                    memcpy((char *)dst_v + (dst * dvs.block + h * dvs.head + r * dvs.row +
+                                            d * dvs.dim) * elem_size,
+                           (const char *)src_v + (src * svs.block + h * svs.head + r * svs.row +
+                                                  d * svs.dim) * elem_size,
+                           (size_t)elem_size);
+                }
+    }
+}
+
 /* Copy-on-write: before a sequence writes into a block it shares, the whole
  * block (K and V, every head, every row) is copied to a private block
  * ([VI] §2.1, COW for prefix sharing). */

@@ -77,6 +77,13 @@ void orc_copy_blocks(void *k_cache, orc_strides ks, void *v_cache, orc_strides v
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t elem_size);
 
+/* Copy block src of (src_k, src_v) to block dst of (dst_k, dst_v), all heads. */
+void orc_swap_blocks(const void *src_k, orc_strides sks, const void *src_v, orc_strides svs,
+                     void *dst_k, orc_strides dks, void *dst_v, orc_strides dvs,
+                     const int32_t *src_dst, int32_t num_pairs,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t elem_size);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ EXPORTED = (
     "pa_allocator_destroy", "pa_seq_create", "pa_seq_fork", "pa_seq_append", "pa_seq_free",
     "pa_seq_length", "pa_seq_block_table", "pa_allocator_stats", "pa_block_refcount",
     "pa_batch_append", "pa_batch_tables", "pa_seq_create_prefix", "pa_seq_append_tokens",
-    "pa_batch_append_tokens", "pa_prefix_cache_stats",
+    "pa_batch_append_tokens", "pa_prefix_cache_stats", "pa_allocator_set_swap_space",
+    "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
 )
 
 
@@ -60,6 +61,12 @@ class AllocatorStats(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_free", ctypes.c_int32),
                 ("num_used", ctypes.c_int32), ("num_shared", ctypes.c_int32),
                 ("cow_copies", ctypes.c_int64)]
+
+
+class SwapStats(ctypes.Structure):
+    _fields_ = [("num_host_blocks", ctypes.c_int32), ("num_host_free", ctypes.c_int32),
+                ("swapped_seqs", ctypes.c_int32), ("swap_out_blocks", ctypes.c_int64),
+                ("swap_in_blocks", ctypes.c_int64)]
 
 
 class PrefixStats(ctypes.Structure):
@@ -100,6 +107,13 @@ def _declare(lib):
         "pa_seq_append_tokens": (st, [vp, i64, pi32, i32, pi64, pi32, i32, pi32]),
         "pa_batch_append_tokens": (st, [vp, i32, pi64, pi32, pi32, pi64, pi32, i32, pi32]),
         "pa_prefix_cache_stats": (st, [vp, ctypes.POINTER(PrefixStats)]),
+        "pa_allocator_set_swap_space": (st, [vp, i32]),
+        "pa_seq_swap_out": (st, [vp, i64, pi32, i32, pi32]),
+        "pa_seq_swap_in": (st, [vp, i64, pi32, i32, pi32]),
+        "pa_seq_is_swapped": (st, [vp, i64, pi32]),
+        "pa_swap_stats": (st, [vp, ctypes.POINTER(SwapStats)]),
+        "pa_swap_blocks": (st, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, ctypes.c_int,
+                                vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -171,6 +185,21 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     n = src_dst.numel() // 2
     _check(_lib.pa_copy_blocks(_p(k_cache), _p(v_cache), _p(src_dst), n, hkv, d, bs, nb,
                                _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst, stream=None) -> None:
+    """Copy whole blocks src_dst[i][0] of (src_k, src_v) to src_dst[i][1] of
+    (dst_k, dst_v): one pool on the device, the other a pinned host pool of the
+    same block layout (``torch.empty(..., pin_memory=True)``).  src_dst must
+    live on the device or in pinned host memory."""
+    nb_s, hkv, bs, d = _geometry(src_k)
+    nb_d, hkv2, bs2, d2 = _geometry(dst_k)
+    if (hkv, bs, d) != (hkv2, bs2, d2) or src_k.dtype != dst_k.dtype:
+        raise PAError(PA_ERR_INVALID_ARG, "pa_swap_blocks: pools differ in geometry or dtype")
+    n = src_dst.numel() // 2
+    _check(_lib.pa_swap_blocks(_p(src_k), _p(src_v), nb_s, _p(dst_k), _p(dst_v), nb_d,
+                               _p(src_dst), n, hkv, d, bs, _dtype_code(src_k),
+                               ctypes.c_void_p(_stream(stream))))
 
 
 def pa_decode_default_partition(num_seqs, num_kv_heads, block_size, max_context_len) -> int:
@@ -329,6 +358,35 @@ class Allocator:
                                            _i32p(flat), _i64p(slots), _i32p(pairs),
                                            pairs.shape[0], ctypes.byref(ncow)))
         return slots[:total], pairs[:ncow.value]
+
+    def set_swap_space(self, num_host_blocks: int):
+        _check(_lib.pa_allocator_set_swap_space(self._h, num_host_blocks))
+
+    def _swap(self, fn, seq_id):
+        np = self._np
+        cap = len(self.block_table(seq_id)) or 1
+        pairs = np.zeros((cap, 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, seq_id, _i32p(pairs), cap, ctypes.byref(n)))
+        return pairs[:n.value]
+
+    def swap_out(self, seq_id: int):
+        """Returns pairs [n][2] (device block, host block) to copy out."""
+        return self._swap(_lib.pa_seq_swap_out, seq_id)
+
+    def swap_in(self, seq_id: int):
+        """Returns pairs [n][2] (host block, device block) to copy in."""
+        return self._swap(_lib.pa_seq_swap_in, seq_id)
+
+    def is_swapped(self, seq_id: int) -> bool:
+        r = ctypes.c_int32(0)
+        _check(_lib.pa_seq_is_swapped(self._h, seq_id, ctypes.byref(r)))
+        return bool(r.value)
+
+    def swap_stats(self) -> dict:
+        st = SwapStats()
+        _check(_lib.pa_swap_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in SwapStats._fields_}
 
     def prefix_stats(self) -> dict:
         st = PrefixStats()

@@ -11,7 +11,9 @@
 //        copy-on-write for shared prefixes, a free list popped at its end;
 //        allocation first reuses blocks shareable with the request's prefix,
 //        and cold blocks leave under an LRU policy.
-//   [NV] practical advice — the prefix-cache hit rate as a serving metric.
+//   [NV] practical advice — the prefix-cache hit rate as a serving metric;
+//        best practice 5 — preemption swaps a request's KV cache out to CPU
+//        memory and back in when room returns.
 //
 // State: refcount[b] per block (0 free, 1 owned, >1 shared), a free stack
 // (top = back of the vector), and per sequence its table and length.  Every
@@ -27,6 +29,12 @@
 // tokens.  Released registered blocks wait in an LRU queue instead of the
 // free stack; taking a block pops the stack first, then the oldest queued
 // block, whose key (and its registered descendants' keys) it drops.
+//
+// Swap space.  A host pool of blocks with its own free stack.  Swapping a
+// sequence out gives every table entry a host block (pairs for the copy) and
+// releases its device blocks as pa_seq_free does; swapping in takes fresh
+// device blocks and returns the host ones.  A swapped sequence's table holds
+// host block ids.
 #include <algorithm>
 #include <new>
 #include <unordered_map>
@@ -43,6 +51,7 @@ struct Sequence {
     bool chain = true;             // every position so far came with a token id
     std::vector<int32_t> pending;  // token ids of the partial last block
     int32_t parent = -1;           // block of the last registered full block
+    bool swapped = false;          // table holds host block ids
 };
 
 // 64-bit FNV-1a over the parent id and the block's token ids.
@@ -88,6 +97,12 @@ struct pa_allocator {
     size_t lru_size = 0;
     int64_t queried_blocks = 0, hit_blocks = 0;
     int32_t num_registered = 0;
+
+    // swap space
+    int32_t num_host_blocks = 0;
+    std::vector<int32_t> host_stack;  // top = back
+    int32_t num_swapped = 0;
+    int64_t swap_out_blocks = 0, swap_in_blocks = 0;
 
     bool cache_ready() const { return !registered.empty(); }
     // Per-block prefix-cache arrays, sized on first use.
@@ -328,6 +343,9 @@ pa_status pa_seq_fork(pa_allocator *a, int64_t parent, int64_t child) {
     if (a->seqs.count(child))
         return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_fork: sequence %lld exists",
                         (long long)child);
+    if (it->second.swapped)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_fork: sequence %lld is swapped out",
+                        (long long)parent);
     try {
         Sequence copy = it->second;
         for (int32_t b : copy.table) a->add_ref(b);
@@ -360,6 +378,9 @@ pa_status batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids
             return pa::fail(PA_ERR_INVALID_ARG, "append: n_tokens[%d] = %d", i, n_tokens[i]);
         if ((int64_t)it->second.length + n_tokens[i] > INT32_MAX)
             return pa::fail(PA_ERR_INVALID_ARG, "append: sequence length overflows int32");
+        if (it->second.swapped)
+            return pa::fail(PA_ERR_INVALID_ARG, "append: sequence %lld is swapped out",
+                            (long long)seq_ids[i]);
         seqs[i] = &it->second;
         int64_t blocks;
         bool c;
@@ -505,8 +526,13 @@ pa_status pa_seq_free(pa_allocator *a, int64_t seq_id) {
     if (it == a->seqs.end())
         return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_free: no sequence %lld", (long long)seq_id);
     const std::vector<int32_t> &t = it->second.table;
-    for (auto r = t.rbegin(); r != t.rend(); ++r)
-        if (a->drop_ref(*r)) a->release(*r);
+    if (it->second.swapped) {
+        for (auto r = t.rbegin(); r != t.rend(); ++r) a->host_stack.push_back(*r);
+        --a->num_swapped;
+    } else {
+        for (auto r = t.rbegin(); r != t.rend(); ++r)
+            if (a->drop_ref(*r)) a->release(*r);
+    }
     a->seqs.erase(it);
     return pa::ok();
 }
@@ -547,6 +573,9 @@ pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs, const int64_t
         if (it == a->seqs.end())
             return pa::fail(PA_ERR_NOT_FOUND, "pa_batch_tables: no sequence %lld",
                             (long long)seq_ids[i]);
+        if (it->second.swapped)
+            return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_tables: sequence %lld is swapped out",
+                            (long long)seq_ids[i]);
         if ((int32_t)it->second.table.size() > stride)
             return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_tables: sequence %lld has %zu blocks > "
                             "stride %d", (long long)seq_ids[i], it->second.table.size(), stride);
@@ -576,6 +605,109 @@ pa_status pa_block_refcount(const pa_allocator *a, int32_t block, int32_t *refco
     if (block < 0 || block >= a->num_blocks)
         return pa::fail(PA_ERR_INVALID_ARG, "pa_block_refcount: block %d out of range", block);
     *refcount = a->refcount[block];
+    return pa::ok();
+}
+
+pa_status pa_allocator_set_swap_space(pa_allocator *a, int32_t num_host_blocks) {
+    const char *fn = "pa_allocator_set_swap_space";
+    if (!a || num_host_blocks < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    if (a->num_swapped > 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: %d sequences are swapped out", fn,
+                        a->num_swapped);
+    try {
+        std::vector<int32_t> st(num_host_blocks);
+        for (int32_t i = 0; i < num_host_blocks; ++i) st[i] = num_host_blocks - 1 - i;
+        a->host_stack.swap(st);
+    } catch (...) {
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: out of host memory", fn);
+    }
+    a->num_host_blocks = num_host_blocks;
+    return pa::ok();
+}
+
+pa_status pa_seq_swap_out(pa_allocator *a, int64_t seq_id, int32_t *pairs_out, int32_t cap,
+                          int32_t *n_pairs) {
+    const char *fn = "pa_seq_swap_out";
+    if (!a || !n_pairs || cap < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return pa::fail(PA_ERR_NOT_FOUND, "%s: no sequence %lld", fn, (long long)seq_id);
+    Sequence &s = it->second;
+    if (s.swapped)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: sequence %lld is swapped out", fn,
+                        (long long)seq_id);
+    const size_t n = s.table.size();
+    if ((int64_t)n > cap || (n > 0 && !pairs_out))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: %zu pairs, cap %d", fn, n, cap);
+    if (n > a->host_stack.size())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "%s: need %zu host blocks, %zu free", fn, n,
+                        a->host_stack.size());
+    for (size_t j = 0; j < n; ++j) {
+        const int32_t h = a->host_stack.back();
+        a->host_stack.pop_back();
+        pairs_out[2 * j] = s.table[j];
+        pairs_out[2 * j + 1] = h;
+    }
+    for (size_t j = n; j-- > 0;)  // device blocks released last entry first
+        if (a->drop_ref(s.table[j])) a->release(s.table[j]);
+    for (size_t j = 0; j < n; ++j) s.table[j] = pairs_out[2 * j + 1];
+    s.swapped = true;
+    ++a->num_swapped;
+    a->swap_out_blocks += (int64_t)n;
+    *n_pairs = (int32_t)n;
+    return pa::ok();
+}
+
+pa_status pa_seq_swap_in(pa_allocator *a, int64_t seq_id, int32_t *pairs_out, int32_t cap,
+                         int32_t *n_pairs) {
+    const char *fn = "pa_seq_swap_in";
+    if (!a || !n_pairs || cap < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return pa::fail(PA_ERR_NOT_FOUND, "%s: no sequence %lld", fn, (long long)seq_id);
+    Sequence &s = it->second;
+    if (!s.swapped)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: sequence %lld is not swapped out", fn,
+                        (long long)seq_id);
+    const size_t n = s.table.size();
+    if ((int64_t)n > cap || (n > 0 && !pairs_out))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: %zu pairs, cap %d", fn, n, cap);
+    if (n > a->num_free())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "%s: need %zu blocks, %zu free", fn, n,
+                        a->num_free());
+    for (size_t j = 0; j < n; ++j) {
+        pairs_out[2 * j] = s.table[j];
+        pairs_out[2 * j + 1] = a->take();
+    }
+    for (size_t j = n; j-- > 0;) a->host_stack.push_back(s.table[j]);  // capacity kept
+    for (size_t j = 0; j < n; ++j) s.table[j] = pairs_out[2 * j + 1];
+    s.swapped = false;
+    s.chain = false;  // fresh private blocks: the registered chain is gone
+    s.pending.clear();
+    --a->num_swapped;
+    a->swap_in_blocks += (int64_t)n;
+    *n_pairs = (int32_t)n;
+    return pa::ok();
+}
+
+pa_status pa_seq_is_swapped(const pa_allocator *a, int64_t seq_id, int32_t *swapped) {
+    if (!a || !swapped) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_is_swapped: NULL argument");
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_is_swapped: no sequence %lld",
+                        (long long)seq_id);
+    *swapped = it->second.swapped ? 1 : 0;
+    return pa::ok();
+}
+
+pa_status pa_swap_stats(const pa_allocator *a, pa_swap_stats_t *out) {
+    if (!a || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_swap_stats: NULL argument");
+    out->num_host_blocks = a->num_host_blocks;
+    out->num_host_free = (int32_t)a->host_stack.size();
+    out->swapped_seqs = a->num_swapped;
+    out->swap_out_blocks = a->swap_out_blocks;
+    out->swap_in_blocks = a->swap_in_blocks;
     return pa::ok();
 }
 

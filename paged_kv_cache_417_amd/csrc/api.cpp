@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdint>
 
+#include <hip/hip_runtime_api.h>
+
 #include "launch.h"
 #include "pa_internal.h"
 
@@ -51,6 +53,20 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_
     return ps;
 }
 
+// Address at which the GPU reaches memory p: p itself for device memory, the
+// mapped address for pinned host memory; nullptr for anything else
+// (pageable host memory, which a kernel must never touch).
+const void *device_view(const void *p) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of the failed query
+        return nullptr;
+    }
+    if (at.type == hipMemoryTypeDevice) return p;
+    if (at.type == hipMemoryTypeHost && at.devicePointer) return at.devicePointer;
+    return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +103,36 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, i
         return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     int rc = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, num_kv_heads, head_dim,
                                     block_size, num_blocks, dtype, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks, void *dst_k,
+                         void *dst_v, int32_t dst_blocks, const int32_t *src_dst,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void *stream) {
+    const char *fn = "pa_swap_blocks";
+    if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_pairs %d", fn, num_pairs);
+    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, src_blocks)) return st;
+    if (dst_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: dst_blocks %d", fn, dst_blocks);
+    if (!src_k || !src_v || !dst_k || !dst_v || (num_pairs > 0 && !src_dst))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+        !aligned(src_dst, 4))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (num_pairs == 0) return pa::ok();
+    const void *sk = device_view(src_k), *sv = device_view(src_v);
+    const void *dk = device_view(dst_k), *dv = device_view(dst_v);
+    const void *pr = device_view(src_dst);
+    if (!sk || !sv || !dk || !dv || !pr)
+        return pa::fail(PA_ERR_INVALID_ARG,
+                        "%s: a pool or the pair list is neither device memory nor pinned host "
+                        "memory", fn);
+    int rc = pa::launch_swap_blocks(sk, sv, src_blocks, const_cast<void *>(dk),
+                                    const_cast<void *>(dv), dst_blocks,
+                                    static_cast<const int32_t *>(pr), num_pairs, num_kv_heads,
+                                    head_dim, block_size, dtype, stream);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
 }

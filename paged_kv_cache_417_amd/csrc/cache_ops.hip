@@ -160,6 +160,27 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
     st16(base + dst * block_bytes + chunk * 16, ld16(base + src * block_bytes + chunk * 16));
 }
 
+// Block copy between two pools (swap out: device -> pinned host; swap in:
+// host -> device).  One thread per 16 bytes of a block region, so the PCIe
+// side sees long runs of 16-byte accesses.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const char *__restrict__ src_k, const char *__restrict__ src_v, char *__restrict__ dst_k,
+    char *__restrict__ dst_v, const int32_t *__restrict__ src_dst, int32_t num_pairs,
+    int64_t block_bytes, int32_t src_blocks, int32_t dst_blocks) {
+    const int64_t per_region = block_bytes / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)num_pairs * 2 * per_region) return;
+    const int64_t chunk = idx % per_region;
+    const int64_t pr = idx / per_region;
+    const int32_t pair = (int32_t)(pr >> 1);
+    const int32_t src = src_dst[2 * pair];
+    const int32_t dst = src_dst[2 * pair + 1];
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+    const char *from = (pr & 1) ? src_v : src_k;
+    char *to = (pr & 1) ? dst_v : dst_k;
+    st16(to + dst * block_bytes + chunk * 16, ld16(from + src * block_bytes + chunk * 16));
+}
+
 }  // namespace
 
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
@@ -204,6 +225,22 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int
     hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                        (char *)k_cache, (char *)v_cache, src_dst, num_pairs, block_bytes,
                        num_blocks);
+    return (int)hipGetLastError();
+}
+
+int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks, void *dst_k,
+                       void *dst_v, int32_t dst_blocks, const int32_t *src_dst,
+                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, pa_dtype dtype, void *stream) {
+    if (num_pairs == 0) return 0;
+    const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : 4;
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem;
+    const int64_t total = (int64_t)num_pairs * 2 * (block_bytes / 16);
+    if ((total + 255) / 256 > 0xffffffffLL) return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       (const char *)src_k, (const char *)src_v, (char *)dst_k, (char *)dst_v,
+                       src_dst, num_pairs, block_bytes, src_blocks, dst_blocks);
     return (int)hipGetLastError();
 }
 

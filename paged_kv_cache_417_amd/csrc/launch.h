@@ -70,6 +70,10 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
 int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, pa_dtype dtype, void *stream);
+int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks, void *dst_k,
+                       void *dst_v, int32_t dst_blocks, const int32_t *src_dst,
+                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, pa_dtype dtype, void *stream);
 
 // bf16 decode on the matrix cores (any group size up to 16).
 int launch_decode_mfma(const DecodeParams &p, void *stream);

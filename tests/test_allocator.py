@@ -257,3 +257,125 @@ def test_prefix_errors_change_nothing():
     with pytest.raises(pa.OutOfBlocks):
         a.append_tokens(1, [0] * 9)
     assert (a.stats(), a.prefix_stats(), list(a.block_table(1))) == before
+
+
+# -- swap space: the C++ allocator against the model -----------------------------
+
+def same_swap_state(a: pa.Allocator, m: AllocatorModel):
+    assert a.stats() == m.stats()
+    assert a.prefix_stats() == m.prefix_stats()
+    assert a.swap_stats() == m.swap_stats()
+    for b in range(m.num_blocks):
+        assert a.refcount(b) == m.refcount[b]
+    for sid, table in m.tables.items():
+        assert list(a.block_table(sid)) == table
+        assert a.is_swapped(sid) == (sid in m.swapped)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_swap_operations_match_model(seed):
+    """Appends (with and without token ids), prefix-cached prompts, forks,
+    frees, swap-outs and swap-ins on small device and host pools: pairs,
+    tables, refcounts and all counters agree exactly, failures included."""
+    rng = np.random.default_rng(200 + seed)
+    nb, bs, nh = int(rng.choice([16, 32])), int(rng.choice([1, 2, 4])), int(rng.choice([8, 24]))
+    order = rng.permutation(nb)
+    a = pa.Allocator(nb, bs, free_order=order)
+    m = AllocatorModel(nb, bs, free_order=order)
+    a.set_swap_space(nh)
+    m.set_swap_space(nh)
+    stems = [list(rng.integers(0, 3, int(rng.integers(1, 3 * bs + 2)))) for _ in range(3)]
+    live, next_id = [], 1
+    for step in range(500):
+        op = int(rng.integers(8))
+        resident = [s for s in live if s not in m.swapped]
+        swapped = [s for s in live if s in m.swapped]
+        if op == 0 or not live:
+            toks = [int(x) for x in stems[int(rng.integers(3))]] + [int(rng.integers(3))]
+            assert a.create_prefix(next_id, toks, len(toks) - 1) == \
+                m.create_prefix(next_id, toks, len(toks) - 1)
+            live.append(next_id)
+            try:
+                want = m.append(next_id, len(toks) - m.lengths[next_id],
+                                tokens=toks[m.lengths[next_id]:])
+            except OutOfBlocks:
+                want = None
+            rest = toks[a.length(next_id):]
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append_tokens(next_id, rest)
+            else:
+                s, p = a.append_tokens(next_id, rest)
+                assert list(s) == want[0] and [tuple(x) for x in p] == want[1]
+            next_id += 1
+        elif op in (1, 2) and resident:
+            sid = resident[int(rng.integers(len(resident)))]
+            k = int(rng.integers(0, 2 * bs + 1))
+            toks = [int(x) for x in rng.integers(0, 3, k)]
+            try:
+                want = m.append(sid, k, tokens=toks)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append_tokens(sid, toks)
+            else:
+                s, p = a.append_tokens(sid, toks)
+                assert list(s) == want[0] and [tuple(x) for x in p] == want[1]
+        elif op == 3 and resident:
+            parent = resident[int(rng.integers(len(resident)))]
+            a.fork(parent, next_id)
+            m.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op == 4 and resident:
+            sid = resident[int(rng.integers(len(resident)))]
+            try:
+                want = m.swap_out(sid)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.swap_out(sid)
+            else:
+                assert [tuple(x) for x in a.swap_out(sid)] == want
+        elif op == 5 and swapped:
+            sid = swapped[int(rng.integers(len(swapped)))]
+            try:
+                want = m.swap_in(sid)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.swap_in(sid)
+            else:
+                assert [tuple(x) for x in a.swap_in(sid)] == want
+        elif op == 6 and swapped:
+            sid = swapped[int(rng.integers(len(swapped)))]
+            with pytest.raises(pa.PAError):
+                a.append(sid, 1)
+            with pytest.raises(pa.PAError):
+                a.fork(sid, 99999)
+        elif live:
+            sid = live.pop(int(rng.integers(len(live))))
+            a.free(sid)
+            m.free(sid)
+        if step % 25 == 0:
+            same_swap_state(a, m)
+    same_swap_state(a, m)
+    assert m.swap_out_blocks > 0 and m.swap_in_blocks > 0
+
+
+def test_swap_space_cannot_shrink_under_swapped_sequences():
+    a = pa.Allocator(8, 4)
+    a.set_swap_space(4)
+    a.create(1)
+    a.append(1, 5)
+    a.swap_out(1)
+    with pytest.raises(pa.PAError):
+        a.set_swap_space(8)
+    with pytest.raises(pa.PAError):
+        a.batch_tables([1], 4)
+    a.swap_in(1)
+    a.set_swap_space(8)
+    assert a.swap_stats()["num_host_free"] == 8

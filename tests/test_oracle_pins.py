@@ -334,6 +334,30 @@ def test_copy_blocks_copies_whole_blocks():
         assert (kp[b] == k0[b]).all() and (vp[b] == v0[b]).all()
 
 
+def test_swap_blocks_moves_whole_blocks_between_pools():
+    # [NV] best practice 5 / [VI] §2.1: blocks leave for a host pool and come
+    # back; every other block of either pool stays as it was.
+    bs, h, d = 4, 2, 8
+    rng = np.random.default_rng(43)
+    kd = rng.standard_normal((6, h, bs, d)).astype(np.float32)
+    vd = rng.standard_normal((6, h, d, bs)).astype(np.float32)
+    kh = rng.standard_normal((3, h, bs, d)).astype(np.float32)
+    vh = rng.standard_normal((3, h, d, bs)).astype(np.float32)
+    kd0, vd0, kh0, vh0 = kd.copy(), vd.copy(), kh.copy(), vh.copy()
+    out = np.array([[5, 2], [1, 0]])
+    oracle.swap_blocks(kd, vd, kh, vh, out, "bhrd", "bhdr")
+    assert (kh[2] == kd0[5]).all() and (kh[0] == kd0[1]).all() and (kh[1] == kh0[1]).all()
+    assert (vh[2] == vd0[5]).all() and (vh[0] == vd0[1]).all() and (vh[1] == vh0[1]).all()
+    assert (kd == kd0).all() and (vd == vd0).all()
+    kd[[5, 1]] = 0.0
+    vd[[5, 1]] = 0.0
+    oracle.swap_blocks(kh, vh, kd, vd, np.array([[2, 3], [0, 4]]), "bhrd", "bhdr")
+    assert (kd[3] == kd0[5]).all() and (kd[4] == kd0[1]).all()
+    assert (vd[3] == vd0[5]).all() and (vd[4] == vd0[1]).all()
+    for b in (0, 2):
+        assert (kd[b] == kd0[b]).all() and (vd[b] == vd0[b]).all()
+
+
 def test_widen_is_exact():
     x = np.array([1.0, -2.5, 3.0e-39, np.inf, 65504.0, 1.0e38], dtype=np.float32)
     b = torch.from_numpy(x).to(torch.bfloat16)
