@@ -35,6 +35,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+FP8 = 2  # OCP E4M3 codes stored as uint8
 
 
 def build(force: bool = True) -> str:
@@ -65,7 +66,15 @@ def _load():
         lib.orc_widen.argtypes = [vp, i64, ctypes.c_int]
         lib.orc_decode.restype = None
         lib.orc_decode.argtypes = [vp, vp, ctypes.c_int, vp, _Strides, vp, _Strides,
-                                   ctypes.c_int, vp, i32, vp, i32, i32, i32, i32, i32, dbl]
+                                   ctypes.c_int, vp, i32, vp, i32, i32, i32, i32, i32, dbl, dbl,
+                                   dbl]
+        lib.orc_e4m3_decode.restype = dbl
+        lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_cache_write_fp8.restype = None
+        lib.orc_cache_write_fp8.argtypes = [vp, vp, ctypes.c_int, vp, _Strides, vp, _Strides, vp,
+                                            i32, i32, i32, i32, ctypes.c_float, ctypes.c_float]
         lib.orc_prefill.restype = None
         lib.orc_prefill.argtypes = [vp, vp, ctypes.c_int, vp, _Strides, vp, _Strides,
                                     ctypes.c_int, vp, i32, vp, vp, i32, i32, i32, i32, i32, dbl]
@@ -88,7 +97,10 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle takes float32 or bf16 bits (uint16), got {a.dtype}")
+    if a.dtype == np.uint8:
+        return FP8
+    raise TypeError(f"oracle takes float32, bf16 bits (uint16) or E4M3 codes (uint8), "
+                    f"got {a.dtype}")
 
 
 def _strides(pool: np.ndarray, axes: str) -> _Strides:
@@ -135,10 +147,11 @@ def unpage(pool: np.ndarray, axes: str, table, length: int, head: int) -> np.nda
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale,
-           k_axes="bhrd", v_axes="bhrd") -> np.ndarray:
+           k_axes="bhrd", v_axes="bhrd", k_scale=1.0, v_scale=1.0) -> np.ndarray:
     """Paged decode attention, fp64 ([VE] §3.1 and §3.3).
 
-    q: [S][Hq][D] (fp32 or bf16 bits); pools: 4-D with the given axes;
+    q: [S][Hq][D] (fp32 or bf16 bits); pools: 4-D with the given axes (fp32,
+    bf16 bits, or E4M3 codes whose values are multiplied by k_scale / v_scale);
     block_tables: [S][stride] int32; context_lens: [S] int32.
     Returns out[S][Hq][D] float64.
     """
@@ -155,8 +168,38 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale,
                    _ptr(k_cache), _strides(k_cache, k_axes),
                    _ptr(v_cache), _strides(v_cache, v_axes), _dtype_code(k_cache),
                    _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-                   s, hq, hkv, d, bs, float(scale))
+                   s, hq, hkv, d, bs, float(scale), float(k_scale), float(v_scale))
     return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP E4M3 codes (uint8), float64."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e4m3_decode(int(x)) for x in c.reshape(-1)]).reshape(c.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest OCP E4M3 codes of float32 values (ties to even, saturating)."""
+    lib = _load()
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([lib.orc_e4m3_encode(float(v)) for v in a.reshape(-1)],
+                    dtype=np.uint8).reshape(a.shape)
+
+
+def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                    k_axes="bhrd", v_axes="bhrd") -> None:
+    """Quantizing cache write into uint8 E4M3 pools: code = nearest E4M3 of
+    (x / scale) computed in binary32."""
+    lib = _load()
+    k_new, v_new = _c(k_new), _c(v_new)
+    slots = _c(slot_mapping, np.int64)
+    t, hkv, d = k_new.shape
+    _, hk2, bs, d2 = pool_dims(k_cache, k_axes)
+    assert (hk2, d2) == (hkv, d) and k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    lib.orc_cache_write_fp8(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
+                            _strides(k_cache, k_axes), _ptr(v_cache), _strides(v_cache, v_axes),
+                            _ptr(slots), t, hkv, d, bs, float(k_scale), float(v_scale))
 
 
 def prefill(q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,

@@ -17,8 +17,46 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* OCP 8-bit floating point, E4M3 variant: a sign bit, 4 exponent bits with
+ * bias 7 and 3 mantissa bits.  Exponent field 0 holds the subnormals
+ * m * 2^-9; otherwise the value is (1 + m/8) * 2^(e-7).  There are no
+ * infinities: S.1111.111 is NaN, so the largest magnitude is 448. */
+double orc_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* The E4M3 code nearest to x, by search over every finite code; a tie goes
+ * to the code whose last bit is 0 (round half to even).  Magnitudes beyond
+ * 448, infinities included, saturate to +-448; NaN gives 0x7F. */
+uint8_t orc_e4m3_encode(float x)
+{
+    if (isnan(x)) return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isinf(x)) return (uint8_t)(sign | 0x7E);
+    double a = fabs((double)x);
+    int best = 0;
+    double best_err = a;  /* code 0 is +0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(orc_e4m3_decode((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
 double orc_widen(const void *base, int64_t index, int dtype)
 {
+    if (dtype == ORC_FP8) {
+        uint8_t c;
+        memcpy(&c, (const char *)base + index, 1);
+        return orc_e4m3_decode(c);
+    }
     if (dtype == ORC_F32) {
         float f;
         memcpy(&f, (const char *)base + index * 4, 4);
@@ -93,7 +131,7 @@ void orc_decode(double *out, const void *q, int q_dtype,
                 const int32_t *block_tables, int32_t table_stride,
                 const int32_t *context_lens, int32_t num_seqs,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                int32_t block_size, double scale)
+                int32_t block_size, double scale, double k_scale, double v_scale)
 {
     int32_t group = num_q_heads / num_kv_heads;
     int32_t max_len = 0;
@@ -111,6 +149,11 @@ void orc_decode(double *out, const void *q, int q_dtype,
             int32_t kvh = h / group;
             orc_unpage(k_cache, ks, kv_dtype, table, block_size, L, kvh, head_dim, K);
             orc_unpage(v_cache, vs, kv_dtype, table, block_size, L, kvh, head_dim, V);
+            /* stored values times the cache's scale (exact in double) */
+            for (int64_t i = 0; i < (int64_t)L * head_dim; ++i) {
+                K[i] *= k_scale;
+                V[i] *= v_scale;
+            }
             int64_t qoff = ((int64_t)s * num_q_heads + h) * head_dim;
             for (int32_t d = 0; d < head_dim; ++d)
                 qv[d] = orc_widen(q, qoff + d, q_dtype);
@@ -193,6 +236,32 @@ void orc_cache_write(const void *k_new, const void *v_new,
                 memcpy((char *)v_cache + vdst * elem_size, (const char *)v_new + src * elem_size, (size_t)elem_size);
             }
         }
+    }
+}
+
+/* fp8 cache write: each element of the new rows is divided by its cache's
+ * scale in binary32 (correctly rounded) and stored as the nearest E4M3 code
+ * (orc_e4m3_encode).  Slots and layout as in orc_cache_write. */
+void orc_cache_write_fp8(const void *k_new, const void *v_new, int in_dtype,
+                         uint8_t *k_cache, orc_strides ks, uint8_t *v_cache, orc_strides vs,
+                         const int64_t *slot_mapping, int32_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         float k_scale, float v_scale)
+{
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        int64_t b = slot / block_size, r = slot % block_size;
+        for (int32_t h = 0; h < num_kv_heads; ++h)
+            for (int32_t d = 0; d < head_dim; ++d) {
+                int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + d;
+                float kx = (float)orc_widen(k_new, src, in_dtype);
+                float vx = (float)orc_widen(v_new, src, in_dtype);
+                k_cache[b * ks.block + h * ks.head + r * ks.row + d * ks.dim] =
+                    orc_e4m3_encode(kx / k_scale);
+                v_cache[b * vs.block + h * vs.head + r * vs.row + d * vs.dim] =
+                    orc_e4m3_encode(vx / v_scale);
+            }
     }
 }
 

@@ -25,7 +25,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };  /* FP8: OCP E4M3 codes */
 
 /* Element strides of one paged pool: element (block b, kv head h, row r, dim d)
  * sits at b*block + h*head + r*row + d*dim. */
@@ -33,7 +33,19 @@ typedef struct {
     int64_t block, head, row, dim;
 } orc_strides;
 
-/* Widen one stored element (fp32 or bf16 bits) to double, exactly. */
+/* OCP E4M3 code -> value (NaN for S.1111.111), and value -> nearest code
+ * (ties to the even code, saturating at +-448, NaN -> 0x7F). */
+double orc_e4m3_decode(uint8_t c);
+uint8_t orc_e4m3_encode(float x);
+
+/* Quantizing cache write: code = nearest E4M3 of (x / scale) in binary32. */
+void orc_cache_write_fp8(const void *k_new, const void *v_new, int in_dtype,
+                         uint8_t *k_cache, orc_strides ks, uint8_t *v_cache, orc_strides vs,
+                         const int64_t *slot_mapping, int32_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         float k_scale, float v_scale);
+
+/* Widen one stored element (fp32, bf16 bits or an E4M3 code) to double, exactly. */
 double orc_widen(const void *base, int64_t index, int dtype);
 
 /* Un-page one sequence of one kv head: out[t][d] for t < len. */
@@ -52,7 +64,7 @@ void orc_decode(double *out, const void *q, int q_dtype,
                 const int32_t *block_tables, int32_t table_stride,
                 const int32_t *context_lens, int32_t num_seqs,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                int32_t block_size, double scale);
+                int32_t block_size, double scale, double k_scale, double v_scale);
 
 /* Paged causal prefill over a chunk of new query rows per request. */
 void orc_prefill(double *out, const void *q, int q_dtype,

@@ -28,6 +28,13 @@ MUTANTS = {
     "copy_k_only": ("memcpy((char *)v_cache + (dst * vs.block + vo) * elem_size,",
                     "if (0) memcpy((char *)v_cache + (dst * vs.block + vo) * elem_size,"),
     "bf16_widen": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = ((uint32_t)h << 16) | 1u;"),
+    "e4m3_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    "e4m3_ties_up": ("(err == best_err && (c & 1) == 0 && (best & 1) == 1)",
+                     "(err == best_err)"),
+    "e4m3_no_saturation": ("if (isinf(x)) return (uint8_t)(sign | 0x7E);",
+                           "if (isinf(x)) return (uint8_t)(sign | 0x7F);"),
+    "fp8_scale_dropped": ("K[i] *= k_scale;", "K[i] *= 1.0;"),
+    "fp8_write_scale": ("orc_e4m3_encode(vx / v_scale);", "orc_e4m3_encode(vx * v_scale);"),
 }
 
 

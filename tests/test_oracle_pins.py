@@ -364,3 +364,84 @@ def test_widen_is_exact():
     bbits = b.view(torch.int16).numpy().view(np.uint16)
     assert (oracle.widen(bbits) == b.to(torch.float64).numpy()).all()
     assert (oracle.widen(x) == x.astype(np.float64)).all()
+
+
+# -- fp8 (OCP E4M3) codec and the quantized cache -------------------------------
+# The pages give no fp8 format or scale; the reading here (OCP E4M3, one scale per
+# cache, values beyond 448 saturate) is pinned against torch's float8_e4m3fn,
+# which follows the same OCP definition.
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all() and nan.sum() == 2  # 0x7F and 0xFF
+    assert (ours[~nan] == ref[~nan]).all()
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_matches_torch_in_range_with_ties():
+    finite = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = oracle.e4m3_decode(finite)
+    mids = (vals[:-1] + vals[1:]) / 2  # every tie between neighbouring codes
+    rng = np.random.default_rng(7)
+    rand = rng.uniform(-460, 460, 4000)
+    small = rng.uniform(-0.02, 0.02, 2000)
+    x = np.concatenate([vals, -vals, mids, -mids, rand, small]).astype(np.float32)
+    x = x[np.abs(x) < 464]  # torch gives NaN past 464; this oracle saturates there
+    ours = oracle.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (ours == ref).all()
+
+
+def test_e4m3_encode_round_trip_saturation_and_nan():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert (oracle.e4m3_encode(oracle.e4m3_decode(codes).astype(np.float32)) == codes).all()
+    big = np.array([464.0, 470.0, 1e9, np.inf, -500.0, -np.inf], dtype=np.float32)
+    assert list(oracle.e4m3_encode(big)) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert oracle.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] == 0x7F
+    # monotone: a larger value never gets a smaller magnitude code
+    x = np.sort(np.random.default_rng(3).uniform(0, 450, 3000)).astype(np.float32)
+    v = oracle.e4m3_decode(oracle.e4m3_encode(x))
+    assert (np.diff(v) >= 0).all()
+
+
+def test_cache_write_fp8_quantizes_each_element_by_its_cache_scale():
+    bs, h, d, nb = 4, 2, 8, 3
+    rng = np.random.default_rng(5)
+    k_new = (rng.standard_normal((5, h, d)) * 3).astype(np.float32)
+    v_new = (rng.standard_normal((5, h, d)) * 3).astype(np.float32)
+    kp = np.full((nb, h, bs, d), 0xAA, dtype=np.uint8)
+    vp = np.full((nb, h, d, bs), 0xAA, dtype=np.uint8)
+    slots = np.array([0, 5, 11, -1, 6])
+    ks, vs = np.float32(0.05), np.float32(0.0625)
+    oracle.cache_write_fp8(k_new, v_new, kp, vp, slots, ks, vs, "bhrd", "bhdr")
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, r = slot // bs, slot % bs
+        want_k = torch.from_numpy(k_new[t] / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+        want_v = torch.from_numpy(v_new[t] / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert (kp[b, :, r, :] == want_k.numpy()).all()
+        assert (vp[b, :, :, r] == want_v.numpy()).all()
+    assert (kp[0, :, 2] == 0xAA).all()  # slot 2 untouched; the -1 slot wrote nothing
+
+
+def test_decode_on_fp8_pools_uses_scaled_values():
+    # an fp8 pool decodes exactly like an fp32 pool holding code value * scale
+    bs, h, d = 4, 2, 8
+    rng = np.random.default_rng(9)
+    codes_k = rng.integers(0, 256, (4, h, bs, d)).astype(np.uint8)
+    codes_v = rng.integers(0, 256, (4, h, d, bs)).astype(np.uint8)
+    for c in (codes_k, codes_v):
+        c[(c & 0x7F) == 0x7F] = 0x10  # no NaN codes
+    ks, vs = 0.03125, 0.75  # products with E4M3 values stay exact in fp32
+    fk = (oracle.e4m3_decode(codes_k) * ks).astype(np.float32)
+    fv = (oracle.e4m3_decode(codes_v) * vs).astype(np.float32)
+    q = rng.standard_normal((2, 4, d)).astype(np.float32)
+    tables = np.array([[2, 0, 3], [1, 3, 0]], dtype=np.int32)
+    lens = np.array([11, 6], dtype=np.int32)
+    a = oracle.decode(q, codes_k, codes_v, tables, lens, 0.35, "bhrd", "bhdr", ks, vs)
+    b = oracle.decode(q, fk, fv, tables, lens, 0.35, "bhrd", "bhdr")
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
