@@ -55,7 +55,15 @@ typedef enum {
     PA_ERR_DEVICE = 5         /* the HIP runtime refused a launch              */
 } pa_status;
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+typedef enum {
+    PA_DTYPE_F32 = 0,
+    PA_DTYPE_BF16 = 1,
+    /* OCP 8-bit float, E4M3 variant (bias 7, no infinities, NaN = S.1111.111,
+     * largest magnitude 448); a cache of such codes has one scale per K or V
+     * cache: value = code * scale.  Accepted by the fp8 calls and by the
+     * block copies. */
+    PA_DTYPE_FP8_E4M3 = 2
+} pa_dtype;
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char *pa_last_error(void);
@@ -190,6 +198,40 @@ pa_status pa_prefill_chunk(float *out, const void *q,
                            int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks,
                            float scale, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* fp8 KV cache                                                               */
+/* ------------------------------------------------------------------------ */
+/* The pages name no fp8 format or scale convention; this library's: K and V
+ * caches of OCP E4M3 codes (PA_DTYPE_FP8_E4M3, 1 byte per element, the same
+ * block layouts as above), each with one fp32 scale: value = code * scale.
+ * Halving the bytes per token halves what decode must stream from HBM
+ * ([VE] §1 / §3.3: decode is bound by memory bandwidth). */
+
+/* Quantizing cache write: element x of a new row is stored as the nearest
+ * E4M3 code of x / scale (binary32 division, correctly rounded; ties to the
+ * even code; magnitudes past 448, infinities included, saturate to +-448; a
+ * NaN input stores 0x7F).  k_new / v_new [num_tokens][Hkv][D] in in_dtype
+ * (F32 or BF16); slots, skipping and errors as pa_cache_write; scales finite
+ * and > 0. */
+pa_status pa_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dtype,
+                             void *k_cache, void *v_cache, const int64_t *slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, float k_scale,
+                             float v_scale, void *stream);
+
+/* pa_decode_ex over fp8 caches: q is bf16 [S][Hq][D]; a K code's value is
+ * code * k_scale and a V code's code * v_scale.  Codes are widened to bf16
+ * exactly; the scales enter in fp32 (k_scale with the softmax scale, v_scale
+ * on the output).  Every other argument, the workspace and the error
+ * behaviour are those of pa_decode_ex. */
+pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, int32_t block_table_stride,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, float scale, float k_scale, float v_scale,
+                        int32_t max_context_len, int32_t partition_size, void *workspace,
+                        size_t workspace_bytes, uint32_t flags, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator                                                       */

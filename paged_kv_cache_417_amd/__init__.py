@@ -27,6 +27,7 @@ PA_ERR_UNSUPPORTED = 4
 PA_ERR_DEVICE = 5
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
+PA_DTYPE_FP8_E4M3 = 2  # OCP E4M3 codes, stored in torch.uint8 tensors
 PA_DECODE_KV_REUSE = 1
 
 # Axis order of the two pools, in the letters b (block), h (kv head),
@@ -44,6 +45,7 @@ EXPORTED = (
     "pa_batch_append", "pa_batch_tables", "pa_seq_create_prefix", "pa_seq_append_tokens",
     "pa_batch_append_tokens", "pa_prefix_cache_stats", "pa_allocator_set_swap_space",
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
+    "pa_cache_write_fp8", "pa_decode_fp8",
 )
 
 
@@ -114,6 +116,10 @@ def _declare(lib):
         "pa_swap_stats": (st, [vp, ctypes.POINTER(SwapStats)]),
         "pa_swap_blocks": (st, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, ctypes.c_int,
                                 vp]),
+        "pa_cache_write_fp8": (st, [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                    f32, vp]),
+        "pa_decode_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                               f32, i32, i32, vp, sz, ctypes.c_uint32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -145,6 +151,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PA_DTYPE_BF16
     if t.dtype == torch.float32:
         return PA_DTYPE_F32
+    if t.dtype == torch.uint8:
+        return PA_DTYPE_FP8_E4M3
     return 99  # rejected by the library as an invalid dtype
 
 
@@ -238,6 +246,31 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _check(_lib.pa_decode_ex(*args, PA_DECODE_KV_REUSE, ctypes.c_void_p(_stream(stream))))
     else:
         _check(_lib.pa_decode(*args, ctypes.c_void_p(_stream(stream))))
+
+
+def pa_cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                       stream=None) -> None:
+    """Quantizing write of bf16/fp32 rows into uint8 (E4M3) caches."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    _check(_lib.pa_cache_write_fp8(_p(k_new), _p(v_new), _dtype_code(k_new), _p(k_cache),
+                                   _p(v_cache), _p(slot_mapping), k_new.shape[0], hkv, d, bs, nb,
+                                   float(k_scale), float(v_scale),
+                                   ctypes.c_void_p(_stream(stream))))
+
+
+def pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                  max_context_len, partition_size=0, workspace=None, stream=None,
+                  kv_reuse=False) -> None:
+    """Paged decode over uint8 (E4M3) caches; q is bf16."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    s, hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_fp8(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                              block_tables.shape[1], _p(context_lens), s, hq, hkv, d, bs, nb,
+                              float(scale), float(k_scale), float(v_scale), int(max_context_len),
+                              int(partition_size), _p(workspace), ws_bytes,
+                              PA_DECODE_KV_REUSE if kv_reuse else 0,
+                              ctypes.c_void_p(_stream(stream))))
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,

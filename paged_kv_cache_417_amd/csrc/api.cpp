@@ -17,6 +17,9 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
 bool supported_block_size(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 bool valid_dtype(pa_dtype t) { return t == PA_DTYPE_F32 || t == PA_DTYPE_BF16; }
+// Element types a block copy can move (it only moves bytes).
+bool valid_block_dtype(pa_dtype t) { return valid_dtype(t) || t == PA_DTYPE_FP8_E4M3; }
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kMaxGroup = 16;
@@ -90,12 +93,37 @@ pa_status pa_cache_write(const void *k_new, const void *v_new, void *k_cache, vo
     return pa::ok();
 }
 
+pa_status pa_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dtype,
+                             void *k_cache, void *v_cache, const int64_t *slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, float k_scale, float v_scale,
+                             void *stream) {
+    const char *fn = "pa_cache_write_fp8";
+    if (num_tokens < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_tokens %d", fn, num_tokens);
+    if (!valid_dtype(in_dtype))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: input dtype %d", fn, (int)in_dtype);
+    if (!valid_scale(k_scale) || !valid_scale(v_scale))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: scales must be finite and > 0", fn);
+    if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
+    if (!k_cache || !v_cache || (num_tokens > 0 && (!k_new || !v_new || !slot_mapping)))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    int rc = pa::launch_cache_write_fp8(k_new, v_new, in_dtype, k_cache, v_cache, slot_mapping,
+                                        num_tokens, num_kv_heads, head_dim, block_size,
+                                        num_blocks, k_scale, v_scale, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int32_t num_blocks, pa_dtype dtype, void *stream) {
     const char *fn = "pa_copy_blocks";
     if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_pairs %d", fn, num_pairs);
-    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (!valid_block_dtype(dtype))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
     if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
     if (!k_cache || !v_cache || (num_pairs > 0 && !src_dst))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -113,7 +141,8 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_block
                          int32_t block_size, pa_dtype dtype, void *stream) {
     const char *fn = "pa_swap_blocks";
     if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_pairs %d", fn, num_pairs);
-    if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (!valid_block_dtype(dtype))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
     if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, src_blocks)) return st;
     if (dst_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: dst_blocks %d", fn, dst_blocks);
     if (!src_k || !src_v || !dst_k || !dst_v || (num_pairs > 0 && !src_dst))
@@ -167,14 +196,22 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                         dtype, 0u, stream);
 }
 
-pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const void *v_cache,
-                       const int32_t *block_tables, int32_t block_table_stride,
-                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                       int32_t num_blocks, float scale, int32_t max_context_len,
-                       int32_t partition_size, void *workspace, size_t workspace_bytes,
-                       pa_dtype dtype, uint32_t flags, void *stream) {
-    const char *fn = "pa_decode";
+}  // extern "C"
+
+namespace {
+
+// Shared body of the decode entry points.  fp8: the caches hold E4M3 codes
+// scaled by k_scale / v_scale and q is bf16 (dtype must be BF16).
+pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t max_context_len, int32_t partition_size, void *workspace,
+                      size_t workspace_bytes, pa_dtype dtype, uint32_t flags, bool fp8,
+                      float k_scale, float v_scale, void *stream) {
+    if (fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale)))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: scales must be finite and > 0", fn);
     if (flags & ~(uint32_t)PA_DECODE_KV_REUSE)
         return pa::fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
     if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
@@ -231,8 +268,10 @@ pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const voi
     p.max_context_len = max_context_len;
     p.partition_size = ps;
     p.np_max = (int32_t)np_max;
-    p.scale_log2 = scale * kLog2e;
+    p.scale_log2 = fp8 ? scale * k_scale * kLog2e : scale * kLog2e;
     p.kv_reuse = (flags & PA_DECODE_KV_REUSE) != 0;
+    p.kv_fp8 = fp8;
+    p.v_scale = fp8 ? v_scale : 1.f;
     if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_max, &p.ws_ml,
                                              &p.ws_o);
     int rc = dtype == PA_DTYPE_BF16 ? pa::launch_decode_mfma(p, stream)
@@ -241,6 +280,37 @@ pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const voi
     rc = pa::launch_decode_reduce(p, stream);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: reduce launch failed (hip error %d)", fn, rc);
     return pa::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, int32_t block_table_stride,
+                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t max_context_len,
+                       int32_t partition_size, void *workspace, size_t workspace_bytes,
+                       pa_dtype dtype, uint32_t flags, void *stream) {
+    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, block_table_stride,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, max_context_len, partition_size, workspace,
+                       workspace_bytes, dtype, flags, false, 1.f, 1.f, stream);
+}
+
+pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, int32_t block_table_stride,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, float scale, float k_scale, float v_scale,
+                        int32_t max_context_len, int32_t partition_size, void *workspace,
+                        size_t workspace_bytes, uint32_t flags, void *stream) {
+    return decode_impl("pa_decode_fp8", out, q, k_cache, v_cache, block_tables,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, max_context_len, partition_size,
+                       workspace, workspace_bytes, PA_DTYPE_BF16, flags, true, k_scale, v_scale,
+                       stream);
 }
 
 pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,

@@ -9,7 +9,8 @@
 //
 // Layout: k_cache [NB][Hkv][BS][D] (token rows contiguous),
 //         v_cache [NB][Hkv][D][BS] (dimension rows contiguous).
-// Both kernels only move bits: no value is converted.
+// The bf16/fp32 write and the block copies only move bits; the fp8 write
+// quantizes to OCP E4M3 codes with one scale per cache.
 #include "device_common.h"
 #include "launch.h"
 
@@ -142,6 +143,61 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     }
 }
 
+// Nearest E4M3 codes of x / scale for four values, packed lowest first.  The
+// division is binary32, correctly rounded; the hardware conversion rounds to
+// nearest even but turns magnitudes past 448 into NaN, so values are clamped
+// to +-448 first (saturation), and a NaN input gets the code 0x7F.
+__device__ __forceinline__ uint32_t e4m3_quant4(const float *x, float scale) {
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(x[i] / scale, -448.f), 448.f);
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)w, true);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (x[i] != x[i]) w = (w & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+    return w;
+}
+
+// fp8 cache write: one thread per (token, kv head, 16 dims).  K: the 16
+// codes are one 16-byte store into the token's row; V: one byte into each of
+// the 16 dim rows.
+template <typename T>
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const T *__restrict__ k_new, const T *__restrict__ v_new, uint8_t *__restrict__ k_cache,
+    uint8_t *__restrict__ v_cache, const int64_t *__restrict__ slots, int32_t num_tokens,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    float k_scale, float v_scale) {
+    const int32_t chunks = head_dim / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)num_tokens * num_kv_heads * chunks) return;
+    const int32_t c = (int32_t)(idx % chunks);
+    const int64_t th = idx / chunks;  // token * Hkv + head
+    const int32_t h = (int32_t)(th % num_kv_heads);
+    const int64_t slot = slots[th / num_kv_heads];
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const int64_t b = slot / block_size;
+    const int32_t o = (int32_t)(slot % block_size);
+    const int64_t src = th * head_dim + (int64_t)c * 16;
+    float kx[16], vx[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        kx[i] = (float)k_new[src + i];
+        vx[i] = (float)v_new[src + i];
+    }
+    u32x4 kw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kw[i] = e4m3_quant4(kx + 4 * i, k_scale);
+    st16(k_cache + ((b * num_kv_heads + h) * block_size + o) * head_dim + (int64_t)c * 16, kw);
+    uint8_t *vrow = v_cache + ((b * num_kv_heads + h) * head_dim + (int64_t)c * 16) * block_size + o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t vw = e4m3_quant4(vx + 4 * i, v_scale);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vrow[(int64_t)(4 * i + e) * block_size] = (uint8_t)(vw >> (8 * e));
+    }
+}
+
 // One thread per 16 bytes of one pair's K or V block region (both regions are
 // Hkv*BS*D contiguous elements).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
@@ -218,7 +274,7 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, pa_dtype dtype, void *stream) {
     if (num_pairs == 0) return 0;
-    const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : 4;
+    const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : dtype == PA_DTYPE_FP8_E4M3 ? 1 : 4;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem;
     const int64_t total = (int64_t)num_pairs * 2 * (block_bytes / 16);
     const dim3 grid((unsigned)((total + 255) / 256));
@@ -233,7 +289,7 @@ int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks,
                        int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, pa_dtype dtype, void *stream) {
     if (num_pairs == 0) return 0;
-    const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : 4;
+    const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : dtype == PA_DTYPE_FP8_E4M3 ? 1 : 4;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem;
     const int64_t total = (int64_t)num_pairs * 2 * (block_bytes / 16);
     if ((total + 255) / 256 > 0xffffffffLL) return (int)hipErrorInvalidValue;
@@ -241,6 +297,29 @@ int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks,
     hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                        (const char *)src_k, (const char *)src_v, (char *)dst_k, (char *)dst_v,
                        src_dst, num_pairs, block_bytes, src_blocks, dst_blocks);
+    return (int)hipGetLastError();
+}
+
+int launch_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dtype,
+                           void *k_cache, void *v_cache, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float k_scale,
+                           float v_scale, void *stream) {
+    if (num_tokens == 0) return 0;
+    const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 16);
+    const int64_t groups = (threads + 255) / 256;
+    if (groups > 0xffffffffLL) return (int)hipErrorInvalidValue;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (in_dtype == PA_DTYPE_BF16)
+        hipLaunchKernelGGL(cache_write_fp8_kernel<__bf16>, dim3((unsigned)groups), dim3(256), 0, s,
+                           (const __bf16 *)k_new, (const __bf16 *)v_new, (uint8_t *)k_cache,
+                           (uint8_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                           block_size, num_blocks, k_scale, v_scale);
+    else
+        hipLaunchKernelGGL(cache_write_fp8_kernel<float>, dim3((unsigned)groups), dim3(256), 0, s,
+                           (const float *)k_new, (const float *)v_new, (uint8_t *)k_cache,
+                           (uint8_t *)v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                           block_size, num_blocks, k_scale, v_scale);
     return (int)hipGetLastError();
 }
 

@@ -35,6 +35,14 @@
 // scores and zero V elements (NaN-poisoned rows cannot leak), and their
 // addresses are clamped onto the last valid token so no unallocated block is
 // touched.
+//
+// fp8 cache (OCP E4M3 codes, one scale per cache).  The same walk reads half
+// the bytes: a lane's 16 K dims of a token are one 16-byte load, its 8 V
+// tokens of a dim one 8-byte load.  Codes become bf16 exactly in registers
+// (e4m3x8_to_bf16x8) and feed the same MFMAs; the K scale is folded into the
+// score scale and the V scale into the output, both in fp32.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,6 +90,58 @@ __device__ __forceinline__ void load_step(StepRegs<D> &r, const uint16_t *__rest
     for (int j = 0; j < D / 16; ++j)
         r.vt[j] = NT && BS <= 32 ? ld16_nt(vp + (int64_t)j * 16 * BS)
                                  : ld16(vp + (int64_t)j * 16 * BS);
+}
+
+// fp8 step registers: K codes of tiles a and b (16 dims per 16-byte load:
+// k-slots 2p and 2p+1), V codes (8 tokens of one dim per 8-byte load).
+template <int D>
+struct StepRaw8 {
+    u32x4 k[2][D / 64];
+    u32x2 vt[D / 16];
+};
+
+template <int D, int BS, bool TAIL, bool NT>
+__device__ __forceinline__ void load_step_fp8(StepRaw8<D> &r, const uint8_t *__restrict__ kc,
+                                              const uint8_t *__restrict__ vc, int32_t t0,
+                                              int32_t L, int32_t bidA, int32_t bidB, int32_t hkv,
+                                              int32_t kvh, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+    int ta = t0 + 8 * (n >> 2) + (n & 3);
+    int tb = ta + 4;
+    int tv = t0 + 8 * g;
+    if (TAIL) {
+        ta = min(ta, L - 1);
+        tb = min(tb, L - 1);
+        tv = min(tv, (L - 1) & ~7);
+    }
+    const int32_t ba = (BS == 16 && ta - t0 >= 16) ? bidB : bidA;
+    const int32_t bb = (BS == 16 && tb - t0 >= 16) ? bidB : bidA;
+    const int32_t bv = (BS == 16 && tv - t0 >= 16) ? bidB : bidA;
+    const uint8_t *ka = kc + (((int64_t)ba * hkv + kvh) * BS + (ta % BS)) * D + 16 * g;
+    const uint8_t *kb = kc + (((int64_t)bb * hkv + kvh) * BS + (tb % BS)) * D + 16 * g;
+    const uint8_t *vp = vc + (((int64_t)bv * hkv + kvh) * D + n) * BS + (tv % BS);
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        r.k[0][c] = NT ? ld16_nt(ka + 64 * c) : ld16(ka + 64 * c);
+        r.k[1][c] = NT ? ld16_nt(kb + 64 * c) : ld16(kb + 64 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+        r.vt[j] = NT && BS <= 32 ? ld8_nt(vp + (int64_t)j * 16 * BS) : ld8(vp + (int64_t)j * 16 * BS);
+}
+
+// fp8 codes -> the bf16 step registers compute_step takes (exact).
+template <int D>
+__device__ __forceinline__ void widen_step(const StepRaw8<D> &r, StepRegs<D> &o) {
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        o.ka[2 * c] = e4m3x8_to_bf16x8(u32x2{r.k[0][c][0], r.k[0][c][1]});
+        o.ka[2 * c + 1] = e4m3x8_to_bf16x8(u32x2{r.k[0][c][2], r.k[0][c][3]});
+        o.kb[2 * c] = e4m3x8_to_bf16x8(u32x2{r.k[1][c][0], r.k[1][c][1]});
+        o.kb[2 * c + 1] = e4m3x8_to_bf16x8(u32x2{r.k[1][c][2], r.k[1][c][3]});
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) o.vt[j] = e4m3x8_to_bf16x8(r.vt[j]);
 }
 
 template <int D, bool TAIL>
@@ -148,10 +208,11 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
 }
 
 // Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
-// in 256 registers without spills.
-template <int D, int BS, bool NT>
+// in 256 registers without spills.  FP8: the cache holds E4M3 codes.
+template <int D, int BS, bool NT, bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
     DecodeParams p) {
+    using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
     const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
     const int kvh = item.kvh;
     const int s = item.seq;
@@ -226,25 +287,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     };
     // Step s covers tokens t_begin + 32 s .. +31.  Loads clamp past the end
     // of the context (a no-op except in the tail step), compute masks there.
-    auto issue = [&](StepRegs<D> &r, int32_t st) {
+    auto issue = [&](Regs &r, int32_t st) {
         const int32_t t0 = t_begin + 32 * st;
         const int32_t bA = block_id(t0 / BS);
         const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, b_last)) : bA;
-        load_step<D, BS, true, NT>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
-    };
-    auto consume = [&](const StepRegs<D> &r, int32_t st) {
-        const int32_t t0 = t_begin + 32 * st;
-        if (has_tail && st == nsteps - 1)
-            compute_step<D, true>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        if constexpr (FP8)
+            load_step_fp8<D, BS, true, NT>(r, reinterpret_cast<const uint8_t *>(p.k_cache),
+                                           reinterpret_cast<const uint8_t *>(p.v_cache), t0, L,
+                                           bA, bB, p.num_kv_heads, kvh, lane);
         else
-            compute_step<D, false>(r, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+            load_step<D, BS, true, NT>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
+    };
+    auto consume = [&](const Regs &raw, int32_t st) {
+        const int32_t t0 = t_begin + 32 * st;
+        const StepRegs<D> *rp;
+        StepRegs<D> wide;
+        if constexpr (FP8) {
+            widen_step<D>(raw, wide);
+            rp = &wide;
+        } else {
+            rp = &raw;
+        }
+        if (has_tail && st == nsteps - 1)
+            compute_step<D, true>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        else
+            compute_step<D, false>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
     };
 
     // Two register buffers in ping-pong: while one step is consumed the next
     // one's loads are in flight.  No buffer is ever copied into the other, so
     // the wait before a step's math covers that step's loads only.
     if (nsteps > 0) {
-        StepRegs<D> ra, rb;
+        Regs ra, rb;
         issue(ra, 0);
         int32_t st = 0;
         for (; st + 1 < nsteps; st += 2) {
@@ -259,8 +333,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     lsum = rows4_sum(lsum);
     if (!live) return;
     const float qnan = __builtin_nanf("");
+    // An fp8 cache's V scale multiplies the output (1 for bf16).
+    const float vs = FP8 ? p.v_scale : 1.f;
     if (np == 1) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const float inv = lsum > 0.f ? vs / lsum : 0.f;
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
             floatx4 o = acc[j] * inv;
@@ -272,7 +348,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         float *o_part = p.ws_o + slot * D;
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-            floatx4 o = acc[j];
+            floatx4 o = FP8 ? acc[j] * vs : acc[j];
             if (bad_block) o = floatx4{qnan, qnan, qnan, qnan};
             *reinterpret_cast<floatx4 *>(o_part + 16 * j + 4 * g) = o;
         }
@@ -286,10 +362,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
-    if (p.kv_reuse)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false>), grid, dim3(64), 0, s, p);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, true>), grid, dim3(64), 0, s, p);
+    if (p.kv_fp8) {
+        if (p.kv_reuse)
+            hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false, true>), grid, dim3(64), 0, s, p);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<D, BS, true, true>), grid, dim3(64), 0, s, p);
+    } else if (p.kv_reuse) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false, false>), grid, dim3(64), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, BS, true, false>), grid, dim3(64), 0, s, p);
+    }
 }
 
 }  // namespace

@@ -24,6 +24,31 @@ __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 8-byte global loads (one dwordx2 per lane), plain and nontemporal.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+__device__ __forceinline__ u32x2 ld8_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+
+// Eight OCP E4M3 codes (bytes of w, lowest first) -> eight bf16 values, in
+// order.  The hardware conversion to fp32 is exact, and an E4M3 value has at
+// most four significant bits, so the top half of each fp32 is the same value
+// in bf16: no rounding anywhere.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);  // codes 4h, 4h+1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);   // codes 4h+2, 4h+3
+        r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]),
+                                         0x07060302u);
+        r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]),
+                                             0x07060302u);
+    }
+    return r;
+}
+
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -31,8 +31,10 @@ struct DecodeParams {
     int32_t max_context_len;
     int32_t partition_size;
     int32_t np_max;    // ceil(max_context_len / partition_size), >= 1
-    float scale_log2;  // scale * log2(e)
+    float scale_log2;  // scale * log2(e) (times the K scale for an fp8 cache)
     bool kv_reuse;     // keep K/V cached (shared blocks) instead of streaming them
+    bool kv_fp8;       // K/V hold OCP E4M3 codes (q stays bf16)
+    float v_scale;     // value of a V code = code * v_scale (1 for bf16)
 };
 
 struct PrefillParams {
@@ -66,6 +68,14 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                        const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                        int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
                        void *stream);
+
+// Quantizing write into an fp8 (OCP E4M3) cache: code = nearest E4M3 of
+// x / scale (binary32 division), saturating at +-448.
+int launch_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dtype,
+                           void *k_cache, void *v_cache, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float k_scale,
+                           float v_scale, void *stream);
 
 int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

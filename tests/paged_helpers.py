@@ -17,6 +17,8 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy()
+    if t.dtype == torch.uint8:  # E4M3 codes
+        return t.numpy()
     raise TypeError(t.dtype)
 
 
@@ -46,11 +48,13 @@ def gather_blocks(k_pool, v_pool, tables, lengths, rows, block_size):
 
 
 def oracle_decode_rows(q, k_pool, v_pool, tables, lengths, rows, block_size, scale,
-                       k_axes, v_axes):
-    """fp64 oracle outputs for sequences ``rows`` of a device batch."""
+                       k_axes, v_axes, k_scale=1.0, v_scale=1.0):
+    """fp64 oracle outputs for sequences ``rows`` of a device batch (pools of
+    fp32, bf16 or E4M3 codes with their scales)."""
     k_sub, v_sub, t_sub, l_sub = gather_blocks(k_pool, v_pool, tables, lengths, rows, block_size)
     q_sub = host_bits(q[torch.as_tensor(list(rows), device=q.device, dtype=torch.long)])
-    return oracle.decode(q_sub, k_sub, v_sub, t_sub, l_sub, scale, k_axes, v_axes)
+    return oracle.decode(q_sub, k_sub, v_sub, t_sub, l_sub, scale, k_axes, v_axes,
+                         k_scale, v_scale)
 
 
 def chunked_checksum(t: torch.Tensor, chunk: int = 1 << 28) -> tuple[int, int]:

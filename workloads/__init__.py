@@ -20,6 +20,9 @@ Workload shapes (one per named case):
                 partitions of 512) plus 4 prefill chunks of 512 new tokens over
                 4096 cached ones; 32 query / 8 kv heads, head_dim 128, bf16,
                 8,192-block pool
+  fp8 variants  any decode shape with dtype "fp8": K/V pools of OCP E4M3 codes
+                of N(0,1) / 2^-6 (torch's float8_e4m3fn cast), poison code 0x7F,
+                q in bf16
   chat          (prefix cache) 128 requests, each opening with one of 16
                 system prompts of 2048 + j tokens (j = 1 + i mod 15) and going
                 on with 16..512 user tokens; token ids uniform over 32,000
@@ -49,7 +52,7 @@ class DecodeShape:
     head_dim: int
     block_size: int
     num_blocks: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (E4M3 K/V codes, bf16 q)
     seed: int
     partition_size: int = 0  # 0: library default
 
@@ -59,6 +62,11 @@ class DecodeShape:
 
     @property
     def torch_dtype(self):
+        """dtype of the K/V pools (uint8 codes for fp8)."""
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[self.dtype]
+
+    @property
+    def q_dtype(self):
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
 
@@ -123,6 +131,20 @@ def randn(shape, dtype, generator: torch.Generator, device) -> torch.Tensor:
     return x.to(dtype)
 
 
+# Scale of the fp8 workloads' K and V caches: value = code * FP8_SCALE, so
+# N(0,1) rows (|x| < 7 in practice) use codes up to about 448.
+FP8_SCALE = 2.0 ** -6
+FP8_NAN = 0x7F  # poison code for fp8 pools (an E4M3 NaN)
+
+
+def randn_fp8_codes(shape, generator: torch.Generator, device, scale=FP8_SCALE) -> torch.Tensor:
+    """N(0,1) drawn in fp32, divided by ``scale`` (a power of two, so exact),
+    clamped to +-448 and cast with torch's float8_e4m3fn conversion; returned
+    as the uint8 codes."""
+    x = torch.randn(shape, generator=generator, device=device, dtype=torch.float32) / scale
+    return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
 def make_generator(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -131,10 +153,11 @@ def make_generator(seed: int, device) -> torch.Generator:
 
 def empty_pools(num_blocks, num_kv_heads, block_size, head_dim, dtype, device,
                 k_axes="bhrd", v_axes="bhrd"):
-    """Two NaN-filled pools with the requested axis orders."""
+    """Two NaN-filled pools (NaN codes for fp8) with the requested axis orders."""
     dims = {"b": num_blocks, "h": num_kv_heads, "r": block_size, "d": head_dim}
-    k = torch.full([dims[a] for a in k_axes], float("nan"), dtype=dtype, device=device)
-    v = torch.full([dims[a] for a in v_axes], float("nan"), dtype=dtype, device=device)
+    fill = FP8_NAN if dtype == torch.uint8 else float("nan")
+    k = torch.full([dims[a] for a in k_axes], fill, dtype=dtype, device=device)
+    v = torch.full([dims[a] for a in v_axes], fill, dtype=dtype, device=device)
     return k, v
 
 
@@ -164,10 +187,15 @@ def fill_used_blocks(k_pool, v_pool, tables, lengths, block_size, generator,
         hi = min(lo + chunk_blocks, len(ids))
         idx = torch.as_tensor(ids[lo:hi], device=dev)
         for pool, axes in ((k_pool, k_axes), (v_pool, v_axes)):
-            data = randn((hi - lo, h, block_size, d), pool.dtype, generator, dev)
+            if pool.dtype == torch.uint8:
+                data = randn_fp8_codes((hi - lo, h, block_size, d), generator, dev)
+                poison = FP8_NAN
+            else:
+                data = randn((hi - lo, h, block_size, d), pool.dtype, generator, dev)
+                poison = float("nan")
             rows = torch.arange(block_size, device=dev).view(1, 1, block_size, 1)
             keep = rows < torch.as_tensor(valid_rows[lo:hi], device=dev).view(-1, 1, 1, 1)
-            data = torch.where(keep, data, torch.full_like(data, float("nan")))
+            data = torch.where(keep, data, torch.full_like(data, poison))
             pool.view(pool.shape)[idx] = _to_axes(data, axes)
 
 
@@ -198,7 +226,7 @@ def make_decode_case(shape: DecodeShape, device, k_axes="bhrd", v_axes="bhrd",
     k_pool, v_pool = empty_pools(nb, shape.num_kv_heads, shape.block_size, shape.head_dim,
                                  shape.torch_dtype, device, k_axes, v_axes)
     fill_used_blocks(k_pool, v_pool, tables, lens, shape.block_size, gen, k_axes, v_axes)
-    q = randn((len(lens), shape.num_q_heads, shape.head_dim), shape.torch_dtype, gen, device)
+    q = randn((len(lens), shape.num_q_heads, shape.head_dim), shape.q_dtype, gen, device)
     return DecodeCase(shape, lens, perm, tables, q, k_pool, v_pool, k_axes, v_axes)
 
 
