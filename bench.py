@@ -117,7 +117,7 @@ def _oracle_helpers():
     return oracle, gather_blocks, host_bits
 
 
-def oracle_decode_sample(case, budget_s: float, tables=None, lengths=None):
+def oracle_decode_sample(case, budget_s: float, tables=None, lengths=None, scales=(1.0, 1.0)):
     """The fp64 oracle, single-threaded, on whole sequences of a decode batch
     (all heads) until the time budget is spent or the batch is done.
     Returns (sequences done, context tokens, seconds)."""
@@ -131,7 +131,8 @@ def oracle_decode_sample(case, budget_s: float, tables=None, lengths=None):
                                                    sh.block_size)
         q_sub = host_bits(case.q[s:s + 1])
         t0 = time.perf_counter()
-        oracle.decode(q_sub, k_sub, v_sub, t_sub, l_sub, sh.scale, case.k_axes, case.v_axes)
+        oracle.decode(q_sub, k_sub, v_sub, t_sub, l_sub, sh.scale, case.k_axes, case.v_axes,
+                      scales[0], scales[1])
         elapsed += time.perf_counter() - t0
         done += 1
         tokens += int(l_sub[0])
@@ -149,8 +150,8 @@ def cpu_baseline(case, budget_s: float):
                       f"tokens), all {sh.num_q_heads} heads, fp64, one thread, {elapsed:.1f} s"}
 
 
-def cpu_decode_row(case, budget_s, tables=None, lengths=None):
-    done, tokens, elapsed = oracle_decode_sample(case, budget_s, tables, lengths)
+def cpu_decode_row(case, budget_s, tables=None, lengths=None, scales=(1.0, 1.0)):
+    done, tokens, elapsed = oracle_decode_sample(case, budget_s, tables, lengths, scales)
     n = len(case.lengths if lengths is None else lengths)
     return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {n} sequences ({tokens} context tokens), all heads, fp64, "
@@ -545,6 +546,39 @@ def row_gqa(pa, wl, torch, np, reps, cpu_budget):
     return r
 
 
+def row_fp8(pa, wl, torch, np, reps, cpu_budget):
+    """The 7B-shaped decode batch (same lengths, tables and pool size) with an
+    fp8 (OCP E4M3) K/V cache, one scale per cache: half the K/V bytes."""
+    sh = wl.DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "fp8", wl.MHA_7B.seed)
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
+    dev = "cuda"
+    lens = case.lengths
+    S, maxlen = len(lens), int(max(lens))
+    t_dev = torch.as_tensor(case.tables, device=dev)
+    l_dev = torch.as_tensor(lens, device=dev)
+    out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, 0, dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.pa_decode_fp8(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale,
+                         wl.FP8_SCALE, wl.FP8_SCALE, maxlen, 0, ws)
+
+    for _ in range(3):
+        call()
+    med, _ = events_time(torch, call, reps, stream)
+    b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, e_kv=1)
+    gbps = b / (med * 1e-3) / 1e9
+    r = {"us": med * 1e3, "algorithmic_bytes": b, "GBps": gbps,
+         "frac_of_8TBps": gbps * 1e9 / 8e12, "tokens_per_s": S / (med * 1e-3), "bound": "hbm",
+         "workload": "7B-shaped decode with fp8 (E4M3) K/V: 64 seqs, ctx U[128,4096], 32/32 "
+                     "heads, head_dim 128, block 16, 200000-block pool, one scale per cache"}
+    if cpu_budget > 0:
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, scales=(wl.FP8_SCALE, wl.FP8_SCALE))
+    return r
+
+
 def row_long(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.MIXED_DECODE
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
@@ -804,7 +838,8 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
 
 
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
-          "long-context split-K decode", "mixed step (cache write + decode + prefill)",
+          "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
+          "mixed step (cache write + decode + prefill)",
           "swap out / in (pinned host pool)")
 
 
@@ -955,6 +990,10 @@ def main():
         mark_phase(torch)
         rows["decode_prefix_shared"], rows["copy_blocks_cow"] = row_prefix_shared(
             pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
+        log("bench: row fp8 decode")
+        mark_phase(torch)
+        rows["decode_fp8"] = row_fp8(pa, wl, torch, np, args.reps, args.row_cpu_budget)
         torch.cuda.empty_cache()
         log("bench: row long-context split-K")
         mark_phase(torch)
