@@ -289,6 +289,13 @@ pa_status pa_seq_free(pa_allocator *a, int64_t seq_id);
 
 pa_status pa_seq_length(const pa_allocator *a, int64_t seq_id, int32_t *len);
 
+/* Blocks an append of n_tokens would take now, counting a copy-on-write
+ * block (what pa_seq_append checks against the free count). */
+pa_status pa_seq_blocks_needed(const pa_allocator *a, int64_t seq_id, int32_t n_tokens,
+                               int32_t *blocks);
+/* Entries in the sequence's table (host blocks while swapped out). */
+pa_status pa_seq_num_blocks(const pa_allocator *a, int64_t seq_id, int32_t *n_blocks);
+
 /* Copy the sequence's block table (physical ids, logical order) to out
  * [cap]; *n_out gets its length.  INVALID_ARG if cap is too small. */
 pa_status pa_seq_block_table(const pa_allocator *a, int64_t seq_id,
@@ -442,6 +449,86 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_block
                          const int32_t *src_dst, int32_t num_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Continuous-batching scheduler                                              */
+/* ------------------------------------------------------------------------ */
+/* Requests join the running batch at every step and leave as soon as they
+ * finish ([VE] §3.2); one step mixes prompt chunks and decode ([VI] §1); new
+ * requests wait in a queue and get blocks when admitted, and finished ones
+ * release theirs at once ([VI] §2.2); admission is first-come first-served
+ * and a request that cannot get room is preempted by moving its cache to
+ * host memory ([NV] best practice 5).  The policy, step by step:
+ *   1. Decode set: running requests whose prompt is written, in admission
+ *      order, one position each.  While the pool cannot hold those, the most
+ *      recently admitted running request is preempted: swapped out if the
+ *      host pool holds its blocks, else sent back to the head of the waiting
+ *      queue to start over (recompute).
+ *   2. The decode positions are appended.
+ *   3. The step's token budget (max_batched_tokens minus the decode count)
+ *      goes to requests still in their prompt, in admission order:
+ *      min(rest of prompt, budget, max_prefill_chunk) positions each while
+ *      the pool holds them.
+ *   4. Swapped requests return in arrival order while fewer than
+ *      max_num_seqs run and the pool holds their blocks (no work that step).
+ *   5. Waiting requests are admitted in queue order while fewer than
+ *      max_num_seqs run, budget remains and the pool holds their first chunk;
+ *      a request given token ids first reuses its cached prompt blocks
+ *      (pa_seq_create_prefix, leaving its last position to compute).
+ * The step writing a prompt's last chunk yields the request's first token,
+ * each decode one more; at max_new tokens the request finishes and its
+ * blocks are freed (pa_sched_complete).  Request ids are the allocator's
+ * sequence ids.  Host memory only; not thread-safe. */
+
+typedef struct pa_sched pa_sched;
+
+/* One step's plan.  The caller provides every array (host memory) with the
+ * capacities shown; the step fills them and the counts.  Order of work on
+ * the GPU: copy swap_out_pairs device -> host (pa_swap_blocks), then
+ * swap_in_pairs host -> device, then cow_pairs (pa_copy_blocks), then write
+ * the K/V of the new positions into slots (decode positions first, one per
+ * decode entry, then each prefill chunk's positions in order), then run the
+ * prefill chunks and the decode batch. */
+typedef struct {
+    int64_t *decode_ids;      /* [cap_seqs] requests decoding this step */
+    int32_t *decode_lens;     /* [cap_seqs] their context length after the append */
+    int64_t *prefill_ids;     /* [cap_seqs] requests writing a prompt chunk */
+    int32_t *prefill_starts;  /* [cap_seqs] first position of the chunk */
+    int32_t *prefill_lens;    /* [cap_seqs] positions in the chunk */
+    int64_t *preempted_ids;   /* [cap_seqs] sent back to start over */
+    int32_t cap_seqs;         /* >= max_num_seqs */
+    int64_t *slots;           /* [cap_slots] slots of the step's new positions */
+    int32_t cap_slots;        /* >= max_batched_tokens */
+    int32_t *cow_pairs;       /* [cap_cow][2] (src, dst) */
+    int32_t cap_cow;          /* >= max_num_seqs */
+    int32_t *swap_out_pairs;  /* [cap_swap_pairs][2] (device block, host block) */
+    int32_t *swap_in_pairs;   /* [cap_swap_pairs][2] (host block, device block) */
+    int32_t cap_swap_pairs;   /* >= the allocator's num_blocks */
+    int32_t n_decode, n_prefill, n_preempted, n_slots, n_cow, n_swap_out, n_swap_in;
+} pa_sched_plan_t;
+
+typedef struct {
+    int32_t waiting, running, swapped;
+    int64_t finished, swap_preemptions, recompute_preemptions;
+} pa_sched_stats_t;
+
+/* The scheduler borrows the allocator (which must outlive it, and whose swap
+ * space, if any, enables preemption by swap). */
+pa_status pa_sched_create(pa_allocator *a, int32_t max_num_seqs, int32_t max_batched_tokens,
+                          int32_t max_prefill_chunk, pa_sched **out);
+void pa_sched_destroy(pa_sched *s);
+/* Queue a request: n_prompt >= 1 prompt positions, max_new >= 1 tokens to
+ * generate; tokens [n_prompt] (host) or NULL (no prefix-cache reuse). */
+pa_status pa_sched_add(pa_sched *s, int64_t id, int32_t n_prompt, int32_t max_new,
+                       const int32_t *tokens);
+/* Plan the next step (see above).  INVALID_ARG if the previous plan was not
+ * completed or the plan arrays are short; the allocator then is unchanged. */
+pa_status pa_sched_step(pa_sched *s, pa_sched_plan_t *plan);
+/* The planned step ran: count its tokens and free finished requests, whose
+ * ids go to finished_ids [cap >= running requests]. */
+pa_status pa_sched_complete(pa_sched *s, int64_t *finished_ids, int32_t cap,
+                            int32_t *n_finished);
+pa_status pa_sched_stats(const pa_sched *s, pa_sched_stats_t *out);
 
 #ifdef __cplusplus
 }

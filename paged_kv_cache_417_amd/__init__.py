@@ -45,7 +45,9 @@ EXPORTED = (
     "pa_batch_append", "pa_batch_tables", "pa_seq_create_prefix", "pa_seq_append_tokens",
     "pa_batch_append_tokens", "pa_prefix_cache_stats", "pa_allocator_set_swap_space",
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
-    "pa_cache_write_fp8", "pa_decode_fp8",
+    "pa_cache_write_fp8", "pa_decode_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
+    "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
+    "pa_sched_stats",
 )
 
 
@@ -69,6 +71,25 @@ class SwapStats(ctypes.Structure):
     _fields_ = [("num_host_blocks", ctypes.c_int32), ("num_host_free", ctypes.c_int32),
                 ("swapped_seqs", ctypes.c_int32), ("swap_out_blocks", ctypes.c_int64),
                 ("swap_in_blocks", ctypes.c_int64)]
+
+
+class SchedPlan(ctypes.Structure):
+    _P64, _P32 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+    _fields_ = [("decode_ids", _P64), ("decode_lens", _P32), ("prefill_ids", _P64),
+                ("prefill_starts", _P32), ("prefill_lens", _P32), ("preempted_ids", _P64),
+                ("cap_seqs", ctypes.c_int32), ("slots", _P64), ("cap_slots", ctypes.c_int32),
+                ("cow_pairs", _P32), ("cap_cow", ctypes.c_int32), ("swap_out_pairs", _P32),
+                ("swap_in_pairs", _P32), ("cap_swap_pairs", ctypes.c_int32),
+                ("n_decode", ctypes.c_int32), ("n_prefill", ctypes.c_int32),
+                ("n_preempted", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("n_cow", ctypes.c_int32), ("n_swap_out", ctypes.c_int32),
+                ("n_swap_in", ctypes.c_int32)]
+
+
+class SchedStats(ctypes.Structure):
+    _fields_ = [("waiting", ctypes.c_int32), ("running", ctypes.c_int32),
+                ("swapped", ctypes.c_int32), ("finished", ctypes.c_int64),
+                ("swap_preemptions", ctypes.c_int64), ("recompute_preemptions", ctypes.c_int64)]
 
 
 class PrefixStats(ctypes.Structure):
@@ -116,6 +137,14 @@ def _declare(lib):
         "pa_swap_stats": (st, [vp, ctypes.POINTER(SwapStats)]),
         "pa_swap_blocks": (st, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, ctypes.c_int,
                                 vp]),
+        "pa_seq_blocks_needed": (st, [vp, i64, i32, pi32]),
+        "pa_seq_num_blocks": (st, [vp, i64, pi32]),
+        "pa_sched_create": (st, [vp, i32, i32, i32, ctypes.POINTER(vp)]),
+        "pa_sched_destroy": (None, [vp]),
+        "pa_sched_add": (st, [vp, i64, i32, i32, pi32]),
+        "pa_sched_step": (st, [vp, ctypes.POINTER(SchedPlan)]),
+        "pa_sched_complete": (st, [vp, pi64, i32, pi32]),
+        "pa_sched_stats": (st, [vp, ctypes.POINTER(SchedStats)]),
         "pa_cache_write_fp8": (st, [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     f32, vp]),
         "pa_decode_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, f32,
@@ -461,3 +490,74 @@ class Allocator:
         r = ctypes.c_int32(0)
         _check(_lib.pa_block_refcount(self._h, block, ctypes.byref(r)))
         return r.value
+
+
+class Scheduler:
+    """Owner of one ``pa_sched`` (continuous batching over an Allocator)."""
+
+    def __init__(self, alloc: "Allocator", max_num_seqs: int, max_batched_tokens: int,
+                 max_prefill_chunk: int):
+        import numpy as np
+        self._np = np
+        self.alloc = alloc  # keeps the allocator alive
+        self.max_num_seqs = int(max_num_seqs)
+        self.max_batched_tokens = int(max_batched_tokens)
+        h = ctypes.c_void_p()
+        _check(_lib.pa_sched_create(alloc._h, self.max_num_seqs, self.max_batched_tokens,
+                                    int(max_prefill_chunk), ctypes.byref(h)))
+        self._h = h
+        n, t, nb = self.max_num_seqs, self.max_batched_tokens, alloc.num_blocks
+        self._a = {"decode_ids": np.zeros(n, np.int64), "decode_lens": np.zeros(n, np.int32),
+                   "prefill_ids": np.zeros(n, np.int64), "prefill_starts": np.zeros(n, np.int32),
+                   "prefill_lens": np.zeros(n, np.int32), "preempted_ids": np.zeros(n, np.int64),
+                   "slots": np.zeros(t, np.int64), "cow_pairs": np.zeros((n, 2), np.int32),
+                   "swap_out_pairs": np.zeros((nb, 2), np.int32),
+                   "swap_in_pairs": np.zeros((nb, 2), np.int32)}
+        self._plan = SchedPlan()
+        for k, v in self._a.items():
+            setattr(self._plan, k, (_i64p if v.dtype == np.int64 else _i32p)(v))
+        self._plan.cap_seqs, self._plan.cap_slots, self._plan.cap_cow = n, t, n
+        self._plan.cap_swap_pairs = nb
+        self._fin = np.zeros(n, np.int64)
+
+    def close(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, rid: int, n_prompt: int, max_new: int, tokens=None):
+        np = self._np
+        t = None
+        if tokens is not None:
+            self._tok = np.ascontiguousarray(tokens, dtype=np.int32)
+            t = _i32p(self._tok)
+        _check(_lib.pa_sched_add(self._h, rid, n_prompt, max_new, t))
+
+    def step(self) -> dict:
+        """Plan one step; returns copies of the filled plan arrays."""
+        _check(_lib.pa_sched_step(self._h, ctypes.byref(self._plan)))
+        p, a = self._plan, self._a
+        return {"decode": list(zip(a["decode_ids"][:p.n_decode].tolist(),
+                                   a["decode_lens"][:p.n_decode].tolist())),
+                "prefill": list(zip(a["prefill_ids"][:p.n_prefill].tolist(),
+                                    a["prefill_starts"][:p.n_prefill].tolist(),
+                                    a["prefill_lens"][:p.n_prefill].tolist())),
+                "preempted": a["preempted_ids"][:p.n_preempted].tolist(),
+                "slots": a["slots"][:p.n_slots].copy(),
+                "cow": a["cow_pairs"][:p.n_cow].copy(),
+                "swap_out": a["swap_out_pairs"][:p.n_swap_out].copy(),
+                "swap_in": a["swap_in_pairs"][:p.n_swap_in].copy()}
+
+    def complete(self) -> list:
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_sched_complete(self._h, _i64p(self._fin), len(self._fin),
+                                      ctypes.byref(n)))
+        return self._fin[:n.value].tolist()
+
+    def stats(self) -> dict:
+        st = SchedStats()
+        _check(_lib.pa_sched_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in SchedStats._fields_}

@@ -537,6 +537,34 @@ pa_status pa_seq_free(pa_allocator *a, int64_t seq_id) {
     return pa::ok();
 }
 
+pa_status pa_seq_blocks_needed(const pa_allocator *a, int64_t seq_id, int32_t n_tokens,
+                               int32_t *blocks) {
+    if (!a || !blocks || n_tokens < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_blocks_needed: bad arguments");
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_blocks_needed: no sequence %lld",
+                        (long long)seq_id);
+    if (it->second.swapped)
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_blocks_needed: sequence %lld is swapped out",
+                        (long long)seq_id);
+    int64_t b;
+    bool cow;
+    a->needs(it->second, n_tokens, &b, &cow);
+    *blocks = (int32_t)b;
+    return pa::ok();
+}
+
+pa_status pa_seq_num_blocks(const pa_allocator *a, int64_t seq_id, int32_t *n_blocks) {
+    if (!a || !n_blocks) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_num_blocks: NULL argument");
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end())
+        return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_num_blocks: no sequence %lld",
+                        (long long)seq_id);
+    *n_blocks = (int32_t)it->second.table.size();
+    return pa::ok();
+}
+
 pa_status pa_seq_length(const pa_allocator *a, int64_t seq_id, int32_t *len) {
     if (!a || !len) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_length: NULL argument");
     auto it = a->seqs.find(seq_id);
