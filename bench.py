@@ -274,6 +274,92 @@ def row_prefix_cache(pa, wl, np, cpu_budget):
     return out
 
 
+def row_serving(pa, wl, torch, np, cpu_budget):
+    """Continuous batching end to end: 256 requests (prompts U{128..2048},
+    outputs U{16..256}) all queued at once, 7B-shaped attention geometry
+    (32/32 heads, head_dim 128, block 16, bf16), a 16,384-block pool with a
+    4,096-block pinned swap space, at most 128 running requests, 4,096 tokens
+    and 1,024-token prompt chunks per step.  Each step: the C++ scheduler's
+    plan, then swap/COW copies, the cache write of the new positions (N(0,1)
+    rows), the prompt chunks and the decode batch on the GPU.  No model: the
+    rate counts attention, cache and scheduling work only."""
+    from paged_kv_cache_417_amd.driver import ServingLoop
+    dev = "cuda"
+    hq = hkv = 32
+    d, bs = 128, 16
+    rng = np.random.default_rng(wl.SEED_BASE + 8)
+    n_req = 256
+    prompts = rng.integers(128, 2048, n_req, endpoint=True)
+    outs = rng.integers(16, 256, n_req, endpoint=True)
+    loop = ServingLoop(num_blocks=16384, block_size=bs, num_q_heads=hq, num_kv_heads=hkv,
+                       head_dim=d, max_num_seqs=128, max_batched_tokens=4096,
+                       max_prefill_chunk=1024, max_context_len=2048 + 256, host_blocks=4096,
+                       free_order=rng.permutation(16384))
+    gen = wl.make_generator(wl.SEED_BASE + 8, dev)
+
+    def rows(entries):
+        n = sum(len(p) for _, p in entries)
+        return (wl.randn((n, hkv, d), torch.bfloat16, gen, dev),
+                wl.randn((n, hkv, d), torch.bfloat16, gen, dev))
+
+    def qs(entries):
+        return wl.randn((sum(len(p) for _, p in entries), hq, d), torch.bfloat16, gen, dev)
+
+    for r in range(n_req):
+        loop.add(r, int(prompts[r]), int(outs[r]))
+    steps, dec_rows, pre_rows = 0, 0, 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while loop.sched.stats()["finished"] < n_req and steps < 5000:
+        plan, _, _, _ = loop.step(rows, qs)
+        steps += 1
+        dec_rows += len(plan["decode"])
+        pre_rows += sum(x[2] for x in plan["prefill"])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = loop.sched.stats()
+    # host cost of the scheduler alone, replayed on a fresh allocator (no GPU work)
+    a2 = pa.Allocator(16384, bs, free_order=np.random.default_rng(wl.SEED_BASE + 8).permutation(16384))
+    a2.set_swap_space(4096)
+    s2 = pa.Scheduler(a2, 128, 4096, 1024)
+    for r in range(n_req):
+        s2.add(r, int(prompts[r]), int(outs[r]))
+    h0 = time.perf_counter()
+    n2 = 0
+    while s2.stats()["finished"] < n_req and n2 < 5000:
+        s2.step()
+        s2.complete()
+        n2 += 1
+    host_us = (time.perf_counter() - h0) * 1e6 / max(n2, 1)
+    out = {"wall_s": wall, "steps": steps, "generated_tokens": int(outs.sum()),
+           "prompt_tokens": int(prompts.sum()),
+           "generated_tokens_per_s": int(outs.sum()) / wall,
+           "prompt_tokens_per_s": int(prompts.sum()) / wall,
+           "mean_decode_batch": dec_rows / max(steps, 1), "ms_per_step": wall * 1e3 / steps,
+           "sched_host_us_per_step": host_us, "swap_preemptions": st["swap_preemptions"],
+           "recompute_preemptions": st["recompute_preemptions"],
+           "workload": "serving loop: 256 requests, prompts U[128,2048], outputs U[16,256], "
+                       "7B-shaped attention (32/32 heads, D 128, block 16, bf16), 16384-block "
+                       "pool + 4096 swap blocks, 128 seqs / 4096 tokens / 1024-token chunks per step"}
+    if cpu_budget > 0:
+        from oracle.allocator_model import AllocatorModel
+        from oracle.scheduler_model import SchedulerModel
+        m = AllocatorModel(16384, bs, free_order=np.random.default_rng(wl.SEED_BASE + 8).permutation(16384))
+        m.set_swap_space(4096)
+        ms = SchedulerModel(m, 128, 4096, 1024)
+        for r in range(n_req):
+            ms.add(r, int(prompts[r]), int(outs[r]))
+        n3, t3 = 0, time.perf_counter()
+        while ms.stats()["finished"] < n_req and time.perf_counter() - t3 < cpu_budget:
+            ms.complete(ms.step())
+            n3 += 1
+        out["cpu_oracle"] = {"value": (time.perf_counter() - t3) * 1e6 / n3, "unit": "us/step",
+                             "cores": 1, "kind": "oracle",
+                             "sample": f"first {n3} scheduler steps on the Python reference model"}
+    del loop
+    return out
+
+
 PCIE_GBPS = 64.0  # PCIe 5.0 x16, per direction, nominal
 
 
@@ -840,7 +926,7 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
           "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
-          "swap out / in (pinned host pool)")
+          "swap out / in (pinned host pool)", "serving loop (continuous batching)")
 
 
 def mark_phase(torch):
@@ -1013,6 +1099,10 @@ def main():
         log("bench: row swap")
         mark_phase(torch)
         rows["swap"] = row_swap(pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
+        log("bench: row serving loop")
+        mark_phase(torch)
+        rows["serving"] = row_serving(pa, wl, torch, np, args.row_cpu_budget)
         torch.cuda.empty_cache()
         result["rows"] = rows
         for k, v in rows.items():

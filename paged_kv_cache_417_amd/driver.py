@@ -1,0 +1,92 @@
+"""Continuous-batching serving loop over the C ABI (argument marshalling only).
+
+``ServingLoop`` owns the device K/V pools, an optional pinned host pool for
+swap space, the allocator and the scheduler.  Each ``step()`` asks the C++
+scheduler for a plan and carries it out on the GPU, in the order the plan
+requires: swap-out copies, swap-in copies, copy-on-write copies, the cache
+write of the step's new positions, the prompt chunks (pa_prefill_chunk) and
+the decode batch (pa_decode).  There is no model: the caller supplies the K/V
+rows of every new position and the q rows of every query (``rows_fn``,
+``q_fn``, each called once per batch with a list of (request id, positions)
+and returning the rows of all entries back to back), so the loop exercises
+the whole library end to end on synthetic data.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (Allocator, Scheduler, decode_workspace, kv_cache_shapes, pa_cache_write,
+               pa_copy_blocks, pa_decode, pa_prefill_chunk, pa_swap_blocks)
+
+
+class ServingLoop:
+    def __init__(self, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                 max_num_seqs, max_batched_tokens, max_prefill_chunk, max_context_len,
+                 host_blocks=0, free_order=None, device="cuda", dtype=torch.bfloat16):
+        self.bs, self.hq, self.hkv, self.d = block_size, num_q_heads, num_kv_heads, head_dim
+        self.max_ctx = int(max_context_len)
+        self.dev, self.dtype = device, dtype
+        kshape, vshape = kv_cache_shapes(num_blocks, num_kv_heads, block_size, head_dim)
+        self.k = torch.full(kshape, float("nan"), dtype=dtype, device=device)
+        self.v = torch.full(vshape, float("nan"), dtype=dtype, device=device)
+        self.alloc = Allocator(num_blocks, block_size, free_order=free_order)
+        self.hk = self.hv = None
+        if host_blocks:
+            self.alloc.set_swap_space(host_blocks)
+            hk, hv = kv_cache_shapes(host_blocks, num_kv_heads, block_size, head_dim)
+            self.hk = torch.empty(hk, dtype=dtype, pin_memory=True)
+            self.hv = torch.empty(hv, dtype=dtype, pin_memory=True)
+        self.sched = Scheduler(self.alloc, max_num_seqs, max_batched_tokens, max_prefill_chunk)
+        self.stride = -(-self.max_ctx // block_size) + 1
+        self.pad = num_blocks - 1
+        self.ws = decode_workspace(max_num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   self.max_ctx, 0, device)
+        self.scale = head_dim ** -0.5
+
+    def add(self, rid, n_prompt, max_new, tokens=None):
+        if n_prompt + max_new > self.max_ctx:
+            raise ValueError("request longer than max_context_len")
+        self.sched.add(rid, n_prompt, max_new, tokens)
+
+    def step(self, rows_fn, q_fn):
+        """One scheduler step on the GPU.  rows_fn(entries) -> (k, v)
+        [total][Hkv][D]; q_fn(entries) -> q [total][Hq][D], entries being
+        [(request id, positions)].  Returns (plan, decode output or None,
+        prefill output or None, finished ids)."""
+        dev = self.dev
+        p = self.sched.step()
+        if len(p["swap_out"]):
+            pa_swap_blocks(self.k, self.v, self.hk, self.hv, torch.as_tensor(p["swap_out"], device=dev))
+        if len(p["swap_in"]):
+            pa_swap_blocks(self.hk, self.hv, self.k, self.v, torch.as_tensor(p["swap_in"], device=dev))
+        if len(p["cow"]):
+            pa_copy_blocks(self.k, self.v, torch.as_tensor(p["cow"], device=dev))
+        # new positions: decode positions first, then each chunk's
+        dec_entries = [(rid, np.array([ctx - 1])) for rid, ctx in p["decode"]]
+        pre_entries = [(rid, np.arange(start, start + n)) for rid, start, n in p["prefill"]]
+        if dec_entries or pre_entries:
+            k, v = rows_fn(dec_entries + pre_entries)
+            pa_cache_write(k, v, self.k, self.v, torch.as_tensor(p["slots"], device=dev))
+        pre_out = dec_out = None
+        if p["prefill"]:
+            ids = [x[0] for x in p["prefill"]]
+            t, ctx = self.alloc.batch_tables(ids, self.stride, self.pad)
+            qlens = np.array([x[2] for x in p["prefill"]], dtype=np.int32)
+            # the chunk's context ends at its last new position
+            ctx = np.array([x[1] + x[2] for x in p["prefill"]], dtype=np.int32)
+            cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+            pre_out = torch.empty((int(cu[-1]), self.hq, self.d), device=dev)
+            pa_prefill_chunk(pre_out, q_fn(pre_entries), self.k, self.v,
+                             torch.as_tensor(t, device=dev),
+                             torch.as_tensor(cu, device=dev), torch.as_tensor(ctx, device=dev),
+                             self.scale, int(qlens.max()), self.max_ctx)
+        if p["decode"]:
+            ids = [x[0] for x in p["decode"]]
+            t, lens = self.alloc.batch_tables(ids, self.stride, self.pad)
+            q = q_fn(dec_entries)
+            dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
+            pa_decode(dec_out, q, self.k, self.v, torch.as_tensor(t, device=dev),
+                      torch.as_tensor(lens, device=dev), self.scale, self.max_ctx, 0, self.ws)
+        fin = self.sched.complete()
+        return p, dec_out, pre_out, fin

@@ -145,6 +145,23 @@ def randn_fp8_codes(shape, generator: torch.Generator, device, scale=FP8_SCALE) 
     return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+def det_rows(key: int, positions, heads: int, dim: int, dtype, device, salt: int = 0):
+    """Rows [len(positions)][heads][dim] in [-2, 2) that depend only on (key,
+    position, head, dim, salt): an integer hash per element (multiply-xorshift
+    rounds on 32-bit words), so a row can be regenerated later to check what a
+    cache holds."""
+    m = 0xFFFFFFFF
+    pos = torch.as_tensor(np.asarray(positions), device=device, dtype=torch.int64).view(-1, 1, 1)
+    h = torch.arange(heads, device=device, dtype=torch.int64).view(1, -1, 1)
+    d = torch.arange(dim, device=device, dtype=torch.int64).view(1, 1, -1)
+    x = (int(key) * 0x9E3779B1 + pos * 0x85EBCA77 + h * 0xC2B2AE3D + d * 0x27D4EB2F
+         + int(salt) * 0x165667B1) & m
+    x = ((x ^ (x >> 15)) * 0x2C1B3C6D) & m
+    x = ((x ^ (x >> 12)) * 0x297A2D39) & m
+    x = x ^ (x >> 15)
+    return ((x & 0xFFFF).to(torch.float32) * (4.0 / 65536.0) - 2.0).to(dtype)
+
+
 def make_generator(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
