@@ -77,7 +77,8 @@ def _load():
                                             i32, i32, i32, i32, ctypes.c_float, ctypes.c_float]
         lib.orc_prefill.restype = None
         lib.orc_prefill.argtypes = [vp, vp, ctypes.c_int, vp, _Strides, vp, _Strides,
-                                    ctypes.c_int, vp, i32, vp, vp, i32, i32, i32, i32, i32, dbl]
+                                    ctypes.c_int, vp, i32, vp, vp, i32, i32, i32, i32, i32, dbl,
+                                    dbl, dbl]
         lib.orc_cache_write.restype = None
         lib.orc_cache_write.argtypes = [vp, vp, vp, _Strides, vp, _Strides, vp, i32, i32, i32,
                                         i32, i32]
@@ -203,7 +204,7 @@ def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_sca
 
 
 def prefill(q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,
-            k_axes="bhrd", v_axes="bhrd") -> np.ndarray:
+            k_axes="bhrd", v_axes="bhrd", k_scale=1.0, v_scale=1.0) -> np.ndarray:
     """Paged causal prefill of query chunks, fp64 ([VI] §1, mixed phases).
 
     q: [Tq][Hq][D]; cu_q_lens: [R+1] prefix sums of new rows per request;
@@ -223,7 +224,8 @@ def prefill(q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,
                     _ptr(k_cache), _strides(k_cache, k_axes),
                     _ptr(v_cache), _strides(v_cache, v_axes), _dtype_code(k_cache),
                     _ptr(block_tables), block_tables.shape[1], _ptr(cu_q_lens),
-                    _ptr(context_lens), r, hq, hkv, d, bs, float(scale))
+                    _ptr(context_lens), r, hq, hkv, d, bs, float(scale), float(k_scale),
+                    float(v_scale))
     return out
 
 

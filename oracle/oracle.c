@@ -178,7 +178,8 @@ void orc_prefill(double *out, const void *q, int q_dtype,
                  const int32_t *block_tables, int32_t table_stride,
                  const int32_t *cu_q_lens, const int32_t *context_lens,
                  int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
-                 int32_t head_dim, int32_t block_size, double scale)
+                 int32_t head_dim, int32_t block_size, double scale, double k_scale,
+                 double v_scale)
 {
     int32_t group = num_q_heads / num_kv_heads;
     int32_t max_len = 1;
@@ -197,6 +198,10 @@ void orc_prefill(double *out, const void *q, int q_dtype,
             int32_t kvh = h / group;
             orc_unpage(k_cache, ks, kv_dtype, table, block_size, ctx, kvh, head_dim, K);
             orc_unpage(v_cache, vs, kv_dtype, table, block_size, ctx, kvh, head_dim, V);
+            for (int64_t e = 0; e < (int64_t)ctx * head_dim; ++e) {  /* cache scales */
+                K[e] *= k_scale;
+                V[e] *= v_scale;
+            }
             for (int32_t i = 0; i < qlen; ++i) {
                 int32_t pos = ctx - qlen + i;
                 int64_t row = ((int64_t)(q0 + i) * num_q_heads + h) * head_dim;

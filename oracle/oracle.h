@@ -73,7 +73,8 @@ void orc_prefill(double *out, const void *q, int q_dtype,
                  const int32_t *block_tables, int32_t table_stride,
                  const int32_t *cu_q_lens, const int32_t *context_lens,
                  int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
-                 int32_t head_dim, int32_t block_size, double scale);
+                 int32_t head_dim, int32_t block_size, double scale, double k_scale,
+                 double v_scale);
 
 /* Scatter new K/V rows [T][Hkv][D] into their slots, byte for byte. */
 void orc_cache_write(const void *k_new, const void *v_new,

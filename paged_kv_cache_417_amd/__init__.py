@@ -45,7 +45,7 @@ EXPORTED = (
     "pa_batch_append", "pa_batch_tables", "pa_seq_create_prefix", "pa_seq_append_tokens",
     "pa_batch_append_tokens", "pa_prefix_cache_stats", "pa_allocator_set_swap_space",
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
-    "pa_cache_write_fp8", "pa_decode_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
+    "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats",
 )
@@ -145,6 +145,8 @@ def _declare(lib):
         "pa_sched_step": (st, [vp, ctypes.POINTER(SchedPlan)]),
         "pa_sched_complete": (st, [vp, pi64, i32, pi32]),
         "pa_sched_stats": (st, [vp, ctypes.POINTER(SchedStats)]),
+        "pa_prefill_chunk_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                      i32, i32, i32, i32, f32, f32, f32, vp]),
         "pa_cache_write_fp8": (st, [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     f32, vp]),
         "pa_decode_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, f32,
@@ -300,6 +302,19 @@ def pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k
                               int(partition_size), _p(workspace), ws_bytes,
                               PA_DECODE_KV_REUSE if kv_reuse else 0,
                               ctypes.c_void_p(_stream(stream))))
+
+
+def pa_prefill_chunk_fp8(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,
+                         k_scale, v_scale, max_q_len, max_context_len, stream=None) -> None:
+    """Chunked causal prefill over uint8 (E4M3) caches; q is bf16."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    tq, hq, _ = q.shape
+    _check(_lib.pa_prefill_chunk_fp8(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                     block_tables.shape[1], _p(cu_q_lens), _p(context_lens),
+                                     context_lens.shape[0], tq, int(max_q_len),
+                                     int(max_context_len), hq, hkv, d, bs, nb, float(scale),
+                                     float(k_scale), float(v_scale),
+                                     ctypes.c_void_p(_stream(stream))))
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_lens, scale,

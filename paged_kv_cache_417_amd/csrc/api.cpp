@@ -313,14 +313,21 @@ pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const vo
                        stream);
 }
 
-pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,
-                           const int32_t *block_tables, int32_t block_table_stride,
-                           const int32_t *cu_q_lens, const int32_t *context_lens, int32_t num_reqs,
-                           int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
-                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t block_size, int32_t num_blocks, float scale, pa_dtype dtype,
-                           void *stream) {
-    const char *fn = "pa_prefill_chunk";
+}  // extern "C"
+
+namespace {
+
+// Shared body of the prefill entry points (fp8: E4M3 caches with scales).
+pa_status prefill_impl(const char *fn, float *out, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_tables,
+                       int32_t block_table_stride, const int32_t *cu_q_lens,
+                       const int32_t *context_lens, int32_t num_reqs, int32_t total_q_tokens,
+                       int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, pa_dtype dtype, bool fp8, float k_scale,
+                       float v_scale, void *stream) {
+    if (fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale)))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: scales must be finite and > 0", fn);
     if (num_reqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0)
         return pa::fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
     if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
@@ -360,11 +367,45 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     p.head_dim = head_dim;
     p.block_size = block_size;
     p.num_blocks = num_blocks;
-    p.scale_log2 = scale * kLog2e;
+    p.scale_log2 = fp8 ? scale * k_scale * kLog2e : scale * kLog2e;
+    p.kv_fp8 = fp8;
+    p.v_scale = fp8 ? v_scale : 1.f;
     int rc = pa::launch_prefill(p, stream);
     if (rc == -1) return pa::fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", fn);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, int32_t block_table_stride,
+                           const int32_t *cu_q_lens, const int32_t *context_lens, int32_t num_reqs,
+                           int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale, pa_dtype dtype,
+                           void *stream) {
+    return prefill_impl("pa_prefill_chunk", out, q, k_cache, v_cache, block_tables,
+                        block_table_stride, cu_q_lens, context_lens, num_reqs, total_q_tokens,
+                        max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, dtype, false, 1.f, 1.f, stream);
+}
+
+pa_status pa_prefill_chunk_fp8(float *out, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               int32_t block_table_stride, const int32_t *cu_q_lens,
+                               const int32_t *context_lens, int32_t num_reqs,
+                               int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, float scale, float k_scale,
+                               float v_scale, void *stream) {
+    return prefill_impl("pa_prefill_chunk_fp8", out, q, k_cache, v_cache, block_tables,
+                        block_table_stride, cu_q_lens, context_lens, num_reqs, total_q_tokens,
+                        max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, PA_DTYPE_BF16, true, k_scale, v_scale,
+                        stream);
 }
 
 }  // extern "C"

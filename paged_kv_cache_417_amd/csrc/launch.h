@@ -55,7 +55,9 @@ struct PrefillParams {
     int32_t head_dim;
     int32_t block_size;
     int32_t num_blocks;
-    float scale_log2;
+    float scale_log2;  // scale * log2(e) (times the K scale for an fp8 cache)
+    bool kv_fp8;       // K/V hold OCP E4M3 codes (q stays bf16)
+    float v_scale;     // value of a V code = code * v_scale (1 for bf16)
 };
 
 // Workspace layout shared by the decode kernels and the split-K reduce.

@@ -55,11 +55,15 @@ __device__ __forceinline__ int k_row(int kk) {
     return ((kk >> 2) & 1) * 16 + 4 * (kk >> 3) + (kk & 3);
 }
 
-template <int D, int BS>
+// A thread's share of one step's K and V: 8 elements per chunk, as bf16
+// (16 bytes) or, for an fp8 cache, as E4M3 codes (8 bytes) widened to bf16
+// when stored to LDS.
+template <int D, int BS, bool FP8>
 struct Stage {
-    static constexpr int kPasses = D / 64;  // 16-byte loads per thread for K (and for V)
-    u32x4 k[kPasses];
-    u32x4 v[kPasses];
+    static constexpr int kPasses = D / 64;  // chunks per thread for K (and for V)
+    using Word = std::conditional_t<FP8, u32x2, u32x4>;
+    Word k[kPasses];
+    Word v[kPasses];
 };
 
 // Global -> registers for keys t0 .. t0+31, whose blocks are bidA (keys
@@ -71,50 +75,67 @@ struct Stage {
 // instead (t0 < nkeys always).  Such keys sit past every position of the
 // workgroup, so the causal mask drops their scores and stage_store zeroes
 // their V elements: they contribute exactly nothing.
-template <int D, int BS>
-__device__ __forceinline__ void stage_load(Stage<D, BS> &st, const PrefillParams &p, int kvh,
-                                           int32_t t0, int32_t nkeys, int32_t bidA,
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillParams &p,
+                                           int kvh, int32_t t0, int32_t nkeys, int32_t bidA,
                                            int32_t bidB, int tid) {
-    const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
-    const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+    using E = std::conditional_t<FP8, uint8_t, uint16_t>;  // one stored element
+    const E *kc = reinterpret_cast<const E *>(p.k_cache);
+    const E *vc = reinterpret_cast<const E *>(p.v_cache);
     const int64_t hkv = p.num_kv_heads;
     const int32_t rowA = t0 % BS, rowB = (t0 + 16) % BS;
-    const uint16_t *kA = kc + ((bidA * hkv + kvh) * BS + rowA) * D;
-    const uint16_t *kB = kc + ((bidB * hkv + kvh) * BS + rowB) * D;
-    const uint16_t *vA = vc + (bidA * hkv + kvh) * (int64_t)D * BS + rowA;
-    const uint16_t *vB = vc + (bidB * hkv + kvh) * (int64_t)D * BS + rowB;
+    const E *kA = kc + ((bidA * hkv + kvh) * BS + rowA) * D;
+    const E *kB = kc + ((bidB * hkv + kvh) * BS + rowB) * D;
+    const E *vA = vc + (bidA * hkv + kvh) * (int64_t)D * BS + rowA;
+    const E *vB = vc + (bidB * hkv + kvh) * (int64_t)D * BS + rowB;
     const int32_t nvalid = nkeys - t0;  // keys of the tile that exist, >= 1
 #pragma unroll
-    for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
+    for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
-        // K: D/8 chunks of 16 bytes per key
+        // K: D/8 chunks of 8 elements per key
         int kk = idx / (D / 8);
         const int ch = idx % (D / 8);
         if (kk >= nvalid) kk = 0;
         const bool k_in_b = BS == 16 && kk >= 16;
-        const uint16_t *kp = (k_in_b ? kB : kA) + (k_in_b ? kk - 16 : kk) * D + ch * 8;
+        const E *kp = (k_in_b ? kB : kA) + (k_in_b ? kk - 16 : kk) * D + ch * 8;
         // V^T: 4 chunks of 8 keys per dim
         const int dim = idx >> 2;
         int cv = idx & 3;
         if (8 * cv >= nvalid) cv = 0;
         const bool v_in_b = BS == 16 && cv >= 2;
-        const uint16_t *vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cv - 2 : cv);
-        st.k[ps] = ld16(kp);
-        st.v[ps] = ld16(vp);
+        const E *vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cv - 2 : cv);
+        if constexpr (FP8) {
+            st.k[ps] = ld8(kp);
+            st.v[ps] = ld8(vp);
+        } else {
+            st.k[ps] = ld16(kp);
+            st.v[ps] = ld16(vp);
+        }
     }
 }
 
 // Registers -> LDS.  On the last step (TAIL) the V elements of keys at or
 // past nkeys are cleared here rather than right after their load, so the
 // loads of a step never wait before the previous step's math.
-template <int D, int BS, bool TAIL>
-__device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D, BS> &st,
-                                            int tid, int32_t t0, int32_t nkeys) {
+// An fp8 stage is widened to bf16 here (exactly), so LDS and the math are
+// the same for both caches.
+template <int D, int BS, bool TAIL, bool FP8>
+__device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
+                                            const Stage<D, BS, FP8> &st, int tid, int32_t t0,
+                                            int32_t nkeys) {
 #pragma unroll
-    for (int ps = 0; ps < Stage<D, BS>::kPasses; ++ps) {
+    for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         const int kk = idx / (D / 8), ch = idx % (D / 8);
-        *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = st.k[ps];
+        u32x4 kw, vw;
+        if constexpr (FP8) {
+            kw = e4m3x8_to_bf16x8(st.k[ps]);
+            vw = e4m3x8_to_bf16x8(st.v[ps]);
+        } else {
+            kw = st.k[ps];
+            vw = st.v[ps];
+        }
+        *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = kw;
         const int dim = idx >> 2, chv = idx & 3;
         if constexpr (TAIL) {
             const int32_t t = t0 + 8 * chv;
@@ -122,18 +143,19 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf, Stage<D
             for (int w = 0; w < 4; ++w) {
                 const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
                                       (t + 2 * w + 1 < nkeys ? 0xffff0000u : 0u);
-                st.v[ps][w] &= keep;
+                vw[w] &= keep;
             }
         }
-        *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = st.v[ps];
+        *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = vw;
     }
 }
 
 // Two waves per SIMD (two workgroups per CU): one workgroup's MFMAs run
 // while the other waits at its barrier or on LDS.
-template <int D, int BS>
+template <int D, int BS, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void prefill_kernel(
     PrefillParams p) {
+    using St = Stage<D, BS, FP8>;
     __shared__ PrefillSmem<D> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -246,10 +268,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         return b;
     };
-    auto stage = [&](Stage<D, BS> &st, int32_t t0) {
+    auto stage = [&](St &st, int32_t t0) {
         const int32_t bA = block_id(t0 / BS);
         const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, nblk - 1)) : bA;
-        stage_load<D, BS>(st, p, kvh, t0, nkeys, bA, bB, tid);
+        stage_load<D, BS, FP8>(st, p, kvh, t0, nkeys, bA, bB, tid);
     };
 
     // Two register stages: while step it computes from LDS, the loads of
@@ -258,13 +280,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // a load has two steps of math to arrive.
     const int32_t ntiles = (nkeys + kTile - 1) / kTile;
     const int32_t last_t0 = (ntiles - 1) * kTile;
-    Stage<D, BS> stA, stB;
+    St stA, stB;
     stage(stA, 0);
     stage(stB, min(kTile, last_t0));  // a tile past the end re-reads the last one, unused
     if (kTile <= nkeys)
-        stage_store<D, BS, false>(sm, 0, stA, tid, 0, nkeys);
+        stage_store<D, BS, false, FP8>(sm, 0, stA, tid, 0, nkeys);
     else
-        stage_store<D, BS, true>(sm, 0, stA, tid, 0, nkeys);
+        stage_store<D, BS, true, FP8>(sm, 0, stA, tid, 0, nkeys);
     __syncthreads();
 
     // One 32-key step.  MASK: some column of the workgroup may sit before
@@ -272,7 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // workgroup's first position need no mask for any column; they run a
     // body compiled without it.
     // cur holds step it + 1's loads, nxt receives step it + 2's.
-    auto step = [&](int32_t it, auto mask_tag, Stage<D, BS> &cur, Stage<D, BS> &nxt) {
+    auto step = [&](int32_t it, auto mask_tag, St &cur, St &nxt) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = it & 1;
         const int32_t t0 = it * kTile;
@@ -371,9 +393,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         if (more) {
             if (t0 + 2 * kTile <= nkeys)
-                stage_store<D, BS, false>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
+                stage_store<D, BS, false, FP8>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
             else
-                stage_store<D, BS, true>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
+                stage_store<D, BS, true, FP8>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
         }
         __syncthreads();
     };
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     for (int ct = 0; ct < 2; ++ct) {
         const float lt = rows4_sum(l[ct]);
         if (pos[ct] < 0) continue;
-        const float inv = 1.f / lt;
+        const float inv = (FP8 ? p.v_scale : 1.f) / lt;  // an fp8 V scale enters here
         float *orow = p.out + qoff[ct];
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
@@ -418,7 +440,10 @@ int launch_one(const PrefillParams &p, hipStream_t s) {
     const int64_t nchunks = (p.max_q_len + ppw - 1) / ppw;
     const int64_t wgs = nchunks * p.num_reqs * p.num_kv_heads;
     if (wgs > (1LL << 24) - 1) return -1;
-    hipLaunchKernelGGL((prefill_kernel<D, BS>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+    if (p.kv_fp8)
+        hipLaunchKernelGGL((prefill_kernel<D, BS, true>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, BS, false>), dim3((unsigned)wgs), dim3(256), 0, s, p);
     return (int)hipGetLastError();
 }
 

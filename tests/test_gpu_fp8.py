@@ -181,3 +181,30 @@ def test_fp8_calls_reject_bad_scales(pa):
     # a bf16 write into uint8 pools is refused (pa_cache_write takes no fp8)
     with pytest.raises(pa.PAError):
         pa.pa_cache_write(x, x, kc, vc, slots)
+
+
+@pytest.mark.parametrize("d,bs,g", [(128, 128, 4), (128, 16, 1), (64, 32, 8)])
+def test_fp8_prefill_matches_oracle(pa, d, bs, g):
+    """Causal chunks over fp8 caches (ragged chunk lengths, short and long
+    contexts) against the oracle on the same codes."""
+    sh = wl.PrefillShape(num_reqs=4, new_tokens=0, cached_tokens=0, num_q_heads=2 * g,
+                         num_kv_heads=2, head_dim=d, block_size=bs, dtype="fp8", seed=70 + g)
+    q_lens = [1, 37, 130, 64]
+    ctx = [1, 37, 700, 1100]
+    case = wl.make_prefill_case(sh, "cuda", pa.K_AXES, pa.V_AXES, context_lens=ctx,
+                                q_lens=q_lens)
+    dev = "cuda"
+    out = torch.full((int(case.cu_q_lens[-1]), sh.num_q_heads, d), 7.0, device=dev)
+    pa.pa_prefill_chunk_fp8(out, case.q, case.k_pool, case.v_pool,
+                            torch.as_tensor(case.tables, device=dev),
+                            torch.as_tensor(case.cu_q_lens, device=dev),
+                            torch.as_tensor(case.context_lens, device=dev), sh.scale, S8, S8,
+                            max(q_lens), max(ctx))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host_bits(case.q), host_bits(case.k_pool), host_bits(case.v_pool),
+                         case.tables, case.cu_q_lens, case.context_lens, sh.scale, pa.K_AXES,
+                         pa.V_AXES, S8, S8)
+    got = out.double().cpu().numpy()
+    err = float(np.abs(got - ref).max())
+    say(f"case fp8 prefill d={d} bs={bs} g={g}: max err {err:.3e}")
+    assert np.isfinite(got).all() and err <= TOL

@@ -34,6 +34,7 @@ MUTANTS = {
     "e4m3_no_saturation": ("if (isinf(x)) return (uint8_t)(sign | 0x7E);",
                            "if (isinf(x)) return (uint8_t)(sign | 0x7F);"),
     "fp8_scale_dropped": ("K[i] *= k_scale;", "K[i] *= 1.0;"),
+    "fp8_prefill_v_scale": ("V[e] *= v_scale;", "V[e] *= k_scale;"),
     "fp8_write_scale": ("orc_e4m3_encode(vx / v_scale);", "orc_e4m3_encode(vx * v_scale);"),
 }
 

@@ -445,3 +445,22 @@ def test_decode_on_fp8_pools_uses_scaled_values():
     a = oracle.decode(q, codes_k, codes_v, tables, lens, 0.35, "bhrd", "bhdr", ks, vs)
     b = oracle.decode(q, fk, fv, tables, lens, 0.35, "bhrd", "bhdr")
     assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_prefill_on_fp8_pools_uses_scaled_values():
+    bs, h, d = 4, 2, 8
+    rng = np.random.default_rng(12)
+    codes_k = rng.integers(0, 256, (5, h, bs, d)).astype(np.uint8)
+    codes_v = rng.integers(0, 256, (5, h, d, bs)).astype(np.uint8)
+    for c in (codes_k, codes_v):
+        c[(c & 0x7F) == 0x7F] = 0x21
+    ks, vs = 0.015625, 1.5  # exact products with E4M3 values in fp32
+    fk = (oracle.e4m3_decode(codes_k) * ks).astype(np.float32)
+    fv = (oracle.e4m3_decode(codes_v) * vs).astype(np.float32)
+    q = rng.standard_normal((5, 4, d)).astype(np.float32)
+    tables = np.array([[2, 0, 3, 1], [4, 1, 0, 2]], dtype=np.int32)
+    ctx = np.array([13, 7], dtype=np.int32)
+    cu = np.array([0, 3, 5], dtype=np.int32)
+    a = oracle.prefill(q, codes_k, codes_v, tables, cu, ctx, 0.3, "bhrd", "bhdr", ks, vs)
+    b = oracle.prefill(q, fk, fv, tables, cu, ctx, 0.3, "bhrd", "bhdr")
+    assert np.allclose(a, b, rtol=0, atol=1e-12)

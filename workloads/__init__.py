@@ -319,6 +319,11 @@ class PrefillShape:
 
     @property
     def torch_dtype(self):
+        """dtype of the K/V pools (uint8 codes for fp8)."""
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[self.dtype]
+
+    @property
+    def q_dtype(self):
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
 
@@ -363,6 +368,6 @@ def make_prefill_case(shape: PrefillShape, device, k_axes="bhrd", v_axes="bhrd",
                                  shape.torch_dtype, device, k_axes, v_axes)
     fill_used_blocks(k_pool, v_pool, tables, context_lens, shape.block_size, gen, k_axes, v_axes)
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
-    q = randn((int(cu[-1]), shape.num_q_heads, shape.head_dim), shape.torch_dtype, gen, device)
+    q = randn((int(cu[-1]), shape.num_q_heads, shape.head_dim), shape.q_dtype, gen, device)
     return PrefillCase(shape, context_lens, q_lens, cu, perm, tables, q, k_pool, v_pool, k_axes,
                        v_axes)
