@@ -17,26 +17,33 @@ import numpy as np
 import torch
 
 from . import (Allocator, Scheduler, decode_workspace, kv_cache_shapes, pa_cache_write,
-               pa_copy_blocks, pa_decode, pa_prefill_chunk, pa_swap_blocks)
+               pa_cache_write_fp8, pa_copy_blocks, pa_decode, pa_decode_fp8, pa_prefill_chunk,
+               pa_prefill_chunk_fp8, pa_swap_blocks)
 
 
 class ServingLoop:
     def __init__(self, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
                  max_num_seqs, max_batched_tokens, max_prefill_chunk, max_context_len,
-                 host_blocks=0, free_order=None, device="cuda", dtype=torch.bfloat16):
+                 host_blocks=0, free_order=None, device="cuda", dtype=torch.bfloat16,
+                 fp8_scales=None):
+        """fp8_scales=(k_scale, v_scale): keep the cache as OCP E4M3 codes
+        (uint8 pools) and use the fp8 calls; new rows are still bf16."""
         self.bs, self.hq, self.hkv, self.d = block_size, num_q_heads, num_kv_heads, head_dim
         self.max_ctx = int(max_context_len)
         self.dev, self.dtype = device, dtype
+        self.fp8 = fp8_scales
+        pool_dtype = torch.uint8 if fp8_scales else dtype
+        fill = 0x7F if fp8_scales else float("nan")
         kshape, vshape = kv_cache_shapes(num_blocks, num_kv_heads, block_size, head_dim)
-        self.k = torch.full(kshape, float("nan"), dtype=dtype, device=device)
-        self.v = torch.full(vshape, float("nan"), dtype=dtype, device=device)
+        self.k = torch.full(kshape, fill, dtype=pool_dtype, device=device)
+        self.v = torch.full(vshape, fill, dtype=pool_dtype, device=device)
         self.alloc = Allocator(num_blocks, block_size, free_order=free_order)
         self.hk = self.hv = None
         if host_blocks:
             self.alloc.set_swap_space(host_blocks)
             hk, hv = kv_cache_shapes(host_blocks, num_kv_heads, block_size, head_dim)
-            self.hk = torch.empty(hk, dtype=dtype, pin_memory=True)
-            self.hv = torch.empty(hv, dtype=dtype, pin_memory=True)
+            self.hk = torch.empty(hk, dtype=pool_dtype, pin_memory=True)
+            self.hv = torch.empty(hv, dtype=pool_dtype, pin_memory=True)
         self.sched = Scheduler(self.alloc, max_num_seqs, max_batched_tokens, max_prefill_chunk)
         self.stride = -(-self.max_ctx // block_size) + 1
         self.pad = num_blocks - 1
@@ -67,7 +74,11 @@ class ServingLoop:
         pre_entries = [(rid, np.arange(start, start + n)) for rid, start, n in p["prefill"]]
         if dec_entries or pre_entries:
             k, v = rows_fn(dec_entries + pre_entries)
-            pa_cache_write(k, v, self.k, self.v, torch.as_tensor(p["slots"], device=dev))
+            slots = torch.as_tensor(p["slots"], device=dev)
+            if self.fp8:
+                pa_cache_write_fp8(k, v, self.k, self.v, slots, *self.fp8)
+            else:
+                pa_cache_write(k, v, self.k, self.v, slots)
         pre_out = dec_out = None
         if p["prefill"]:
             ids = [x[0] for x in p["prefill"]]
@@ -77,16 +88,25 @@ class ServingLoop:
             ctx = np.array([x[1] + x[2] for x in p["prefill"]], dtype=np.int32)
             cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
             pre_out = torch.empty((int(cu[-1]), self.hq, self.d), device=dev)
-            pa_prefill_chunk(pre_out, q_fn(pre_entries), self.k, self.v,
-                             torch.as_tensor(t, device=dev),
-                             torch.as_tensor(cu, device=dev), torch.as_tensor(ctx, device=dev),
-                             self.scale, int(qlens.max()), self.max_ctx)
+            args = (torch.as_tensor(t, device=dev), torch.as_tensor(cu, device=dev),
+                    torch.as_tensor(ctx, device=dev), self.scale)
+            if self.fp8:
+                pa_prefill_chunk_fp8(pre_out, q_fn(pre_entries), self.k, self.v, *args, *self.fp8,
+                                     int(qlens.max()), self.max_ctx)
+            else:
+                pa_prefill_chunk(pre_out, q_fn(pre_entries), self.k, self.v, *args,
+                                 int(qlens.max()), self.max_ctx)
         if p["decode"]:
             ids = [x[0] for x in p["decode"]]
             t, lens = self.alloc.batch_tables(ids, self.stride, self.pad)
             q = q_fn(dec_entries)
             dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
-            pa_decode(dec_out, q, self.k, self.v, torch.as_tensor(t, device=dev),
-                      torch.as_tensor(lens, device=dev), self.scale, self.max_ctx, 0, self.ws)
+            t, lens = torch.as_tensor(t, device=dev), torch.as_tensor(lens, device=dev)
+            if self.fp8:
+                pa_decode_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
+                              self.max_ctx, 0, self.ws)
+            else:
+                pa_decode(dec_out, q, self.k, self.v, t, lens, self.scale, self.max_ctx, 0,
+                          self.ws)
         fin = self.sched.complete()
         return p, dec_out, pre_out, fin
