@@ -158,9 +158,11 @@ def cpu_decode_row(case, budget_s, tables=None, lengths=None, scales=(1.0, 1.0))
                       f"one thread, {elapsed:.1f} s"}
 
 
-def cpu_prefill_row(q, k_pool, v_pool, tables, cu, ctx, scale, block_size, budget_s):
+def cpu_prefill_row(q, k_pool, v_pool, tables, cu, ctx, scale, block_size, budget_s,
+                    scales=(1.0, 1.0)):
     """Oracle prefill on single rows of request 0 (each a 1-row chunk at its
-    position, over all keys up to it) until the budget is spent."""
+    position, over all keys up to it) until the budget is spent.  ``scales``
+    are the K and V cache scales of an fp8 pool."""
     oracle, gather_blocks, host_bits = _oracle_helpers()
     import numpy as np
     qlen0 = int(cu[1] - cu[0])
@@ -172,7 +174,8 @@ def cpu_prefill_row(q, k_pool, v_pool, tables, cu, ctx, scale, block_size, budge
         qrow = host_bits(q[int(cu[0]) + i:int(cu[0]) + i + 1])
         t0 = time.perf_counter()
         oracle.prefill(qrow, k_sub, v_sub, t_sub, np.array([0, 1], np.int32),
-                       np.array([pos + 1], np.int32), scale, "bhrd", "bhdr")
+                       np.array([pos + 1], np.int32), scale, "bhrd", "bhdr",
+                       k_scale=scales[0], v_scale=scales[1])
         elapsed += time.perf_counter() - t0
         done += 1
         if elapsed >= budget_s:
@@ -182,9 +185,10 @@ def cpu_prefill_row(q, k_pool, v_pool, tables, cu, ctx, scale, block_size, budge
                       f"visible keys), all heads, fp64, one thread, {elapsed:.1f} s"}
 
 
-def cpu_cache_write_row(k_new, v_new, slots, hkv, d, bs, budget_s):
+def cpu_cache_write_row(k_new, v_new, slots, hkv, d, bs, budget_s, fp8_scale=None):
     """Oracle cache write of the same tokens into a host pool holding just
-    the blocks they touch, repeated until the budget is spent."""
+    the blocks they touch, repeated until the budget is spent.  With
+    ``fp8_scale`` the pools hold E4M3 codes and the write quantizes."""
     oracle, _, host_bits = _oracle_helpers()
     import numpy as np
     slots = np.asarray(slots, dtype=np.int64)
@@ -193,12 +197,16 @@ def cpu_cache_write_row(k_new, v_new, slots, hkv, d, bs, budget_s):
     sub = np.array([remap[int(x) // bs] * bs + int(x) % bs if x >= 0 else -1 for x in slots],
                    dtype=np.int64)
     kh, vh = host_bits(k_new), host_bits(v_new)
-    kp = np.zeros((len(blocks), hkv, bs, d), dtype=kh.dtype)
-    vp = np.zeros((len(blocks), hkv, d, bs), dtype=vh.dtype)
+    pool_dtype = kh.dtype if fp8_scale is None else np.uint8
+    kp = np.zeros((len(blocks), hkv, bs, d), dtype=pool_dtype)
+    vp = np.zeros((len(blocks), hkv, d, bs), dtype=pool_dtype)
     reps, elapsed = 0, 0.0
     while elapsed < budget_s:
         t0 = time.perf_counter()
-        oracle.cache_write(kh, vh, kp, vp, sub, "bhrd", "bhdr")
+        if fp8_scale is None:
+            oracle.cache_write(kh, vh, kp, vp, sub, "bhrd", "bhdr")
+        else:
+            oracle.cache_write_fp8(kh, vh, kp, vp, sub, fp8_scale, fp8_scale, "bhrd", "bhdr")
         elapsed += time.perf_counter() - t0
         reps += 1
     return {"value": reps * len(slots) / elapsed, "unit": "tokens/s", "cores": 1,
@@ -668,11 +676,14 @@ def row_fp8(pa, wl, torch, np, reps, cpu_budget):
 def row_long(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.MIXED_DECODE
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
+    ps = pa.pa_decode_default_partition(len(case.lengths), sh.num_kv_heads, sh.block_size,
+                                        int(case.lengths.max()))
     r = decode_row(pa, torch, case, reps, ps=sh.partition_size)
     if cpu_budget > 0:
         r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     r["workload"] = ("long-context split-K decode: 8 seqs x 32768 tokens, block 128, "
-                     "partitions of 512, 32 q / 8 kv heads, head_dim 128, bf16")
+                     f"partitions of {ps} (library default), 32 q / 8 kv heads, head_dim 128, "
+                     "bf16")
     return r
 
 
@@ -823,14 +834,14 @@ def row_mixed(pa, wl, torch, np, reps, cpu_budget):
     qp = wl.randn((2048, psh.num_q_heads, d), torch.bfloat16, gen, dev)
     out_d = torch.empty((8, dsh.num_q_heads, d), device=dev)
     out_p = torch.empty((2048, psh.num_q_heads, d), device=dev)
-    ws = pa.decode_workspace(8, dsh.num_q_heads, hkv, d, bs, 32768, 512, dev)
+    ws = pa.decode_workspace(8, dsh.num_q_heads, hkv, d, bs, 32768, dsh.partition_size, dev)
     stream = torch.cuda.current_stream()
 
     def cw():
         pa.pa_cache_write(kn, vn, k_pool, v_pool, d_slots)
 
     def dec():
-        pa.pa_decode(out_d, qd, k_pool, v_pool, dt, dl, dsh.scale, 32768, 512, ws)
+        pa.pa_decode(out_d, qd, k_pool, v_pool, dt, dl, dsh.scale, 32768, dsh.partition_size, ws)
 
     def pre():
         pa.pa_prefill_chunk(out_p, qp, k_pool, v_pool, pt, cu, pl, psh.scale, 512, 4608)
@@ -866,9 +877,71 @@ def row_mixed(pa, wl, torch, np, reps, cpu_budget):
                                                 bs, cpu_budget)
         cache_write["cpu_oracle"] = cpu_cache_write_row(kn, vn, slots, hkv, d, bs, cpu_budget)
     mixed = {"us": step_med * 1e3,
-             "workload": "cache write (2056 tokens) + decode 8 x 32768 (split-K 512) + "
+             "workload": "cache write (2056 tokens) + decode 8 x 32768 (split-K, default partitions) + "
                          "prefill 4 x 512 over 4096, one stream"}
     return prefill, cache_write, mixed
+
+
+def row_fp8_prefill(pa, wl, torch, np, reps, cpu_budget):
+    """The mixed step's prompt chunks (4 requests x 512 new tokens over 4096
+    cached, causal) over E4M3 caches: the quantizing write of the chunks' 2048
+    K/V rows and the chunked prefill that reads the pool."""
+    dev = "cuda"
+    psh = wl.PrefillShape(dtype="fp8")
+    case = wl.make_prefill_case(psh, dev, pa.K_AXES, pa.V_AXES)
+    hkv, d, bs = psh.num_kv_heads, psh.head_dim, psh.block_size
+    R, new, ctx = psh.num_reqs, psh.new_tokens, case.context_lens
+    slots = np.concatenate([
+        case.tables[r][np.arange(ctx[r] - new, ctx[r]) // bs].astype(np.int64) * bs
+        + np.arange(ctx[r] - new, ctx[r]) % bs for r in range(R)])
+    gen = wl.make_generator(psh.seed + 1, dev)
+    kn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    vn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    d_slots = torch.as_tensor(slots, device=dev)
+    t_dev = torch.as_tensor(case.tables, device=dev)
+    cu = torch.as_tensor(case.cu_q_lens, device=dev)
+    cl = torch.as_tensor(ctx, device=dev)
+    tq = int(case.cu_q_lens[-1])
+    out = torch.empty((tq, psh.num_q_heads, d), device=dev)
+    stream = torch.cuda.current_stream()
+    sc = wl.FP8_SCALE
+
+    def cw():
+        pa.pa_cache_write_fp8(kn, vn, case.k_pool, case.v_pool, d_slots, sc, sc)
+
+    def pre():
+        pa.pa_prefill_chunk_fp8(out, case.q, case.k_pool, case.v_pool, t_dev, cu, cl, psh.scale,
+                                sc, sc, new, int(ctx.max()))
+
+    for f in (cw, pre):
+        f()
+    cw_med, _ = events_time(torch, cw, reps, stream)
+    pre_med, _ = events_time(torch, pre, reps, stream)
+    flops = prefill_flops([int(c) for c in ctx], [new] * R, psh.num_q_heads, d)
+    cw_bytes = len(slots) * hkv * d * (2 + 1) * 2  # bf16 rows in, E4M3 codes out, K and V
+    prefill = {"us": pre_med * 1e3, "flops": flops,
+               "TFLOPs": flops / (pre_med * 1e-3) / 1e12,
+               "frac_of_2.5PF_bf16": flops / (pre_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "bound": "mfma (bf16 products after widening the codes)",
+               "gpu_query_rows_per_s": tq / (pre_med * 1e-3),
+               "workload": "chunked prefill over an fp8 (E4M3) cache: 4 requests x 512 new "
+                           "tokens over 4096 cached (causal), 32 q / 8 kv heads, head_dim 128, "
+                           "block 128, one scale per cache, bf16 q"}
+    cache_write = {"us": cw_med * 1e3, "tokens": len(slots), "bytes_moved": cw_bytes,
+                   "GBps": cw_bytes / (cw_med * 1e-3) / 1e9, "bound": "latency",
+                   "gpu_tokens_per_s": len(slots) / (cw_med * 1e-3),
+                   "workload": "quantizing cache write of the 2048 prompt-chunk rows (bf16 in, "
+                               "E4M3 out), 8 kv heads, head_dim 128, block 128"}
+    if cpu_budget > 0:
+        torch.cuda.synchronize()
+        prefill["cpu_oracle"] = cpu_prefill_row(case.q, case.k_pool, case.v_pool, case.tables,
+                                                case.cu_q_lens, ctx, psh.scale, bs, cpu_budget,
+                                                scales=(sc, sc))
+        # The oracle's E4M3 encode searches the code table: 512 of the tokens
+        # keep one repetition near a second.
+        cache_write["cpu_oracle"] = cpu_cache_write_row(kn[:512], vn[:512], slots[:512], hkv, d,
+                                                        bs, cpu_budget, fp8_scale=sc)
+    return prefill, cache_write
 
 
 # ---------------------------------------------------------------------------
@@ -926,6 +999,7 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
           "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
+          "fp8 prompt chunks (quantizing write + prefill)",
           "swap out / in (pinned host pool)", "serving loop (continuous batching)")
 
 
@@ -1089,6 +1163,12 @@ def main():
         mark_phase(torch)
         rows["prefill_chunk"], rows["cache_write"], rows["mixed_step"] = row_mixed(
             pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
+        log("bench: row fp8 prefill")
+        mark_phase(torch)
+        rows["prefill_chunk_fp8"], rows["cache_write_fp8"] = row_fp8_prefill(
+            pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
         rows["allocator"] = {"host_us_per_step": h["alloc_us"],
                              "workload": "batch append of one token to 64 sequences + dense "
                                          "tables [64][stride] (host, C ABI)"}

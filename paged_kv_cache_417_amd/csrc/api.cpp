@@ -44,15 +44,21 @@ pa_status check_geometry(const char *fn, int32_t num_kv_heads, int32_t head_dim,
 
 // Partition size in tokens: a multiple of 32 (the decode step) and of the
 // block size.  Start at 512 and halve while the grid would leave the 256
-// compute units short of work (about 8 waves each).
+// compute units short of work (about 8 waves each).  With few (sequence,
+// kv head) pairs -- a handful of long contexts -- every wave streams a full
+// partition, and longer partitions amortise each wave's start-up (length,
+// table slice, first loads) and shrink the merge: grow up to 4096 tokens
+// while the grid keeps at least 1024 waves (4 per compute unit).
 int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                           int32_t max_context_len) {
     const int32_t unit = block_size > 32 ? block_size : 32;
+    const int64_t max_len = max_context_len > 0 ? max_context_len : 1;
     int32_t ps = 512;
     const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-    while (ps / 2 >= unit && (ps / 2) % unit == 0 &&
-           pairs * ceil_div(max_context_len > 0 ? max_context_len : 1, ps) < 2048)
+    while (ps / 2 >= unit && (ps / 2) % unit == 0 && pairs * ceil_div(max_len, ps) < 2048)
         ps /= 2;
+    if (pairs <= 256)
+        while (ps < 4096 && pairs * ceil_div(max_len, 2 * ps) >= 1024) ps *= 2;
     return ps;
 }
 

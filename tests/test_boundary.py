@@ -86,7 +86,14 @@ def test_default_partition_is_a_multiple_of_step_and_block():
     for bs in (16, 32, 64, 128):
         for s, hkv, maxlen in ((64, 32, 4096), (4, 8, 201), (8, 8, 32768), (1, 1, 10)):
             ps = pa.pa_decode_default_partition(s, hkv, bs, maxlen)
-            assert ps % 32 == 0 and ps % bs == 0 and 32 <= ps <= 512
+            assert ps % 32 == 0 and ps % bs == 0 and 32 <= ps <= 4096
+    # Many (sequence, kv head) pairs keep 512; a few long contexts grow the
+    # partition while the grid keeps >= 1024 waves; short ones shrink it.
+    assert pa.pa_decode_default_partition(64, 32, 16, 4096) == 512
+    assert pa.pa_decode_default_partition(128, 8, 16, 8192) == 512
+    assert pa.pa_decode_default_partition(8, 8, 128, 32768) == 2048  # 64 pairs x 16 partitions
+    assert pa.pa_decode_default_partition(4, 8, 16, 201) == 32
+    assert pa.pa_decode_default_partition(4, 8, 128, 201) == 128
 
 
 def test_decode_zero_sequences_is_a_no_op():

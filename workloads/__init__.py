@@ -75,8 +75,7 @@ MHA_7B = DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "bf16", SEED_BASE +
 GQA = DecodeShape("gqa", 128, 32, 8, 128, 16, 200_000, "bf16", SEED_BASE + 3)
 PREFIX_SHARED = DecodeShape("prefix_shared", 128, 32, 32, 128, 16, 200_000, "bf16",
                             SEED_BASE + 4)
-MIXED_DECODE = DecodeShape("mixed", 8, 32, 8, 128, 128, 8_192, "bf16", SEED_BASE + 5,
-                           partition_size=512)
+MIXED_DECODE = DecodeShape("mixed", 8, 32, 8, 128, 128, 8_192, "bf16", SEED_BASE + 5)
 
 SHAPES = {s.name: s for s in (TINY_F32, MHA_7B, GQA, PREFIX_SHARED, MIXED_DECODE)}
 
