@@ -107,6 +107,11 @@ def events_time(torch, fn, reps, stream):
     return ms[len(ms) // 2], ms
 
 
+def spread(ms) -> dict:
+    """p10 / p90 of a row's per-call times (sorted milliseconds), in us."""
+    return {"p10_us": ms[len(ms) // 10] * 1e3, "p90_us": ms[(9 * len(ms)) // 10] * 1e3}
+
+
 def warm(torch, fn, seconds: float) -> None:
     """Untimed calls of fn() for about `seconds`: the matrix-bound prefill
     runs well below its steady rate until the chip's clocks have ramped
@@ -724,10 +729,10 @@ def row_fp8(pa, wl, torch, np, reps, cpu_budget):
 
     for _ in range(3):
         call()
-    med, _ = events_time(torch, call, reps, stream)
+    med, all_ms = events_time(torch, call, reps, stream)
     b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, e_kv=1)
     gbps = b / (med * 1e-3) / 1e9
-    r = {"us": med * 1e3, "algorithmic_bytes": b, "GBps": gbps,
+    r = {"us": med * 1e3, **spread(all_ms), "algorithmic_bytes": b, "GBps": gbps,
          "frac_of_8TBps": gbps * 1e9 / 8e12, "tokens_per_s": S / (med * 1e-3), "bound": "hbm",
          "workload": "7B-shaped decode with fp8 (E4M3) K/V: 64 seqs, ctx U[128,4096], 32/32 "
                      "heads, head_dim 128, block 16, 200000-block pool, one scale per cache"}
@@ -770,10 +775,10 @@ def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=
 
     for _ in range(3):
         call()
-    med, _ = events_time(torch, call, reps, stream)
+    med, all_ms = events_time(torch, call, reps, stream)
     b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size)
     gbps = b / (med * 1e-3) / 1e9
-    return {"us": med * 1e3, "algorithmic_bytes": b, "GBps": gbps,
+    return {"us": med * 1e3, **spread(all_ms), "algorithmic_bytes": b, "GBps": gbps,
             "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "tokens_per_s": S / (med * 1e-3),
             "bound": "hbm"}
 
@@ -918,11 +923,11 @@ def row_mixed(pa, wl, torch, np, reps, cpu_budget):
         f()
     cw_med, _ = events_time(torch, cw, reps, stream)
     warm(torch, pre, 1.0)
-    pre_med, _ = events_time(torch, pre, reps, stream)
+    pre_med, pre_ms = events_time(torch, pre, reps, stream)
     step_med, _ = events_time(torch, step, reps, stream)
     flops = prefill_flops([4608] * 4, [512] * 4, psh.num_q_heads, d)
     cw_bytes = len(slots) * hkv * d * 2 * 2 * 2  # K and V rows, read + write
-    prefill = {"us": pre_med * 1e3, "flops": flops,
+    prefill = {"us": pre_med * 1e3, **spread(pre_ms), "flops": flops,
                "TFLOPs": flops / (pre_med * 1e-3) / 1e12,
                "frac_of_2.5PF_bf16": flops / (pre_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                "bound": "mfma",
@@ -981,10 +986,10 @@ def row_fp8_prefill(pa, wl, torch, np, reps, cpu_budget):
         f()
     cw_med, _ = events_time(torch, cw, reps, stream)
     warm(torch, pre, 1.0)
-    pre_med, _ = events_time(torch, pre, reps, stream)
+    pre_med, pre_ms = events_time(torch, pre, reps, stream)
     flops = prefill_flops([int(c) for c in ctx], [new] * R, psh.num_q_heads, d)
     cw_bytes = len(slots) * hkv * d * (2 + 1) * 2  # bf16 rows in, E4M3 codes out, K and V
-    prefill = {"us": pre_med * 1e3, "flops": flops,
+    prefill = {"us": pre_med * 1e3, **spread(pre_ms), "flops": flops,
                "TFLOPs": flops / (pre_med * 1e-3) / 1e12,
                "frac_of_2.5PF_bf16": flops / (pre_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                "bound": "mfma (bf16 products after widening the codes)",

@@ -109,3 +109,20 @@ def test_length_recipes():
     plan = wl.prefix_plan()
     assert all(2049 <= x <= 2063 for x in plan.shared_lens)
     assert plan.tail_lens.min() >= 1 and plan.tail_lens.max() <= 512
+
+
+def test_kernel_names_and_spread():
+    # demangled libpa names, the tracer's mangled bf16 instantiation, others skipped
+    assert bench.kernel_short_name(
+        "void pa::(anonymous namespace)::decode_reduce_kernel(pa::DecodeParams)") == \
+        "decode_reduce_kernel"
+    assert bench.kernel_short_name(
+        "_ZN2pa12_GLOBAL__N_122cache_write_fp8_kernelIDF16bEEvPKT_S4_PhS5_PKliiiiiff") == \
+        "cache_write_fp8_kernel<__bf16>"
+    assert bench.kernel_short_name("at::native::vectorized_elementwise_kernel<4>") is None
+    s = bench.spread([0.001 * i for i in range(1, 21)])  # 1 .. 20 us
+    assert s["p10_us"] == pytest.approx(3.0) and s["p90_us"] == pytest.approx(19.0)
+
+
+def test_host_threads_is_bounded():
+    assert 1 <= bench.host_threads() <= 16
