@@ -28,8 +28,20 @@
 //   causal mask + online softmax : keys past a column's position get -inf
 //       (a select, so no value of a masked key reaches the result); the
 //       running max is shared by the four lanes of a column.
-//   O^T += V^T P^T : A = V^T rows from LDS, B = P as a bf16 high part plus a
-//       bf16 remainder (two MFMAs), keeping P's error near 2^-16.
+//   O^T += V^T P^T : v_mfma_f32_16x16x32_f16, A = V^T rows from LDS held as
+//       fp16, B = P rounded to fp16 (relative error 2^-11, one MFMA per
+//       tile).  V reaches LDS as fp16: a bf16 V element converts exactly
+//       when its magnitude is below 2^16 (the largest such bf16 value is
+//       65280; elements below 2^-14 may lose bits under 2^-24, an absolute
+//       error under 6e-8), and an E4M3 code always does.  The weights are
+//       lifted by 2^7 before rounding (they stay below 2^15) so that weights
+//       down to 2^-21 of the running maximum keep full fp16 precision.
+//   Exact fallback: while staging a bf16 V tile the workgroup tracks the
+//       largest V element.  If any staged element is 2^16 or more in
+//       magnitude, infinite or NaN, the workgroup discards its result and
+//       runs the whole walk again with V in bf16 and P as a bf16 high part
+//       plus a bf16 remainder (two MFMAs per tile, P's error near 2^-16), so
+//       every input gets a result of at least that accuracy.
 #include <type_traits>
 
 #include "device_common.h"
@@ -42,6 +54,11 @@ constexpr int kWaves = 4;
 constexpr int kPairs = kWaves * 32;  // (position, head) pairs per workgroup
 constexpr int kTile = 32;            // keys per step
 constexpr float kRescaleMargin = 8.f;  // log2 units; weights stay below 2^8
+// fp16 weights are computed as 2^kF16Lift times the true weight: below
+// 2^(8 + 7) = 32768, within fp16's range, with fp16's normal range reaching
+// down to 2^-21 of the running maximum.  The sum l carries the same factor,
+// so it cancels in o / l.
+constexpr float kF16Lift = 7.f;
 
 template <int D>
 struct PrefillSmem {
@@ -119,24 +136,33 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
 // loads of a step never wait before the previous step's math.
 // An fp8 stage is widened to bf16 here (exactly), so LDS and the math are
 // the same for both caches.
-template <int D, int BS, bool TAIL, bool FP8>
+// F16: V is stored as fp16 (E4M3 codes convert exactly; bf16 elements
+// convert exactly below 65536 in magnitude).  vmax collects what tells
+// whether any did not: the largest staged element's fp32 bits as a signed
+// integer (vmax.x: the largest positive one) and as an unsigned one (vmax.y:
+// the negative one of largest magnitude, if any).  Integer maxima order
+// finite values, infinities and NaNs alike, so no NaN can hide a large
+// element.  On the last step
+// (TAIL) the V elements of keys at or past nkeys are cleared first, so
+// neither they nor their magnitude reach LDS or vmax; +0 has the same bits
+// in bf16 and fp16.
+template <int D, int BS, bool TAIL, bool FP8, bool F16>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                                             const Stage<D, BS, FP8> &st, int tid, int32_t t0,
-                                            int32_t nkeys) {
+                                            int32_t nkeys, u32x2 &vmax) {
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         const int kk = idx / (D / 8), ch = idx % (D / 8);
+        const int dim = idx >> 2, chv = idx & 3;
         u32x4 kw, vw;
         if constexpr (FP8) {
             kw = e4m3x8_to_bf16x8(st.k[ps]);
-            vw = e4m3x8_to_bf16x8(st.v[ps]);
+            vw = F16 ? e4m3x8_to_f16x8(st.v[ps]) : e4m3x8_to_bf16x8(st.v[ps]);
         } else {
             kw = st.k[ps];
             vw = st.v[ps];
         }
-        *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = kw;
-        const int dim = idx >> 2, chv = idx & 3;
         if constexpr (TAIL) {
             const int32_t t = t0 + 8 * chv;
 #pragma unroll
@@ -146,6 +172,18 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                 vw[w] &= keep;
             }
         }
+        if constexpr (F16 && !FP8) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t lo = vw[w] << 16, hi = vw[w] & 0xffff0000u;
+                vmax.x = (uint32_t)max(max((int32_t)vmax.x, (int32_t)lo), (int32_t)hi);
+                vmax.y = max(max(vmax.y, lo), hi);
+                vw[w] = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(
+                                  f32x2{__uint_as_float(lo), __uint_as_float(hi)}, f16x2));
+            }
+        }
+        *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = kw;
         *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = vw;
     }
 }
@@ -237,12 +275,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     }
 
     const int32_t *table = p.block_tables + (int64_t)r * p.table_stride;
-    float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+    float m[2], l[2];
     floatx4 acc[2][D / 16];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // The request's block-table entries live in one VGPR per wave, 64 at a
     // time (lane j holds the entry of logical block win + j); block ids are
@@ -250,7 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // K/V loads.  Entries past the last block of visible keys are not read.
     const int32_t nblk = (nkeys + BS - 1) / BS;
     int32_t win = 0;
-    int32_t tbl = lane < nblk ? table[lane] : 0;
+    int32_t tbl = 0;
     bool bad = false;
     auto block_id = [&](int32_t j) -> int32_t {
         if (j - win >= 64) {
@@ -274,154 +308,218 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         stage_load<D, BS, FP8>(st, p, kvh, t0, nkeys, bA, bB, tid);
     };
 
-    // Two register stages: while step it computes from LDS, the loads of
-    // step it + 2 are in flight and those of step it + 1 (issued one step
-    // earlier) are stored to the other LDS buffer at the end of the step, so
-    // a load has two steps of math to arrive.
     const int32_t ntiles = (nkeys + kTile - 1) / kTile;
     const int32_t last_t0 = (ntiles - 1) * kTile;
-    St stA, stB;
-    stage(stA, 0);
-    stage(stB, min(kTile, last_t0));  // a tile past the end re-reads the last one, unused
-    if (kTile <= nkeys)
-        stage_store<D, BS, false, FP8>(sm, 0, stA, tid, 0, nkeys);
-    else
-        stage_store<D, BS, true, FP8>(sm, 0, stA, tid, 0, nkeys);
-    __syncthreads();
-
-    // One 32-key step.  MASK: some column of the workgroup may sit before
-    // a key of the step (causal mask needed).  Steps ending at or before the
-    // workgroup's first position need no mask for any column; they run a
-    // body compiled without it.
-    // cur holds step it + 1's loads, nxt receives step it + 2's.
-    auto step = [&](int32_t it, auto mask_tag, St &cur, St &nxt) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const int buf = it & 1;
-        const int32_t t0 = it * kTile;
-        const bool more = it + 1 < ntiles;
-        stage(nxt, min(t0 + 2 * kTile, last_t0));  // past the end: re-read, never stored
-
-        if (wave_maxpos >= t0) {
-            u32x4 ka[D / 32], kb[D / 32];
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                ka[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][n][kslot_dim(ks, g)]);
-                kb[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 + n][kslot_dim(ks, g)]);
-            }
-            bf16x8 ph[2], pl[2];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qb[ct][ks], sa,
-                                                                 0, 0, 0);
-                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qb[ct][ks], sb,
-                                                                 0, 0, 0);
-                }
-                float sr[8];  // unscaled scores of keys t0 + 8g + i
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sr[i] = sa[i];
-                    sr[4 + i] = sb[i];
-                }
-                bool vis[8];
-                float mr = kNegInf;  // this lane's largest visible score
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    vis[i] = !MASK || t0 + 8 * g + i <= pos[ct];
-                    mr = fmaxf(mr, vis[i] ? sr[i] : kNegInf);
-                }
-                // Lazy rescaling: the exponent base m[ct] moves only when a
-                // weight of the step would reach 2^kRescaleMargin, so the
-                // accumulators are rescaled on few steps.  The test needs no
-                // cross-lane max: if no lane's own max passes the bound,
-                // every weight of the column stays below it.  When some
-                // lane's does (a wave-uniform branch), the exact column max
-                // becomes the new base of every column.
-                if (__any(mr * sc > m[ct] + kRescaleMargin)) {
-                    const float cm = rows4_max(mr);
-                    const float mx = cm == kNegInf ? kNegInf : cm * sc;
-                    const float m_new = fmaxf(m[ct], mx);
-                    const float f = m_new == kNegInf ? 1.f : fast_exp2(m[ct] - m_new);
-                    l[ct] *= f;
-#pragma unroll
-                    for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
-                    m[ct] = m_new;
-                }
-                // A column with no visible key yet keeps m = -inf; subtract 0
-                // then so every weight is exp2(-inf) = 0 rather than NaN.
-                const float msub = m[ct] == kNegInf ? 0.f : m[ct];
-                // P = hi + lo: hi keeps the top 16 bits of each fp32 weight
-                // (a bf16 value), lo = P - hi is exact in fp32 and rounded to
-                // bf16, so P enters the bf16 products with ~16 bits.
-                float pv[8];
-                uint32_t hb[8];
-                float lo[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float arg = fmaf(sr[i], sc, -msub);
-                    pv[i] = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
-                    hb[i] = __float_as_uint(pv[i]);
-                    lo[i] = pv[i] - __uint_as_float(hb[i] & 0xffff0000u);
-                }
-                const float sum =
-                    ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-                u32x4 hw, lw;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    hw[k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
-                    lw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                             f32x2{lo[2 * k], lo[2 * k + 1]}, bf16x2));
-                }
-                ph[ct] = as_bf16x8(hw);
-                pl[ct] = as_bf16x8(lw);
-                l[ct] += sum;
-            }
-            // The P V products run at raised wave priority: the other
-            // workgroup's wave on this SIMD, most likely in its softmax,
-            // then issues its vector ALU work only into the matrix core's
-            // gaps instead of delaying this chain of MFMAs (6% faster on the
-            // 4 x 512 over 4096 chunk, at any raised level; raising it over
-            // Q K^T as well gained nothing).
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int j = 0; j < D / 16; ++j) {
-                const bf16x8 vv =
-                    as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.v[buf][16 * j + n][8 * g]));
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, ph[ct], acc[ct][j], 0,
-                                                                         0, 0);
-                    acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pl[ct], acc[ct][j], 0,
-                                                                         0, 0);
-                }
-            }
-            __builtin_amdgcn_s_setprio(0);
-        }
-        if (more) {
-            if (t0 + 2 * kTile <= nkeys)
-                stage_store<D, BS, false, FP8>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
-            else
-                stage_store<D, BS, true, FP8>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
-        }
-        __syncthreads();
-    };
-    // Even steps find step it + 1 in stB, odd steps in stA.  The loop runs
-    // steps in pairs so each body names its stages at compile time: the two
-    // are never copied into each other or selected at run time, and each
-    // wait covers one stage's loads.  The unmasked run is cut to an even
+    // Steps ending at or before the workgroup's first position need no
+    // causal mask for any column.  The unmasked run is cut to an even
     // length; a step it leaves over runs with the mask, which is exact.
     const int32_t wg_minpos = base_pos + i_begin;  // first position of the workgroup's rows
     const int32_t nomask = min(ntiles, (wg_minpos + 1) / kTile) & ~1;
-    int32_t it = 0;
-    for (; it < nomask; it += 2) {
-        step(it, std::false_type{}, stB, stA);
-        step(it + 1, std::false_type{}, stA, stB);
-    }
-    for (; it < ntiles; it += 2) {
-        step(it, std::true_type{}, stB, stA);
-        if (it + 1 < ntiles) step(it + 1, std::true_type{}, stA, stB);
+
+    // The whole walk over the keys.  F16: P and V enter the products as
+    // fp16; otherwise V stays bf16 and P is split into a bf16 high part and
+    // a bf16 remainder.  Returns true when a staged bf16 V element has no
+    // exact fp16 value (the F16 result must then be discarded).
+    auto run = [&](auto f16_tag) -> bool {
+        constexpr bool F16 = decltype(f16_tag)::value;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            m[ct] = kNegInf;
+            l[ct] = 0.f;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        win = 0;
+        tbl = lane < nblk ? table[lane] : 0;
+        u32x2 vmax = {0u, 0u};  // largest staged V bits (bf16 cache, F16 walk)
+
+        // Two register stages: while step it computes from LDS, the loads of
+        // step it + 2 are in flight and those of step it + 1 (issued one step
+        // earlier) are stored to the other LDS buffer at the end of the step,
+        // so a load has two steps of math to arrive.
+        St stA, stB;
+        stage(stA, 0);
+        stage(stB, min(kTile, last_t0));  // a tile past the end re-reads the last one, unused
+        if (kTile <= nkeys)
+            stage_store<D, BS, false, FP8, F16>(sm, 0, stA, tid, 0, nkeys, vmax);
+        else
+            stage_store<D, BS, true, FP8, F16>(sm, 0, stA, tid, 0, nkeys, vmax);
+        __syncthreads();
+
+        // One 32-key step.  MASK: some column of the workgroup may sit before
+        // a key of the step (causal mask needed).
+        // cur holds step it + 1's loads, nxt receives step it + 2's.
+        auto step = [&](int32_t it, auto mask_tag, St &cur, St &nxt) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const int buf = it & 1;
+            const int32_t t0 = it * kTile;
+            const bool more = it + 1 < ntiles;
+            stage(nxt, min(t0 + 2 * kTile, last_t0));  // past the end: re-read, never stored
+
+            if (wave_maxpos >= t0) {
+                u32x4 ka[D / 32], kb[D / 32];
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    ka[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][n][kslot_dim(ks, g)]);
+                    kb[ks] =
+                        *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 + n][kslot_dim(ks, g)]);
+                }
+                // Wave priority: the math of a step (Q K^T and the softmax
+                // at 2, P V at 1) runs ahead of the co-resident workgroup's
+                // staging (its K/V loads, LDS stores and barrier at 0), so a
+                // SIMD's two waves keep the matrix core and the vector ALU
+                // busy rather than both waiting at barriers.  A/B on the
+                // 4 x 512 over 4096 chunk: 190 us with P V alone raised,
+                // 179 us with all the math at 1, 178 us as here.
+                floatx4 sa[2], sb[2];
+                __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    sa[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    sb[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks) {
+                        sa[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(ka[ks]), qb[ct][ks], sa[ct], 0, 0, 0);
+                        sb[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(kb[ks]), qb[ct][ks], sb[ct], 0, 0, 0);
+                    }
+                }
+                u32x4 vv[D / 16];
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j)
+                    vv[j] = *reinterpret_cast<const u32x4 *>(&sm.v[buf][16 * j + n][8 * g]);
+                u32x4 ph[2], pl[2];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    float sr[8];  // unscaled scores of keys t0 + 8g + i
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sr[i] = sa[ct][i];
+                        sr[4 + i] = sb[ct][i];
+                    }
+                    bool vis[8];
+                    float mr = kNegInf;  // this lane's largest visible score
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        vis[i] = !MASK || t0 + 8 * g + i <= pos[ct];
+                        mr = fmaxf(mr, vis[i] ? sr[i] : kNegInf);
+                    }
+                    // Lazy rescaling: the exponent base m[ct] moves only when
+                    // a weight of the step would reach 2^kRescaleMargin, so
+                    // the accumulators are rescaled on few steps.  The test
+                    // needs no cross-lane max: if no lane's own max passes
+                    // the bound, every weight of the column stays below it.
+                    // When some lane's does (a wave-uniform branch), the
+                    // exact column max becomes the new base of every column.
+                    if (__any(mr * sc > m[ct] + kRescaleMargin)) {
+                        const float cm = rows4_max(mr);
+                        const float mx = cm == kNegInf ? kNegInf : cm * sc;
+                        const float m_new = fmaxf(m[ct], mx);
+                        const float f = m_new == kNegInf ? 1.f : fast_exp2(m[ct] - m_new);
+                        l[ct] *= f;
+#pragma unroll
+                        for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
+                        m[ct] = m_new;
+                    }
+                    // A column with no visible key yet keeps m = -inf; its
+                    // weights are all exp2(-inf) = 0, so any finite base
+                    // serves.  F16 lifts every weight by 2^kF16Lift.
+                    const float msub =
+                        (m[ct] == kNegInf ? 0.f : m[ct]) - (F16 ? kF16Lift : 0.f);
+                    float pv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float arg = fmaf(sr[i], sc, -msub);
+                        pv[i] = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
+                    }
+                    const float sum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
+                                      ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                    if constexpr (F16) {
+                        // P rounded to fp16 (nearest even)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            ph[ct][k] = __builtin_bit_cast(
+                                uint32_t,
+                                __builtin_convertvector(f32x2{pv[2 * k], pv[2 * k + 1]}, f16x2));
+                    } else {
+                        // P = hi + lo: hi keeps the top 16 bits of each fp32
+                        // weight (a bf16 value), lo = P - hi is exact in fp32
+                        // and rounded to bf16, so P enters the bf16 products
+                        // with ~16 bits.
+                        uint32_t hb[8];
+                        float lo[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            hb[i] = __float_as_uint(pv[i]);
+                            lo[i] = pv[i] - __uint_as_float(hb[i] & 0xffff0000u);
+                        }
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            ph[ct][k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
+                            pl[ct][k] = __builtin_bit_cast(
+                                uint32_t,
+                                __builtin_convertvector(f32x2{lo[2 * k], lo[2 * k + 1]}, bf16x2));
+                        }
+                    }
+                    l[ct] += sum;
+                }
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j) {
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        if constexpr (F16) {
+                            acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                as_f16x8(vv[j]), as_f16x8(ph[ct]), acc[ct][j], 0, 0, 0);
+                        } else {
+                            acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(vv[j]), as_bf16x8(ph[ct]), acc[ct][j], 0, 0, 0);
+                            acc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(vv[j]), as_bf16x8(pl[ct]), acc[ct][j], 0, 0, 0);
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+            }
+            if (more) {
+                if (t0 + 2 * kTile <= nkeys)
+                    stage_store<D, BS, false, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys,
+                                                        vmax);
+                else
+                    stage_store<D, BS, true, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys,
+                                                       vmax);
+            }
+            __syncthreads();
+        };
+        // Even steps find step it + 1 in stB, odd steps in stA.  The loop
+        // runs steps in pairs so each body names its stages at compile time:
+        // the two are never copied into each other or selected at run time,
+        // and each wait covers one stage's loads.
+        int32_t it = 0;
+        for (; it < nomask; it += 2) {
+            step(it, std::false_type{}, stB, stA);
+            step(it + 1, std::false_type{}, stA, stB);
+        }
+        for (; it < ntiles; it += 2) {
+            step(it, std::true_type{}, stB, stA);
+            if (it + 1 < ntiles) step(it + 1, std::true_type{}, stA, stB);
+        }
+        if constexpr (F16 && !FP8) {
+            // |V| >= 2^16 (fp32 bits 0x47800000, the first bf16 magnitude
+            // past 65504), an infinity, or a NaN (which would convert
+            // exactly: it only costs the second walk)
+            const bool over = (int32_t)vmax.x >= 0x47800000 ||
+                              (vmax.y & 0x7fffffffu) >= 0x47800000u;
+            return __syncthreads_or(over ? 1 : 0) != 0;
+        } else {
+            return false;
+        }
+    };
+    // fp16 walk first; a bf16 cache holding a V element beyond fp16's range
+    // is walked again with the bf16 products (an E4M3 code always fits).
+    if (run(std::true_type{})) {
+        if constexpr (!FP8) run(std::false_type{});
     }
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
