@@ -24,10 +24,6 @@ __device__ __forceinline__ u32x4 ld16_nt(const void *p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
-
 // 8-byte global loads (one dwordx2 per lane), plain and nontemporal.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
@@ -49,21 +45,6 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
                                          0x07060302u);
         r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]),
                                              0x07060302u);
-    }
-    return r;
-}
-
-// Eight OCP E4M3 codes -> eight fp16 values, in order.  Exact: every E4M3
-// value (at most 448 in magnitude, four significant bits, no smaller than
-// 2^-9) is an fp16 value, and the fp32 -> fp16 rounding has nothing to round.
-__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(u32x2 w) {
-    u32x4 r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);  // codes 4h, 4h+1
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);   // codes 4h+2, 4h+3
-        r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
-        r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2));
     }
     return r;
 }
