@@ -103,13 +103,33 @@ struct Stage {
     Word v[kPasses];
 };
 
+// Which V^T chunk (dimension, chunk of 8 keys) a thread moves in pass ps.
+// With one block per step the four chunks of a dimension go to adjacent
+// threads.  With 16-key blocks at D = 128, pass ps covers block ps (keys
+// 16ps .. 16ps+15) for every dimension, two threads per dimension, so each
+// pass reads from a single block.
+template <int D, int BS>
+__device__ __forceinline__ void v_chunk(int ps, int tid, int &dim, int &cv) {
+    if constexpr (BS == 16 && D == 128) {
+        dim = tid >> 1;
+        cv = 2 * ps + (tid & 1);
+    } else {
+        const int idx = ps * 256 + tid;
+        dim = idx >> 2;
+        cv = idx & 3;
+    }
+}
+
 // Global -> registers for keys t0 .. t0+31, whose blocks are bidA (keys
 // t0 .. t0+15) and bidB (keys t0+16 .. t0+31; the same block unless
 // BS == 16).  The step's base addresses are wave-uniform; each thread adds a
-// fixed offset.  Every call issues the same loads with no branch, so the
-// compiler can wait for one stage while the next is in flight: a K row or V
-// chunk that lies wholly at or past nkeys is read from the tile's first key
-// instead (t0 < nkeys always).  Such keys sit past every position of the
+// fixed 32-bit offset, so where a pass reads one block the loads take the
+// base from scalar registers and no per-lane 64-bit address arithmetic is
+// left in the step.  Every call issues the same loads with no branch, so
+// the compiler can wait for one stage while the next is in flight: a K row
+// or V chunk that lies wholly at or past nkeys is read from the first key
+// of its pass's block instead (t0 < nkeys always, and when keys t0+16 .. do
+// not exist, bidB is bidA).  Such keys sit past every position of the
 // workgroup, so the causal mask drops their scores and stage_store zeroes
 // their V elements: they contribute exactly nothing.
 template <int D, int BS, bool FP8>
@@ -126,21 +146,40 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
     const E *vA = vc + (bidA * hkv + kvh) * (int64_t)D * BS + rowA;
     const E *vB = vc + (bidB * hkv + kvh) * (int64_t)D * BS + rowB;
     const int32_t nvalid = nkeys - t0;  // keys of the tile that exist, >= 1
+    // a pass reads a single block: always with BS >= 32; with BS == 16 when
+    // D == 128 (K pass ps holds keys 16ps .. 16ps+15, V as v_chunk says)
+    constexpr bool kOneBlock = BS >= 32 || D == 128;
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         // K: D/8 chunks of 8 elements per key
-        int kk = idx / (D / 8);
+        const int kk = idx / (D / 8);
         const int ch = idx % (D / 8);
-        if (kk >= nvalid) kk = 0;
-        const bool k_in_b = BS == 16 && kk >= 16;
-        const E *kp = (k_in_b ? kB : kA) + (k_in_b ? kk - 16 : kk) * D + ch * 8;
-        // V^T: 4 chunks of 8 keys per dim
-        const int dim = idx >> 2;
-        int cv = idx & 3;
-        if (8 * cv >= nvalid) cv = 0;
-        const bool v_in_b = BS == 16 && cv >= 2;
-        const E *vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cv - 2 : cv);
+        int dim, cv;
+        v_chunk<D, BS>(ps, tid, dim, cv);
+        const E *kp, *vp;
+        if constexpr (kOneBlock) {
+            // byte offsets from the pass's block base: the thread's own
+            // chunk, or the same chunk of the block's first key (K) / the
+            // block's first chunk of the dimension (V) when it lies past nkeys
+            const int kb0 = BS == 16 ? 16 * ps : 0;  // first key of the pass's block
+            const int vb0 = BS == 16 ? 2 * ps : 0;   // its first V chunk
+            const uint32_t k_own = (uint32_t)(((kk - kb0) * D + ch * 8) * sizeof(E));
+            const uint32_t k_first = (uint32_t)(ch * 8 * sizeof(E));
+            const uint32_t v_own = (uint32_t)((dim * BS + 8 * (cv - vb0)) * sizeof(E));
+            const uint32_t v_first = (uint32_t)(dim * BS * sizeof(E));
+            const char *kbase = reinterpret_cast<const char *>(BS == 16 && ps == 1 ? kB : kA);
+            const char *vbase = reinterpret_cast<const char *>(BS == 16 && ps == 1 ? vB : vA);
+            kp = reinterpret_cast<const E *>(kbase + (kk >= nvalid ? k_first : k_own));
+            vp = reinterpret_cast<const E *>(vbase + (8 * cv >= nvalid ? v_first : v_own));
+        } else {
+            const int kc_ = kk >= nvalid ? 0 : kk;
+            const bool k_in_b = kc_ >= 16;
+            kp = (k_in_b ? kB : kA) + (k_in_b ? kc_ - 16 : kc_) * D + ch * 8;
+            const int cc = 8 * cv >= nvalid ? 0 : cv;
+            const bool v_in_b = cc >= 2;
+            vp = (v_in_b ? vB : vA) + dim * BS + 8 * (v_in_b ? cc - 2 : cc);
+        }
         if constexpr (FP8) {
             st.k[ps] = ld8(kp);
             st.v[ps] = ld8(vp);
@@ -153,19 +192,16 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
 
 // Registers -> LDS.  On the last step (TAIL) the V elements of keys at or
 // past nkeys are cleared here rather than right after their load, so the
-// loads of a step never wait before the previous step's math.
-// An fp8 stage is widened to bf16 here (exactly), so LDS and the math are
-// the same for both caches.
-// F16: V is stored as fp16 (E4M3 codes convert exactly; bf16 elements
-// convert exactly below 65536 in magnitude).  vmax collects what tells
-// whether any did not: the largest staged element's fp32 bits as a signed
-// integer (vmax.x: the largest positive one) and as an unsigned one (vmax.y:
-// the negative one of largest magnitude, if any).  Integer maxima order
-// finite values, infinities and NaNs alike, so no NaN can hide a large
-// element.  On the last step
-// (TAIL) the V elements of keys at or past nkeys are cleared first, so
-// neither they nor their magnitude reach LDS or vmax; +0 has the same bits
-// in bf16 and fp16.
+// loads of a step never wait before the previous step's math; they are
+// cleared before any conversion, so neither they nor their magnitude reach
+// LDS or vmax (+0 has the same bits in bf16 and fp16).  K is stored as
+// bf16 (an fp8 stage is widened exactly).  V is stored as bf16 or, when F16,
+// as fp16: E4M3 codes convert exactly, and bf16 elements convert exactly
+// below 2^16 in magnitude.  vmax collects what tells whether any did not:
+// the largest staged element's fp32 bits as a signed integer (vmax.x, the
+// largest positive one) and as an unsigned one (vmax.y, the negative one of
+// largest magnitude, if any).  Integer maxima order finite values,
+// infinities and NaNs alike, so no NaN can hide a large element.
 template <int D, int BS, bool TAIL, bool FP8, bool F16>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                                             const Stage<D, BS, FP8> &st, int tid, int32_t t0,
@@ -174,7 +210,8 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
     for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
         const int kk = idx / (D / 8), ch = idx % (D / 8);
-        const int dim = idx >> 2, chv = idx & 3;
+        int dim, chv;
+        v_chunk<D, BS>(ps, tid, dim, chv);
         u32x4 kw, vw;
         if constexpr (FP8) {
             kw = e4m3x8_to_bf16x8(st.k[ps]);
