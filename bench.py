@@ -1073,6 +1073,90 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
     return out
 
 
+NUM_CUS = 256  # MI355X
+NUM_SIMDS = NUM_CUS * 4
+NUM_XCCS = 8
+
+
+def prefill_only(pa, wl, torch, reps):
+    """The mixed step's prompt chunks alone (4 x 512 new tokens over 4096
+    cached, bf16 and fp8 caches): `reps` timed calls each, for the counter
+    runs.  Prints one JSON line."""
+    out = {}
+    for dtype in ("bf16", "fp8"):
+        psh = wl.PrefillShape(dtype=dtype)
+        case = wl.make_prefill_case(psh, "cuda", pa.K_AXES, pa.V_AXES)
+        t_dev = torch.as_tensor(case.tables, device="cuda")
+        cu = torch.as_tensor(case.cu_q_lens, device="cuda")
+        cl = torch.as_tensor(case.context_lens, device="cuda")
+        mx = int(case.context_lens.max())
+        o = torch.empty((int(case.cu_q_lens[-1]), psh.num_q_heads, psh.head_dim), device="cuda")
+
+        def call():
+            if dtype == "fp8":
+                pa.pa_prefill_chunk_fp8(o, case.q, case.k_pool, case.v_pool, t_dev, cu, cl,
+                                        psh.scale, wl.FP8_SCALE, wl.FP8_SCALE, psh.new_tokens, mx)
+            else:
+                pa.pa_prefill_chunk(o, case.q, case.k_pool, case.v_pool, t_dev, cu, cl,
+                                    psh.scale, psh.new_tokens, mx)
+
+        warm(torch, call, 1.0)
+        med, all_ms = events_time(torch, call, reps, torch.cuda.current_stream())
+        flops = prefill_flops([int(c) for c in case.context_lens],
+                              [psh.new_tokens] * psh.num_reqs, psh.num_q_heads, psh.head_dim)
+        out[dtype] = {"us": med * 1e3, "TFLOPs": flops / (med * 1e-3) / 1e12, "flops": flops}
+        del case
+        torch.cuda.empty_cache()
+    print(json.dumps({"prefill_only": out}), flush=True)
+
+
+def prefill_counter_summary(dirs):
+    """Markdown table of SQ counters per prefill dispatch (bf16 and fp8 cache
+    instantiations) from rocprofv3 --pmc runs, with the matrix-core busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs, rocprof's MfmaUtil)
+    and the vector-ALU busy share (SQ_ACTIVE_INST_VALU over GRBM_GUI_ACTIVE x
+    CUs, rocprof's VALUBusy)."""
+    rows = []
+    for i, d in enumerate(dirs):
+        rows += [dict(r, run=i) for r in _read_counters(d)]
+    per = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        if "prefill_kernel<128, 128, " in name:  # demangled
+            kind = "fp8" if "prefill_kernel<128, 128, true>" in name else "bf16"
+        elif "prefill_kernelILi128ELi128ELb" in name:  # mangled: ...ELb1E = fp8
+            kind = "fp8" if "prefill_kernelILi128ELi128ELb1E" in name else "bf16"
+        else:
+            continue
+        key = (kind, r.get("Counter_Name"))
+        disp = (r["run"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        per.setdefault(key, {}).setdefault(disp, 0.0)
+        per[key][disp] += float(r["Counter_Value"])
+    lines = ["| cache | counter | mean per dispatch | dispatches |", "|---|---|---|---|"]
+    means = {}
+    for (kind, c), v in sorted(per.items()):
+        m = sum(v.values()) / len(v)
+        means[(kind, c)] = m
+        lines.append(f"| {kind} | {c} | {m:.4g} | {len(v)} |")
+    lines.append("")
+    for kind in ("bf16", "fp8"):
+        g = means.get((kind, "GRBM_GUI_ACTIVE"))
+        if not g:
+            continue
+        # the csv sums the counter over the 8 XCCs; each counts the same clock
+        g /= NUM_XCCS
+        lines.append(f"- {kind}: {g:.4g} GPU cycles per dispatch (GRBM_GUI_ACTIVE / {NUM_XCCS})")
+        mf = means.get((kind, "SQ_VALU_MFMA_BUSY_CYCLES"))
+        va = means.get((kind, "SQ_ACTIVE_INST_VALU"))
+        if mf is not None:
+            lines.append(f"- {kind}: matrix core busy {100 * mf / (g * NUM_SIMDS):.1f}% "
+                         f"(rocprof's MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles))")
+        if va is not None:
+            lines.append(f"- {kind}: vector ALU busy {100 * va / (g * NUM_CUS):.1f}% "
+                         f"(rocprof's VALUBusy: SQ_ACTIVE_INST_VALU / (CUs x cycles))")
+    return "\n".join(lines)
+
+
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
           "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
@@ -1170,9 +1254,16 @@ def main():
                     help="summarise two rocprofv3 --pmc runs into the traffic file and exit")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="print a per-kernel table of a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunks (bf16 and fp8 caches), for counter runs")
+    ap.add_argument("--prefill-counter-summary", nargs="+", metavar="PMC_DIR",
+                    help="summarise rocprofv3 --pmc runs of --prefill-only and exit")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.prefill_counter_summary:
+        print(prefill_counter_summary(args.prefill_counter_summary))
         return
     if args.pmc_summary:
         import workloads as wl
@@ -1194,6 +1285,9 @@ def main():
     import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.prefill_only:
+        prefill_only(pa, wl, torch, args.reps)
+        return
     mark_phase(torch)
     case, h = headline(args, pa, wl, torch, np)
     K, W = args.steps, args.warmup

@@ -126,3 +126,33 @@ def test_kernel_names_and_spread():
 
 def test_host_threads_is_bounded():
     assert 1 <= bench.host_threads() <= 16
+
+
+def test_prefill_counter_summary_per_run_and_xcc(tmp_path):
+    """Counters of two runs with overlapping dispatch ids stay apart; the
+    clock counter (summed over the 8 XCCs in the csv) is divided back; the
+    shares follow rocprof's MfmaUtil and VALUBusy definitions."""
+    bf16 = "void pa::(anonymous namespace)::prefill_kernel<128, 128, false>(pa::PrefillParams)"
+    fp8 = "_ZN2pa12_GLOBAL__N_114prefill_kernelILi128ELi128ELb1EEEvNS_13PrefillParamsE"
+    cyc = 400_000.0  # per XCC
+    runs = {
+        "a": [(1, bf16, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (1, bf16, "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * cyc * bench.NUM_SIMDS),
+              (2, fp8, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (2, fp8, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cyc * bench.NUM_SIMDS),
+              (3, "other_kernel", "GRBM_GUI_ACTIVE", 1.0)],
+        "b": [(1, bf16, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (1, bf16, "SQ_ACTIVE_INST_VALU", 0.75 * cyc * bench.NUM_CUS)],
+    }
+    for name, rows in runs.items():
+        os.makedirs(tmp_path / name)
+        with open(tmp_path / name / f"{name}_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writerows(rows)
+    text = bench.prefill_counter_summary([str(tmp_path / "a"), str(tmp_path / "b")])
+    assert "bf16: 4e+05 GPU cycles" in text
+    assert "bf16: matrix core busy 25.0%" in text
+    assert "bf16: vector ALU busy 75.0%" in text
+    assert "fp8: matrix core busy 50.0%" in text
+    assert "other_kernel" not in text
