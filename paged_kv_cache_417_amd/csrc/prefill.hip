@@ -332,7 +332,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     }
 
     const int32_t *table = p.block_tables + (int64_t)r * p.table_stride;
-    float m[2], l[2];
+    // Per column tile: running max m, sum l, and two values that change only
+    // with m: the rescale threshold m + kRescaleMargin and the exponent base
+    // msub (m, or 0 while no key is visible, less the fp16 lift).
+    float m[2], l[2], mthr[2], msub[2];
     floatx4 acc[2][D / 16];
 
     // The request's block-table entries live in one VGPR per wave, 64 at a
@@ -383,6 +386,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         for (int ct = 0; ct < 2; ++ct) {
             m[ct] = kNegInf;
             l[ct] = 0.f;
+            mthr[ct] = kNegInf;
+            msub[ct] = F16 ? -kF16Lift : 0.f;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                     // the bound, every weight of the column stays below it.
                     // When some lane's does (a wave-uniform branch), the
                     // exact column max becomes the new base of every column.
-                    if (__any(mr * sc > m[ct] + kRescaleMargin)) {
+                    if (__any(mr * sc > mthr[ct])) {
                         const float cm = rows4_max(mr);
                         const float mx = cm == kNegInf ? kNegInf : cm * sc;
                         const float m_new = fmaxf(m[ct], mx);
@@ -478,16 +483,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
                         for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
                         m[ct] = m_new;
+                        mthr[ct] = m_new + kRescaleMargin;
+                        msub[ct] = (m_new == kNegInf ? 0.f : m_new) - (F16 ? kF16Lift : 0.f);
                     }
                     // A column with no visible key yet keeps m = -inf; its
                     // weights are all exp2(-inf) = 0, so any finite base
                     // serves.  F16 lifts every weight by 2^kF16Lift.
-                    const float msub =
-                        (m[ct] == kNegInf ? 0.f : m[ct]) - (F16 ? kF16Lift : 0.f);
                     float pv[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const float arg = fmaf(sr[i], sc, -msub);
+                        const float arg = fmaf(sr[i], sc, -msub[ct]);
                         pv[i] = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
                     }
                     const float sum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
