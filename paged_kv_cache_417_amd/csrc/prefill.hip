@@ -132,7 +132,9 @@ __device__ __forceinline__ void v_chunk(int ps, int tid, int &dim, int &cv) {
 // not exist, bidB is bidA).  Such keys sit past every position of the
 // workgroup, so the causal mask drops their scores and stage_store zeroes
 // their V elements: they contribute exactly nothing.
-template <int D, int BS, bool FP8>
+// FULL: all 32 keys of the tile exist (the caller checked), so no offset
+// needs the clamp.
+template <int D, int BS, bool FP8, bool FULL>
 __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillParams &p,
                                            int kvh, int32_t t0, int32_t nkeys, int32_t bidA,
                                            int32_t bidB, int tid) {
@@ -170,8 +172,9 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
             const uint32_t v_first = (uint32_t)(dim * BS * sizeof(E));
             const char *kbase = reinterpret_cast<const char *>(BS == 16 && ps == 1 ? kB : kA);
             const char *vbase = reinterpret_cast<const char *>(BS == 16 && ps == 1 ? vB : vA);
-            kp = reinterpret_cast<const E *>(kbase + (kk >= nvalid ? k_first : k_own));
-            vp = reinterpret_cast<const E *>(vbase + (8 * cv >= nvalid ? v_first : v_own));
+            kp = reinterpret_cast<const E *>(kbase + (!FULL && kk >= nvalid ? k_first : k_own));
+            vp = reinterpret_cast<const E *>(vbase +
+                                             (!FULL && 8 * cv >= nvalid ? v_first : v_own));
         } else {
             const int kc_ = kk >= nvalid ? 0 : kk;
             const bool k_in_b = kc_ >= 16;
@@ -365,7 +368,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     auto stage = [&](St &st, int32_t t0) {
         const int32_t bA = block_id(t0 / BS);
         const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, nblk - 1)) : bA;
-        stage_load<D, BS, FP8>(st, p, kvh, t0, nkeys, bA, bB, tid);
+        // both branches issue the same loads, so the waits after the join
+        // still count one stage
+        if (t0 + kTile <= nkeys)
+            stage_load<D, BS, FP8, true>(st, p, kvh, t0, nkeys, bA, bB, tid);
+        else
+            stage_load<D, BS, FP8, false>(st, p, kvh, t0, nkeys, bA, bB, tid);
     };
 
     const int32_t ntiles = (nkeys + kTile - 1) / kTile;
