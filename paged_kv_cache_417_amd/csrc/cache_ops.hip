@@ -19,8 +19,26 @@ namespace {
 
 constexpr int32_t kRunBatch = 256;  // tokens per call from which V is written by runs
 
+// Index arithmetic of the one-thread-per-16-byte-chunk paths: the grid is
+// bounded by 2^32 threads, so indices are 32-bit, and head_dim / VEC and the
+// block size are powers of two (shifts, not divisions).
+struct ChunkIndex {
+    uint32_t th;  // token * Hkv + head
+    int32_t h, c;
+};
+template <typename T>
+__device__ __forceinline__ ChunkIndex chunk_index(uint32_t idx, int32_t num_kv_heads,
+                                                  int32_t head_dim) {
+    constexpr int VEC = 16 / sizeof(T);
+    const uint32_t cshift = __builtin_ctz((uint32_t)(head_dim / VEC));
+    const uint32_t th = idx >> cshift;
+    return ChunkIndex{th, (int32_t)(th % (uint32_t)num_kv_heads),
+                      (int32_t)(idx & ((1u << cshift) - 1))};
+}
+
 // K: one thread per (token, kv head, 16-byte chunk of the head's row): one
-// 16-byte store into the token's row of its block.
+// 16-byte store into the token's row of its block.  The row is loaded before
+// the slot is known, so the two loads overlap.
 template <typename T>
 __device__ __forceinline__ void write_k(const T *__restrict__ k_new, T *__restrict__ k_cache,
                                         const int64_t *__restrict__ slots, int64_t idx,
@@ -28,17 +46,15 @@ __device__ __forceinline__ void write_k(const T *__restrict__ k_new, T *__restri
                                         int32_t head_dim, int32_t block_size,
                                         int32_t num_blocks) {
     constexpr int VEC = 16 / sizeof(T);
-    const int32_t chunks = head_dim / VEC;
-    if (idx >= (int64_t)num_tokens * num_kv_heads * chunks) return;
-    const int32_t c = (int32_t)(idx % chunks);
-    const int64_t th = idx / chunks;  // token * Hkv + head
-    const int32_t h = (int32_t)(th % num_kv_heads);
-    const int64_t slot = slots[th / num_kv_heads];
+    if (idx >= (int64_t)num_tokens * num_kv_heads * (head_dim / VEC)) return;
+    const ChunkIndex ci = chunk_index<T>((uint32_t)idx, num_kv_heads, head_dim);
+    const u32x4 row = ld16(k_new + (int64_t)ci.th * head_dim + ci.c * VEC);
+    const int64_t slot = slots[ci.th / (uint32_t)num_kv_heads];
     if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
-    const int64_t b = slot / block_size;
-    const int32_t o = (int32_t)(slot % block_size);
-    st16(k_cache + ((b * num_kv_heads + h) * block_size + o) * head_dim + (int64_t)c * VEC,
-         ld16(k_new + th * head_dim + (int64_t)c * VEC));
+    const uint32_t bshift = __builtin_ctz((uint32_t)block_size);
+    const int64_t b = slot >> bshift;
+    const int32_t o = (int32_t)(slot & (block_size - 1));
+    st16(k_cache + ((b * num_kv_heads + ci.h) * block_size + o) * head_dim + ci.c * VEC, row);
 }
 
 // V (dimension rows of a block): one thread per (run of VEC consecutive
@@ -104,21 +120,19 @@ __device__ __forceinline__ void write_v_tokens(const T *__restrict__ v_new,
                                                int32_t head_dim, int32_t block_size,
                                                int32_t num_blocks) {
     constexpr int VEC = 16 / sizeof(T);
-    const int32_t chunks = head_dim / VEC;
-    if (idx >= (int64_t)num_tokens * num_kv_heads * chunks) return;
-    const int32_t c = (int32_t)(idx % chunks);
-    const int64_t th = idx / chunks;
-    const int32_t h = (int32_t)(th % num_kv_heads);
-    const int64_t slot = slots[th / num_kv_heads];
-    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
-    const int64_t b = slot / block_size;
-    const int32_t o = (int32_t)(slot % block_size);
+    if (idx >= (int64_t)num_tokens * num_kv_heads * (head_dim / VEC)) return;
+    const ChunkIndex ci = chunk_index<T>((uint32_t)idx, num_kv_heads, head_dim);
     union {
         u32x4 v;
         T e[VEC];
     } u;
-    u.v = ld16(v_new + th * head_dim + (int64_t)c * VEC);
-    T *col = v_cache + ((b * num_kv_heads + h) * head_dim + (int64_t)c * VEC) * block_size + o;
+    u.v = ld16(v_new + (int64_t)ci.th * head_dim + ci.c * VEC);  // overlaps the slot load
+    const int64_t slot = slots[ci.th / (uint32_t)num_kv_heads];
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const uint32_t bshift = __builtin_ctz((uint32_t)block_size);
+    const int64_t b = slot >> bshift;
+    const int32_t o = (int32_t)(slot & (block_size - 1));
+    T *col = v_cache + ((b * num_kv_heads + ci.h) * head_dim + ci.c * VEC) * block_size + o;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) col[(int64_t)e * block_size] = u.e[e];
 }
