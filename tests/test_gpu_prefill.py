@@ -270,7 +270,8 @@ def test_mixed_step_end_to_end(pa):
     (block 128, partitions of 512) and 4 prompt chunks of 512 new tokens over
     4096 cached; the allocator assigns every slot, one pa_cache_write stores
     all 8 + 2048 new K/V rows, then pa_decode and pa_prefill_chunk run on one
-    stream.  Sampled rows of both are checked against the oracle."""
+    stream.  Sampled rows of both are checked against the oracle; the step
+    with the prefill on a second stream gives the same bits."""
     dev = "cuda"
     dsh, psh = wl.MIXED_DECODE, wl.MIXED_PREFILL
     hkv, d, bs = dsh.num_kv_heads, dsh.head_dim, dsh.block_size
@@ -329,3 +330,20 @@ def test_mixed_step_end_to_end(pa):
                 for (r, i), want in ref.items())
     say(f"  decode err {err_d:.3e} prefill err {err_p:.3e}")
     assert err_d <= TOL and err_p <= TOL
+
+    # the same step with the decode and the prefill on two created streams
+    # (both default priority), the prefill's stream waiting for the decode's
+    # at its start: bit-identical, repeated
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    dt_d, dl_d = torch.as_tensor(dt, device=dev), torch.as_tensor(dl, device=dev)
+    pt_d, pl_d = torch.as_tensor(pt, device=dev), torch.as_tensor(pl, device=dev)
+    cu_d = torch.as_tensor(cu, device=dev)
+    for rep in range(3):
+        out_d2, out_p2 = torch.full_like(out_d, 7.0), torch.full_like(out_p, 7.0)
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(s1)
+        pa.pa_decode(out_d2, qd, k_pool, v_pool, dt_d, dl_d, dsh.scale, 32768, 512, ws, stream=s1)
+        pa.pa_prefill_chunk(out_p2, qp, k_pool, v_pool, pt_d, cu_d, pl_d, psh.scale, 512, 4608,
+                            stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(out_d2, out_d) and torch.equal(out_p2, out_p), rep
