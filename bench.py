@@ -626,11 +626,13 @@ def headline(args, pa, wl, torch, np):
 
     if args.calibrate:
         calibrate_copy(pa, torch, np, case, alloc)
+    copy_ref = copy_reference(pa, torch, np, case, alloc, args.reps)
 
     res = {
         "S": S, "ms_step": ms_step, "dec_avg_ms": dec_avg_ms, "dec_ms": dec_ms,
         "bytes_avg": bytes_avg, "achieved": achieved, "ps": ps_used,
         "seq_len": float(h_lens[-1].mean()), "alloc_us": alloc_us, "host_rate": host_rate,
+        "copy_ref": copy_ref,
     }
     return case, res
 
@@ -698,6 +700,32 @@ def calibrate_copy(pa, torch, np, case, alloc):
     pa.pa_copy_blocks(case.k_pool, case.v_pool, d)
     torch.cuda.synchronize()
     log(f"bench: calibration copy of {CALIB_PAIRS} blocks done")
+
+
+def copy_reference(pa, torch, np, case, alloc, reps):
+    """A plain device copy on the same pool, as a second reference beside the
+    8 TB/s peak: pa_copy_blocks over CALIB_PAIRS pairs of blocks that no
+    sequence uses (K and V regions of 128 KiB each), 1 GiB read and 1 GiB
+    written per call, event-timed."""
+    st = alloc.stats()
+    free = case.perm[st["num_used"]:-1]  # never handed out (the last entry is the pad block)
+    pairs = np.stack([free[:CALIB_PAIRS], free[CALIB_PAIRS:2 * CALIB_PAIRS]], axis=1)
+    d = torch.as_tensor(pairs.astype(np.int32), device="cuda")
+    block_bytes = case.k_pool[0].numel() * case.k_pool.element_size()
+    moved = CALIB_PAIRS * 2 * block_bytes  # read, and as many written
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.pa_copy_blocks(case.k_pool, case.v_pool, d)
+
+    for _ in range(3):
+        call()
+    med, ms = events_time(torch, call, reps, stream)
+    gbps = 2 * moved / (med * 1e-3) / 1e9
+    return {"us": med * 1e3, **spread(ms), "bytes_read": moved, "bytes_written": moved,
+            "GBps_read_plus_write": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
+            "workload": f"pa_copy_blocks of {CALIB_PAIRS} unused block pairs of the headline pool "
+                        f"(K and V, {block_bytes // 1024} KiB each)"}
 
 
 # ---------------------------------------------------------------------------
@@ -1329,6 +1357,7 @@ def main():
         },
         "host_allocator_us_per_step": h["alloc_us"],
         "host_inclusive_tokens_per_s": h["host_rate"],
+        "copy_reference": h["copy_ref"],
     }
     if args.cpu_budget > 0:
         log("bench: CPU baseline (oracle)")
