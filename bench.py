@@ -790,7 +790,8 @@ def row_long(pa, wl, torch, np, reps, cpu_budget):
     return r
 
 
-def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=False):
+def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=False,
+               groups=None, max_group=0):
     sh = case.shape
     dev = "cuda"
     lens = case.lengths if lengths is None else lengths
@@ -804,9 +805,17 @@ def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=
                              maxlen, ps, dev)
     stream = torch.cuda.current_stream()
 
+    if groups is not None:
+        g_dev = [torch.as_tensor(a, device=dev) for a in groups]
+
     def call():
-        pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, ps,
-                     ws, kv_reuse=kv_reuse)
+        if groups is None:
+            pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen,
+                         ps, ws, kv_reuse=kv_reuse)
+        else:
+            pa.pa_decode_grouped(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale,
+                                 maxlen, g_dev[0], g_dev[1], g_dev[2], max_group, ps, ws,
+                                 kv_reuse=kv_reuse)
 
     for _ in range(3):
         call()
@@ -867,11 +876,19 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
     q = wl.randn((len(ids), sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     case = wl.DecodeCase(sh, lens, order, tables, q, k_pool, v_pool, pa.K_AXES, pa.V_AXES)
-    # The allocator reports shared blocks, so the batch is decoded with the
-    # cache-keeping load policy; the streaming policy is timed beside it.
+    # The allocator reports shared blocks: the batch is decoded with the
+    # samples of each prompt as one group (pa_decode_grouped: the shared
+    # partitions are read once per group) and the cache-keeping load policy.
+    # Per-sequence decode with that policy and with the streaming one are
+    # timed beside it.
     assert alloc.stats()["num_shared"] > 0
-    r = decode_row(pa, torch, case, reps, kv_reuse=True)
+    ps = pa.pa_decode_default_partition(len(ids), sh.num_kv_heads, sh.block_size,
+                                        int(lens.max()))
+    groups = pa.decode_groups(tables, lens, np.arange(len(ids)) // samples, sh.block_size, ps)
+    r = decode_row(pa, torch, case, reps, kv_reuse=True, groups=groups, max_group=samples)
+    r["us_per_sequence"] = decode_row(pa, torch, case, reps, kv_reuse=True)["us"]
     r["us_streaming_policy"] = decode_row(pa, torch, case, reps)["us"]
+    r["shared_partitions_per_group"] = int(groups[2][0])
     # unique bytes: each physical block's valid rows once
     unique_tokens = 0
     seen = set()
@@ -888,7 +905,9 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     r["GBps_unique"] = r["unique_bytes"] / (r["us"] * 1e-6) / 1e9
     r["frac_unique_of_8TBps"] = r["GBps_unique"] / PEAK_HBM_GBPS
     r["workload"] = ("prefix-shared decode: 16 prompts of 2048+j tokens x 8 samples sharing "
-                     "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16")
+                     "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16; us: "
+                     "pa_decode_grouped (one group per prompt), us_per_sequence: pa_decode_ex "
+                     "with the cache-keeping policy")
     if cpu_budget > 0:
         r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     cow = {"us": copy_med * 1e3, "pairs": int(len(pairs)), "bytes_moved": copy_bytes,

@@ -199,6 +199,44 @@ pa_status pa_prefill_chunk(float *out, const void *q,
                            int32_t block_size, int32_t num_blocks,
                            float scale, pa_dtype dtype, void *stream);
 
+/* Paged decode of a batch whose sequences share leading blocks (parallel
+ * sampling, forked prompts: [VE] §3.1 KV sharing; [VI] §1 shared prompt
+ * prefixes).  Same result as pa_decode_ex with the same arguments, bit for
+ * bit, but a partition that every member of a group holds in the same
+ * physical blocks is read once for the whole group: one wave computes it
+ * for up to 16 / (num_q_heads / num_kv_heads) members at once.
+ *   group_offsets  [num_groups + 1] int32 device: group g is the run of
+ *                  sequences group_offsets[g] .. group_offsets[g + 1] - 1;
+ *                  the first is its leader, whose table is read.
+ *   seq_group      [num_seqs] int32 device: the group of each sequence, or
+ *                  -1.  A sequence is in group g only if seq_group[s] == g
+ *                  and s lies in g's run (and among its first
+ *                  max_group_size members); otherwise it is decoded alone.
+ *   group_shared   [num_groups] int32 device: leading partitions (of
+ *                  partition_size tokens) whose block-table entries are the
+ *                  same for every member.  Each member shares at most its
+ *                  partition count - 1.  A member whose own entries differ
+ *                  from the leader's over a shared partition gets a NaN row.
+ *   num_groups     >= 0 (0: pa_decode_ex).
+ *   max_group_size host bound of the group sizes (>= 1 when num_groups > 0).
+ * dtype must be BF16 (the fp32 path has no grouped kernel: UNSUPPORTED).
+ * Workspace, flags and errors as pa_decode_ex. */
+pa_status pa_decode_grouped(float *out, const void *q,
+                            const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables,
+                            int32_t block_table_stride,
+                            const int32_t *context_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale,
+                            int32_t max_context_len, int32_t partition_size,
+                            const int32_t *group_offsets,
+                            const int32_t *seq_group,
+                            const int32_t *group_shared, int32_t num_groups,
+                            int32_t max_group_size, void *workspace,
+                            size_t workspace_bytes, pa_dtype dtype,
+                            uint32_t flags, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* fp8 KV cache                                                               */
 /* ------------------------------------------------------------------------ */

@@ -47,7 +47,7 @@ EXPORTED = (
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
-    "pa_sched_stats",
+    "pa_sched_stats", "pa_decode_grouped",
 )
 
 
@@ -151,6 +151,9 @@ def _declare(lib):
                                     f32, vp]),
         "pa_decode_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, f32,
                                f32, i32, i32, vp, sz, ctypes.c_uint32, vp]),
+        "pa_decode_grouped": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
+                                   i32, i32, vp, vp, vp, i32, i32, vp, sz, ctypes.c_int,
+                                   ctypes.c_uint32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -277,6 +280,52 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _check(_lib.pa_decode_ex(*args, PA_DECODE_KV_REUSE, ctypes.c_void_p(_stream(stream))))
     else:
         _check(_lib.pa_decode(*args, ctypes.c_void_p(_stream(stream))))
+
+
+def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, group_offsets, seq_group, group_shared, max_group_size,
+                      partition_size=0, workspace=None, stream=None, kv_reuse=False) -> None:
+    """Paged decode with groups of sequences that share leading blocks: each
+    group's shared partitions are read once (int32 device tensors:
+    group_offsets [G+1], seq_group [S], group_shared [G])."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    s, hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_grouped(
+        _p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
+        _p(context_lens), s, hq, hkv, d, bs, nb, float(scale), int(max_context_len),
+        int(partition_size), _p(group_offsets), _p(seq_group), _p(group_shared),
+        group_shared.numel(), int(max_group_size), _p(workspace), ws_bytes,
+        _dtype_code(k_cache), PA_DECODE_KV_REUSE if kv_reuse else 0,
+        ctypes.c_void_p(_stream(stream))))
+
+
+def decode_groups(tables, lens, seq_group, block_size, partition_size):
+    """Host-side group arrays for pa_decode_grouped.  seq_group [S] (numpy) gives
+    each sequence's group id, or -1; ids run 0..G-1 in sequence order and each
+    group's members are consecutive.  A group shares the partitions covered by
+    the leading block-table entries every member has in common with the first
+    member, counting full blocks of every member's context only.  Returns int32
+    (group_offsets [G+1], seq_group [S], group_shared [G])."""
+    import numpy as np
+    seq_group = np.asarray(seq_group, dtype=np.int32)
+    G = int(seq_group.max()) + 1 if seq_group.size else 0
+    offsets = np.zeros(G + 1, np.int32)
+    shared = np.zeros(G, np.int32)
+    for g in range(G):
+        members = np.flatnonzero(seq_group == g)
+        if members.size == 0 or members[-1] - members[0] + 1 != members.size:
+            raise ValueError(f"group {g}: members must be consecutive and non-empty")
+        if g > 0 and members[0] < offsets[g]:
+            raise ValueError("group ids must follow sequence order")
+        offsets[g] = members[0]
+        offsets[g + 1] = members[-1] + 1
+        full = int(min(int(lens[m]) for m in members)) // block_size
+        rows = np.asarray(tables)[members, :full]
+        same = (rows == rows[0]).all(axis=0)
+        common = int(np.argmin(same)) if not same.all() else full
+        shared[g] = common * block_size // partition_size
+    return offsets, seq_group, shared
 
 
 def pa_cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale,

@@ -206,6 +206,12 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
 
 namespace {
 
+// Groups of sequences sharing leading blocks (pa_decode_grouped).
+struct GroupArgs {
+    const int32_t *offsets, *seq_group, *shared;
+    int32_t num_groups, max_group_size;
+};
+
 // Shared body of the decode entry points.  fp8: the caches hold E4M3 codes
 // scaled by k_scale / v_scale and q is bf16 (dtype must be BF16).
 pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_cache,
@@ -215,13 +221,26 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
                       int32_t block_size, int32_t num_blocks, float scale,
                       int32_t max_context_len, int32_t partition_size, void *workspace,
                       size_t workspace_bytes, pa_dtype dtype, uint32_t flags, bool fp8,
-                      float k_scale, float v_scale, void *stream) {
+                      float k_scale, float v_scale, void *stream,
+                      const GroupArgs *grp = nullptr) {
     if (fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale)))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: scales must be finite and > 0", fn);
     if (flags & ~(uint32_t)PA_DECODE_KV_REUSE)
         return pa::fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
     if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
     if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
+    if (grp) {
+        if (dtype != PA_DTYPE_BF16)
+            return pa::fail(PA_ERR_UNSUPPORTED, "%s: bf16 or fp8 caches only", fn);
+        if (grp->num_groups < 0 ||
+            (grp->num_groups > 0 && (!grp->offsets || !grp->seq_group || !grp->shared ||
+                                     grp->max_group_size < 1)))
+            return pa::fail(PA_ERR_INVALID_ARG, "%s: num_groups %d, max_group_size %d, group arrays %s",
+                            fn, grp->num_groups, grp->max_group_size,
+                            grp->offsets && grp->seq_group && grp->shared ? "set" : "NULL");
+        if (!aligned(grp->offsets, 4) || !aligned(grp->seq_group, 4) || !aligned(grp->shared, 4))
+            return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned group array", fn);
+    }
     if (pa_status st = check_geometry(fn, num_kv_heads, head_dim, block_size, num_blocks)) return st;
     if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
         return pa::fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %d not a multiple of num_kv_heads %d",
@@ -280,6 +299,21 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
     p.v_scale = fp8 ? v_scale : 1.f;
     if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_max, &p.ws_ml,
                                              &p.ws_o);
+    if (grp && grp->num_groups > 0 && np_max > 1) {
+        // one wave serves 16 / G members; chunks cover max_group_size members
+        const int64_t mpw = kMaxGroup / (num_q_heads / num_kv_heads);
+        const int64_t chunks = (grp->max_group_size + mpw - 1) / mpw;
+        if ((np_max - 1) * chunks * grp->num_groups * num_kv_heads > kMaxDecodeItems)
+            return pa::fail(PA_ERR_UNSUPPORTED, "%s: %lld group work items > %lld", fn,
+                            (long long)((np_max - 1) * chunks * grp->num_groups * num_kv_heads),
+                            (long long)kMaxDecodeItems);
+        p.seq_group = grp->seq_group;
+        p.grp_offsets = grp->offsets;
+        p.grp_shared = grp->shared;
+        p.num_groups = grp->num_groups;
+        p.grp_chunks = (int32_t)chunks;
+        p.grp_cover = (int32_t)(chunks * mpw);
+    }
     int rc = dtype == PA_DTYPE_BF16 ? pa::launch_decode_mfma(p, stream)
                                     : pa::launch_decode_valu(p, dtype, stream);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
@@ -303,6 +337,23 @@ pa_status pa_decode_ex(float *out, const void *q, const void *k_cache, const voi
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, max_context_len, partition_size, workspace,
                        workspace_bytes, dtype, flags, false, 1.f, 1.f, stream);
+}
+
+pa_status pa_decode_grouped(float *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, int32_t block_table_stride,
+                            const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, int32_t max_context_len,
+                            int32_t partition_size, const int32_t *group_offsets,
+                            const int32_t *seq_group, const int32_t *group_shared,
+                            int32_t num_groups, int32_t max_group_size, void *workspace,
+                            size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
+                            void *stream) {
+    const GroupArgs grp{group_offsets, seq_group, group_shared, num_groups, max_group_size};
+    return decode_impl("pa_decode_grouped", out, q, k_cache, v_cache, block_tables,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, max_context_len, partition_size,
+                       workspace, workspace_bytes, dtype, flags, false, 1.f, 1.f, stream, &grp);
 }
 
 pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const void *v_cache,

@@ -207,6 +207,20 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
     }
 }
 
+// Leading partitions of sequence s (np partitions in all) that its group
+// computes; 0 when s is in no group.  The per-sequence kernel and the group
+// kernel both decide membership with this one function, so every partition
+// is computed by exactly one of them.  The last partition is never shared,
+// so the merge always sees at least two partitions or none is shared.
+__device__ __forceinline__ int32_t shared_parts(const DecodeParams &p, int s, int32_t np) {
+    if (!p.seq_group) return 0;
+    const int32_t g = p.seq_group[s];
+    if (g < 0 || g >= p.num_groups) return 0;
+    const int32_t lo = p.grp_offsets[g], hi = p.grp_offsets[g + 1];
+    if (lo < 0 || s < lo || s >= hi || s - lo >= p.grp_cover) return 0;
+    return max(0, min(p.grp_shared[g], np - 1));
+}
+
 // Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
 // in 256 registers without spills.  FP8: the cache holds E4M3 codes.
 template <int D, int BS, bool NT, bool FP8>
@@ -224,7 +238,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
     const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
     const int part = decode_partition(item.slot, np, p.np_max);
-    if (part < 0) return;
+    if (part < 0 || part < shared_parts(p, s, np)) return;  // shared: the group kernel's
 
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h = kvh * G + n;  // this lane's query head (live when n < G)
@@ -369,8 +383,176 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
 }
 
+// Shared partitions of a group of sequences, one wave per (kv head, group,
+// member chunk, partition).  The wave reads the partition's K/V once, through
+// the leader's block table, and serves 16 / G members at once: MFMA column n
+// is member n / G of the chunk, query head n % G of the kv head (the same
+// layout the per-sequence kernel gives the G heads of one sequence), so each
+// member's partial is computed exactly as the per-sequence kernel would.
+// A member whose own table differs from the leader's over the partition gets
+// NaN partials (its row comes out NaN); a bad block id makes every member's
+// partials NaN.
+template <int D, int BS, bool NT, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_group_kernel(
+    DecodeParams p) {
+    using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
+    const uint32_t item = blockIdx.x;
+    const uint32_t r1 = item / (uint32_t)p.num_kv_heads;
+    const int kvh = (int)(item - r1 * (uint32_t)p.num_kv_heads);
+    const uint32_t r2 = r1 / (uint32_t)p.num_groups;
+    const int grp = (int)(r1 - r2 * (uint32_t)p.num_groups);
+    const int part = (int)(r2 / (uint32_t)p.grp_chunks);
+    const int chunk = (int)(r2 - (uint32_t)part * (uint32_t)p.grp_chunks);
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g = lane >> 4;
+
+    const int32_t lo = p.grp_offsets[grp];
+    if (lo < 0 || lo >= p.num_seqs) return;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int mpw = 16 / G;  // members per wave
+    // this lane's column: member s_n, query head h
+    const int32_t s_n = lo + chunk * mpw + n / G;
+    const int h = kvh * G + n % G;
+    // a column past the group's run may hold the next group's sequence: only
+    // this group's members are served here
+    bool live = n < mpw * G && s_n < p.num_seqs && p.seq_group[s_n] == grp;
+    if (live) {
+        const int32_t L = p.context_lens[s_n];
+        const int32_t nb = (L + BS - 1) / BS;
+        const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
+        const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
+        live = part < shared_parts(p, s_n, np);
+    }
+    if (!__any(live)) return;
+
+    // q as the B operand: column n = (member, head)
+    bf16x8 qb[D / 32];
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
+                           ((int64_t)(live ? s_n : 0) * p.num_q_heads + (live ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        u32x4 v = ld16(qrow + kslot_dim(ks, g));
+        if (!live) v = u32x4{0u, 0u, 0u, 0u};
+        qb[ks] = as_bf16x8(v);
+    }
+
+    const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
+    const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
+    const int32_t *table = p.block_tables + (int64_t)lo * p.table_stride;
+    // A shared partition lies wholly inside every live member's context.
+    const int32_t t_begin = part * p.partition_size;
+    const int32_t t_end = t_begin + p.partition_size;
+    const int32_t L = t_end;  // no token of the partition is masked
+    const int32_t nsteps = p.partition_size / 32;
+    const int32_t b_first = t_begin / BS, b_last = (t_end - 1) / BS;
+
+    // Each live member's table must equal the leader's over the partition:
+    // lanes compare 64 entries at a time, member by member.
+    bool bad_table = false;
+    for (int k = 0; k < mpw; ++k) {
+        const int32_t s_k = lo + chunk * mpw + k;
+        if (!__shfl(live ? 1 : 0, k * G, 64)) continue;  // column k * G is member k
+        const int32_t *mt = p.block_tables + (int64_t)s_k * p.table_stride;
+        bool diff = false;
+        for (int32_t b = b_first; b <= b_last; b += 64) {
+            const int32_t j = b + lane;
+            diff = diff || (j <= b_last && mt[j] != table[j]);
+        }
+        if (__any(diff) && n / G == k) bad_table = true;
+    }
+
+    float m = kNegInf, lsum = 0.f;
+    floatx4 acc[D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    int32_t win = b_first;
+    int32_t tbl = (win + lane <= b_last) ? table[win + lane] : 0;
+    bool bad_block = false;
+    auto block_id = [&](int32_t j) -> int32_t {
+        if (j - win >= 64) {
+            win = j;
+            tbl = (win + lane <= b_last) ? table[win + lane] : 0;
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), on this rare path only
+        }
+        int32_t b = __builtin_amdgcn_readlane(tbl, j - win);
+        if ((uint32_t)b >= (uint32_t)p.num_blocks) {
+            bad_block = true;
+            b = 0;
+        }
+        return b;
+    };
+    auto issue = [&](Regs &r, int32_t st) {
+        const int32_t t0 = t_begin + 32 * st;
+        const int32_t bA = block_id(t0 / BS);
+        const int32_t bB = BS == 16 ? block_id(min((t0 + 16) / BS, b_last)) : bA;
+        if constexpr (FP8)
+            load_step_fp8<D, BS, true, NT>(r, reinterpret_cast<const uint8_t *>(p.k_cache),
+                                           reinterpret_cast<const uint8_t *>(p.v_cache), t0, L,
+                                           bA, bB, p.num_kv_heads, kvh, lane);
+        else
+            load_step<D, BS, true, NT>(r, kc, vc, t0, L, bA, bB, p.num_kv_heads, kvh, lane);
+    };
+    auto consume = [&](const Regs &raw, int32_t st) {
+        const int32_t t0 = t_begin + 32 * st;
+        const StepRegs<D> *rp;
+        StepRegs<D> wide;
+        if constexpr (FP8) {
+            widen_step<D>(raw, wide);
+            rp = &wide;
+        } else {
+            rp = &raw;
+        }
+        compute_step<D, false>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+    };
+    // the same ping-pong as the per-sequence kernel (the partition is whole)
+    {
+        Regs ra, rb;
+        issue(ra, 0);
+        int32_t st = 0;
+        for (; st + 1 < nsteps; st += 2) {
+            issue(rb, st + 1);
+            consume(ra, st);
+            if (st + 2 < nsteps) issue(ra, st + 2);
+            consume(rb, st + 1);
+        }
+        if (st < nsteps) consume(ra, st);
+    }
+
+    lsum = rows4_sum(lsum);
+    if (!live) return;
+    const float qnan = __builtin_nanf("");
+    const float vs = FP8 ? p.v_scale : 1.f;
+    const bool bad = bad_block || bad_table;
+    const int64_t slot = ((int64_t)s_n * p.num_q_heads + h) * p.np_max + part;
+    float *o_part = p.ws_o + slot * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        floatx4 o = FP8 ? acc[j] * vs : acc[j];
+        if (bad) o = floatx4{qnan, qnan, qnan, qnan};
+        *reinterpret_cast<floatx4 *>(o_part + 16 * j + 4 * g) = o;
+    }
+    if (g == 0) {
+        p.ws_ml[2 * slot] = bad ? qnan : m;
+        p.ws_ml[2 * slot + 1] = bad ? qnan : lsum;
+    }
+}
+
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
+    if (p.seq_group && p.num_groups > 0 && p.np_max > 1) {
+        // partitions that can be shared: all but a sequence's last
+        const dim3 ggrid((unsigned)((int64_t)(p.np_max - 1) * p.grp_chunks * p.num_groups *
+                                    p.num_kv_heads));
+#define PA_GROUP(NTv, FP8v) \
+    hipLaunchKernelGGL((decode_group_kernel<D, BS, NTv, FP8v>), ggrid, dim3(64), 0, s, p)
+        if (p.kv_fp8) {
+            if (p.kv_reuse) PA_GROUP(false, true); else PA_GROUP(true, true);
+        } else {
+            if (p.kv_reuse) PA_GROUP(false, false); else PA_GROUP(true, false);
+        }
+#undef PA_GROUP
+    }
     const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
     if (p.kv_fp8) {
         if (p.kv_reuse)

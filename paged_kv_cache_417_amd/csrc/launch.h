@@ -35,6 +35,18 @@ struct DecodeParams {
     bool kv_reuse;     // keep K/V cached (shared blocks) instead of streaming them
     bool kv_fp8;       // K/V hold OCP E4M3 codes (q stays bf16)
     float v_scale;     // value of a V code = code * v_scale (1 for bf16)
+    // Groups of sequences that share leading blocks (null seq_group: none).
+    // Sequence s belongs to group g = seq_group[s] when 0 <= g < num_groups,
+    // grp_offsets[g] <= s < grp_offsets[g + 1] and s - grp_offsets[g] <
+    // grp_cover; its first min(grp_shared[g], np(s) - 1) partitions are then
+    // computed once for the whole group, through the table of sequence
+    // grp_offsets[g] (the leader).
+    const int32_t *seq_group;
+    const int32_t *grp_offsets;
+    const int32_t *grp_shared;
+    int32_t num_groups;
+    int32_t grp_cover;    // members per group the group kernel's chunks cover
+    int32_t grp_chunks;   // member chunks per group (16 / G members each)
 };
 
 struct PrefillParams {
@@ -87,7 +99,10 @@ int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks,
                        int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, pa_dtype dtype, void *stream);
 
-// bf16 decode on the matrix cores (any group size up to 16).
+// bf16 decode on the matrix cores (any group size up to 16).  With groups
+// (p.seq_group), the shared partitions are computed by one wave per (kv
+// head, group, member chunk, partition) for every member at once, and the
+// per-sequence kernel skips them.
 int launch_decode_mfma(const DecodeParams &p, void *stream);
 // Vector-ALU decode (fp32 or bf16, any group size up to 16).
 int launch_decode_valu(const DecodeParams &p, pa_dtype dtype, void *stream);

@@ -140,3 +140,33 @@ def test_error_text_is_thread_local_and_cleared():
     assert b"head_dim" in lib.pa_last_error()
     assert lib.pa_decode(*decode_args(S=0, out=NULL, q=NULL, tables=NULL, lens=NULL)) == pa.PA_OK
     assert lib.pa_last_error() == b""
+
+
+def grouped_args(offsets=FAKE, seq_group=FAKE, shared=FAKE, ngroups=1, gmax=8, flags=0, **over):
+    a = list(decode_args(**over))
+    dtype = a[18]
+    return tuple(a[:16]) + (offsets, seq_group, shared, ngroups, gmax, a[16], a[17], dtype,
+                            flags, STREAM)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ngroups=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(offsets=NULL), pa.PA_ERR_INVALID_ARG),
+    (dict(seq_group=NULL), pa.PA_ERR_INVALID_ARG),
+    (dict(shared=NULL), pa.PA_ERR_INVALID_ARG),
+    (dict(gmax=0), pa.PA_ERR_INVALID_ARG),
+    (dict(offsets=MISALIGNED), pa.PA_ERR_INVALID_ARG),
+    (dict(flags=4), pa.PA_ERR_INVALID_ARG),
+    (dict(dtype=pa.PA_DTYPE_F32), pa.PA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_grouped_rejects(kw, status):
+    assert lib.pa_decode_grouped(*grouped_args(**kw)) == status
+    assert lib.pa_last_error()
+
+
+def test_decode_grouped_empty_batch_and_no_groups_are_ok():
+    none = dict(S=0, out=NULL, q=NULL, tables=NULL, lens=NULL)
+    assert lib.pa_decode_grouped(*grouped_args(**none)) == pa.PA_OK
+    assert lib.pa_decode_grouped(*grouped_args(offsets=NULL, seq_group=NULL, shared=NULL,
+                                               ngroups=0, gmax=0, **none)) == pa.PA_OK

@@ -304,3 +304,103 @@ def test_prefix_cache_hits_decode_like_fresh_prompts(pa):
     err = float(np.abs(got - ref).max())
     say(f"  cached == fresh bit for bit over {S} requests; oracle rows {sample} err {err:.3e}")
     assert err <= TOL
+
+
+def _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups, ps, max_group):
+    """Per-sequence decode (kv reuse) and grouped decode of one batch."""
+    dev = "cuda"
+    S = q.shape[0]
+    maxlen = int(lens.max())
+    t_dev = torch.as_tensor(tables, device=dev)
+    l_dev = torch.as_tensor(lens, device=dev)
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, ps, dev)
+    ref = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
+    pa.pa_decode(ref, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, ps, ws, kv_reuse=True)
+    off, sg, shd = (torch.as_tensor(a, device=dev) for a in groups)
+    got = torch.full_like(ref, 7.0)
+    pa.pa_decode_grouped(got, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, off, sg, shd,
+                         max_group, ps, ws, kv_reuse=True)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def test_grouped_decode_matches_per_sequence(pa):
+    """pa_decode_grouped on the prefix-shared batch (16 groups of 8 samples,
+    2048 shared tokens = 4 partitions of 512): bit-identical to pa_decode;
+    a member whose table is changed inside a shared partition gets a NaN
+    row and every other row stays bit-identical."""
+    sh = wl.PREFIX_SHARED
+    dev = "cuda"
+    plan = wl.prefix_plan()
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    n_prompts, samples = plan.tail_lens.shape
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    maxlen = int(lens.max())
+    ps = pa.pa_decode_default_partition(S, sh.num_kv_heads, sh.block_size, maxlen)
+    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, sh.block_size, ps)
+    assert list(groups[2]) == [2048 // ps] * n_prompts
+    gen = wl.make_generator(sh.seed + 9, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    say(f"case grouped decode: {n_prompts} groups of {samples}, ps {ps}")
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups, ps, samples)
+    assert torch.isfinite(ref).all()
+    assert torch.equal(got, ref)
+
+    # member 3 of group 0 points one shared-partition entry at another block
+    bad = tables.copy()
+    bad[3, 5] = order[alloc.stats()["num_used"]]  # a block nobody holds
+    ref2, got2 = _decode_pair(pa, sh, q, k_pool, v_pool, bad, lens, groups, ps, samples)
+    assert torch.isnan(got2[3]).all()
+    keep = torch.ones(S, dtype=torch.bool, device=dev)
+    keep[3] = False
+    assert torch.equal(got2[keep], ref2[keep])
+
+
+def test_grouped_decode_chunks_caps_and_loners(pa):
+    """GQA heads (4 members per wave, groups of 6 in two chunks), 64-token
+    partitions, a group left ungrouped, a group whose shared count is far
+    too large (the leader keeps its own table and stays exact, members whose
+    tables diverge get NaN rows), and an empty group run."""
+    sh = wl.DecodeShape("grp", 18, 32, 8, 128, 16, 4096, "bf16", wl.SEED_BASE + 44)
+    dev = "cuda"
+    plan = wl.prefix_plan(num_prompts=3, samples=6, prompt_len=300, seed=sh.seed, max_tail=200)
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    ps = 64
+    seq_group = np.array([0] * 6 + [1] * 6 + [-1] * 6, np.int32)
+    off, sg, shd = pa.decode_groups(tables, lens, seq_group, sh.block_size, ps)
+    assert list(shd) == [300 // 16 * 16 // ps] * 2
+    gen = wl.make_generator(sh.seed + 1, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    say("case grouped decode: GQA chunks, loners")
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), ps, 6)
+    assert torch.isfinite(ref).all() and torch.equal(got, ref)
+
+    # group 1 claims 100 shared partitions: capped per member at its own
+    # count - 1; past the prompt the members' tables differ from the leader's
+    shd_big = shd.copy()
+    shd_big[1] = 100
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd_big), ps, 6)
+    assert torch.equal(got[:6], ref[:6]) and torch.equal(got[12:], ref[12:])
+    assert torch.equal(got[6], ref[6])  # the leader reads its own table
+    for s in range(7, 12):
+        np_s = -(-int(lens[s]) // ps)
+        if np_s - 1 > shd[1]:  # a shared partition past the common prefix
+            assert torch.isnan(got[s]).all(), s
+        else:
+            assert torch.equal(got[s], ref[s]), s
+
+    # an empty run between two groups, and max_group_size below a group's size
+    # (members past it are decoded alone): still bit-identical
+    off2 = np.array([0, 6, 6, 12], np.int32)
+    sg2 = np.array([0] * 6 + [2] * 6 + [-1] * 6, np.int32)
+    shd2 = np.array([shd[0], 7, shd[1]], np.int32)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off2, sg2, shd2), ps, 3)
+    assert torch.equal(got, ref)
