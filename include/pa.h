@@ -271,6 +271,25 @@ pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const vo
                         int32_t max_context_len, int32_t partition_size, void *workspace,
                         size_t workspace_bytes, uint32_t flags, void *stream);
 
+/* pa_decode_grouped over fp8 (E4M3) caches with their scales, as
+ * pa_decode_fp8; group arguments as pa_decode_grouped. */
+pa_status pa_decode_grouped_fp8(float *out, const void *q,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *block_tables,
+                                int32_t block_table_stride,
+                                const int32_t *context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, float scale, float k_scale,
+                                float v_scale, int32_t max_context_len,
+                                int32_t partition_size,
+                                const int32_t *group_offsets,
+                                const int32_t *seq_group,
+                                const int32_t *group_shared,
+                                int32_t num_groups, int32_t max_group_size,
+                                void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream);
+
 /* pa_prefill_chunk over fp8 caches: q is bf16; codes are widened to bf16
  * exactly when staged, k_scale joins the softmax scale and v_scale the
  * output, in fp32.  Everything else as pa_prefill_chunk. */

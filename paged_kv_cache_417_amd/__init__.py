@@ -47,7 +47,7 @@ EXPORTED = (
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
-    "pa_sched_stats", "pa_decode_grouped",
+    "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8",
 )
 
 
@@ -154,6 +154,9 @@ def _declare(lib):
         "pa_decode_grouped": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                    i32, i32, vp, vp, vp, i32, i32, vp, sz, ctypes.c_int,
                                    ctypes.c_uint32, vp]),
+        "pa_decode_grouped_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                       f32, f32, f32, i32, i32, vp, vp, vp, i32, i32, vp, sz,
+                                       ctypes.c_uint32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -326,6 +329,22 @@ def decode_groups(tables, lens, seq_group, block_size, partition_size):
         common = int(np.argmin(same)) if not same.all() else full
         shared[g] = common * block_size // partition_size
     return offsets, seq_group, shared
+
+
+def pa_decode_grouped_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                          v_scale, max_context_len, group_offsets, seq_group, group_shared,
+                          max_group_size, partition_size=0, workspace=None, stream=None,
+                          kv_reuse=False) -> None:
+    """pa_decode_grouped over uint8 (E4M3) caches; q is bf16."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    s, hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_grouped_fp8(
+        _p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
+        _p(context_lens), s, hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
+        int(max_context_len), int(partition_size), _p(group_offsets), _p(seq_group),
+        _p(group_shared), group_shared.numel(), int(max_group_size), _p(workspace), ws_bytes,
+        PA_DECODE_KV_REUSE if kv_reuse else 0, ctypes.c_void_p(_stream(stream))))
 
 
 def pa_cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale,

@@ -356,6 +356,25 @@ pa_status pa_decode_grouped(float *out, const void *q, const void *k_cache, cons
                        workspace, workspace_bytes, dtype, flags, false, 1.f, 1.f, stream, &grp);
 }
 
+pa_status pa_decode_grouped_fp8(float *out, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                int32_t block_table_stride, const int32_t *context_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                float scale, float k_scale, float v_scale,
+                                int32_t max_context_len, int32_t partition_size,
+                                const int32_t *group_offsets, const int32_t *seq_group,
+                                const int32_t *group_shared, int32_t num_groups,
+                                int32_t max_group_size, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream) {
+    const GroupArgs grp{group_offsets, seq_group, group_shared, num_groups, max_group_size};
+    return decode_impl("pa_decode_grouped_fp8", out, q, k_cache, v_cache, block_tables,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, max_context_len, partition_size,
+                       workspace, workspace_bytes, PA_DTYPE_BF16, flags, true, k_scale, v_scale,
+                       stream, &grp);
+}
+
 pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *block_tables, int32_t block_table_stride,
                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

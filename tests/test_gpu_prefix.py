@@ -404,3 +404,37 @@ def test_grouped_decode_chunks_caps_and_loners(pa):
     shd2 = np.array([shd[0], 7, shd[1]], np.int32)
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off2, sg2, shd2), ps, 3)
     assert torch.equal(got, ref)
+
+
+def test_grouped_decode_fp8_matches_per_sequence(pa):
+    """pa_decode_grouped_fp8 against pa_decode_fp8 on a small prefix-shared
+    batch whose pools hold E4M3 codes: bit-identical."""
+    sh = wl.DecodeShape("grp8", 12, 8, 2, 128, 16, 2048, "bf16", wl.SEED_BASE + 45)
+    dev = "cuda"
+    plan = wl.prefix_plan(num_prompts=3, samples=4, prompt_len=200, seed=sh.seed, max_tail=100)
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    sc = wl.FP8_SCALE
+    k8 = (k_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (v_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+    ps = 64
+    off, sg, shd = pa.decode_groups(tables, lens, np.arange(S) // 4, sh.block_size, ps)
+    assert (shd == 3).all()  # 200 tokens: 12 common full blocks = 3 partitions of 64
+    gen = wl.make_generator(sh.seed + 2, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    maxlen = int(lens.max())
+    t_dev, l_dev = torch.as_tensor(tables, device=dev), torch.as_tensor(lens, device=dev)
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, ps, dev)
+    ref = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
+    got = torch.full_like(ref, 7.0)
+    say("case grouped decode fp8")
+    pa.pa_decode_fp8(ref, q, k8, v8, t_dev, l_dev, sh.scale, sc, sc, maxlen, ps, ws)
+    pa.pa_decode_grouped_fp8(got, q, k8, v8, t_dev, l_dev, sh.scale, sc, sc, maxlen,
+                             *(torch.as_tensor(a, device=dev) for a in (off, sg, shd)), 4, ps,
+                             ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all() and torch.equal(got, ref)
