@@ -221,13 +221,12 @@ __device__ __forceinline__ int32_t shared_parts(const DecodeParams &p, int s, in
     return max(0, min(p.grp_shared[g], np - 1));
 }
 
-// Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
-// in 256 registers without spills.  FP8: the cache holds E4M3 codes.
+// One per-sequence work item: (kv head, sequence, partition slot) of the
+// 1-D grid index.
 template <int D, int BS, bool NT, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
-    DecodeParams p) {
+__device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t index) {
     using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
-    const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
+    const DecodeItem item = decode_item(index, p.num_kv_heads, p.num_seqs);
     const int kvh = item.kvh;
     const int s = item.seq;
     const int lane = threadIdx.x;
@@ -393,10 +392,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 // NaN partials (its row comes out NaN); a bad block id makes every member's
 // partials NaN.
 template <int D, int BS, bool NT, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_group_kernel(
-    DecodeParams p) {
+__device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_t item) {
     using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
-    const uint32_t item = blockIdx.x;
     const uint32_t r1 = item / (uint32_t)p.num_kv_heads;
     const int kvh = (int)(item - r1 * (uint32_t)p.num_kv_heads);
     const uint32_t r2 = r1 / (uint32_t)p.num_groups;
@@ -538,22 +535,47 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
 }
 
+// Two waves per SIMD: the two step buffers (64 VGPRs each at D = 128) fit
+// in 256 registers without spills.  FP8: the cache holds E4M3 codes.
+template <int D, int BS, bool NT, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
+    DecodeParams p) {
+    decode_seq_item<D, BS, NT, FP8>(p, blockIdx.x);
+}
+
+// Grouped decode in one grid: the first group_items workgroups compute the
+// groups' shared partitions, the rest are the per-sequence items (which skip
+// those partitions).  One launch, so the shared partitions' waves and the
+// per-sequence ones fill the chip together instead of draining in turn.
+template <int D, int BS, bool NT, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_grouped_kernel(
+    DecodeParams p, uint32_t group_items) {
+    if (blockIdx.x < group_items)
+        decode_group_item<D, BS, NT, FP8>(p, blockIdx.x);
+    else
+        decode_seq_item<D, BS, NT, FP8>(p, blockIdx.x - group_items);
+}
+
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
+    const int64_t seq_items = (int64_t)p.np_max * p.num_kv_heads * p.num_seqs;
     if (p.seq_group && p.num_groups > 0 && p.np_max > 1) {
-        // partitions that can be shared: all but a sequence's last
-        const dim3 ggrid((unsigned)((int64_t)(p.np_max - 1) * p.grp_chunks * p.num_groups *
-                                    p.num_kv_heads));
-#define PA_GROUP(NTv, FP8v) \
-    hipLaunchKernelGGL((decode_group_kernel<D, BS, NTv, FP8v>), ggrid, dim3(64), 0, s, p)
+        // shared partitions: all but a sequence's last
+        const int64_t group_items =
+            (int64_t)(p.np_max - 1) * p.grp_chunks * p.num_groups * p.num_kv_heads;
+        const dim3 grid((unsigned)(group_items + seq_items));
+#define PA_GROUPED(NTv, FP8v)                                                                     \
+    hipLaunchKernelGGL((decode_grouped_kernel<D, BS, NTv, FP8v>), grid, dim3(64), 0, s, p,      \
+                       (uint32_t)group_items)
         if (p.kv_fp8) {
-            if (p.kv_reuse) PA_GROUP(false, true); else PA_GROUP(true, true);
+            if (p.kv_reuse) PA_GROUPED(false, true); else PA_GROUPED(true, true);
         } else {
-            if (p.kv_reuse) PA_GROUP(false, false); else PA_GROUP(true, false);
+            if (p.kv_reuse) PA_GROUPED(false, false); else PA_GROUPED(true, false);
         }
-#undef PA_GROUP
+#undef PA_GROUPED
+        return;
     }
-    const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
+    const dim3 grid((unsigned)seq_items);
     if (p.kv_fp8) {
         if (p.kv_reuse)
             hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false, true>), grid, dim3(64), 0, s, p);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     constexpr int QD = D / 4;            // dims per lane in q.k
     constexpr int DPL = D / 64;          // dims per lane in P V
     const int BS = p.block_size;
-    const DecodeItem item = decode_item(p.num_kv_heads, p.num_seqs);
+    const DecodeItem item = decode_item(blockIdx.x, p.num_kv_heads, p.num_seqs);
     const int kvh = item.kvh;
     const int s = item.seq;
     const int lane = threadIdx.x;

@@ -134,8 +134,7 @@ __device__ __forceinline__ int kslot_dim(int ks, int g) {
 struct DecodeItem {
     int kvh, seq, slot;
 };
-__device__ __forceinline__ DecodeItem decode_item(int num_kv_heads, int num_seqs) {
-    const uint32_t i = blockIdx.x;
+__device__ __forceinline__ DecodeItem decode_item(uint32_t i, int num_kv_heads, int num_seqs) {
     const uint32_t rest = i / (uint32_t)num_kv_heads;
     return DecodeItem{(int)(i - rest * (uint32_t)num_kv_heads),
                       (int)(rest % (uint32_t)num_seqs), (int)(rest / (uint32_t)num_seqs)};
