@@ -186,7 +186,12 @@ pa_status pa_decode_ex(float *out, const void *q,
  *   max_q_len, max_context_len  host-known bounds (size the grid).
  * A request whose qlen exceeds its context, exceeds max_q_len, or whose
  * context exceeds max_context_len or its table, or a table entry outside
- * [0, num_blocks), gets NaN rows; nothing is read out of range.  bf16 only. */
+ * [0, num_blocks), gets NaN rows; nothing is read out of range.  bf16 only.
+ * Precision: Q K^T in bf16 with fp32 accumulation; the softmax weights
+ * enter P V rounded to fp16 (relative error 2^-11) against V converted to
+ * fp16, exact for every V element below 2^16 in magnitude.  A workgroup
+ * that meets a larger, infinite or NaN V element recomputes its rows with
+ * the weights split into bf16 high and low parts (error near 2^-16). */
 pa_status pa_prefill_chunk(float *out, const void *q,
                            const void *k_cache, const void *v_cache,
                            const int32_t *block_tables,
@@ -290,9 +295,9 @@ pa_status pa_decode_grouped_fp8(float *out, const void *q,
                                 void *workspace, size_t workspace_bytes,
                                 uint32_t flags, void *stream);
 
-/* pa_prefill_chunk over fp8 caches: q is bf16; codes are widened to bf16
- * exactly when staged, k_scale joins the softmax scale and v_scale the
- * output, in fp32.  Everything else as pa_prefill_chunk. */
+/* pa_prefill_chunk over fp8 caches: q is bf16; K codes are widened to bf16
+ * and V codes to fp16 exactly when staged, k_scale joins the softmax scale
+ * and v_scale the output, in fp32.  Everything else as pa_prefill_chunk. */
 pa_status pa_prefill_chunk_fp8(float *out, const void *q, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,
                                int32_t block_table_stride, const int32_t *cu_q_lens,
