@@ -349,6 +349,13 @@ def test_grouped_decode_matches_per_sequence(pa):
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups, ps, samples)
     assert torch.isfinite(ref).all()
     assert torch.equal(got, ref)
+    # and against the fp64 oracle on sampled members of several groups
+    rows = [0, 3, samples - 1, 7 * samples + 2, S - 1]
+    want = oracle_decode_rows(q, k_pool, v_pool, tables, lens, rows, sh.block_size, sh.scale,
+                              pa.K_AXES, pa.V_AXES)
+    err = float(np.abs(got[torch.as_tensor(rows, device=dev)].double().cpu().numpy() - want).max())
+    say(f"  grouped rows {rows} max err {err:.3e}")
+    assert err <= TOL
 
     # member 3 of group 0 points one shared-partition entry at another block
     bad = tables.copy()
