@@ -445,3 +445,35 @@ def test_grouped_decode_fp8_matches_per_sequence(pa):
                              ws)
     torch.cuda.synchronize()
     assert torch.isfinite(ref).all() and torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("bad", ["runs_past_the_batch", "ids_out_of_range", "negative_shared",
+                                 "decreasing_offsets"])
+def test_grouped_decode_malformed_groups_decode_alone(pa, bad):
+    """Group arrays that name no valid group leave every sequence to the
+    per-sequence path: the output equals pa_decode bit for bit."""
+    sh = wl.DecodeShape("grpbad", 12, 8, 8, 128, 16, 2048, "bf16", wl.SEED_BASE + 46)
+    dev = "cuda"
+    plan = wl.prefix_plan(num_prompts=3, samples=4, prompt_len=200, seed=sh.seed, max_tail=100)
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    ps = 64
+    off = np.array([0, 4, 8, 12], np.int32)
+    sg = (np.arange(S) // 4).astype(np.int32)
+    shd = np.full(3, 3, np.int32)
+    if bad == "runs_past_the_batch":
+        off = off + S
+    elif bad == "ids_out_of_range":
+        sg = sg + 3
+    elif bad == "negative_shared":
+        shd = shd - 6
+    else:
+        off = off[::-1].copy()
+    gen = wl.make_generator(sh.seed + 3, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    say(f"case grouped decode, malformed groups: {bad}")
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), ps, 4)
+    assert torch.isfinite(ref).all() and torch.equal(got, ref)
