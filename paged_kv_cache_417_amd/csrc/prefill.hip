@@ -340,6 +340,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // msub (m, or 0 while no key is visible, less the fp16 lift).
     float m[2], l[2], mthr[2], msub[2];
     floatx4 acc[2][D / 16];
+    // F16 walk: the sum of each column's weights rides in the matrix core as
+    // one more product against a tile whose row 0 is all ones (row 0 of the
+    // result, lane (0, n), holds column n's sum of the fp16 weights)
+    floatx4 accl[2];
 
     // The request's block-table entries live in one VGPR per wave, 64 at a
     // time (lane j holds the entry of logical block win + j); block ids are
@@ -394,6 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         for (int ct = 0; ct < 2; ++ct) {
             m[ct] = kNegInf;
             l[ct] = 0.f;
+            accl[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
             mthr[ct] = kNegInf;
             msub[ct] = F16 ? -kF16Lift : 0.f;
 #pragma unroll
@@ -487,7 +492,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                         const float mx = cm == kNegInf ? kNegInf : cm * sc;
                         const float m_new = fmaxf(m[ct], mx);
                         const float f = m_new == kNegInf ? 1.f : fast_exp2(m[ct] - m_new);
-                        l[ct] *= f;
+                        if constexpr (F16)
+                            accl[ct] *= f;
+                        else
+                            l[ct] *= f;
 #pragma unroll
                         for (int j = 0; j < D / 16; ++j) acc[ct][j] *= f;
                         m[ct] = m_new;
@@ -503,8 +511,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                         const float arg = fmaf(sr[i], sc, -msub[ct]);
                         pv[i] = fast_exp2(MASK && !vis[i] ? kNegInf : arg);
                     }
-                    const float sum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
-                                      ((pv[4] + pv[5]) + (pv[6] + pv[7]));
                     if constexpr (F16) {
                         // P rounded to fp16 (nearest even)
 #pragma unroll
@@ -531,8 +537,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                 uint32_t,
                                 __builtin_convertvector(f32x2{lo[2 * k], lo[2 * k + 1]}, bf16x2));
                         }
+                        l[ct] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
+                                 ((pv[4] + pv[5]) + (pv[6] + pv[7]));
                     }
-                    l[ct] += sum;
                 }
                 __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -549,6 +556,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                 as_bf16x8(vv[j]), as_bf16x8(pl[ct]), acc[ct][j], 0, 0, 0);
                         }
                     }
+                }
+                if constexpr (F16) {
+                    const uint32_t one2 = n == 0 ? 0x3c003c00u : 0u;  // fp16 1.0 pairs in row 0
+                    const u32x4 ones = {one2, one2, one2, one2};
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        accl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            as_f16x8(ones), as_f16x8(ph[ct]), accl[ct], 0, 0, 0);
                 }
                 __builtin_amdgcn_s_setprio(0);
             }
@@ -588,15 +603,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     };
     // fp16 walk first; a bf16 cache holding a V element beyond fp16's range
     // is walked again with the bf16 products (an E4M3 code always fits).
+    bool f16_walk = true;
     if (run(std::true_type{})) {
-        if constexpr (!FP8) run(std::false_type{});
+        if constexpr (!FP8) {
+            run(std::false_type{});
+            f16_walk = false;
+        }
     }
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     const float qnan = __builtin_nanf("");
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        const float lt = rows4_sum(l[ct]);
+        const float lt = f16_walk ? __shfl(accl[ct][0], n, 64) : rows4_sum(l[ct]);
         if (pos[ct] < 0) continue;
         const float inv = (FP8 ? p.v_scale : 1.f) / lt;  // an fp8 V scale enters here
         float *orow = p.out + qoff[ct];
