@@ -54,17 +54,29 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// Eight OCP E4M3 codes -> eight fp16 values, in order.  Exact: every E4M3
-// value (at most 448 in magnitude, four significant bits, no smaller than
-// 2^-9) is an fp16 value, and the fp32 -> fp16 rounding has nothing to round.
+// Eight OCP E4M3 codes (bytes of w, lowest first) -> eight fp16 or bf16
+// values, in order, two codes per v_cvt_scalef32_pk_* with scale 1.  Exact:
+// every E4M3 value (at most 448 in magnitude, four significant bits, no
+// smaller than 2^-9) is an fp16 and a bf16 value.
 __device__ __forceinline__ u32x4 e4m3x8_to_f16x8(u32x2 w) {
     u32x4 r;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);  // codes 4h, 4h+1
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);   // codes 4h+2, 4h+3
-        r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
-        r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2));
+        r[2 * h] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.f, false));
+        r[2 * h + 1] = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.f, true));
+    }
+    return r;
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8_pk(u32x2 w) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        r[2 * h] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, false));
+        r[2 * h + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, true));
     }
     return r;
 }
@@ -217,8 +229,8 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
         v_chunk<D, BS>(ps, tid, dim, chv);
         u32x4 kw, vw;
         if constexpr (FP8) {
-            kw = e4m3x8_to_bf16x8(st.k[ps]);
-            vw = F16 ? e4m3x8_to_f16x8(st.v[ps]) : e4m3x8_to_bf16x8(st.v[ps]);
+            kw = e4m3x8_to_bf16x8_pk(st.k[ps]);
+            vw = F16 ? e4m3x8_to_f16x8(st.v[ps]) : e4m3x8_to_bf16x8_pk(st.v[ps]);
         } else {
             kw = st.k[ps];
             vw = st.v[ps];
