@@ -189,8 +189,9 @@ pa_status pa_decode_ex(float *out, const void *q,
  * [0, num_blocks), gets NaN rows; nothing is read out of range.  bf16 only.
  * Precision: Q K^T in bf16 with fp32 accumulation; the softmax weights
  * enter P V rounded to fp16 (relative error 2^-11) against V converted to
- * fp16, exact for every V element below 2^16 in magnitude.  A workgroup
- * that meets a larger, infinite or NaN V element recomputes its rows with
+ * fp16, exact for every V element below 2^16 in magnitude.  A larger one
+ * turns the workgroup's fp32 sums non-finite; a workgroup whose sums end
+ * non-finite (that, or an infinite or NaN input) recomputes its rows with
  * the weights split into bf16 high and low parts (error near 2^-16). */
 pa_status pa_prefill_chunk(float *out, const void *q,
                            const void *k_cache, const void *v_cache,

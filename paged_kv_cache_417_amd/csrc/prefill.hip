@@ -208,19 +208,15 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
 // Registers -> LDS.  On the last step (TAIL) the V elements of keys at or
 // past nkeys are cleared here rather than right after their load, so the
 // loads of a step never wait before the previous step's math; they are
-// cleared before any conversion, so neither they nor their magnitude reach
-// LDS or vmax (+0 has the same bits in bf16 and fp16).  K is stored as
-// bf16 (an fp8 stage is widened exactly).  V is stored as bf16 or, when F16,
-// as fp16: E4M3 codes convert exactly, and bf16 elements convert exactly
-// below 2^16 in magnitude.  vmax collects what tells whether any did not:
-// the largest staged element's fp32 bits as a signed integer (vmax.x, the
-// largest positive one) and as an unsigned one (vmax.y, the negative one of
-// largest magnitude, if any).  Integer maxima order finite values,
-// infinities and NaNs alike, so no NaN can hide a large element.
+// cleared before any conversion, so no stale value reaches LDS (+0 has the
+// same bits in bf16 and fp16).  K is stored as bf16 (an fp8 stage is widened
+// exactly).  V is stored as bf16 or, when F16, as fp16: E4M3 codes convert
+// exactly, and bf16 elements convert exactly below 2^16 in magnitude; one at
+// or past it becomes an fp16 infinity, which the walk's end detects.
 template <int D, int BS, bool TAIL, bool FP8, bool F16>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                                             const Stage<D, BS, FP8> &st, int tid, int32_t t0,
-                                            int32_t nkeys, u32x2 &vmax) {
+                                            int32_t nkeys) {
 #pragma unroll
     for (int ps = 0; ps < Stage<D, BS, FP8>::kPasses; ++ps) {
         const int idx = ps * 256 + tid;
@@ -248,8 +244,6 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t lo = vw[w] << 16, hi = vw[w] & 0xffff0000u;
-                vmax.x = (uint32_t)max(max((int32_t)vmax.x, (int32_t)lo), (int32_t)hi);
-                vmax.y = max(max(vmax.y, lo), hi);
                 vw[w] = __builtin_bit_cast(
                     uint32_t, __builtin_convertvector(
                                   f32x2{__uint_as_float(lo), __uint_as_float(hi)}, f16x2));
@@ -418,7 +412,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         win = 0;
         tbl = lane < nblk ? table[lane] : 0;
-        u32x2 vmax = {0u, 0u};  // largest staged V bits (bf16 cache, F16 walk)
 
         // Two register stages: while step it computes from LDS, the loads of
         // step it + 2 are in flight and those of step it + 1 (issued one step
@@ -428,9 +421,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         stage(stA, 0);
         stage(stB, min(kTile, last_t0));  // a tile past the end re-reads the last one, unused
         if (kTile <= nkeys)
-            stage_store<D, BS, false, FP8, F16>(sm, 0, stA, tid, 0, nkeys, vmax);
+            stage_store<D, BS, false, FP8, F16>(sm, 0, stA, tid, 0, nkeys);
         else
-            stage_store<D, BS, true, FP8, F16>(sm, 0, stA, tid, 0, nkeys, vmax);
+            stage_store<D, BS, true, FP8, F16>(sm, 0, stA, tid, 0, nkeys);
         __syncthreads();
 
         // One 32-key step.  MASK: some column of the workgroup may sit before
@@ -581,11 +574,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             }
             if (more) {
                 if (t0 + 2 * kTile <= nkeys)
-                    stage_store<D, BS, false, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys,
-                                                        vmax);
+                    stage_store<D, BS, false, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
                 else
-                    stage_store<D, BS, true, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys,
-                                                       vmax);
+                    stage_store<D, BS, true, FP8, F16>(sm, buf ^ 1, cur, tid, t0 + kTile, nkeys);
             }
             __syncthreads();
         };
@@ -603,12 +594,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             if (it + 1 < ntiles) step(it + 1, std::true_type{}, stA, stB);
         }
         if constexpr (F16 && !FP8) {
-            // |V| >= 2^16 (fp32 bits 0x47800000, the first bf16 magnitude
-            // past 65504), an infinity, or a NaN (which would convert
-            // exactly: it only costs the second walk)
-            const bool over = (int32_t)vmax.x >= 0x47800000 ||
-                              (vmax.y & 0x7fffffffu) >= 0x47800000u;
-            return __syncthreads_or(over ? 1 : 0) != 0;
+            // A staged V element of magnitude 2^16 or more (the first bf16
+            // one past fp16's 65504) became an fp16 infinity.  Every staged
+            // key is in a step that some wave of the workgroup computes, and
+            // any fp16 weight times an infinity is an infinity or a NaN, so
+            // the element leaves a non-finite value in that wave's
+            // accumulators; rescaling and later sums keep it non-finite.
+            // With every element below 2^16 the sums stay far inside fp32's
+            // range (weights below 2^15 here), so a non-finite sum of a
+            // lane's accumulators means the fp16 walk was not exact (or V
+            // held an infinity or a NaN, which the second walk handles too).
+            float s = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j)
+                    s += (acc[ct][j][0] + acc[ct][j][1]) + (acc[ct][j][2] + acc[ct][j][3]);
+            return __syncthreads_or(__builtin_isfinite(s) ? 0 : 1) != 0;
         } else {
             return false;
         }
