@@ -161,7 +161,7 @@ def test_prefill_last_row_matches_decode(pa):
     assert diff <= TOL
 
 
-@pytest.mark.parametrize("mode", ["whole_pool", "one_element", "infinite"])
+@pytest.mark.parametrize("mode", ["whole_pool", "one_element", "last_key", "infinite"])
 def test_prefill_v_beyond_fp16_range(pa, mode):
     """V elements that fp16 cannot hold (beyond 65504, or infinite) send the
     workgroups that stage them through the bf16 high/low walk: the result
@@ -174,6 +174,11 @@ def test_prefill_v_beyond_fp16_range(pa, mode):
     big = 2.0 ** 20
     if mode == "whole_pool":
         case.v_pool.mul_(big)  # exact in bf16; every used V element is scaled
+    elif mode == "last_key":
+        # one element of request 0's last key (199): only its last row sees it,
+        # the other rows of that row's workgroup meet it with a zero weight
+        at = {"b": int(case.tables[0][199 // 16]), "h": 1, "r": 199 % 16, "d": 5}
+        case.v_pool[tuple(at[ax] for ax in case.v_axes)] = 3.0e5
     else:
         # one element of request 0's key 3 (seen by every row of request 0)
         at = {"b": int(case.tables[0][0]), "h": 1, "r": 3, "d": 5}  # kv head 1, dim 5
