@@ -95,8 +95,12 @@ constexpr float kF16Lift = 7.f;
 template <int D>
 struct PrefillSmem {
     uint16_t k[2][kTile][D + 8];   // K rows in MFMA row order, 16 B pad per row
-    uint16_t v[2][D][kTile + 8];   // V^T: one row of 32 keys per dim, 16 B pad
+    uint16_t v[2][D][kTile];       // V^T: one row of 32 keys per dim, chunks swizzled
 };
+
+// V^T row r keeps its four 16-byte chunks in the order c ^ v_swz(r), a
+// function of bits 1..3 of r alone
+__device__ __forceinline__ int v_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // LDS row of key kk (0..31) of a step: tile a's row n is key 8*(n/4) + n%4,
 // tile b's row n (stored at 16 + n) is that key + 4.
@@ -250,7 +254,7 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
             }
         }
         *reinterpret_cast<u32x4 *>(&sm.k[buf][k_row(kk)][ch * 8]) = kw;
-        *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][chv * 8]) = vw;
+        *reinterpret_cast<u32x4 *>(&sm.v[buf][dim][8 * (chv ^ v_swz(dim))]) = vw;
     }
 }
 
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 u32x4 vv[D / 16];
 #pragma unroll
                 for (int j = 0; j < D / 16; ++j)
-                    vv[j] = *reinterpret_cast<const u32x4 *>(&sm.v[buf][16 * j + n][8 * g]);
+                    vv[j] = *reinterpret_cast<const u32x4 *>(&sm.v[buf][16 * j + n][8 * (g ^ v_swz(n))]);
                 u32x4 ph[2], pl[2];
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
