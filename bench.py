@@ -884,11 +884,11 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     assert alloc.stats()["num_shared"] > 0
     ps = pa.pa_decode_default_partition(len(ids), sh.num_kv_heads, sh.block_size,
                                         int(lens.max()))
-    groups = pa.decode_groups(tables, lens, np.arange(len(ids)) // samples, sh.block_size, ps)
+    groups = pa.decode_groups(tables, lens, np.arange(len(ids)) // samples, sh.block_size)[:3]
     r = decode_row(pa, torch, case, reps, kv_reuse=True, groups=groups, max_group=samples)
     r["us_per_sequence"] = decode_row(pa, torch, case, reps, kv_reuse=True)["us"]
     r["us_streaming_policy"] = decode_row(pa, torch, case, reps)["us"]
-    r["shared_partitions_per_group"] = int(groups[2][0])
+    r["shared_partitions_per_group"] = int(groups[2][0]) * sh.block_size // ps
     # unique bytes: each physical block's valid rows once
     unique_tokens = 0
     seen = set()

@@ -189,10 +189,16 @@ pa_status pa_decode_ex(float *out, const void *q,
  * [0, num_blocks), gets NaN rows; nothing is read out of range.  bf16 only.
  * Precision: Q K^T in bf16 with fp32 accumulation; the softmax weights
  * enter P V rounded to fp16 (relative error 2^-11) against V converted to
- * fp16, exact for every V element below 2^16 in magnitude.  A larger one
- * turns the workgroup's fp32 sums non-finite; a workgroup whose sums end
- * non-finite (that, or an infinite or NaN input) recomputes its rows with
- * the weights split into bf16 high and low parts (error near 2^-16). */
+ * fp16, which is exact for a V element of magnitude in [2^-14, 2^16) and
+ * loses bits below 2^-24 for a smaller one (an absolute error under 3e-8
+ * per element).  A V element of 2^16 or more, infinite or NaN turns the
+ * workgroup's fp32 sums non-finite, and the workgroup recomputes its rows
+ * with V in bf16 and the weights split into bf16 high and low parts (error
+ * near 2^-16).
+ * Non-finite V: an output element (row, head, dim) is NaN exactly when a
+ * key its row sees (keys 0..p) holds an infinite or NaN V element in that
+ * dim; the definition gives an infinity or a NaN there.  No other output
+ * element is affected: a key past a row's position never reaches it. */
 pa_status pa_prefill_chunk(float *out, const void *q,
                            const void *k_cache, const void *v_cache,
                            const int32_t *block_tables,
@@ -218,11 +224,14 @@ pa_status pa_prefill_chunk(float *out, const void *q,
  *                  -1.  A sequence is in group g only if seq_group[s] == g
  *                  and s lies in g's run (and among its first
  *                  max_group_size members); otherwise it is decoded alone.
- *   group_shared   [num_groups] int32 device: leading partitions (of
- *                  partition_size tokens) whose block-table entries are the
- *                  same for every member.  Each member shares at most its
- *                  partition count - 1.  A member whose own entries differ
- *                  from the leader's over a shared partition gets a NaN row.
+ *   group_shared   [num_groups] int32 device: leading block-table entries
+ *                  (blocks) that every member holds equal to the leader's
+ *                  (pa_decode_groups derives them).  The library shares the
+ *                  whole partitions they cover at the partition size it runs
+ *                  with, so the count does not depend on partition_size;
+ *                  each member shares at most its partition count - 1.  A
+ *                  member whose own entries differ from the leader's over a
+ *                  shared partition gets a NaN row.
  *   num_groups     >= 0 (0: pa_decode_ex).
  *   max_group_size host bound of the group sizes (>= 1 when num_groups > 0).
  * dtype must be BF16 (the fp32 path has no grouped kernel: UNSUPPORTED).
@@ -242,6 +251,31 @@ pa_status pa_decode_grouped(float *out, const void *q,
                             int32_t max_group_size, void *workspace,
                             size_t workspace_bytes, pa_dtype dtype,
                             uint32_t flags, void *stream);
+
+/* Group arrays for pa_decode_grouped from host block tables ([VE] §3.1:
+ * sequences forked from one prompt hold its physical blocks).  Host memory
+ * only; nothing is enqueued.
+ *   block_tables   [num_seqs][block_table_stride] int32 host.
+ *   context_lens   [num_seqs] int32 host, >= 0.
+ *   seq_group      [num_seqs] int32 host: the caller's grouping, a group id
+ *                  in [0, num_groups) or -1 (decoded alone).  Each group's
+ *                  members are consecutive, and group ids first appear in
+ *                  increasing order from 0, each group non-empty.
+ *   group_offsets  [num_groups + 1] out: group g's run starts at
+ *                  group_offsets[g] (its first member, the leader) and ends
+ *                  where the next group's starts (the last at its last
+ *                  member + 1).
+ *   group_shared   [num_groups] out: the leading table entries every member
+ *                  holds equal to the leader's, counted over the blocks that
+ *                  every member's context fills completely.
+ *   max_group_size out: the largest member count (0 with no group).
+ * INVALID_ARG (nothing written) for a malformed grouping or a negative
+ * length. */
+pa_status pa_decode_groups(const int32_t *block_tables, int32_t block_table_stride,
+                           const int32_t *context_lens, const int32_t *seq_group,
+                           int32_t num_seqs, int32_t block_size, int32_t num_groups,
+                           int32_t *group_offsets, int32_t *group_shared,
+                           int32_t *max_group_size);
 
 /* ------------------------------------------------------------------------ */
 /* fp8 KV cache                                                               */
@@ -298,7 +332,9 @@ pa_status pa_decode_grouped_fp8(float *out, const void *q,
 
 /* pa_prefill_chunk over fp8 caches: q is bf16; K codes are widened to bf16
  * and V codes to fp16 exactly when staged, k_scale joins the softmax scale
- * and v_scale the output, in fp32.  Everything else as pa_prefill_chunk. */
+ * and v_scale the output, in fp32.  A V NaN code (S.1111.111) is treated as
+ * a non-finite V element is by pa_prefill_chunk.  Everything else as
+ * pa_prefill_chunk. */
 pa_status pa_prefill_chunk_fp8(float *out, const void *q, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,
                                int32_t block_table_stride, const int32_t *cu_q_lens,

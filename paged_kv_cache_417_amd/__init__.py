@@ -47,7 +47,7 @@ EXPORTED = (
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_is_swapped", "pa_swap_stats", "pa_swap_blocks",
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
-    "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8",
+    "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
 )
 
 
@@ -154,6 +154,7 @@ def _declare(lib):
         "pa_decode_grouped": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                    i32, i32, vp, vp, vp, i32, i32, vp, sz, ctypes.c_int,
                                    ctypes.c_uint32, vp]),
+        "pa_decode_groups": (st, [pi32, i32, pi32, pi32, i32, i32, i32, pi32, pi32, pi32]),
         "pa_decode_grouped_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, i32, i32, vp, vp, vp, i32, i32, vp, sz,
                                        ctypes.c_uint32, vp]),
@@ -303,32 +304,30 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         ctypes.c_void_p(_stream(stream))))
 
 
-def decode_groups(tables, lens, seq_group, block_size, partition_size):
-    """Host-side group arrays for pa_decode_grouped.  seq_group [S] (numpy) gives
-    each sequence's group id, or -1; ids run 0..G-1 in sequence order and each
-    group's members are consecutive.  A group shares the partitions covered by
-    the leading block-table entries every member has in common with the first
-    member, counting full blocks of every member's context only.  Returns int32
-    (group_offsets [G+1], seq_group [S], group_shared [G])."""
+def decode_groups(tables, lens, seq_group, block_size):
+    """Group arrays for pa_decode_grouped (pa_decode_groups on host arrays).
+    seq_group [S] gives each sequence's group id, or -1; ids run 0..G-1 in
+    sequence order and each group's members are consecutive.  Returns int32
+    numpy arrays (group_offsets [G+1], seq_group [S], group_shared [G]) and
+    the largest group size; group_shared counts the leading blocks every
+    member holds equal to the first member.  Raises ValueError for a
+    malformed grouping."""
     import numpy as np
-    seq_group = np.asarray(seq_group, dtype=np.int32)
-    G = int(seq_group.max()) + 1 if seq_group.size else 0
+    seq_group = np.ascontiguousarray(seq_group, dtype=np.int32)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    S = len(seq_group)
+    G = int(seq_group.max()) + 1 if S else 0
     offsets = np.zeros(G + 1, np.int32)
-    shared = np.zeros(G, np.int32)
-    for g in range(G):
-        members = np.flatnonzero(seq_group == g)
-        if members.size == 0 or members[-1] - members[0] + 1 != members.size:
-            raise ValueError(f"group {g}: members must be consecutive and non-empty")
-        if g > 0 and members[0] < offsets[g]:
-            raise ValueError("group ids must follow sequence order")
-        offsets[g] = members[0]
-        offsets[g + 1] = members[-1] + 1
-        full = int(min(int(lens[m]) for m in members)) // block_size
-        rows = np.asarray(tables)[members, :full]
-        same = (rows == rows[0]).all(axis=0)
-        common = int(np.argmin(same)) if not same.all() else full
-        shared[g] = common * block_size // partition_size
-    return offsets, seq_group, shared
+    shared = np.zeros(max(G, 1), np.int32)
+    largest = ctypes.c_int32(0)
+    st = _lib.pa_decode_groups(_i32p(tables), tables.shape[1] if tables.ndim == 2 else 1,
+                               _i32p(lens), _i32p(seq_group), S, int(block_size), G,
+                               _i32p(offsets), _i32p(shared), ctypes.byref(largest))
+    if st == PA_ERR_INVALID_ARG:
+        raise ValueError(_lib.pa_last_error().decode(errors="replace"))
+    _check(st)
+    return offsets, seq_group, shared[:G], largest.value
 
 
 def pa_decode_grouped_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,

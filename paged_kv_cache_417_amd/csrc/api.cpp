@@ -95,6 +95,8 @@ pa_status pa_cache_write(const void *k_new, const void *v_new, void *k_cache, vo
         return pa::fail(PA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
     int rc = pa::launch_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
                                     num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
+    if (rc == pa::kLaunchTooLarge)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many threads for one launch (%d)", fn, rc);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
 }
@@ -119,6 +121,8 @@ pa_status pa_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_d
     int rc = pa::launch_cache_write_fp8(k_new, v_new, in_dtype, k_cache, v_cache, slot_mapping,
                                         num_tokens, num_kv_heads, head_dim, block_size,
                                         num_blocks, k_scale, v_scale, stream);
+    if (rc == pa::kLaunchTooLarge)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many threads for one launch (%d)", fn, rc);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
 }
@@ -137,6 +141,8 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, i
         return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     int rc = pa::launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, num_kv_heads, head_dim,
                                     block_size, num_blocks, dtype, stream);
+    if (rc == pa::kLaunchTooLarge)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many threads for one launch (%d)", fn, rc);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
 }
@@ -168,6 +174,8 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_block
                                     const_cast<void *>(dv), dst_blocks,
                                     static_cast<const int32_t *>(pr), num_pairs, num_kv_heads,
                                     head_dim, block_size, dtype, stream);
+    if (rc == pa::kLaunchTooLarge)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many threads for one launch (%d)", fn, rc);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     return pa::ok();
 }

@@ -268,7 +268,7 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                                    : k_threads;
     const int64_t k_groups = (k_threads + 255) / 256;
     const int64_t groups = k_groups + (v_threads + 255) / 256;
-    if (groups > 0xffffffffLL / 256) return (int)hipErrorInvalidValue;
+    if (!grid_fits(groups * 256)) return kLaunchTooLarge;
     const dim3 grid((unsigned)groups);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 #define PA_LAUNCH(T, R)                                                                         \
@@ -291,6 +291,7 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int
     const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : dtype == PA_DTYPE_FP8_E4M3 ? 1 : 4;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem;
     const int64_t total = (int64_t)num_pairs * 2 * (block_bytes / 16);
+    if (!grid_fits(total)) return kLaunchTooLarge;
     const dim3 grid((unsigned)((total + 255) / 256));
     hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                        (char *)k_cache, (char *)v_cache, src_dst, num_pairs, block_bytes,
@@ -306,7 +307,7 @@ int launch_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks,
     const int64_t elem = dtype == PA_DTYPE_BF16 ? 2 : dtype == PA_DTYPE_FP8_E4M3 ? 1 : 4;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem;
     const int64_t total = (int64_t)num_pairs * 2 * (block_bytes / 16);
-    if ((total + 255) / 256 > 0xffffffffLL) return (int)hipErrorInvalidValue;
+    if (!grid_fits(total)) return kLaunchTooLarge;
     const dim3 grid((unsigned)((total + 255) / 256));
     hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                        (const char *)src_k, (const char *)src_v, (char *)dst_k, (char *)dst_v,
@@ -322,7 +323,7 @@ int launch_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dty
     if (num_tokens == 0) return 0;
     const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 16);
     const int64_t groups = (threads + 255) / 256;
-    if (groups > 0xffffffffLL) return (int)hipErrorInvalidValue;
+    if (!grid_fits(threads)) return kLaunchTooLarge;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (in_dtype == PA_DTYPE_BF16)
         hipLaunchKernelGGL(cache_write_fp8_kernel<__bf16>, dim3((unsigned)groups), dim3(256), 0, s,

@@ -208,17 +208,20 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
 }
 
 // Leading partitions of sequence s (np partitions in all) that its group
-// computes; 0 when s is in no group.  The per-sequence kernel and the group
-// kernel both decide membership with this one function, so every partition
-// is computed by exactly one of them.  The last partition is never shared,
-// so the merge always sees at least two partitions or none is shared.
+// computes; 0 when s is in no group.  The group's shared count is in blocks;
+// the partitions it covers wholly are shared.  The per-sequence kernel and
+// the group kernel both decide membership with this one function, so every
+// partition is computed by exactly one of them.  The last partition is never
+// shared, so the merge always sees at least two partitions or none is
+// shared.
 __device__ __forceinline__ int32_t shared_parts(const DecodeParams &p, int s, int32_t np) {
     if (!p.seq_group) return 0;
     const int32_t g = p.seq_group[s];
     if (g < 0 || g >= p.num_groups) return 0;
     const int32_t lo = p.grp_offsets[g], hi = p.grp_offsets[g + 1];
     if (lo < 0 || s < lo || s >= hi || s - lo >= p.grp_cover) return 0;
-    return max(0, min(p.grp_shared[g], np - 1));
+    const int64_t parts = (int64_t)p.grp_shared[g] * p.block_size / p.partition_size;
+    return (int32_t)max((int64_t)0, min(parts, (int64_t)np - 1));
 }
 
 // One per-sequence work item: (kv head, sequence, partition slot) of the

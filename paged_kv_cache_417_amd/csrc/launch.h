@@ -12,6 +12,13 @@
 
 namespace pa {
 
+// Launcher result for a call whose grid would not fit one launch (a 1-D
+// grid holds fewer than 2^32 threads); the C-ABI layer reports it as
+// PA_ERR_UNSUPPORTED.
+constexpr int kLaunchTooLarge = -2;
+// Whether `threads` threads fit a 1-D grid of 256-thread workgroups.
+inline bool grid_fits(int64_t threads) { return threads >= 0 && threads <= 0xffffffffLL - 255; }
+
 struct DecodeParams {
     float *out;
     const void *q;

@@ -20,8 +20,10 @@
 //   staging : the workgroup copies K [32 keys][D] and V^T [D][32 keys] of the
 //       step from the paged pools into LDS (double-buffered; the next step's
 //       global loads are in flight while the current step computes).  K rows
-//       are stored in MFMA row order and both tiles are padded by 16 bytes
-//       per row so the 16 lanes of a read phase hit distinct LDS banks.
+//       are stored in MFMA row order and padded by 16 bytes per row; V^T
+//       rows are unpadded with their 16-byte chunks XOR-swizzled by row, so
+//       that both the stage stores and the MFMA reads spread over the LDS
+//       banks.
 //   S^T = K Q^T : v_mfma_f32_16x16x32_bf16, A = K rows (tile a: keys
 //       8*(n/4) + n%4, tile b: those + 4), B = the wave's q columns; lane
 //       (g, n) ends with the scores of keys 8g .. 8g+7 of column n.
@@ -30,18 +32,24 @@
 //       running max is shared by the four lanes of a column.
 //   O^T += V^T P^T : v_mfma_f32_16x16x32_f16, A = V^T rows from LDS held as
 //       fp16, B = P rounded to fp16 (relative error 2^-11, one MFMA per
-//       tile).  V reaches LDS as fp16: a bf16 V element converts exactly
-//       when its magnitude is below 2^16 (the largest such bf16 value is
-//       65280; elements below 2^-14 may lose bits under 2^-24, an absolute
-//       error under 6e-8), and an E4M3 code always does.  The weights are
-//       lifted by 2^7 before rounding (they stay below 2^15) so that weights
-//       down to 2^-21 of the running maximum keep full fp16 precision.
-//   Exact fallback: while staging a bf16 V tile the workgroup tracks the
-//       largest V element.  If any staged element is 2^16 or more in
-//       magnitude, infinite or NaN, the workgroup discards its result and
-//       runs the whole walk again with V in bf16 and P as a bf16 high part
-//       plus a bf16 remainder (two MFMAs per tile, P's error near 2^-16), so
-//       every input gets a result of at least that accuracy.
+//       tile).  V reaches LDS as fp16: a bf16 V element of magnitude in
+//       [2^-14, 2^16) converts exactly; a smaller one lands in fp16's
+//       subnormal range and keeps its bits down to 2^-24 only (an absolute
+//       error under 2^-25, about 3e-8, per element); an E4M3 code always
+//       converts exactly.  The weights are lifted by 2^7 before rounding
+//       (they stay below 2^15) so that weights down to 2^-21 of the running
+//       maximum keep full fp16 precision.
+//   Exact fallback: a staged V element that fp16 cannot carry (a bf16
+//       element of 2^16 or more in magnitude, an infinity or a NaN, or an
+//       E4M3 NaN code) leaves a non-finite value in the accumulators of a
+//       wave of the workgroup, which the end of the walk detects.  The
+//       workgroup then discards its result and walks again with V in bf16
+//       and P as a bf16 high part plus a bf16 remainder (two MFMAs per tile,
+//       P's error near 2^-16).  In that walk non-finite V elements are staged
+//       as zeros, and an output element (row, head, dim) becomes NaN exactly
+//       when a key its row sees holds a non-finite V element in that dim: a
+//       key past a row's position never reaches the row, as in the
+//       definition.
 #include <type_traits>
 
 #include "device_common.h"
@@ -93,9 +101,13 @@ constexpr float kRescaleMargin = 8.f;  // log2 units; weights stay below 2^8
 constexpr float kF16Lift = 7.f;
 
 template <int D>
-struct PrefillSmem {
+struct __attribute__((aligned(16))) PrefillSmem {
     uint16_t k[2][kTile][D + 8];   // K rows in MFMA row order, 16 B pad per row
     uint16_t v[2][D][kTile];       // V^T: one row of 32 keys per dim, chunks swizzled
+    // Exact walk only: bit kk of nf[buf][dim] is set when key t0 + kk of the
+    // staged step holds a non-finite V element in that dimension (staged as
+    // zero).  Byte c is written by the thread that stages chunk c.
+    uint32_t nf[2][D];
 };
 
 // V^T row r keeps its four 16-byte chunks in the order c ^ v_swz(r), a
@@ -217,6 +229,9 @@ __device__ __forceinline__ void stage_load(Stage<D, BS, FP8> &st, const PrefillP
 // exactly).  V is stored as bf16 or, when F16, as fp16: E4M3 codes convert
 // exactly, and bf16 elements convert exactly below 2^16 in magnitude; one at
 // or past it becomes an fp16 infinity, which the walk's end detects.
+// In the exact walk (!F16) a non-finite V element (a bf16 infinity or NaN,
+// an E4M3 NaN code) is staged as zero and its key is marked in sm.nf, so
+// that the walk can send it only to the columns that see its key.
 template <int D, int BS, bool TAIL, bool FP8, bool F16>
 __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                                             const Stage<D, BS, FP8> &st, int tid, int32_t t0,
@@ -228,9 +243,25 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
         int dim, chv;
         v_chunk<D, BS>(ps, tid, dim, chv);
         u32x4 kw, vw;
+        uint32_t nfbits = 0;  // exact walk: element e of the chunk is non-finite
         if constexpr (FP8) {
             kw = e4m3x8_to_bf16x8_pk(st.k[ps]);
-            vw = F16 ? e4m3x8_to_f16x8(st.v[ps]) : e4m3x8_to_bf16x8_pk(st.v[ps]);
+            if constexpr (F16) {
+                vw = e4m3x8_to_f16x8(st.v[ps]);
+            } else {
+                // byte b is a NaN code when its low seven bits are all set:
+                // adding 1 to those bits then carries into bit 7 (no carry
+                // leaves the byte)
+                u32x2 c = st.v[ps];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t t = ((c[h] & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+                    c[h] &= ~((t >> 7) * 0xffu);  // NaN codes -> +0
+                    nfbits |= (((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) |
+                               ((t >> 28) & 8u)) << (4 * h);
+                }
+                vw = e4m3x8_to_bf16x8_pk(c);
+            }
         } else {
             kw = st.k[ps];
             vw = st.v[ps];
@@ -242,8 +273,23 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                 const uint32_t keep = (t + 2 * w < nkeys ? 0x0000ffffu : 0u) |
                                       (t + 2 * w + 1 < nkeys ? 0xffff0000u : 0u);
                 vw[w] &= keep;
+                if constexpr (!F16 && FP8)
+                    nfbits &= ~((t + 2 * w < nkeys ? 0u : 1u) << (2 * w) |
+                                (t + 2 * w + 1 < nkeys ? 0u : 2u) << (2 * w));
             }
         }
+        if constexpr (!F16 && !FP8) {
+            // bf16 infinities and NaNs (all exponent bits set) -> +0
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t e = vw[w] & 0x7f807f80u;
+                const bool lo_nf = (e & 0xffffu) == 0x7f80u, hi_nf = (e >> 16) == 0x7f80u;
+                vw[w] &= (lo_nf ? 0xffff0000u : 0xffffffffu) & (hi_nf ? 0x0000ffffu : 0xffffffffu);
+                nfbits |= (lo_nf ? 1u : 0u) << (2 * w) | (hi_nf ? 2u : 0u) << (2 * w);
+            }
+        }
+        if constexpr (!F16)
+            reinterpret_cast<uint8_t *>(&sm.nf[buf][dim])[chv] = (uint8_t)nfbits;
         if constexpr (F16 && !FP8) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -354,6 +400,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // one more product against a tile whose row 0 is all ones (row 0 of the
     // result, lane (0, n), holds column n's sum of the fp16 weights)
     floatx4 accl[2];
+    // Exact walk: bit 4j + i of nfl[ct] marks accumulator acc[ct][j][i] as
+    // reached by a non-finite V element of a visible key.
+    uint32_t nfl[2] = {0u, 0u};
 
     // The request's block-table entries live in one VGPR per wave, 64 at a
     // time (lane j holds the entry of logical block win + j); block ids are
@@ -411,6 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             accl[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
             mthr[ct] = kNegInf;
             msub[ct] = F16 ? -kF16Lift : 0.f;
+            nfl[ct] = 0u;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[ct][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
@@ -566,6 +616,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                         }
                     }
                 }
+                if constexpr (!F16) {
+                    // Non-finite V elements were staged as zeros.  Accumulator
+                    // (dim, column) is marked when one of them sits at a key the
+                    // column sees (keys t0 .. pos); marked outputs become NaN,
+                    // and no other column is touched by them.
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int32_t rel = pos[ct] - t0;
+                        const uint32_t vm = rel < 0 ? 0u : rel >= 31 ? ~0u : (2u << rel) - 1u;
+#pragma unroll
+                        for (int j = 0; j < D / 16; ++j) {
+                            const u32x4 nm =
+                                *reinterpret_cast<const u32x4 *>(&sm.nf[buf][16 * j + 4 * g]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                nfl[ct] |= (nm[i] & vm) != 0u ? 1u << (4 * j + i) : 0u;
+                        }
+                    }
+                }
                 if constexpr (F16) {
                     const uint32_t one2 = n == 0 ? 0x3c003c00u : 0u;  // fp16 1.0 pairs in row 0
                     const u32x4 ones = {one2, one2, one2, one2};
@@ -597,17 +666,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             step(it, std::true_type{}, stB, stA);
             if (it + 1 < ntiles) step(it + 1, std::true_type{}, stA, stB);
         }
-        if constexpr (F16 && !FP8) {
-            // A staged V element of magnitude 2^16 or more (the first bf16
-            // one past fp16's 65504) became an fp16 infinity.  Every staged
-            // key is in a step that some wave of the workgroup computes, and
-            // any fp16 weight times an infinity is an infinity or a NaN, so
-            // the element leaves a non-finite value in that wave's
-            // accumulators; rescaling and later sums keep it non-finite.
-            // With every element below 2^16 the sums stay far inside fp32's
-            // range (weights below 2^15 here), so a non-finite sum of a
-            // lane's accumulators means the fp16 walk was not exact (or V
-            // held an infinity or a NaN, which the second walk handles too).
+        if constexpr (F16) {
+            // A staged bf16 V element of magnitude 2^16 or more (the first
+            // one past fp16's 65504) became an fp16 infinity; an infinite or
+            // NaN bf16 element or an E4M3 NaN code is staged as it is.  Every
+            // staged key is in a step that some wave of the workgroup
+            // computes, and any fp16 weight, zero included, times an infinity
+            // or a NaN is an infinity or a NaN, so such an element leaves a
+            // non-finite value in that wave's accumulators whether or not
+            // the wave's columns see its key (a masked key's zero weight
+            // gives 0 * inf = NaN); rescaling and later sums keep it
+            // non-finite.  With every element finite and below 2^16 the sums
+            // stay far inside fp32's range (weights below 2^15 here), so a
+            // non-finite sum of a lane's accumulators means the fp16 walk's
+            // result cannot be kept.
             float s = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
@@ -619,14 +691,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             return false;
         }
     };
-    // fp16 walk first; a bf16 cache holding a V element beyond fp16's range
-    // is walked again with the bf16 products (an E4M3 code always fits).
+    // fp16 walk first.  A workgroup that staged a V element the fp16 walk
+    // cannot carry exactly (beyond fp16's range, or not finite) walks again
+    // with the exact products and non-finite elements kept to the columns
+    // that see them.
     bool f16_walk = true;
     if (run(std::true_type{})) {
-        if constexpr (!FP8) {
-            run(std::false_type{});
-            f16_walk = false;
-        }
+        run(std::false_type{});
+        f16_walk = false;
     }
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
@@ -640,6 +712,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
             floatx4 o = acc[ct][j] * inv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((nfl[ct] >> (4 * j + i)) & 1u) o[i] = qnan;
             if (any_bad) o = floatx4{qnan, qnan, qnan, qnan};
             *reinterpret_cast<floatx4 *>(orow + 16 * j + 4 * g) = o;
         }

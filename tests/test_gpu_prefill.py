@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import workloads as wl
-from paged_helpers import gather_blocks, host_bits, oracle_decode_rows
+from paged_helpers import (chunked_checksum, gather_blocks, host_bits, oracle_decode_all,
+                           oracle_prefill_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +52,7 @@ def run_prefill(pa, case, cu=None, ctx=None, max_q_len=None, max_ctx=None):
     return out
 
 
-def oracle_prefill_all(case):
+def oracle_prefill_case(case):
     rows = list(range(len(case.context_lens)))
     k_sub, v_sub, t_sub, l_sub = gather_blocks(case.k_pool, case.v_pool, case.tables,
                                                case.context_lens, rows, case.shape.block_size)
@@ -59,24 +60,8 @@ def oracle_prefill_all(case):
                           case.shape.scale, case.k_axes, case.v_axes)
 
 
-def oracle_prefill_rows(case, picks):
-    """Oracle output for selected (request, row) pairs: each is the 1-row
-    chunk at its absolute position p over keys 0..p."""
-    sh = case.shape
-    out = {}
-    for r, i in picks:
-        p = int(case.context_lens[r] - case.q_lens[r] + i)
-        k_sub, v_sub, t_sub, _ = gather_blocks(case.k_pool, case.v_pool, case.tables[[r]],
-                                               [p + 1], [0], sh.block_size)
-        qrow = host_bits(case.q[int(case.cu_q_lens[r]) + i:int(case.cu_q_lens[r]) + i + 1])
-        out[(r, i)] = oracle.prefill(qrow, k_sub, v_sub, t_sub, np.array([0, 1], np.int32),
-                                     np.array([p + 1], np.int32), sh.scale, case.k_axes,
-                                     case.v_axes)[0]
-    return out
-
-
 def check_all(case, out):
-    ref = oracle_prefill_all(case)
+    ref = oracle_prefill_case(case)
     got = out.double().cpu().numpy()
     assert np.isfinite(got).all()
     err = float(np.abs(got - ref).max()) if ref.size else 0.0
@@ -161,55 +146,99 @@ def test_prefill_last_row_matches_decode(pa):
     assert diff <= TOL
 
 
-@pytest.mark.parametrize("mode", ["whole_pool", "one_element", "last_key", "infinite"])
+def check_nonfinite(ref, got):
+    """Non-finite V elements: the device output is non-finite exactly where
+    the definition's is (NaN standing for an infinity is allowed), and
+    within the bar, relative to max(1, |ref|), everywhere else."""
+    nf = ~np.isfinite(ref)
+    assert np.array_equal(nf, ~np.isfinite(got)), (
+        f"non-finite mismatch: {int((nf != ~np.isfinite(got)).sum())} elements")
+    fin = ~nf
+    rel = float((np.abs(got[fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))).max())
+    return int(nf.sum()), rel
+
+
+@pytest.mark.parametrize("mode", ["whole_pool", "one_element", "last_key", "infinite",
+                                  "inf_last_key", "nan_in_chunk"])
 def test_prefill_v_beyond_fp16_range(pa, mode):
-    """V elements that fp16 cannot hold (beyond 65504, or infinite) send the
-    workgroups that stage them through the bf16 high/low walk: the result
-    keeps its accuracy relative to the size of V instead of overflowing."""
+    """V elements that fp16 cannot hold (beyond 65504, infinite or NaN) send
+    the workgroups that stage them through the bf16 high/low walk: the
+    result keeps its accuracy relative to the size of V instead of
+    overflowing, and a non-finite element reaches exactly the rows that see
+    its key (the other rows of the same workgroup meet it with a zero
+    weight and must stay finite)."""
     ctx, ql = [200, 70, 33], [40, 70, 33]
     sh = wl.PrefillShape(num_reqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
                          block_size=16, seed=404)
     say(f"case prefill V beyond fp16 range ({mode})")
     case = wl.make_prefill_case(sh, "cuda", pa.K_AXES, pa.V_AXES, context_lens=ctx, q_lens=ql)
     big = 2.0 ** 20
+
+    def put(key, value, head=1, dim=5):
+        # request 0's key `key`: rows at positions >= key see it (the chunk
+        # holds positions 160..199, 32 per workgroup from 160)
+        at = {"b": int(case.tables[0][key // 16]), "h": head, "r": key % 16, "d": dim}
+        case.v_pool[tuple(at[ax] for ax in case.v_axes)] = value
+
     if mode == "whole_pool":
         case.v_pool.mul_(big)  # exact in bf16; every used V element is scaled
+    elif mode == "one_element":
+        put(3, 3.0e5)          # seen by every row of request 0
     elif mode == "last_key":
-        # one element of request 0's last key (199): only its last row sees it,
-        # the other rows of that row's workgroup meet it with a zero weight
-        at = {"b": int(case.tables[0][199 // 16]), "h": 1, "r": 199 % 16, "d": 5}
-        case.v_pool[tuple(at[ax] for ax in case.v_axes)] = 3.0e5
-    else:
-        # one element of request 0's key 3 (seen by every row of request 0)
-        at = {"b": int(case.tables[0][0]), "h": 1, "r": 3, "d": 5}  # kv head 1, dim 5
-        case.v_pool[tuple(at[ax] for ax in case.v_axes)] = (
-            float("inf") if mode == "infinite" else 3.0e5)
+        put(199, 3.0e5)        # seen by the last row only
+    elif mode == "infinite":
+        put(3, float("inf"))
+    elif mode == "inf_last_key":
+        put(199, float("inf"))
+    else:  # a NaN inside the chunk: rows 20..39 see it, rows 0..19 do not
+        put(180, float("nan"))
+        put(185, float("-inf"), head=0, dim=77)
     out = run_prefill(pa, case)
-    ref = oracle_prefill_all(case)
+    ref = oracle_prefill_case(case)
     got = out.double().cpu().numpy()
-    if mode == "infinite":
-        # every row of request 0 weighs the infinite element: dim 5 of the
-        # query heads of kv head 1 is +inf exactly (the device may give NaN
-        # there, where a zero weight part meets the infinity); nothing else
-        # is touched
-        hmask = np.zeros(got.shape, bool)
-        hmask[:40, 4:8, 5] = True
-        assert np.isposinf(ref[hmask]).all() and not np.isfinite(got[hmask]).any()
-        fin = ~hmask
-        err = float(np.abs(got[fin] - ref[fin]).max())
-        say(f"  max err outside the infinite column {err:.3e}")
-        assert err <= TOL
-        return
-    assert np.isfinite(got).all()
     if mode == "whole_pool":
         # the same problem with V scaled by 2^20: the error scales with V
+        assert np.isfinite(got).all()
         err = float(np.abs(got - ref).max()) / big
         say(f"  max err / 2^20 {err:.3e}")
         assert err <= TOL
         return
-    rel = float((np.abs(got - ref) / np.maximum(1.0, np.abs(ref))).max())
-    say(f"  max err relative to max(1, |ref|) {rel:.3e}")
+    n_nf, rel = check_nonfinite(ref, got)
+    say(f"  {n_nf} non-finite outputs where the oracle's are; elsewhere max err relative "
+        f"to max(1, |ref|) {rel:.3e}")
+    want_nf = {"one_element": 0, "last_key": 0, "infinite": 40 * 4, "inf_last_key": 4,
+               "nan_in_chunk": 20 * 4 + 15 * 4}[mode]
+    assert n_nf == want_nf
     assert rel <= TOL
+
+
+def test_prefill_fp8_nan_code_reaches_only_rows_that_see_it(pa):
+    """An E4M3 NaN code (0x7F) in V inside a chunk: only the rows at or past
+    its key get NaN in that (head, dim); the rest of the workgroup stays
+    within the bar."""
+    sh = wl.PrefillShape(num_reqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=32, dtype="fp8", seed=405)
+    say("case fp8 prefill with a V NaN code")
+    case = wl.make_prefill_case(sh, "cuda", pa.K_AXES, pa.V_AXES, context_lens=[300, 64],
+                                q_lens=[64, 64])
+    key = 270  # request 0's chunk holds positions 236..299
+    at = {"b": int(case.tables[0][key // 32]), "h": 0, "r": key % 32, "d": 9}
+    case.v_pool[tuple(at[ax] for ax in case.v_axes)] = 0x7F
+    dev = "cuda"
+    sc = wl.FP8_SCALE
+    out = torch.full((128, 8, 128), 7.0, device=dev)
+    pa.pa_prefill_chunk_fp8(out, case.q, case.k_pool, case.v_pool,
+                            torch.as_tensor(case.tables, device=dev),
+                            torch.as_tensor(case.cu_q_lens, device=dev),
+                            torch.as_tensor(case.context_lens, device=dev), sh.scale, sc, sc, 64,
+                            300)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host_bits(case.q), host_bits(case.k_pool), host_bits(case.v_pool),
+                         case.tables, case.cu_q_lens, case.context_lens, sh.scale, pa.K_AXES,
+                         pa.V_AXES, sc, sc)
+    n_nf, rel = check_nonfinite(ref, out.double().cpu().numpy())
+    say(f"  {n_nf} NaN outputs (rows {300 - key} x 4 heads); elsewhere max err {rel:.3e}")
+    assert n_nf == (300 - key) * 4 and rel <= TOL
 
 
 def test_prefill_determinism_and_permutation(pa):
@@ -252,21 +281,35 @@ def test_prefill_bad_inputs(pa):
     assert torch.isnan(out2[20:30]).all() and torch.isfinite(out2[:20]).all()
 
 
-def test_prefill_full_size_mixed_chunks(pa):
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_full_size_mixed_chunks(pa, kv):
     """Four 512-row chunks over 4096 cached tokens (block 128, 32 q / 8 kv
-    heads, head_dim 128): sampled rows against the oracle."""
-    sh = wl.MIXED_PREFILL
-    say("case prefill full size 4 x 512 over 4096")
+    heads, head_dim 128), on a bf16 and on an fp8 cache: every row of every
+    head against the fp64 oracle (one task per 32 rows on the host
+    threads)."""
+    sh = wl.MIXED_PREFILL if kv == "bf16" else wl.PrefillShape(dtype="fp8")
+    say(f"case prefill full size 4 x 512 over 4096 ({kv} cache)")
     case = wl.make_prefill_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
-    out = run_prefill(pa, case)
+    dev = "cuda"
+    sc = 1.0
+    if kv == "fp8":
+        # the codes hold N(0,1) draws divided by the cache scale
+        sc = wl.FP8_SCALE
+        out = torch.full((case.q.shape[0], sh.num_q_heads, sh.head_dim), 7.0, device=dev)
+        pa.pa_prefill_chunk_fp8(out, case.q, case.k_pool, case.v_pool,
+                                torch.as_tensor(case.tables, device=dev),
+                                torch.as_tensor(case.cu_q_lens, device=dev),
+                                torch.as_tensor(case.context_lens, device=dev), sh.scale, sc, sc,
+                                512, int(case.context_lens.max()))
+        torch.cuda.synchronize()
+    else:
+        out = run_prefill(pa, case)
     assert torch.isfinite(out).all()
-    picks = [(0, 0), (0, 511), (1, 1), (1, 255), (2, 128), (2, 383), (3, 31), (3, 510)]
-    ref = oracle_prefill_rows(case, picks)
-    err = 0.0
-    for (r, i), want in ref.items():
-        got = out[int(case.cu_q_lens[r]) + i].double().cpu().numpy()
-        err = max(err, float(np.abs(got - want).max()))
-    say(f"  sampled rows max err {err:.3e}")
+    ref = oracle_prefill_all(case.q, case.k_pool, case.v_pool, case.tables, case.cu_q_lens,
+                             case.context_lens, sh.block_size, sh.scale, case.k_axes,
+                             case.v_axes, sc, sc)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    say(f"  all {case.q.shape[0]} rows x {sh.num_q_heads} heads max err {err:.3e}")
     assert err <= TOL
 
 
@@ -275,8 +318,9 @@ def test_mixed_step_end_to_end(pa):
     (block 128, partitions of 512) and 4 prompt chunks of 512 new tokens over
     4096 cached; the allocator assigns every slot, one pa_cache_write stores
     all 8 + 2048 new K/V rows, then pa_decode and pa_prefill_chunk run on one
-    stream.  Sampled rows of both are checked against the oracle; the step
-    with the prefill on a second stream gives the same bits."""
+    stream.  The write is checked bit for bit, every row of both outputs
+    against the oracle; the step with the prefill on a second stream gives
+    the same bits."""
     dev = "cuda"
     dsh, psh = wl.MIXED_DECODE, wl.MIXED_PREFILL
     hkv, d, bs = dsh.num_kv_heads, dsh.head_dim, dsh.block_size
@@ -306,7 +350,27 @@ def test_mixed_step_end_to_end(pa):
     assert len(slots) == 8 + 2048 and len(pairs) == 0
     kn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
     vn = wl.randn((len(slots), hkv, d), torch.bfloat16, gen, dev)
+    # the step's cache write, bit for bit: the touched blocks against the
+    # oracle's write into a host copy of them, and every other byte of both
+    # pools unchanged (position-weighted checksums)
+    touched = np.unique(slots // bs)
+    tb = torch.as_tensor(touched, device=dev)
+    k_sub, v_sub = host_bits(k_pool[tb]).copy(), host_bits(v_pool[tb]).copy()
+    remap = {int(b): i for i, b in enumerate(touched)}
+    sub_slots = np.array([remap[int(x) // bs] * bs + int(x) % bs for x in slots], np.int64)
+    oracle.cache_write(host_bits(kn), host_bits(vn), k_sub, v_sub, sub_slots, pa.K_AXES,
+                       pa.V_AXES)
+    k_old, v_old = k_pool[tb].clone(), v_pool[tb].clone()
+    sums = (chunked_checksum(k_pool), chunked_checksum(v_pool))
     pa.pa_cache_write(kn, vn, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    torch.cuda.synchronize()
+    assert (host_bits(k_pool[tb]) == k_sub).all() and (host_bits(v_pool[tb]) == v_sub).all()
+    k_new_b, v_new_b = k_pool[tb].clone(), v_pool[tb].clone()
+    k_pool[tb], v_pool[tb] = k_old, v_old
+    assert (chunked_checksum(k_pool), chunked_checksum(v_pool)) == sums
+    k_pool[tb], v_pool[tb] = k_new_b, v_new_b
+    del k_old, v_old, k_new_b, v_new_b
+    say(f"  cache write of {len(slots)} tokens into {len(touched)} blocks bit-exact")
     dt, dl = alloc.batch_tables(dec_ids, 257)
     pt, pl = alloc.batch_tables(pre_ids, 40)
     assert list(dl) == [32768] * 8 and list(pl) == [4608] * 4
@@ -323,17 +387,13 @@ def test_mixed_step_end_to_end(pa):
                         psh.scale, 512, 4608)
     torch.cuda.synchronize()
     assert torch.isfinite(out_d).all() and torch.isfinite(out_p).all()
-    err_d = 0.0
-    for s in (0, 5):
-        ref = oracle_decode_rows(qd, k_pool, v_pool, dt, dl, [s], bs, dsh.scale, pa.K_AXES,
-                                 pa.V_AXES)
-        err_d = max(err_d, float(np.abs(out_d[s].double().cpu().numpy() - ref[0]).max()))
-    case = wl.PrefillCase(psh, pl, np.full(4, 512, np.int32), cu, None, pt, qp, k_pool, v_pool,
-                          pa.K_AXES, pa.V_AXES)
-    ref = oracle_prefill_rows(case, [(0, 0), (1, 300), (3, 511)])
-    err_p = max(float(np.abs(out_p[int(cu[r]) + i].double().cpu().numpy() - want).max())
-                for (r, i), want in ref.items())
-    say(f"  decode err {err_d:.3e} prefill err {err_p:.3e}")
+    # every decode row and every prefill row against the oracle
+    ref_d = oracle_decode_all(qd, k_pool, v_pool, dt, dl, bs, dsh.scale, pa.K_AXES, pa.V_AXES)
+    err_d = float(np.abs(out_d.double().cpu().numpy() - ref_d).max())
+    ref_p = oracle_prefill_all(qp, k_pool, v_pool, pt, cu, pl, bs, psh.scale, pa.K_AXES,
+                               pa.V_AXES)
+    err_p = float(np.abs(out_p.double().cpu().numpy() - ref_p).max())
+    say(f"  decode err {err_d:.3e} (8 rows), prefill err {err_p:.3e} (2048 rows)")
     assert err_d <= TOL and err_p <= TOL
 
     # the same step with the decode and the prefill on two created streams

@@ -6,7 +6,7 @@ filled and shared, so every sample but the last holder copies it first
 
 Checks: the copies and writes are bit-exact and leave the shared source
 intact; decode over shared tables is bit-identical to decode over private
-duplicates of the same content; sampled rows match the fp64 oracle within
+duplicates of the same content; every row matches the fp64 oracle within
 2e-3; forking exactly at a block boundary needs no copy.
 """
 import sys
@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads as wl
-from paged_helpers import host_bits, oracle_decode_rows
+from paged_helpers import host_bits, oracle_decode_all
 
 pytestmark = pytest.mark.gpu
 
@@ -137,15 +137,12 @@ def test_prefix_shared_sampling(pa):
     assert torch.equal(out_shared, out_dup)
     say(f"  shared == duplicated bit for bit over {S} sequences, {len(copy_pairs)} blocks")
 
-    # oracle on sampled sequences: first and last sample of a few prompts,
-    # the longest and the shortest tail
-    rows = sorted({0, samples - 1, 5 * samples, 5 * samples + samples - 1, S - 1,
-                   int(np.argmax(lens)), int(np.argmin(lens))})
-    ref = oracle_decode_rows(q, k_pool, v_pool, tables, lens, rows, sh.block_size, sh.scale,
-                             pa.K_AXES, pa.V_AXES)
-    got = out_shared[torch.as_tensor(rows, device=dev)].double().cpu().numpy()
-    err = float(np.abs(got - ref).max())
-    say(f"  rows {rows} max err {err:.3e}")
+    # every sequence against the fp64 oracle (the shared blocks are copied
+    # to the host once)
+    ref = oracle_decode_all(q, k_pool, v_pool, tables, lens, sh.block_size, sh.scale,
+                            pa.K_AXES, pa.V_AXES)
+    err = float(np.abs(out_shared.double().cpu().numpy() - ref).max())
+    say(f"  all {S} rows max err {err:.3e}")
     assert err <= TOL
 
 
@@ -224,7 +221,7 @@ def test_prefix_cache_hits_decode_like_fresh_prompts(pa):
     K/V rows are a function of (system prompt, position) inside the system
     prompt, so reuse is exact.  Decode over the cached tables must equal, bit
     for bit, decode over the same prompts written in full into private blocks
-    by an allocator without the cache; sampled rows match the fp64 oracle."""
+    by an allocator without the cache; every row matches the fp64 oracle."""
     sh = wl.DecodeShape("prefix_cache", 12, 8, 4, 64, 16, 1024, "bf16", 77)
     dev = "cuda"
     plan = wl.chat_plan(num_system=4, requests=12, system_len=300, max_user=200)
@@ -298,11 +295,9 @@ def test_prefix_cache_hits_decode_like_fresh_prompts(pa):
     torch.cuda.synchronize()
     assert torch.isfinite(out_c).all()
     assert torch.equal(out_c, out_f)
-    sample = [0, 3, S - 1]
-    ref = oracle_decode_rows(q, kc, vc, tc, lc, sample, bs, sh.scale, pa.K_AXES, pa.V_AXES)
-    got = out_c[torch.as_tensor(sample, device=dev)].double().cpu().numpy()
-    err = float(np.abs(got - ref).max())
-    say(f"  cached == fresh bit for bit over {S} requests; oracle rows {sample} err {err:.3e}")
+    ref = oracle_decode_all(q, kc, vc, tc, lc, bs, sh.scale, pa.K_AXES, pa.V_AXES)
+    err = float(np.abs(out_c.double().cpu().numpy() - ref).max())
+    say(f"  cached == fresh bit for bit over {S} requests; oracle, all rows, err {err:.3e}")
     assert err <= TOL
 
 
@@ -341,20 +336,20 @@ def test_grouped_decode_matches_per_sequence(pa):
     tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
     maxlen = int(lens.max())
     ps = pa.pa_decode_default_partition(S, sh.num_kv_heads, sh.block_size, maxlen)
-    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, sh.block_size, ps)
-    assert list(groups[2]) == [2048 // ps] * n_prompts
+    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, sh.block_size)[:3]
+    # the 128 full prompt blocks are common; block 128 was copied on write
+    assert list(groups[2]) == [2048 // sh.block_size] * n_prompts
     gen = wl.make_generator(sh.seed + 9, dev)
     q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     say(f"case grouped decode: {n_prompts} groups of {samples}, ps {ps}")
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups, ps, samples)
     assert torch.isfinite(ref).all()
     assert torch.equal(got, ref)
-    # and against the fp64 oracle on sampled members of several groups
-    rows = [0, 3, samples - 1, 7 * samples + 2, S - 1]
-    want = oracle_decode_rows(q, k_pool, v_pool, tables, lens, rows, sh.block_size, sh.scale,
-                              pa.K_AXES, pa.V_AXES)
-    err = float(np.abs(got[torch.as_tensor(rows, device=dev)].double().cpu().numpy() - want).max())
-    say(f"  grouped rows {rows} max err {err:.3e}")
+    # and every member of every group against the fp64 oracle
+    want = oracle_decode_all(q, k_pool, v_pool, tables, lens, sh.block_size, sh.scale,
+                             pa.K_AXES, pa.V_AXES)
+    err = float(np.abs(got.double().cpu().numpy() - want).max())
+    say(f"  grouped: all {S} rows max err {err:.3e}")
     assert err <= TOL
 
     # member 3 of group 0 points one shared-partition entry at another block
@@ -382,16 +377,17 @@ def test_grouped_decode_chunks_caps_and_loners(pa):
     tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
     ps = 64
     seq_group = np.array([0] * 6 + [1] * 6 + [-1] * 6, np.int32)
-    off, sg, shd = pa.decode_groups(tables, lens, seq_group, sh.block_size, ps)
-    assert list(shd) == [300 // 16 * 16 // ps] * 2
+    off, sg, shd, _ = pa.decode_groups(tables, lens, seq_group, sh.block_size)
+    assert list(shd) == [300 // 16] * 2  # the prompt's full blocks
     gen = wl.make_generator(sh.seed + 1, dev)
     q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     say("case grouped decode: GQA chunks, loners")
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), ps, 6)
     assert torch.isfinite(ref).all() and torch.equal(got, ref)
 
-    # group 1 claims 100 shared partitions: capped per member at its own
-    # count - 1; past the prompt the members' tables differ from the leader's
+    # group 1 claims 100 shared blocks (25 partitions of 64): capped per
+    # member at its own count - 1; past the prompt the members' tables differ
+    # from the leader's
     shd_big = shd.copy()
     shd_big[1] = 100
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd_big), ps, 6)
@@ -399,7 +395,7 @@ def test_grouped_decode_chunks_caps_and_loners(pa):
     assert torch.equal(got[6], ref[6])  # the leader reads its own table
     for s in range(7, 12):
         np_s = -(-int(lens[s]) // ps)
-        if np_s - 1 > shd[1]:  # a shared partition past the common prefix
+        if np_s - 1 > int(shd[1]) * sh.block_size // ps:  # one past the common prefix
             assert torch.isnan(got[s]).all(), s
         else:
             assert torch.equal(got[s], ref[s]), s
@@ -428,8 +424,8 @@ def test_grouped_decode_fp8_matches_per_sequence(pa):
     k8 = (k_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
     v8 = (v_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
     ps = 64
-    off, sg, shd = pa.decode_groups(tables, lens, np.arange(S) // 4, sh.block_size, ps)
-    assert (shd == 3).all()  # 200 tokens: 12 common full blocks = 3 partitions of 64
+    off, sg, shd, _ = pa.decode_groups(tables, lens, np.arange(S) // 4, sh.block_size)
+    assert (shd == 12).all()  # 200 tokens: 12 common full blocks = 3 partitions of 64
     gen = wl.make_generator(sh.seed + 2, dev)
     q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     maxlen = int(lens.max())

@@ -4,7 +4,7 @@ recompute) and paged_kv_cache_417_amd.driver.ServingLoop carries the plans
 out with the device calls.  Every K/V row is a function of (request,
 position), so after any step each running request's cache can be un-paged
 and compared with the rows it must hold, bit for bit; decode and prefill
-outputs are compared with the fp64 oracle on sampled steps."""
+outputs are compared with the fp64 oracle, every row, on every ninth step."""
 import sys
 
 import numpy as np
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as wl
-from paged_helpers import gather_blocks, host_bits, oracle_decode_rows
+from paged_helpers import gather_blocks, host_bits, oracle_decode_all, oracle_prefill_all
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,7 @@ def test_serving_loop_end_to_end(pa, fp8):
         return torch.cat([qrows(rid, pos) for rid, pos in entries])
 
     rng = np.random.default_rng(11)
-    n_req, added, checked, oracle_checks = 30, 0, 0, 0
+    n_req, added, checked, oracle_checks, prefill_checks = 30, 0, 0, 0, 0
     for step in range(4000):
         if added < n_req and step % 3 == 0:
             for _ in range(2):
@@ -92,25 +92,44 @@ def test_serving_loop_end_to_end(pa, fp8):
                     assert np.array_equal(v[j][:, :, :n], vw[j * bs:j * bs + n].transpose(1, 2, 0))
                 checked += 1
         live = [i for i, (rid, _) in enumerate(plan["decode"]) if rid not in fin]
+        ks = (wl.FP8_SCALE, wl.FP8_SCALE) if fp8 else (1.0, 1.0)
         if live and step % 9 == 0:
+            # every decode row of the step against the oracle
             ids = [plan["decode"][i][0] for i in live]
             t, lens = loop.alloc.batch_tables(ids, loop.stride, loop.pad)
             q = torch.cat([qrows(rid, np.array([c - 1])) for rid, c in
                            (plan["decode"][i] for i in live)])
-            sample = list(range(min(3, len(ids))))
-            ks = (wl.FP8_SCALE, wl.FP8_SCALE) if fp8 else (1.0, 1.0)
-            ref = oracle_decode_rows(q, loop.k, loop.v, t, lens, sample, bs, loop.scale,
-                                     pa.K_AXES, pa.V_AXES, *ks)
-            got = dec[torch.as_tensor(live[:len(sample)], device=dev)]
+            ref = oracle_decode_all(q, loop.k, loop.v, t, lens, bs, loop.scale, pa.K_AXES,
+                                    pa.V_AXES, *ks)
+            got = dec[torch.as_tensor(live, device=dev)]
             err = float(np.abs(got.double().cpu().numpy() - ref).max())
             assert err <= TOL
             oracle_checks += 1
+        chunks = [(i, c) for i, c in enumerate(plan["prefill"]) if c[0] not in fin]
+        if chunks and step % 9 == 0:
+            # every row of the step's prompt chunks against the oracle: chunk
+            # (rid, start, n) holds positions start .. start+n-1 over keys
+            # 0 .. start+n-1
+            ids = [c[0] for _, c in chunks]
+            t, _ = loop.alloc.batch_tables(ids, loop.stride, loop.pad)
+            qlens = np.array([c[2] for _, c in chunks], np.int32)
+            ctx = np.array([c[1] + c[2] for _, c in chunks], np.int32)
+            cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+            q = torch.cat([qrows(rid, np.arange(st, st + n)) for _, (rid, st, n) in chunks])
+            ref = oracle_prefill_all(q, loop.k, loop.v, t, cu, ctx, bs, loop.scale, pa.K_AXES,
+                                     pa.V_AXES, *ks)
+            all_cu = np.concatenate([[0], np.cumsum([c[2] for c in plan["prefill"]])])
+            rows_at = np.concatenate([np.arange(all_cu[i], all_cu[i + 1]) for i, _ in chunks])
+            got = pre[torch.as_tensor(rows_at, device=dev)]
+            err = float(np.abs(got.double().cpu().numpy() - ref).max())
+            assert err <= TOL
+            prefill_checks += 1
         if added == n_req and loop.sched.stats()["finished"] == n_req:
             break
     st = loop.sched.stats()
     say(f"case serving loop (fp8 {fp8}): {step + 1} steps, stats {st}, {checked} cache checks, "
-        f"{oracle_checks} oracle checks")
+        f"{oracle_checks} decode and {prefill_checks} prefill oracle checks")
     assert st["finished"] == n_req
     assert st["swap_preemptions"] > 0
     assert loop.alloc.stats()["num_free"] == 72
-    assert checked > 0 and oracle_checks > 0
+    assert checked > 0 and oracle_checks > 0 and prefill_checks > 0
