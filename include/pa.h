@@ -172,6 +172,30 @@ pa_status pa_decode_ex(float *out, const void *q,
                        size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
                        void *stream);
 
+/* Bytes of the device scratch pa_decode_noalloc keeps per GPU. */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pa_decode_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops or
+ * harnesses that forbid allocation).  The split-K partials go to a device
+ * array of PA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from load until the process ends; the call allocates
+ * nothing.  A batch whose partials need more (pa_decode_workspace_size) is
+ * UNSUPPORTED, and nothing is enqueued.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, or
+ * different host threads without ordering) race on it and must be ordered
+ * by the caller.  Nothing in it needs clearing between calls.  Arguments,
+ * flags, results and errors otherwise as pa_decode_ex. */
+pa_status pa_decode_noalloc(float *out, const void *q,
+                            const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, int32_t block_table_stride,
+                            const int32_t *context_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float scale, int32_t max_context_len,
+                            int32_t partition_size, pa_dtype dtype, uint32_t flags,
+                            void *stream);
+
 /* Chunked prefill: one iteration may carry new prompt chunks beside decode
  * rows ([VI] §1, continuous batching mixes requests in different phases).
  * Request r owns query rows cu_q_lens[r] .. cu_q_lens[r+1]-1; its context

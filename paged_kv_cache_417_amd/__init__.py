@@ -29,6 +29,7 @@ PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_DTYPE_FP8_E4M3 = 2  # OCP E4M3 codes, stored in torch.uint8 tensors
 PA_DECODE_KV_REUSE = 1
+PA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the device scratch behind pa_decode_noalloc
 
 # Axis order of the two pools, in the letters b (block), h (kv head),
 # r (row = token within block), d (head dim).
@@ -48,6 +49,7 @@ EXPORTED = (
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
+    "pa_decode_noalloc",
 )
 
 
@@ -154,6 +156,8 @@ def _declare(lib):
         "pa_decode_grouped": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                    i32, i32, vp, vp, vp, i32, i32, vp, sz, ctypes.c_int,
                                    ctypes.c_uint32, vp]),
+        "pa_decode_noalloc": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                   f32, i32, i32, ctypes.c_int, ctypes.c_uint32, vp]),
         "pa_decode_groups": (st, [pi32, i32, pi32, pi32, i32, i32, i32, pi32, pi32, pi32]),
         "pa_decode_grouped_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, i32, i32, vp, vp, vp, i32, i32, vp, sz,
@@ -284,6 +288,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _check(_lib.pa_decode_ex(*args, PA_DECODE_KV_REUSE, ctypes.c_void_p(_stream(stream))))
     else:
         _check(_lib.pa_decode(*args, ctypes.c_void_p(_stream(stream))))
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size=0, stream=None, kv_reuse=False) -> None:
+    """pa_decode without a workspace: the split-K partials use the scratch
+    the library keeps on the device (for callers that cannot allocate)."""
+    nb, hkv, bs, d = _geometry(k_cache)
+    s, hq, _ = q.shape
+    _check(_lib.pa_decode_noalloc(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                  block_tables.shape[1], _p(context_lens), s, hq, hkv, d, bs, nb,
+                                  float(scale), int(max_context_len), int(partition_size),
+                                  _dtype_code(k_cache), PA_DECODE_KV_REUSE if kv_reuse else 0,
+                                  ctypes.c_void_p(_stream(stream))))
 
 
 def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale,
