@@ -46,7 +46,7 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mha_7b_traffic.json")
 DECODE_KERNEL = "decode_mfma_kernel"
-KERNEL_SOURCES = ("decode_mfma.hip", "device_common.h", "launch.h")
+KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip", "device_common.h", "launch.h")
 CALIB_PAIRS = 4096
 HOST_WARM = 4  # untimed steps before the host-inclusive loop's timed ones
 
@@ -162,7 +162,8 @@ def oracle_decode_sample(case, budget_s: float, tables=None, lengths=None, scale
 
 def host_threads() -> int:
     """Worker threads for the all-core oracle run: the cores this process may
-    use, at most 16 (a one-GPU share of the host)."""
+    use, at most 16 (one GPU's share of the host: the box gives a one-GPU job
+    16 CPUs whatever nproc shows; `host_cpus` in the result is nproc)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -203,7 +204,9 @@ def cpu_baseline(case, budget_s: float):
     reps, tokens_all, el_all = oracle_decode_parallel(case, budget_s / 4, threads)
     done, tokens, elapsed = oracle_decode_sample(case, budget_s)
     S = len(case.lengths)
-    return {"value": reps * S / el_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": reps * S / el_all, "unit": "tokens/s", "cores": threads,
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
             "sample": f"the whole batch ({S} sequences, {tokens_all // reps} context tokens, all "
                       f"{sh.num_q_heads} heads) {reps} times, one sequence per task on "
                       f"{threads} threads, fp64, {el_all:.1f} s",
@@ -535,14 +538,21 @@ def cpu_copy_row(pairs, hkv, d, bs, budget_s):
 
 
 def headline(args, pa, wl, torch, np):
+    """The 7B-shaped decode step, over R replicas of the batch (the same
+    lengths in disjoint blocks of the pool, R = args.replicas): step i
+    appends one token to every sequence of replica i mod R and decodes that
+    replica, so each call reads K/V that the previous R - 1 calls did not
+    touch (R x 2.2 GB between two reads of a block, against a 256 MB MALL)."""
     dev = "cuda"
     sh = wl.MHA_7B
     K, W = args.steps, args.warmup
+    R = max(1, args.replicas)
     nsteps = K + W
-    log(f"bench: building {sh.name} batch (S={sh.num_seqs}, NB={sh.num_blocks})")
+    log(f"bench: building {sh.name} batch (S={sh.num_seqs} x {R} replicas, NB={sh.num_blocks})")
     host_steps = min(K, 20)
-    case = wl.make_decode_case(sh, dev, pa.K_AXES, pa.V_AXES,
-                               extra_table_slots=nsteps + host_steps + HOST_WARM + 1)
+    grow = -(-(nsteps + host_steps + HOST_WARM) // R) + 1  # tokens a replica gains at most
+    case = wl.make_decode_case(sh, dev, pa.K_AXES, pa.V_AXES, extra_table_slots=grow,
+                               replicas=R)
     S = sh.num_seqs
     stride = case.tables.shape[1]
     pad = sh.num_blocks - 1
@@ -550,12 +560,13 @@ def headline(args, pa, wl, torch, np):
     # The allocator replays the prompts: with free_order = the batch's
     # permutation it hands out exactly the blocks the batch was laid into.
     alloc = pa.Allocator(sh.num_blocks, sh.block_size, free_order=case.perm)
-    ids = np.arange(S, dtype=np.int64)
+    ids = np.arange(S * R, dtype=np.int64)
     for s in ids:
         alloc.create(int(s))
     alloc.batch_append(ids, case.lengths)
     t_chk, l_chk = alloc.batch_tables(ids, stride, pad)
     assert (t_chk == case.tables).all() and (l_chk == case.lengths).all()
+    rep_ids = [ids[r * S:(r + 1) * S] for r in range(R)]
 
     # Every step's slots, tables and lengths, ahead of time (host cost timed).
     ones = np.ones(S, dtype=np.int32)
@@ -564,8 +575,8 @@ def headline(args, pa, wl, torch, np):
     h_lens = np.zeros((nsteps, S), dtype=np.int32)
     t0 = time.perf_counter()
     for i in range(nsteps):
-        alloc.batch_append(ids, ones, slots_out=h_slots[i])
-        alloc.batch_tables(ids, stride, pad, tables_out=h_tabs[i], lens_out=h_lens[i])
+        alloc.batch_append(rep_ids[i % R], ones, slots_out=h_slots[i])
+        alloc.batch_tables(rep_ids[i % R], stride, pad, tables_out=h_tabs[i], lens_out=h_lens[i])
     alloc_us = (time.perf_counter() - t0) * 1e6 / nsteps
     d_slots = torch.as_tensor(h_slots, device=dev)
     d_tabs = torch.as_tensor(h_tabs, device=dev)
@@ -582,29 +593,37 @@ def headline(args, pa, wl, torch, np):
                              max_len, ps, dev)
     ps_used = ps or pa.pa_decode_default_partition(S, sh.num_kv_heads, sh.block_size, max_len)
     stream = torch.cuda.current_stream()
-    dec_events = []
+    # event pairs made before the loop; Python's garbage collector is off
+    # while it runs (a collector pass between an event and its launch would
+    # sit inside the event's interval)
+    dec_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)]
 
     def step(i, timed):
         pa.pa_cache_write(k_new[i], v_new[i], case.k_pool, case.v_pool, d_slots[i])
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            dec_events[i - W][0].record(stream)
         pa.pa_decode(out, q_all[i], case.k_pool, case.v_pool, d_tabs[i], d_lens[i], sh.scale,
                      max_len, ps, ws)
         if timed:
-            e1.record(stream)
-            dec_events.append((e0, e1))
+            dec_events[i - W][1].record(stream)
 
     log(f"bench: warmup {W} steps, partition {ps_used}")
     for i in range(W):
         step(i, False)
     torch.cuda.synchronize()
     log(f"bench: timing {K} steps")
-    t0 = time.perf_counter()
-    for i in range(W, nsteps):
-        step(i, True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    gc_on = gc.isenabled()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for i in range(W, nsteps):
+            step(i, True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        if gc_on:
+            gc.enable()
     ms_step = (t1 - t0) * 1e3 / K
     dec_ms = [a.elapsed_time(b) for a, b in dec_events]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
@@ -612,16 +631,17 @@ def headline(args, pa, wl, torch, np):
                                  sh.block_size) for i in range(W, nsteps)) / K
     achieved = bytes_avg / (dec_avg_ms * 1e-3) / 1e9
     assert torch.isfinite(out).all()
+    log("bench: decode us per step: " + " ".join(f"{x * 1e3:.0f}" for x in dec_ms))
     log(f"bench: step {ms_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us "
         f"(min {min(dec_ms) * 1e3:.1f}, max {max(dec_ms) * 1e3:.1f}), "
         f"{achieved:.0f} GB/s algorithmic, allocator {alloc_us:.1f} us/step on the host")
 
     # The same step with the host allocator and PCIe uploads inside the loop
     # (pinned staging, double-buffered); reported, never `value`.
-    host_max = max_len + host_steps + HOST_WARM
+    host_max = max_len + grow
     host_ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
                                   host_max, ps, dev)
-    host_rate = host_inclusive_rate(pa, wl, torch, np, case, alloc, ids, stride, pad, k_new,
+    host_rate = host_inclusive_rate(pa, wl, torch, np, case, alloc, rep_ids, stride, pad, k_new,
                                     v_new, q_all, out, host_ws, ps, host_max, host_steps)
 
     if args.calibrate:
@@ -629,23 +649,28 @@ def headline(args, pa, wl, torch, np):
     copy_ref = copy_reference(pa, torch, np, case, alloc, args.reps)
 
     res = {
-        "S": S, "ms_step": ms_step, "dec_avg_ms": dec_avg_ms, "dec_ms": dec_ms,
+        "S": S, "replicas": R, "ms_step": ms_step, "dec_avg_ms": dec_avg_ms, "dec_ms": dec_ms,
         "bytes_avg": bytes_avg, "achieved": achieved, "ps": ps_used,
-        "seq_len": float(h_lens[-1].mean()), "alloc_us": alloc_us, "host_rate": host_rate,
+        "seq_len": float(h_lens[W:].mean()), "alloc_us": alloc_us, "host_rate": host_rate,
         "copy_ref": copy_ref,
     }
-    return case, res
+    # the first replica as a batch of its own, for the CPU baseline
+    first = wl.DecodeCase(sh, case.lengths[:S].copy(), case.perm, case.tables[:S].copy(),
+                          case.q[:S], case.k_pool, case.v_pool, case.k_axes, case.v_axes)
+    return first, res
 
 
-def host_inclusive_rate(pa, wl, torch, np, case, alloc, ids, stride, pad, k_new, v_new, q_all,
-                        out, ws, ps, max_len, steps):
+def host_inclusive_rate(pa, wl, torch, np, case, alloc, rep_ids, stride, pad, k_new, v_new,
+                        q_all, out, ws, ps, max_len, steps):
     """Decode steps with the host allocator and the uploads of slots, tables
-    and lengths inside the loop (pinned staging, double-buffered).  HOST_WARM
-    untimed steps come first, and Python's garbage collector is off during
-    the timed ones: one collector pass (tens of ms) inside 20 steps of
-    ~0.4 ms would otherwise set the figure."""
+    and lengths inside the loop (pinned staging, double-buffered), rotating
+    over the replicas like the timed loop.  HOST_WARM untimed steps come
+    first, and Python's garbage collector is off during the timed ones: one
+    collector pass (tens of ms) inside 20 steps of ~0.4 ms would otherwise
+    set the figure."""
     sh = case.shape
-    S = len(ids)
+    S = len(rep_ids[0])
+    R = len(rep_ids)
     dev = "cuda"
     h_slots = [torch.zeros(S, dtype=torch.int64).pin_memory() for _ in range(2)]
     h_tabs = [torch.zeros((S, stride), dtype=torch.int32).pin_memory() for _ in range(2)]
@@ -667,6 +692,7 @@ def host_inclusive_rate(pa, wl, torch, np, case, alloc, ids, stride, pad, k_new,
             b = i % 2
             if copied[b] is not None:
                 copied[b].synchronize()
+            ids = rep_ids[i % R]
             alloc.batch_append(ids, ones, slots_out=h_slots[b].numpy())
             alloc.batch_tables(ids, stride, pad, tables_out=h_tabs[b].numpy(),
                                lens_out=h_lens[b].numpy())
@@ -732,12 +758,17 @@ def copy_reference(pa, torch, np, case, alloc, reps):
 # the other rows of the path, each on its own workload
 
 
+ROTATE = 4  # disjoint copies of a decode batch visited in turn by the timed calls
+
+
 def row_gqa(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.GQA
-    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
-    r = decode_row(pa, torch, case, reps)
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES, replicas=ROTATE)
+    r = decode_row(pa, torch, case, reps, replicas=ROTATE)
     if cpu_budget > 0:
-        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
+        S = sh.num_seqs
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, tables=case.tables[:S],
+                                         lengths=case.lengths[:S])
     r["workload"] = ("gqa decode: 128 seqs, ctx round(lognormal(ln 1024, 1)) clipped "
                      "[16, 8192], 32 q / 8 kv heads, head_dim 128, block 16, bf16")
     return r
@@ -747,59 +778,62 @@ def row_fp8(pa, wl, torch, np, reps, cpu_budget):
     """The 7B-shaped decode batch (same lengths, tables and pool size) with an
     fp8 (OCP E4M3) K/V cache, one scale per cache: half the K/V bytes."""
     sh = wl.DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "fp8", wl.MHA_7B.seed)
-    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
-    dev = "cuda"
-    lens = case.lengths
-    S, maxlen = len(lens), int(max(lens))
-    t_dev = torch.as_tensor(case.tables, device=dev)
-    l_dev = torch.as_tensor(lens, device=dev)
-    out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
-    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                             maxlen, 0, dev)
-    stream = torch.cuda.current_stream()
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES, replicas=ROTATE)
 
-    def call():
-        pa.pa_decode_fp8(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale,
-                         wl.FP8_SCALE, wl.FP8_SCALE, maxlen, 0, ws)
+    def dec(out, q, k, v, t, l, maxlen, ps, ws):
+        pa.pa_decode_fp8(out, q, k, v, t, l, sh.scale, wl.FP8_SCALE, wl.FP8_SCALE, maxlen, ps,
+                         ws)
 
-    for _ in range(3):
-        call()
-    med, all_ms = events_time(torch, call, reps, stream)
-    b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, e_kv=1)
-    gbps = b / (med * 1e-3) / 1e9
-    r = {"us": med * 1e3, **spread(all_ms), "algorithmic_bytes": b, "GBps": gbps,
-         "frac_of_8TBps": gbps * 1e9 / 8e12, "tokens_per_s": S / (med * 1e-3), "bound": "hbm",
-         "workload": "7B-shaped decode with fp8 (E4M3) K/V: 64 seqs, ctx U[128,4096], 32/32 "
-                     "heads, head_dim 128, block 16, 200000-block pool, one scale per cache"}
+    r = decode_row(pa, torch, case, reps, replicas=ROTATE, decode=dec)
+    r["workload"] = ("7B-shaped decode with fp8 (E4M3) K/V: 64 seqs, ctx U[128,4096], 32/32 "
+                     "heads, head_dim 128, block 16, 200000-block pool, one scale per cache")
     if cpu_budget > 0:
-        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, scales=(wl.FP8_SCALE, wl.FP8_SCALE))
+        S = sh.num_seqs
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, tables=case.tables[:S],
+                                         lengths=case.lengths[:S],
+                                         scales=(wl.FP8_SCALE, wl.FP8_SCALE))
     return r
 
 
 def row_long(pa, wl, torch, np, reps, cpu_budget):
+    """8 x 32768 tokens at block 128: the library's default partitions (the
+    row's figure) and the 512-token partitions the long-context workload
+    names, beside it.  Four copies need 8192 blocks, so the pool holds 8320."""
     sh = wl.MIXED_DECODE
-    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
-    ps = pa.pa_decode_default_partition(len(case.lengths), sh.num_kv_heads, sh.block_size,
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES, replicas=ROTATE,
+                               num_blocks=ROTATE * 2048 + 128)
+    S = sh.num_seqs
+    ps = pa.pa_decode_default_partition(S, sh.num_kv_heads, sh.block_size,
                                         int(case.lengths.max()))
-    r = decode_row(pa, torch, case, reps, ps=sh.partition_size)
+    r = decode_row(pa, torch, case, reps, ps=sh.partition_size, replicas=ROTATE)
+    r512 = decode_row(pa, torch, case, reps, ps=512, replicas=ROTATE)
+    r["at_512_token_partitions"] = {k: r512[k] for k in ("us", "p10_us", "p90_us", "GBps",
+                                                         "frac_of_8TBps")}
     if cpu_budget > 0:
-        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
+        r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, tables=case.tables[:S],
+                                         lengths=case.lengths[:S])
     r["workload"] = ("long-context split-K decode: 8 seqs x 32768 tokens, block 128, "
-                     f"partitions of {ps} (library default), 32 q / 8 kv heads, head_dim 128, "
-                     "bf16")
+                     f"partitions of {ps} (library default; 512 beside it), 32 q / 8 kv heads, "
+                     "head_dim 128, bf16")
     return r
 
 
 def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=False,
-               groups=None, max_group=0):
+               groups=None, max_group=0, replicas=1, decode=None):
+    """Event-timed decode calls on one workload.  With replicas > 1 the case
+    holds that many copies of the batch in disjoint blocks (sequences r*S ..
+    r*S+S-1) and call k decodes copy k mod replicas, so no call re-reads
+    what the previous ones read.  decode: the call to time (pa.pa_decode by
+    default), given (out, q, k_pool, v_pool, tables, lens, maxlen, ps, ws)."""
     sh = case.shape
     dev = "cuda"
     lens = case.lengths if lengths is None else lengths
     tabs = case.tables if tables is None else tables
-    S = len(lens)
+    S = len(lens) // replicas
     maxlen = int(max(lens))
-    t_dev = torch.as_tensor(tabs, device=dev)
-    l_dev = torch.as_tensor(lens, device=dev)
+    t_dev = [torch.as_tensor(tabs[r * S:(r + 1) * S], device=dev) for r in range(replicas)]
+    l_dev = [torch.as_tensor(lens[r * S:(r + 1) * S], device=dev) for r in range(replicas)]
+    q_rep = [case.q[r * S:(r + 1) * S] for r in range(replicas)]
     out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
     ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
                              maxlen, ps, dev)
@@ -807,29 +841,43 @@ def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=
 
     if groups is not None:
         g_dev = [torch.as_tensor(a, device=dev) for a in groups]
+    k = [0]
 
     def call():
-        if groups is None:
-            pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen,
-                         ps, ws, kv_reuse=kv_reuse)
+        r = k[0] % replicas
+        k[0] += 1
+        if decode is not None:
+            decode(out, q_rep[r], case.k_pool, case.v_pool, t_dev[r], l_dev[r], maxlen, ps, ws)
+        elif groups is None:
+            pa.pa_decode(out, q_rep[r], case.k_pool, case.v_pool, t_dev[r], l_dev[r], sh.scale,
+                         maxlen, ps, ws, kv_reuse=kv_reuse)
         else:
-            pa.pa_decode_grouped(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale,
-                                 maxlen, g_dev[0], g_dev[1], g_dev[2], max_group, ps, ws,
-                                 kv_reuse=kv_reuse)
+            pa.pa_decode_grouped(out, q_rep[r], case.k_pool, case.v_pool, t_dev[r], l_dev[r],
+                                 sh.scale, maxlen, g_dev[0], g_dev[1], g_dev[2], max_group, ps,
+                                 ws, kv_reuse=kv_reuse)
 
-    for _ in range(3):
+    for _ in range(max(3, replicas)):
         call()
     med, all_ms = events_time(torch, call, reps, stream)
-    b = decode_bytes(lens, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size)
+    e_kv = 1 if case.k_pool.dtype == torch.uint8 else 2
+    b = decode_bytes(lens[:S], sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                     e_kv=e_kv)
     gbps = b / (med * 1e-3) / 1e9
-    return {"us": med * 1e3, **spread(all_ms), "algorithmic_bytes": b, "GBps": gbps,
-            "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "tokens_per_s": S / (med * 1e-3),
-            "bound": "hbm"}
+    r = {"us": med * 1e3, **spread(all_ms), "algorithmic_bytes": b, "GBps": gbps,
+         "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "tokens_per_s": S / (med * 1e-3),
+         "bound": "hbm"}
+    if replicas > 1:
+        r["rotation"] = (f"{replicas} copies of the batch in disjoint blocks, visited in turn "
+                         f"({replicas * b / 1e9:.2f} GB between two reads of a block)")
+    return r
 
 
-def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
-    """16 prompts x 8 samples sharing the prompt's blocks; 112 copy-on-writes
-    of the partial shared block before the tails are written."""
+def prefix_shared_batch(pa, wl, torch, np, before_tails=None):
+    """The prefix-shared batch: 16 prompts of 2048 + j tokens, each forked
+    into 8 samples; the samples' first appends copy the shared partial block
+    (112 copies), then their tails are written.  before_tails(k_pool,
+    v_pool, pairs_on_device) runs between the copies and the tail writes.
+    Returns (case, alloc, pairs, append_us, samples)."""
     sh = wl.PREFIX_SHARED
     dev = "cuda"
     plan = wl.prefix_plan()
@@ -860,14 +908,9 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     slots, pairs = alloc.batch_append(ids, plan.tail_lens.reshape(-1))
     append_us = (time.perf_counter() - t0) * 1e6
     d_pairs = torch.as_tensor(pairs, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def copy():
-        pa.pa_copy_blocks(k_pool, v_pool, d_pairs)
-
-    copy_med, _ = events_time(torch, copy, reps, stream)  # idempotent: sources are unchanged
-    block_bytes = sh.num_kv_heads * sh.block_size * sh.head_dim * 2
-    copy_bytes = len(pairs) * 2 * block_bytes * 2  # K and V regions, read + write
+    pa.pa_copy_blocks(k_pool, v_pool, d_pairs)
+    if before_tails is not None:
+        before_tails(k_pool, v_pool, d_pairs)
     shape = (len(slots), sh.num_kv_heads, sh.head_dim)
     pa.pa_cache_write(wl.randn(shape, torch.bfloat16, gen, dev),
                       wl.randn(shape, torch.bfloat16, gen, dev), k_pool, v_pool,
@@ -876,6 +919,27 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
     q = wl.randn((len(ids), sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     case = wl.DecodeCase(sh, lens, order, tables, q, k_pool, v_pool, pa.K_AXES, pa.V_AXES)
+    return case, alloc, pairs, append_us, samples
+
+
+def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
+    """16 prompts x 8 samples sharing the prompt's blocks; 112 copy-on-writes
+    of the partial shared block before the tails are written."""
+    sh = wl.PREFIX_SHARED
+    stream = torch.cuda.current_stream()
+    copy_ms = []
+
+    def time_copy(k_pool, v_pool, d_pairs):
+        def copy():
+            pa.pa_copy_blocks(k_pool, v_pool, d_pairs)
+        # idempotent before the tails are written: the sources are unchanged
+        copy_ms.append(events_time(torch, copy, reps, stream)[0])
+
+    case, alloc, pairs, append_us, samples = prefix_shared_batch(pa, wl, torch, np, time_copy)
+    copy_med = copy_ms[0]
+    block_bytes = sh.num_kv_heads * sh.block_size * sh.head_dim * 2
+    copy_bytes = len(pairs) * 2 * block_bytes * 2  # K and V regions, read + write
+    tables, lens, ids = case.tables, case.lengths, range(len(case.lengths))
     # The allocator reports shared blocks: the batch is decoded with the
     # samples of each prompt as one group (pa_decode_grouped: the shared
     # partitions are read once per group) and the cache-keeping load policy.
@@ -904,6 +968,11 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     r["unique_bytes"] = kv_unique + other
     r["GBps_unique"] = r["unique_bytes"] / (r["us"] * 1e-6) / 1e9
     r["frac_unique_of_8TBps"] = r["GBps_unique"] / PEAK_HBM_GBPS
+    # logical bytes count every sharer's read of a shared block: a rate, not
+    # a fraction of the HBM peak
+    r["GBps_logical"] = r.pop("GBps")
+    r.pop("frac_of_8TBps")
+    r["logical_bytes"] = r.pop("algorithmic_bytes")
     r["workload"] = ("prefix-shared decode: 16 prompts of 2048+j tokens x 8 samples sharing "
                      "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16; us: "
                      "pa_decode_grouped (one group per prompt), us_per_sequence: pa_decode_ex "
@@ -1204,6 +1273,187 @@ def prefill_counter_summary(dirs):
     return "\n".join(lines)
 
 
+DECODE_PHASES = ("7B-shaped decode (rotated)", "gqa decode (rotated)", "fp8 decode (rotated)",
+                 "long-context decode, default partitions (rotated)",
+                 "long-context decode, 512-token partitions (rotated)",
+                 "prefix-shared grouped decode", "calibration copy")
+
+
+def decode_only(pa, wl, torch, np, reps, out_json):
+    """Every decode workload alone, for the counter runs: `reps` pa_decode
+    calls per workload (four disjoint copies of each batch visited in turn,
+    except the prefix-shared one), each workload after a spin-kernel marker,
+    then the calibration copy.  Writes each phase's algorithmic bytes per
+    call to out_json."""
+    dev = "cuda"
+    phases = []
+
+    def run(name, case, ps=0, replicas=ROTATE, **kw):
+        mark_phase(torch)
+        r = decode_row(pa, torch, case, reps, ps=ps, replicas=replicas, **kw)
+        phases.append({"phase": name, "algorithmic_bytes": r.get("algorithmic_bytes",
+                                                                 r.get("unique_bytes")),
+                       "us": r["us"], "calls": reps + max(3, replicas)})
+        log(f"bench: {name}: {r['us']:.1f} us")
+        return r
+
+    run(DECODE_PHASES[0], wl.make_decode_case(wl.MHA_7B, dev, pa.K_AXES, pa.V_AXES,
+                                              replicas=ROTATE))
+    torch.cuda.empty_cache()
+    run(DECODE_PHASES[1], wl.make_decode_case(wl.GQA, dev, pa.K_AXES, pa.V_AXES,
+                                              replicas=ROTATE))
+    torch.cuda.empty_cache()
+    sh8 = wl.DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "fp8", wl.MHA_7B.seed)
+
+    def dec8(out, q, k, v, t, l, maxlen, ps, ws):
+        pa.pa_decode_fp8(out, q, k, v, t, l, sh8.scale, wl.FP8_SCALE, wl.FP8_SCALE, maxlen, ps,
+                         ws)
+
+    run(DECODE_PHASES[2], wl.make_decode_case(sh8, dev, pa.K_AXES, pa.V_AXES, replicas=ROTATE),
+        decode=dec8)
+    torch.cuda.empty_cache()
+    long_case = wl.make_decode_case(wl.MIXED_DECODE, dev, pa.K_AXES, pa.V_AXES, replicas=ROTATE,
+                                    num_blocks=ROTATE * 2048 + 128)
+    run(DECODE_PHASES[3], long_case)
+    run(DECODE_PHASES[4], long_case, ps=512)
+    del long_case
+    torch.cuda.empty_cache()
+    # the batch's set-up kernels (cache writes, copy-on-write copies) run
+    # before the next marker: the summary counts only decode kernels there
+    case, alloc, _, _, samples = prefix_shared_batch(pa, wl, torch, np)
+    groups = pa.decode_groups(case.tables, case.lengths, np.arange(len(case.lengths)) // samples,
+                              wl.PREFIX_SHARED.block_size)[:3]
+    r = run(DECODE_PHASES[5], case, replicas=1, kv_reuse=True, groups=groups, max_group=samples)
+    phases[-1]["algorithmic_bytes"] = None  # unique bytes: see the bench row
+    mark_phase(torch)
+    calibrate_copy(pa, torch, np, case, alloc)
+    phases.append({"phase": DECODE_PHASES[6], "bytes_read": CALIB_PAIRS * 2 * (
+        wl.PREFIX_SHARED.num_kv_heads * 16 * 128 * 2), "calls": 1})
+    with open(out_json, "w") as fh:
+        json.dump({"decode_only": phases}, fh, indent=1)
+    print(json.dumps({"decode_only": phases}), flush=True)
+
+
+def _dispatches_by_phase(d, phases):
+    """Counter rows of a rocprofv3 --pmc run, per (phase, kernel short name):
+    {counter: [value per dispatch]}; phases are split at the spin-kernel
+    markers in dispatch order."""
+    rows = _read_counters(d)
+    per_disp = {}
+    for r in rows:
+        key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        e = per_disp.setdefault(key, {"name": r.get("Kernel_Name", ""), "c": {}})
+        c = r.get("Counter_Name")
+        e["c"][c] = e["c"].get(c, 0.0) + float(r["Counter_Value"])
+    out = {}
+    phase = -1
+    for key in sorted(per_disp):
+        e = per_disp[key]
+        if "spin_kernel" in e["name"] or "sleep" in e["name"]:
+            phase += 1
+            continue
+        short = kernel_short_name(e["name"])
+        if short is None or not 0 <= phase < len(phases):
+            continue
+        slot = out.setdefault((phases[phase], short), {})
+        for c, v in e["c"].items():
+            slot.setdefault(c, []).append(v)
+    return out
+
+
+def decode_counter_summary(json_file, dirs):
+    """Markdown summary of rocprofv3 --pmc runs of --decode-only: per
+    workload, HBM bytes per call of its decode kernels (partition kernel +
+    reduce) from FETCH_SIZE / WRITE_SIZE scaled by the calibration copy's
+    reading, against the algorithmic bytes; read requests by size (which
+    tells whether the copy's scale carries over to the decode kernels);
+    matrix-core and vector-ALU busy shares; the raw means."""
+    with open(json_file) as fh:
+        meta = {p["phase"]: p for p in json.load(fh)["decode_only"]}
+    per = {}
+    for d in dirs:
+        for k, v in _dispatches_by_phase(d, DECODE_PHASES).items():
+            for c, vals in v.items():
+                per.setdefault(k, {})[c] = vals
+
+    def mean(cs, c):
+        v = cs.get(c)
+        return sum(v) / len(v) if v else None
+
+    cal = per.get((DECODE_PHASES[6], "copy_blocks_kernel"), {})
+    expect = meta[DECODE_PHASES[6]]["bytes_read"]
+    scale = {c: expect / (mean(cal, c) * 1024) for c in ("FETCH_SIZE", "WRITE_SIZE")
+             if mean(cal, c)}
+    cal_req = mean(cal, "TCC_EA0_RDREQ_sum")
+    bpr = expect / cal_req if cal_req else None  # bytes per counted read request
+    lines = [f"Calibration: pa_copy_blocks of {CALIB_PAIRS} block pairs reads {expect} B and "
+             "writes as many: " + ", ".join(f"{c} scale {v:.4f}" for c, v in scale.items())
+             + (f"; {cal_req:.6g} read requests, {bpr:.2f} B per request" if bpr else ""), "",
+             "| workload | HBM read B/call | HBM write B/call | algorithmic B/call | "
+             "(read+write) / algorithmic |", "|---|---|---|---|---|"]
+    summary = {}
+    for ph in DECODE_PHASES[:6]:
+        rd = wr = 0.0
+        have = False
+        for (p2, k), cs in per.items():
+            if p2 != ph or not k.startswith("decode"):
+                continue
+            if mean(cs, "FETCH_SIZE") is not None and "FETCH_SIZE" in scale:
+                rd += mean(cs, "FETCH_SIZE") * 1024 * scale["FETCH_SIZE"]
+                have = True
+            if mean(cs, "WRITE_SIZE") is not None and "WRITE_SIZE" in scale:
+                wr += mean(cs, "WRITE_SIZE") * 1024 * scale["WRITE_SIZE"]
+        if not have:
+            continue
+        alg = meta[ph].get("algorithmic_bytes")
+        ratio = f"{(rd + wr) / alg:.4f}" if alg else "-"
+        lines.append(f"| {ph} | {rd:.5g} | {wr:.5g} | {alg if alg else 'unique bytes: bench row'}"
+                     f" | {ratio} |")
+        summary[ph] = {"read": rd, "write": wr, "algorithmic": alg}
+    mix = []
+    for (ph, k), cs in per.items():
+        n = mean(cs, "TCC_EA0_RDREQ_sum")
+        if not n or not (k.startswith("decode") or (k == "copy_blocks_kernel" and
+                                                    ph == DECODE_PHASES[6])):
+            continue
+        n32, n128 = mean(cs, "TCC_EA0_RDREQ_32B_sum") or 0, mean(cs, "TCC_BUBBLE_sum") or 0
+        ndram = mean(cs, "TCC_EA0_RDREQ_DRAM_sum") or 0
+        bytes_at = f"{n * bpr:.5g}" if bpr else "-"
+        mix.append(f"| {ph} | {k} | {n:.6g} | {n32 / n:.4f} | {n128 / n:.4f} | "
+                   f"{ndram / n:.4f} | {bytes_at} |")
+    if mix:
+        lines += ["", "| workload | kernel | read requests / dispatch | 32 B share | "
+                  "TCC_BUBBLE (128 B) share | to-DRAM share | requests x calibration B/request |",
+                  "|---|---|---|---|---|---|---|"] + mix
+    busy = []
+    for (ph, k), cs in per.items():
+        g = mean(cs, "GRBM_GUI_ACTIVE")
+        if not g or not k.startswith("decode"):
+            continue
+        g /= NUM_XCCS  # the csv sums the counter over the 8 XCCs
+        parts = [f"{g:.4g} cycles"]
+        if mean(cs, "SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            parts.append(f"matrix core busy "
+                         f"{100 * mean(cs, 'SQ_VALU_MFMA_BUSY_CYCLES') / (g * NUM_SIMDS):.1f}%")
+        if mean(cs, "SQ_ACTIVE_INST_VALU") is not None:
+            parts.append(f"vector ALU busy "
+                         f"{100 * mean(cs, 'SQ_ACTIVE_INST_VALU') / (g * NUM_CUS):.1f}%")
+        busy.append(f"- {ph} / {k}: " + ", ".join(parts))
+    if busy:
+        lines += ["", "Busy shares (rocprof's MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x "
+                  "cycles), VALUBusy = SQ_ACTIVE_INST_VALU / (CUs x cycles)):", ""] + busy
+    lines += ["", "Raw means per dispatch:", "",
+              "| workload | kernel | counter | mean | dispatches |", "|---|---|---|---|---|"]
+    for (ph, k), cs in per.items():
+        if not (k.startswith("decode") or (k == "copy_blocks_kernel" and ph == DECODE_PHASES[6])):
+            continue
+        for c, vals in sorted(cs.items()):
+            if c == "SQ_WAVES" and len(vals) == 0:
+                continue
+            lines.append(f"| {ph} | {k} | {c} | {sum(vals) / len(vals):.6g} | {len(vals)} |")
+    return "\n".join(lines), summary
+
+
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
           "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
@@ -1289,6 +1539,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=4,
+                    help="disjoint copies of the headline batch the steps rotate over")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--rows", type=int, default=1, help="1: also measure the other rows")
@@ -1305,12 +1557,33 @@ def main():
                     help="time only the prefill chunks (bf16 and fp8 caches), for counter runs")
     ap.add_argument("--prefill-counter-summary", nargs="+", metavar="PMC_DIR",
                     help="summarise rocprofv3 --pmc runs of --prefill-only and exit")
+    ap.add_argument("--decode-only", metavar="OUT_JSON",
+                    help="run each decode workload alone (for counter runs), write the "
+                         "phases' algorithmic bytes to OUT_JSON and exit")
+    ap.add_argument("--decode-counter-summary", nargs="+", metavar=("JSON", "PMC_DIR"),
+                    help="summarise rocprofv3 --pmc runs of --decode-only (the JSON it wrote, "
+                         "then the run directories) and exit; updates the traffic file")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return
     if args.prefill_counter_summary:
         print(prefill_counter_summary(args.prefill_counter_summary))
+        return
+    if args.decode_counter_summary:
+        text, summary = decode_counter_summary(args.decode_counter_summary[0],
+                                               args.decode_counter_summary[1:])
+        print(text)
+        head = summary.get(DECODE_PHASES[0])
+        if head and head["read"] > 0 and head["write"] > 0:
+            with open(TRAFFIC_FILE, "w") as fh:
+                json.dump({"kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+                           "kernel_source_sha256": kernel_source_hash(),
+                           "workload": DECODE_PHASES[0],
+                           "hbm_read_bytes_per_call": head["read"],
+                           "hbm_write_bytes_per_call": head["write"],
+                           "algorithmic_bytes_per_call": head["algorithmic"],
+                           "hbm_bytes_per_launch": head["read"] + head["write"]}, fh, indent=1)
         return
     if args.pmc_summary:
         import workloads as wl
@@ -1335,6 +1608,9 @@ def main():
     if args.prefill_only:
         prefill_only(pa, wl, torch, args.reps)
         return
+    if args.decode_only:
+        decode_only(pa, wl, torch, np, args.reps, args.decode_only)
+        return
     mark_phase(torch)
     case, h = headline(args, pa, wl, torch, np)
     K, W = args.steps, args.warmup
@@ -1358,6 +1634,8 @@ def main():
                         "KV, fp32 accumulate; cache write + decode per step",
             "global_batch": h["S"],
             "seq_len": h["seq_len"],
+            "rotation": f"{h['replicas']} copies of the batch in disjoint blocks of the pool; "
+                        f"step i decodes copy i mod {h['replicas']}",
             "partition_size": h["ps"],
             "parallelism": "none (1 GPU)",
         },
@@ -1436,7 +1714,8 @@ def main():
         for k, v in rows.items():
             log(f"bench: {k}: " + ", ".join(
                 f"{a}={b:.4g}" if isinstance(b, float) else
-                (f"{a}={b['value']:.4g} {b['unit']}" if isinstance(b, dict) else f"{a}={b}")
+                (f"{a}={b['value']:.4g} {b['unit']}" if isinstance(b, dict) and "value" in b
+                 else f"{a}={b}")
                 for a, b in v.items() if a != "workload"))
     print(json.dumps(result), flush=True)
 

@@ -156,3 +156,42 @@ def test_prefill_counter_summary_per_run_and_xcc(tmp_path):
     assert "bf16: vector ALU busy 75.0%" in text
     assert "fp8: matrix core busy 50.0%" in text
     assert "other_kernel" not in text
+
+
+def test_decode_counter_summary_splits_workloads_and_scales(tmp_path):
+    """Counter rows of a --decode-only run: dispatches are attributed to the
+    workload of the last spin-kernel marker before them; FETCH_SIZE and
+    WRITE_SIZE are scaled by the calibration copy's reading."""
+    import json
+    dec = "void pa::(anonymous namespace)::decode_mfma_kernel<128, 16, true>(pa::DecodeParams)"
+    red = "pa::(anonymous namespace)::decode_reduce_kernel(pa::DecodeParams)"
+    cop = "pa::(anonymous namespace)::copy_blocks_kernel(char*, char*, int const*, int, long, int)"
+    expect = 1 << 30
+    meta = [{"phase": p, "algorithmic_bytes": 1000 * 1024, "calls": 2}
+            for p in bench.DECODE_PHASES[:6]]
+    meta.append({"phase": bench.DECODE_PHASES[6], "bytes_read": expect, "calls": 1})
+    jf = tmp_path / "d.json"
+    jf.write_text(json.dumps({"decode_only": meta}))
+    seq = [("spin_kernel", {}), (dec, {"FETCH_SIZE": 400.0, "WRITE_SIZE": 3.0}),
+           (red, {"FETCH_SIZE": 10.0, "WRITE_SIZE": 2.0}),
+           (dec, {"FETCH_SIZE": 600.0, "WRITE_SIZE": 5.0}),
+           (red, {"FETCH_SIZE": 10.0, "WRITE_SIZE": 2.0})]
+    for _ in range(5):  # workloads 1..5: no dispatches
+        seq.append(("spin_kernel", {}))
+    seq += [("spin_kernel", {}), (cop, {"FETCH_SIZE": expect / 2048, "WRITE_SIZE": expect / 1024})]
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (k, cs) in enumerate(seq):
+            for c, v in (cs or {"SQ_WAVES": 1.0}).items():
+                w.writerow([i + 1, k, c, v])
+    text, summary = bench.decode_counter_summary(str(jf), [str(d)])
+    head = summary[bench.DECODE_PHASES[0]]
+    # reads: (mean 500 + 10) KiB x scale 2; writes: (4 + 2) KiB x scale 1
+    assert head["read"] == pytest.approx(510 * 1024 * 2)
+    assert head["write"] == pytest.approx(6 * 1024)
+    assert head["algorithmic"] == 1000 * 1024
+    assert bench.DECODE_PHASES[1] not in summary
+    assert "scale 2.0000" in text

@@ -230,11 +230,19 @@ class DecodeCase:
 
 def make_decode_case(shape: DecodeShape, device, k_axes="bhrd", v_axes="bhrd",
                      seed: int | None = None, lengths=None, num_blocks: int | None = None,
-                     extra_table_slots: int = 0) -> DecodeCase:
-    """A full decode batch for ``shape``: lengths, tables, q and poisoned pools."""
+                     extra_table_slots: int = 0, replicas: int = 1) -> DecodeCase:
+    """A full decode batch for ``shape``: lengths, tables, q and poisoned pools.
+
+    replicas > 1: that many copies of the batch (the same lengths) laid into
+    disjoint blocks of the one pool, replica r being sequences r*S .. r*S+S-1
+    of the returned case, each with its own K/V and q draws.  Timing loops
+    that visit the replicas in turn re-read no block of the previous
+    replicas' calls, so no cache level (L2, the MALL) can serve a call from
+    what an earlier one left behind."""
     seed = shape.seed if seed is None else seed
     rng = np.random.default_rng(seed)
     lens = draw_lengths(shape, rng) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    lens = np.tile(lens, int(replicas))
     nb = shape.num_blocks if num_blocks is None else num_blocks
     stride = max(blocks_needed(L + extra_table_slots, shape.block_size) for L in lens) + 1
     perm, tables = assign_blocks(lens, shape.block_size, nb, rng, stride=stride)
