@@ -795,6 +795,24 @@ def row_fp8(pa, wl, torch, np, reps, cpu_budget):
     return r
 
 
+def row_mha_valu(pa, wl, torch, np, reps):
+    """The 7B-shaped decode batch on the vector-ALU kernel (PA_DECODE_VALU),
+    rotated like the headline: the A/B of the matrix-core choice for MHA."""
+    sh = wl.MHA_7B
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES, replicas=ROTATE)
+
+    def dec(out, q, k, v, t, l, maxlen, ps, ws):
+        pa.pa_decode(out, q, k, v, t, l, sh.scale, maxlen, ps, ws, valu=True)
+
+    r = decode_row(pa, torch, case, reps, replicas=ROTATE, decode=dec)
+    r_mfma = decode_row(pa, torch, case, reps, replicas=ROTATE)
+    r["matrix_core_kernel_us"] = r_mfma["us"]
+    r["workload"] = ("7B-shaped decode (64 seqs, ctx U[128,4096], 32/32 heads, head_dim 128, "
+                     "block 16, bf16) on the vector-ALU kernel; matrix_core_kernel_us: the "
+                     "default kernel on the same calls")
+    return r
+
+
 def row_long(pa, wl, torch, np, reps, cpu_budget):
     """8 x 32768 tokens at block 128: the library's default partitions (the
     row's figure) and the 512-token partitions the long-context workload
@@ -1273,10 +1291,12 @@ def prefill_counter_summary(dirs):
     return "\n".join(lines)
 
 
+CAL_PHASE = "calibration copy"
 DECODE_PHASES = ("7B-shaped decode (rotated)", "gqa decode (rotated)", "fp8 decode (rotated)",
                  "long-context decode, default partitions (rotated)",
                  "long-context decode, 512-token partitions (rotated)",
-                 "prefix-shared grouped decode", "calibration copy")
+                 "prefix-shared grouped decode", CAL_PHASE,
+                 "7B-shaped decode on the vector-ALU kernel (rotated)")
 
 
 def decode_only(pa, wl, torch, np, reps, out_json):
@@ -1327,8 +1347,17 @@ def decode_only(pa, wl, torch, np, reps, out_json):
     phases[-1]["algorithmic_bytes"] = None  # unique bytes: see the bench row
     mark_phase(torch)
     calibrate_copy(pa, torch, np, case, alloc)
-    phases.append({"phase": DECODE_PHASES[6], "bytes_read": CALIB_PAIRS * 2 * (
+    phases.append({"phase": CAL_PHASE, "bytes_read": CALIB_PAIRS * 2 * (
         wl.PREFIX_SHARED.num_kv_heads * 16 * 128 * 2), "calls": 1})
+    del case
+    torch.cuda.empty_cache()
+    shv = wl.MHA_7B
+
+    def dec_valu(out, q, k, v, t, l, maxlen, ps, ws):
+        pa.pa_decode(out, q, k, v, t, l, shv.scale, maxlen, ps, ws, valu=True)
+
+    run(DECODE_PHASES[7], wl.make_decode_case(shv, dev, pa.K_AXES, pa.V_AXES, replicas=ROTATE),
+        decode=dec_valu)
     with open(out_json, "w") as fh:
         json.dump({"decode_only": phases}, fh, indent=1)
     print(json.dumps({"decode_only": phases}), flush=True)
@@ -1380,8 +1409,8 @@ def decode_counter_summary(json_file, dirs):
         v = cs.get(c)
         return sum(v) / len(v) if v else None
 
-    cal = per.get((DECODE_PHASES[6], "copy_blocks_kernel"), {})
-    expect = meta[DECODE_PHASES[6]]["bytes_read"]
+    cal = per.get((CAL_PHASE, "copy_blocks_kernel"), {})
+    expect = meta[CAL_PHASE]["bytes_read"]
     scale = {c: expect / (mean(cal, c) * 1024) for c in ("FETCH_SIZE", "WRITE_SIZE")
              if mean(cal, c)}
     cal_req = mean(cal, "TCC_EA0_RDREQ_sum")
@@ -1392,7 +1421,9 @@ def decode_counter_summary(json_file, dirs):
              "| workload | HBM read B/call | HBM write B/call | algorithmic B/call | "
              "(read+write) / algorithmic |", "|---|---|---|---|---|"]
     summary = {}
-    for ph in DECODE_PHASES[:6]:
+    for ph in DECODE_PHASES:
+        if ph == CAL_PHASE:
+            continue
         rd = wr = 0.0
         have = False
         for (p2, k), cs in per.items():
@@ -1414,7 +1445,7 @@ def decode_counter_summary(json_file, dirs):
     for (ph, k), cs in per.items():
         n = mean(cs, "TCC_EA0_RDREQ_sum")
         if not n or not (k.startswith("decode") or (k == "copy_blocks_kernel" and
-                                                    ph == DECODE_PHASES[6])):
+                                                    ph == CAL_PHASE)):
             continue
         n32, n128 = mean(cs, "TCC_EA0_RDREQ_32B_sum") or 0, mean(cs, "TCC_BUBBLE_sum") or 0
         ndram = mean(cs, "TCC_EA0_RDREQ_DRAM_sum") or 0
@@ -1445,7 +1476,7 @@ def decode_counter_summary(json_file, dirs):
     lines += ["", "Raw means per dispatch:", "",
               "| workload | kernel | counter | mean | dispatches |", "|---|---|---|---|---|"]
     for (ph, k), cs in per.items():
-        if not (k.startswith("decode") or (k == "copy_blocks_kernel" and ph == DECODE_PHASES[6])):
+        if not (k.startswith("decode") or (k == "copy_blocks_kernel" and ph == CAL_PHASE)):
             continue
         for c, vals in sorted(cs.items()):
             if c == "SQ_WAVES" and len(vals) == 0:
@@ -1455,7 +1486,8 @@ def decode_counter_summary(json_file, dirs):
 
 
 PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decode + COW copy",
-          "fp8 decode (7B-shaped, E4M3 K/V)", "long-context split-K decode",
+          "fp8 decode (7B-shaped, E4M3 K/V)", "7B-shaped decode, vector-ALU kernel and default",
+          "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
           "fp8 prompt chunks (quantizing write + prefill)",
           "swap out / in (pinned host pool)", "serving loop (continuous batching)")
@@ -1680,6 +1712,10 @@ def main():
         log("bench: row fp8 decode")
         mark_phase(torch)
         rows["decode_fp8"] = row_fp8(pa, wl, torch, np, args.reps, args.row_cpu_budget)
+        torch.cuda.empty_cache()
+        log("bench: row vector-ALU MHA decode")
+        mark_phase(torch)
+        rows["decode_mha_valu"] = row_mha_valu(pa, wl, torch, np, args.reps)
         torch.cuda.empty_cache()
         log("bench: row long-context split-K")
         mark_phase(torch)

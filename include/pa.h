@@ -156,7 +156,14 @@ enum {
      * running at the same time hit in cache; without the flag K/V are
      * streamed with nontemporal loads, which is faster when every block is
      * read once.  Results are bit-identical either way. */
-    PA_DECODE_KV_REUSE = 1
+    PA_DECODE_KV_REUSE = 1,
+    /* bf16 caches: run the vector-ALU kernel (per-token dot products with
+     * quad exchanges, 16-token steps) instead of the matrix-core one.  A
+     * second, independent device implementation of the same definition,
+     * kept for comparison and cross-checks; it is slower on this chip.
+     * Results agree with the default within fp32 rounding (not bit for
+     * bit).  Not available to the grouped and fp8 calls (INVALID_ARG). */
+    PA_DECODE_VALU = 2
 };
 
 /* pa_decode with flags (a bitwise OR of the PA_DECODE_* values; 0 gives

@@ -18,6 +18,12 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
+# Host-sanitizer runs only: PA_HOST_LIB names a CPU-only build of the
+# library's host code (allocator, scheduler, group derivation, error text)
+# made with -fsanitize=address,undefined.  Only the symbols it exports are
+# declared; the device calls are absent from it (using one raises
+# AttributeError), so nothing runs in place of a kernel.
+_HOST_LIB = os.environ.get("PA_HOST_LIB")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = 1
@@ -29,6 +35,7 @@ PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_DTYPE_FP8_E4M3 = 2  # OCP E4M3 codes, stored in torch.uint8 tensors
 PA_DECODE_KV_REUSE = 1
+PA_DECODE_VALU = 2  # bf16: the vector-ALU decode kernel instead of the matrix-core one
 PA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the device scratch behind pa_decode_noalloc
 
 # Axis order of the two pools, in the letters b (block), h (kv head),
@@ -164,15 +171,20 @@ def _declare(lib):
                                        ctypes.c_uint32, vp]),
     }
     for name, (res, args) in sig.items():
+        if _HOST_LIB and not hasattr(lib, name):
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
 
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python paged_kv_cache_417_amd/build.py` (hipcc, gfx950)")
-_lib = ctypes.CDLL(LIB_PATH)
+if _HOST_LIB:
+    _lib = ctypes.CDLL(_HOST_LIB)
+else:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python paged_kv_cache_417_amd/build.py` (hipcc, gfx950)")
+    _lib = ctypes.CDLL(LIB_PATH)
 _declare(_lib)
 
 
@@ -275,17 +287,20 @@ def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, 
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None, kv_reuse=False) -> None:
+              partition_size=0, workspace=None, stream=None, kv_reuse=False,
+              valu=False) -> None:
     """Paged decode; kv_reuse=True (pa_decode_ex with PA_DECODE_KV_REUSE) for
-    batches whose sequences share blocks."""
+    batches whose sequences share blocks; valu=True (PA_DECODE_VALU) runs a
+    bf16 batch on the vector-ALU kernel."""
     nb, hkv, bs, d = _geometry(k_cache)
     s, hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
             _p(context_lens), s, hq, hkv, d, bs, nb, float(scale), int(max_context_len),
             int(partition_size), _p(workspace), ws_bytes, _dtype_code(k_cache))
-    if kv_reuse:
-        _check(_lib.pa_decode_ex(*args, PA_DECODE_KV_REUSE, ctypes.c_void_p(_stream(stream))))
+    flags = (PA_DECODE_KV_REUSE if kv_reuse else 0) | (PA_DECODE_VALU if valu else 0)
+    if flags:
+        _check(_lib.pa_decode_ex(*args, flags, ctypes.c_void_p(_stream(stream))))
     else:
         _check(_lib.pa_decode(*args, ctypes.c_void_p(_stream(stream))))
 

@@ -233,8 +233,13 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
                       const GroupArgs *grp = nullptr) {
     if (fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale)))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: scales must be finite and > 0", fn);
-    if (flags & ~(uint32_t)PA_DECODE_KV_REUSE)
+    if (flags & ~(uint32_t)(PA_DECODE_KV_REUSE | PA_DECODE_VALU))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+    const bool valu = (flags & PA_DECODE_VALU) != 0;
+    if (valu && (fp8 || grp))
+        return pa::fail(PA_ERR_INVALID_ARG,
+                        "%s: PA_DECODE_VALU applies to pa_decode_ex over bf16/fp32 caches only",
+                        fn);
     if (num_seqs < 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d", fn, num_seqs);
     if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "%s: dtype %d", fn, (int)dtype);
     if (grp) {
@@ -322,8 +327,8 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
         p.grp_chunks = (int32_t)chunks;
         p.grp_cover = (int32_t)(chunks * mpw);
     }
-    int rc = dtype == PA_DTYPE_BF16 ? pa::launch_decode_mfma(p, stream)
-                                    : pa::launch_decode_valu(p, dtype, stream);
+    int rc = dtype == PA_DTYPE_BF16 && !valu ? pa::launch_decode_mfma(p, stream)
+                                             : pa::launch_decode_valu(p, dtype, stream);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
     rc = pa::launch_decode_reduce(p, stream);
     if (rc) return pa::fail(PA_ERR_DEVICE, "%s: reduce launch failed (hip error %d)", fn, rc);

@@ -168,15 +168,16 @@ def test_decode_counter_summary_splits_workloads_and_scales(tmp_path):
     cop = "pa::(anonymous namespace)::copy_blocks_kernel(char*, char*, int const*, int, long, int)"
     expect = 1 << 30
     meta = [{"phase": p, "algorithmic_bytes": 1000 * 1024, "calls": 2}
-            for p in bench.DECODE_PHASES[:6]]
-    meta.append({"phase": bench.DECODE_PHASES[6], "bytes_read": expect, "calls": 1})
+            for p in bench.DECODE_PHASES if p != bench.CAL_PHASE]
+    meta.append({"phase": bench.CAL_PHASE, "bytes_read": expect, "calls": 1})
     jf = tmp_path / "d.json"
     jf.write_text(json.dumps({"decode_only": meta}))
     seq = [("spin_kernel", {}), (dec, {"FETCH_SIZE": 400.0, "WRITE_SIZE": 3.0}),
            (red, {"FETCH_SIZE": 10.0, "WRITE_SIZE": 2.0}),
            (dec, {"FETCH_SIZE": 600.0, "WRITE_SIZE": 5.0}),
            (red, {"FETCH_SIZE": 10.0, "WRITE_SIZE": 2.0})]
-    for _ in range(5):  # workloads 1..5: no dispatches
+    cal_at = bench.DECODE_PHASES.index(bench.CAL_PHASE)
+    for _ in range(cal_at - 1):  # the workloads before the calibration: no dispatches
         seq.append(("spin_kernel", {}))
     seq += [("spin_kernel", {}), (cop, {"FETCH_SIZE": expect / 2048, "WRITE_SIZE": expect / 1024})]
     d = tmp_path / "run"

@@ -35,7 +35,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_decode(pa, case, ps=0, lengths=None, tables=None, q=None):
+def run_decode(pa, case, ps=0, lengths=None, tables=None, q=None, valu=False):
     sh = case.shape
     lens = case.lengths if lengths is None else lengths
     tabs = case.tables if tables is None else tables
@@ -47,7 +47,8 @@ def run_decode(pa, case, ps=0, lengths=None, tables=None, q=None):
     out = torch.full((len(lens), sh.num_q_heads, sh.head_dim), 7.0, device=dev)
     ws = pa.decode_workspace(len(lens), sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
                              sh.block_size, maxlen, ps, dev)
-    pa.pa_decode(out, q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, ps, ws)
+    pa.pa_decode(out, q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, ps, ws,
+                 valu=valu)
     torch.cuda.synchronize()
     return out
 
@@ -164,6 +165,42 @@ def test_decode_edge_lengths(pa, dtype, d, bs):
         out = run_decode(pa, case, ps=ps)
         check_rows(pa, case, out, range(len(EDGE)))
         assert (out[0] == 0).all()  # empty context: zero row
+
+
+@pytest.mark.parametrize("d,bs,hq,hkv", [(128, 16, 32, 32), (128, 128, 32, 8), (64, 32, 8, 1)])
+def test_valu_kernel_on_bf16_matches_oracle_and_matrix_core(pa, d, bs, hq, hkv):
+    """PA_DECODE_VALU: the vector-ALU kernel on bf16 caches, a second device
+    implementation, within the bar of the oracle and within fp32 rounding of
+    the matrix-core kernel."""
+    say(f"case valu bf16 d={d} bs={bs} hq={hq} hkv={hkv}")
+    case = small_case(pa, "bf16", hq, hkv, d, bs, EDGE, seed=3 * d + bs + hq)
+    for ps in (0, 256):
+        out = run_decode(pa, case, ps=ps, valu=True)
+        check_rows(pa, case, out, range(len(EDGE)))
+        ref = run_decode(pa, case, ps=ps)
+        assert (out - ref).abs().max().item() <= 1e-5
+        assert (out[0] == 0).all()
+
+
+def test_valu_flag_is_refused_where_it_has_no_kernel(pa):
+    case = small_case(pa, "bf16", 8, 2, 128, 16, [40, 17], seed=4)
+    dev = "cuda"
+    t_dev = torch.as_tensor(case.tables, device=dev)
+    l_dev = torch.as_tensor(case.lengths, device=dev)
+    out = torch.empty((2, 8, 128), device=dev)
+    grp = [torch.as_tensor(a, device=dev) for a in (np.array([0, 2], np.int32),
+                                                      np.array([0, 0], np.int32),
+                                                      np.array([2], np.int32))]
+    import ctypes
+    lib = pa.lib()
+    st = lib.pa_decode_grouped(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(case.q.data_ptr()),
+        ctypes.c_void_p(case.k_pool.data_ptr()), ctypes.c_void_p(case.v_pool.data_ptr()),
+        ctypes.c_void_p(t_dev.data_ptr()), t_dev.shape[1], ctypes.c_void_p(l_dev.data_ptr()),
+        2, 8, 2, 128, 16, case.k_pool.shape[0], 0.1, 40, 0, ctypes.c_void_p(grp[0].data_ptr()),
+        ctypes.c_void_p(grp[1].data_ptr()), ctypes.c_void_p(grp[2].data_ptr()), 1, 2, None, 0,
+        pa.PA_DTYPE_BF16, pa.PA_DECODE_VALU, None)
+    assert st == pa.PA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
@@ -313,18 +350,21 @@ def test_bad_block_inside_a_split_sequence_gives_nan_row(pa, ps):
 # the named batches at full size: every row against the oracle
 
 
-@pytest.mark.parametrize("name,ps", [("mha_7b", 0), ("gqa", 0), ("mixed", 0), ("mixed", 512)])
-def test_full_size_batches(pa, name, ps):
+@pytest.mark.parametrize("name,ps,valu", [("mha_7b", 0, False), ("gqa", 0, False),
+                                          ("mixed", 0, False), ("mixed", 512, False),
+                                          ("mha_7b", 0, True)])
+def test_full_size_batches(pa, name, ps, valu):
     """The 7B-shaped (64 sequences), grouped-query (128) and long-context
     (8 x 32768) batches at full size, in the launch configuration the
     benchmark times (the library's default partitions; the long-context
     batch also at 512-token partitions): every row of every sequence
-    against the fp64 oracle, run on the host threads."""
+    against the fp64 oracle, run on the host threads.  The 7B-shaped batch
+    also on the vector-ALU kernel (PA_DECODE_VALU)."""
     sh = wl.SHAPES[name]
     say(f"case full-size {name}: S={sh.num_seqs} Hq={sh.num_q_heads} Hkv={sh.num_kv_heads} "
-        f"BS={sh.block_size} NB={sh.num_blocks} ps={ps}")
+        f"BS={sh.block_size} NB={sh.num_blocks} ps={ps} valu={valu}")
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
-    out = run_decode(pa, case, ps=ps)
+    out = run_decode(pa, case, ps=ps, valu=valu)
     assert torch.isfinite(out).all()
     ref = oracle_decode_all(case.q, case.k_pool, case.v_pool, case.tables, case.lengths,
                             sh.block_size, sh.scale, case.k_axes, case.v_axes)
