@@ -279,6 +279,49 @@ def cpu_cache_write_row(k_new, v_new, slots, hkv, d, bs, budget_s, fp8_scale=Non
                                         f"pool of their {len(blocks)} blocks, {elapsed:.1f} s"}
 
 
+def allocator_warm(pa, np, case, steps=300):
+    """Warm host cost of one decode step's bookkeeping on the headline batch:
+    a batch append of one token to each of the 64 sequences plus their dense
+    tables, after 30 untimed steps.  `binding_us` goes through the Python
+    binding; `c_abi_us` calls the two C entry points directly with the
+    argument addresses bound once (the library's own cost)."""
+    import ctypes
+    sh = case.shape
+    S = len(case.lengths)
+    a = pa.Allocator(sh.num_blocks, sh.block_size, free_order=case.perm)
+    ids = np.arange(S, dtype=np.int64)
+    for s_ in ids:
+        a.create(int(s_))
+    a.batch_append(ids, case.lengths)
+    stride = int(case.lengths.max() + 2 * steps + 100) // sh.block_size + 2
+    ones = np.ones(S, dtype=np.int32)
+    slots = np.zeros(S, dtype=np.int64)
+    tabs = np.zeros((S, stride), dtype=np.int32)
+    lens = np.zeros(S, dtype=np.int32)
+    pad = sh.num_blocks - 1
+    for _ in range(30):
+        a.batch_append(ids, ones, slots_out=slots)
+        a.batch_tables(ids, stride, pad, tables_out=tabs, lens_out=lens)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        a.batch_append(ids, ones, slots_out=slots)
+        a.batch_tables(ids, stride, pad, tables_out=tabs, lens_out=lens)
+    binding = (time.perf_counter() - t0) * 1e6 / steps
+    lib = pa.lib()
+    pairs = np.zeros((S, 2), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    app = (a._h, S, ids.ctypes.data, ones.ctypes.data, slots.ctypes.data, pairs.ctypes.data, S,
+           ctypes.byref(n))
+    tab = (a._h, S, ids.ctypes.data, tabs.ctypes.data, stride, pad, lens.ctypes.data)
+    f_app, f_tab = lib.pa_batch_append, lib.pa_batch_tables
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        f_app(*app)
+        f_tab(*tab)
+    raw = (time.perf_counter() - t0) * 1e6 / steps
+    return {"binding_us": binding, "c_abi_us": raw, "steps": steps, "stride": stride}
+
+
 def cpu_allocator_row(case, steps):
     """The plain-Python reference model of the allocator replaying the
     headline batch's prompts and then `steps` decode appends of one token to
@@ -1731,9 +1774,15 @@ def main():
         rows["prefill_chunk_fp8"], rows["cache_write_fp8"] = row_fp8_prefill(
             pa, wl, torch, np, args.reps, args.row_cpu_budget)
         torch.cuda.empty_cache()
+        warm_alloc = allocator_warm(pa, np, alloc_case)
         rows["allocator"] = {"host_us_per_step": h["alloc_us"],
+                             "warm_binding_us_per_step": warm_alloc["binding_us"],
+                             "warm_c_abi_us_per_step": warm_alloc["c_abi_us"],
                              "workload": "batch append of one token to 64 sequences + dense "
-                                         "tables [64][stride] (host, C ABI)"}
+                                         "tables [64][stride] (host): host_us_per_step over the "
+                                         "headline's precomputed steps; warm_*: 300 steps after "
+                                         "30 untimed ones, through the binding and through the "
+                                         "C ABI alone"}
         if args.row_cpu_budget > 0:
             rows["allocator"]["cpu_oracle"] = cpu_allocator_row(alloc_case, 20)
         log("bench: row prefix cache")

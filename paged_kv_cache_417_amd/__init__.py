@@ -110,7 +110,9 @@ def _declare(lib):
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)
     st = ctypes.c_int
-    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    # host arrays travel as plain addresses (numpy's .ctypes.data): a typed
+    # pointer cast costs microseconds per argument on every call
+    pi32 = pi64 = ctypes.c_void_p
     sig = {
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_cache_write": (st, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]),
@@ -432,11 +434,13 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, cu_q_lens, context_
 
 
 def _i64p(a):
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    """Address of a C-contiguous int64 numpy array (for a c_void_p argument)."""
+    return a.ctypes.data
 
 
 def _i32p(a):
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    """Address of a C-contiguous int32 numpy array (for a c_void_p argument)."""
+    return a.ctypes.data
 
 
 class Allocator:
@@ -454,6 +458,9 @@ class Allocator:
             fo = _i32p(self._free_order)
         _check(_lib.pa_allocator_create(self.num_blocks, self.block_size, fo, ctypes.byref(h)))
         self._h = h
+        self._pairs_buf = np.zeros((1, 2), dtype=np.int32)
+        self._ncow = ctypes.c_int32(0)
+        self._ncow_ref = ctypes.byref(self._ncow)
 
     def close(self):
         if getattr(self, "_h", None) and _lib is not None:  # _lib is None at interpreter exit
@@ -487,12 +494,18 @@ class Allocator:
         nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
         total = int(nt.sum())
         slots = slots_out if slots_out is not None else np.zeros(max(total, 1), dtype=np.int64)
-        cap = len(ids)
-        pairs = pairs_out if pairs_out is not None else np.zeros((max(cap, 1), 2), dtype=np.int32)
-        ncow = ctypes.c_int32(0)
-        _check(_lib.pa_batch_append(self._h, len(ids), _i64p(ids), _i32p(nt), _i64p(slots),
-                                    _i32p(pairs), pairs.shape[0], ctypes.byref(ncow)))
-        return slots[:total], pairs[:ncow.value]
+        if pairs_out is not None:
+            pairs = pairs_out
+        else:  # a buffer kept across calls; the pairs returned are a copy
+            if self._pairs_buf.shape[0] < len(ids):
+                self._pairs_buf = np.zeros((len(ids), 2), dtype=np.int32)
+            pairs = self._pairs_buf
+        ncow = self._ncow
+        _check(_lib.pa_batch_append(self._h, len(ids), ids.ctypes.data, nt.ctypes.data,
+                                    slots.ctypes.data, pairs.ctypes.data, pairs.shape[0],
+                                    self._ncow_ref))
+        n = ncow.value
+        return slots[:total], (pairs[:n] if pairs_out is not None else pairs[:n].copy())
 
     def create_prefix(self, seq_id: int, tokens, max_cached_tokens=None) -> int:
         """New sequence reusing the cached blocks of the prompt ``tokens``;
@@ -575,8 +588,8 @@ class Allocator:
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         tables = tables_out if tables_out is not None else np.zeros((len(ids), stride), np.int32)
         lens = lens_out if lens_out is not None else np.zeros(len(ids), np.int32)
-        _check(_lib.pa_batch_tables(self._h, len(ids), _i64p(ids), _i32p(tables), stride,
-                                    pad_value, _i32p(lens)))
+        _check(_lib.pa_batch_tables(self._h, len(ids), ids.ctypes.data, tables.ctypes.data,
+                                    stride, pad_value, lens.ctypes.data))
         return tables, lens
 
     def free(self, seq_id: int):
@@ -629,7 +642,8 @@ class Scheduler:
                    "swap_in_pairs": np.zeros((nb, 2), np.int32)}
         self._plan = SchedPlan()
         for k, v in self._a.items():
-            setattr(self._plan, k, (_i64p if v.dtype == np.int64 else _i32p)(v))
+            ptype = ctypes.c_int64 if v.dtype == np.int64 else ctypes.c_int32
+            setattr(self._plan, k, v.ctypes.data_as(ctypes.POINTER(ptype)))
         self._plan.cap_seqs, self._plan.cap_slots, self._plan.cap_cow = n, t, n
         self._plan.cap_swap_pairs = nb
         self._fin = np.zeros(n, np.int64)

@@ -38,7 +38,6 @@
 #include <algorithm>
 #include <new>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "pa_internal.h"
@@ -52,6 +51,7 @@ struct Sequence {
     std::vector<int32_t> pending;  // token ids of the partial last block
     int32_t parent = -1;           // block of the last registered full block
     bool swapped = false;          // table holds host block ids
+    uint64_t stamp = 0;            // batch call that last named it (repeat check)
 };
 
 // 64-bit FNV-1a over the parent id and the block's token ids.
@@ -81,6 +81,11 @@ struct pa_allocator {
     std::unordered_map<int64_t, Sequence> seqs;  // pending reserved to block_size
     int64_t cow_copies = 0;
     int32_t num_shared = 0;
+    // batch calls: a counter that stamps the sequences a call names (so a
+    // repeated id is found without a set), and the call's sequence list,
+    // kept between calls so a warm call allocates nothing
+    uint64_t batch_epoch = 0;
+    mutable std::vector<const Sequence *> batch_seqs;
 
     // prefix cache
     std::vector<char> registered;        // per block
@@ -368,12 +373,21 @@ pa_status batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids
     if (!a) return pa::fail(PA_ERR_INVALID_ARG, "append: NULL allocator");
     if (num_seqs < 0 || (num_seqs > 0 && (!seq_ids || !n_tokens)) || !n_cow || cow_cap < 0)
         return pa::fail(PA_ERR_INVALID_ARG, "append: bad arguments");
-    std::vector<Sequence *> seqs(num_seqs);
+    try {
+        a->batch_seqs.resize(num_seqs);
+    } catch (...) {
+        return pa::fail(PA_ERR_INVALID_ARG, "append: out of host memory");
+    }
+    Sequence **seqs = const_cast<Sequence **>(a->batch_seqs.data());
+    const uint64_t epoch = ++a->batch_epoch;
     int64_t total_blocks = 0, total_tokens = 0, total_cow = 0;
     for (int32_t i = 0; i < num_seqs; ++i) {
         auto it = a->seqs.find(seq_ids[i]);
         if (it == a->seqs.end())
             return pa::fail(PA_ERR_NOT_FOUND, "append: no sequence %lld", (long long)seq_ids[i]);
+        if (it->second.stamp == epoch)
+            return pa::fail(PA_ERR_INVALID_ARG, "append: repeated sequence id in batch");
+        it->second.stamp = epoch;
         if (n_tokens[i] < 0)
             return pa::fail(PA_ERR_INVALID_ARG, "append: n_tokens[%d] = %d", i, n_tokens[i]);
         if ((int64_t)it->second.length + n_tokens[i] > INT32_MAX)
@@ -388,11 +402,6 @@ pa_status batch_append(pa_allocator *a, int32_t num_seqs, const int64_t *seq_ids
         total_blocks += blocks;
         total_tokens += n_tokens[i];
         total_cow += c ? 1 : 0;
-    }
-    if (num_seqs > 1) {
-        std::unordered_set<int64_t> ids(seq_ids, seq_ids + num_seqs);
-        if ((int32_t)ids.size() != num_seqs)
-            return pa::fail(PA_ERR_INVALID_ARG, "append: repeated sequence id in batch");
     }
     if (total_tokens > 0 && !slots_out)
         return pa::fail(PA_ERR_INVALID_ARG, "append: slots_out is NULL");
@@ -596,6 +605,11 @@ pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs, const int64_t
     if (!a || num_seqs < 0 || stride <= 0 ||
         (num_seqs > 0 && (!seq_ids || !tables_out || !context_lens_out)))
         return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_tables: bad arguments");
+    try {
+        a->batch_seqs.resize(num_seqs);
+    } catch (...) {
+        return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_tables: out of host memory");
+    }
     for (int32_t i = 0; i < num_seqs; ++i) {
         auto it = a->seqs.find(seq_ids[i]);
         if (it == a->seqs.end())
@@ -607,9 +621,10 @@ pa_status pa_batch_tables(const pa_allocator *a, int32_t num_seqs, const int64_t
         if ((int32_t)it->second.table.size() > stride)
             return pa::fail(PA_ERR_INVALID_ARG, "pa_batch_tables: sequence %lld has %zu blocks > "
                             "stride %d", (long long)seq_ids[i], it->second.table.size(), stride);
+        a->batch_seqs[i] = &it->second;
     }
     for (int32_t i = 0; i < num_seqs; ++i) {
-        const Sequence &s = a->seqs.find(seq_ids[i])->second;
+        const Sequence &s = *a->batch_seqs[i];
         int32_t *row = tables_out + (int64_t)i * stride;
         std::copy(s.table.begin(), s.table.end(), row);
         std::fill(row + s.table.size(), row + stride, pad_value);
