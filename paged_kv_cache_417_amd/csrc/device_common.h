@@ -32,19 +32,17 @@ __device__ __forceinline__ u32x2 ld8_nt(const void *p) {
 }
 
 // Eight OCP E4M3 codes (bytes of w, lowest first) -> eight bf16 values, in
-// order.  The hardware conversion to fp32 is exact, and an E4M3 value has at
-// most four significant bits, so the top half of each fp32 is the same value
-// in bf16: no rounding anywhere.
+// order, two codes per v_cvt_scalef32_pk_bf16_fp8 with scale 1.  Exact: an
+// E4M3 value has at most four significant bits and lies within bf16's
+// range, so no rounding happens anywhere.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
     u32x4 r;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);  // codes 4h, 4h+1
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);   // codes 4h+2, 4h+3
-        r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]),
-                                         0x07060302u);
-        r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]),
-                                             0x07060302u);
+        r[2 * h] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, false));
+        r[2 * h + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, true));
     }
     return r;
 }

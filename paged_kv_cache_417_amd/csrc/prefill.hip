@@ -62,10 +62,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// Eight OCP E4M3 codes (bytes of w, lowest first) -> eight fp16 or bf16
-// values, in order, two codes per v_cvt_scalef32_pk_* with scale 1.  Exact:
+// Eight OCP E4M3 codes (bytes of w, lowest first) -> eight fp16 values, in
+// order, two codes per v_cvt_scalef32_pk_f16_fp8 with scale 1.  Exact:
 // every E4M3 value (at most 448 in magnitude, four significant bits, no
-// smaller than 2^-9) is an fp16 and a bf16 value.
+// smaller than 2^-9) is an fp16 value.  (The bf16 widening is
+// e4m3x8_to_bf16x8.)
 __device__ __forceinline__ u32x4 e4m3x8_to_f16x8(u32x2 w) {
     u32x4 r;
 #pragma unroll
@@ -74,17 +75,6 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16x8(u32x2 w) {
                                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.f, false));
         r[2 * h + 1] = __builtin_bit_cast(uint32_t,
                                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.f, true));
-    }
-    return r;
-}
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8_pk(u32x2 w) {
-    u32x4 r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        r[2 * h] = __builtin_bit_cast(uint32_t,
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, false));
-        r[2 * h + 1] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, true));
     }
     return r;
 }
@@ -245,7 +235,7 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
         u32x4 kw, vw;
         uint32_t nfbits = 0;  // exact walk: element e of the chunk is non-finite
         if constexpr (FP8) {
-            kw = e4m3x8_to_bf16x8_pk(st.k[ps]);
+            kw = e4m3x8_to_bf16x8(st.k[ps]);
             if constexpr (F16) {
                 vw = e4m3x8_to_f16x8(st.v[ps]);
             } else {
@@ -260,7 +250,7 @@ __device__ __forceinline__ void stage_store(PrefillSmem<D> &sm, int buf,
                     nfbits |= (((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) |
                                ((t >> 28) & 8u)) << (4 * h);
                 }
-                vw = e4m3x8_to_bf16x8_pk(c);
+                vw = e4m3x8_to_bf16x8(c);
             }
         } else {
             kw = st.k[ps];
