@@ -530,6 +530,44 @@ pa_status pa_batch_append_tokens(pa_allocator *a, int32_t num_seqs,
 
 pa_status pa_prefix_cache_stats(const pa_allocator *a, pa_prefix_stats_t *out);
 
+/* Host tier of the prefix cache ([VI] §2.1: cold blocks move to CPU memory
+ * under an LRU policy).  Uses the swap space's host pool (set with
+ * pa_allocator_set_swap_space), sharing its free host blocks with swapping.
+ *
+ * Offload: the oldest released registered blocks (the LRU queue, oldest
+ * first; queued blocks that lost their key are passed over), up to
+ * max_blocks and while host blocks are free, move to host blocks with their
+ * keys; their device blocks become free.  pairs_out [cap][2] host gets
+ * (device block, host block) per move, *n_pairs their count: copy them
+ * device -> host (pa_swap_blocks) before any later cache write or block
+ * copy on the device pool, i.e. enqueue the copy first on the same stream.
+ * Since blocks are queued children first, a host entry's registered
+ * descendants are on the host too. */
+pa_status pa_prefix_cache_offload(pa_allocator *a, int32_t max_blocks, int32_t *pairs_out,
+                                  int32_t cap, int32_t *n_pairs);
+
+/* pa_seq_create_prefix that also reuses host entries: after the prompt's
+ * chain of device hits, each following hit on a host entry takes a free
+ * device block (the entry moves back into it, keeping its key, and its host
+ * block returns to the host stack) while one is free -- the device hits are
+ * held first, so taking blocks never evicts them -- and while pairs_out
+ * [cap][2] has room.  pairs_out gets (host block, device block) per reload,
+ * *n_pairs their count: copy them host -> device (pa_swap_blocks) before the
+ * sequence is decoded.  pa_seq_create_prefix itself stops its chain at a
+ * host entry.  Errors as pa_seq_create_prefix. */
+pa_status pa_seq_create_prefix_ex(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                                  int32_t n_tokens, int32_t max_cached_tokens,
+                                  int32_t *n_cached, int32_t *pairs_out, int32_t cap,
+                                  int32_t *n_pairs);
+
+typedef struct {
+    int32_t host_cached_blocks; /* registered entries on the host now */
+    int64_t offloaded_blocks;   /* moved to the host so far */
+    int64_t reloaded_blocks;    /* brought back by a prompt's hit so far */
+} pa_prefix_host_stats_t;
+
+pa_status pa_prefix_host_stats(const pa_allocator *a, pa_prefix_host_stats_t *out);
+
 /* ------------------------------------------------------------------------ */
 /* Swap space                                                                 */
 /* ------------------------------------------------------------------------ */
@@ -548,7 +586,8 @@ typedef struct {
     int64_t swap_in_blocks;  /* blocks moved in so far */
 } pa_swap_stats_t;
 
-/* Size the host pool.  INVALID_ARG while any sequence is swapped out. */
+/* Size the host pool.  INVALID_ARG while any sequence is swapped out or
+ * any prefix-cache entry is on the host. */
 pa_status pa_allocator_set_swap_space(pa_allocator *a, int32_t num_host_blocks);
 
 /* Swap a resident sequence out.  Every table entry j, in order, gets a host

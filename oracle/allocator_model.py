@@ -77,6 +77,28 @@ cold blocks migrate to CPU memory; [VI] §5, a CPU swap space).  Reading taken:
   * All or nothing: not enough host (or device) blocks raises OutOfBlocks
     with no change.  A swapped sequence cannot be appended to, forked or put
     in a batch table; freeing it returns its host blocks.
+
+Host tier of the prefix cache (the pages: [VI] §2.1, cold blocks migrate to
+CPU memory under an LRU policy).  Reading taken:
+  * Entries are named by nodes: device block b is node b, host block h is
+    node num_blocks + h; a key's parent is a node.
+  * ``offload(max_blocks)`` walks the LRU queue from its oldest entry and
+    moves each registered block, while host blocks are free and fewer than
+    max_blocks moved, to a host block taken from the host stack: the entry
+    keeps its key, its place among its parent's children and its children
+    (whose keys now name the host node as parent).  The device block goes on
+    the free stack.  Pairs (device block, host block) are returned for the
+    copy.  Unregistered queued blocks are passed over.
+  * ``create_prefix_ex(seq, tokens, max_cached)``: the chain of hits as in
+    ``create_prefix``, where host entries may follow device ones.  The device
+    hits are reused first (held); then each host hit, while a device block is
+    free (counting the free stack and the queue after those holds) takes a
+    block with ``_take`` and the entry moves back into it, its host block
+    pushed on the host stack; pairs (host block, device block) are returned.
+    ``create_prefix`` stops its chain at a host entry.
+  * Dropping a subtree (eviction by ``_take``) drops its host entries too;
+    their host blocks go back on the host stack lowest id on top.
+  * ``set_swap_space`` is refused while entries are on the host.
 """
 from __future__ import annotations
 
@@ -115,6 +137,9 @@ class AllocatorModel:
         self.swapped: set[int] = set()
         self.swap_out_blocks = 0
         self.swap_in_blocks = 0
+        # host tier of the prefix cache
+        self.offloaded_blocks = 0
+        self.reloaded_blocks = 0
 
     # -- helpers -----------------------------------------------------------
     def _take(self) -> int:
@@ -123,18 +148,44 @@ class AllocatorModel:
         else:
             b = self.lru.pop(0)
             if b in self.key_of:
-                self._unregister(b)
+                dropped = []
+                self._unregister(b, dropped=dropped)
+                for node in sorted(dropped, reverse=True):  # lowest id on top
+                    self.host_stack.append(node - self.num_blocks)
         assert self.refcount[b] == 0
         self.refcount[b] = 1
         return b
 
-    def _unregister(self, b: int, parent_going: bool = False) -> None:
+    def _unregister(self, b: int, parent_going: bool = False, dropped=None) -> None:
         for c in self.children.pop(b, []):
-            self._unregister(c, parent_going=True)
+            self._unregister(c, parent_going=True, dropped=dropped)
         key = self.key_of.pop(b)
         del self.keys[key]
         if key[0] >= 0 and not parent_going:
             self.children[key[0]].remove(b)
+        if b >= self.num_blocks:
+            dropped.append(b)
+
+    def _move(self, src: int, dst: int) -> None:
+        """Entry ``src`` becomes node ``dst``; its children's keys follow."""
+        key = self.key_of.pop(src)
+        self.keys[key] = dst
+        self.key_of[dst] = key
+        if key[0] >= 0:
+            sib = self.children[key[0]]
+            sib[sib.index(src)] = dst
+        kids = self.children.pop(src, [])
+        for c in kids:
+            old = self.key_of[c]
+            del self.keys[old]
+            new = (dst, old[1])
+            self.keys[new] = c
+            self.key_of[c] = new
+        if kids:
+            self.children[dst] = kids
+
+    def num_host_cached(self) -> int:
+        return sum(1 for n in self.key_of if n >= self.num_blocks)
 
     def _num_free(self) -> int:
         return len(self.stack) + len(self.lru)
@@ -156,32 +207,78 @@ class AllocatorModel:
     def create_prefix(self, seq: int, tokens, max_cached: int) -> int:
         """New sequence starting with the cached blocks of ``tokens``;
         returns the number of cached positions."""
+        return self._create_prefix(seq, tokens, max_cached, host=False)[0]
+
+    def create_prefix_ex(self, seq: int, tokens, max_cached: int, cap: int | None = None):
+        """create_prefix that brings host-tier hits back; returns (cached
+        positions, pairs (host block, device block))."""
+        return self._create_prefix(seq, tokens, max_cached, host=True, cap=cap)
+
+    def _create_prefix(self, seq, tokens, max_cached, host, cap=None):
         if seq in self.tables:
             raise KeyError(f"sequence {seq} exists")
         bs = self.block_size
         tokens = [int(t) for t in tokens]
         self.queried_blocks += len(tokens) // bs
-        table, parent = [], -1
+        chain, parent = [], -1
         for j in range(min(len(tokens), max(max_cached, 0)) // bs):
             b = self.keys.get((parent, tuple(tokens[j * bs:(j + 1) * bs])))
-            if b is None:
+            if b is None or (b >= self.num_blocks and not host):
                 break
+            chain.append(b)
+            parent = b
+        dev = [b for b in chain if b < self.num_blocks]
+        assert chain[:len(dev)] == dev  # host entries only after device ones
+        avail = self._num_free() - sum(1 for b in dev if self.refcount[b] == 0)
+        n_host = min(len(chain) - len(dev), max(avail, 0),
+                     len(chain) if cap is None else cap) if host else 0
+        for b in dev:
             if self.refcount[b] == 0:
                 self.lru.remove(b)
             self.refcount[b] += 1
-            table.append(b)
-            parent = b
+        table, pairs = list(dev), []
+        for node in chain[len(dev):len(dev) + n_host]:
+            d = self._take()
+            self._move(node, d)
+            self.host_stack.append(node - self.num_blocks)
+            pairs.append((node - self.num_blocks, d))
+            table.append(d)
+        self.reloaded_blocks += n_host
         self.hit_blocks += len(table)
         self.tables[seq] = table
         self.lengths[seq] = len(table) * bs
         self.chain[seq] = True
         self.pending[seq] = []
-        self.parent[seq] = parent
-        return len(table) * bs
+        self.parent[seq] = table[-1] if table else -1
+        return len(table) * bs, pairs
+
+    def offload(self, max_blocks: int):
+        """Move up to max_blocks of the oldest queued registered blocks to
+        the host tier; returns pairs (device block, host block)."""
+        pairs = []
+        for b in list(self.lru):
+            if len(pairs) >= max_blocks or not self.host_stack:
+                break
+            if b not in self.key_of:
+                continue
+            h = self.host_stack.pop()
+            self._move(b, self.num_blocks + h)
+            self.lru.remove(b)
+            self.stack.append(b)
+            pairs.append((b, h))
+        self.offloaded_blocks += len(pairs)
+        return pairs
+
+    def host_stats(self) -> dict:
+        return {"host_cached_blocks": self.num_host_cached(),
+                "offloaded_blocks": self.offloaded_blocks,
+                "reloaded_blocks": self.reloaded_blocks}
 
     def set_swap_space(self, num_host_blocks: int) -> None:
         if self.swapped:
             raise ValueError("sequences are swapped out")
+        if self.num_host_cached():
+            raise ValueError("prefix-cache entries are on the host")
         self.num_host_blocks = int(num_host_blocks)
         self.host_stack = list(range(self.num_host_blocks - 1, -1, -1))
 

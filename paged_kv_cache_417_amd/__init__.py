@@ -56,7 +56,8 @@ EXPORTED = (
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
-    "pa_decode_noalloc",
+    "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
+    "pa_prefix_host_stats",
 )
 
 
@@ -101,6 +102,11 @@ class SchedStats(ctypes.Structure):
                 ("swap_preemptions", ctypes.c_int64), ("recompute_preemptions", ctypes.c_int64)]
 
 
+class PrefixHostStats(ctypes.Structure):
+    _fields_ = [("host_cached_blocks", ctypes.c_int32), ("offloaded_blocks", ctypes.c_int64),
+                ("reloaded_blocks", ctypes.c_int64)]
+
+
 class PrefixStats(ctypes.Structure):
     _fields_ = [("queried_blocks", ctypes.c_int64), ("hit_blocks", ctypes.c_int64),
                 ("cached_blocks", ctypes.c_int32), ("cached_free_blocks", ctypes.c_int32)]
@@ -141,6 +147,9 @@ def _declare(lib):
         "pa_seq_append_tokens": (st, [vp, i64, pi32, i32, pi64, pi32, i32, pi32]),
         "pa_batch_append_tokens": (st, [vp, i32, pi64, pi32, pi32, pi64, pi32, i32, pi32]),
         "pa_prefix_cache_stats": (st, [vp, ctypes.POINTER(PrefixStats)]),
+        "pa_seq_create_prefix_ex": (st, [vp, i64, pi32, i32, i32, pi32, pi32, i32, pi32]),
+        "pa_prefix_cache_offload": (st, [vp, i32, pi32, i32, pi32]),
+        "pa_prefix_host_stats": (st, [vp, ctypes.POINTER(PrefixHostStats)]),
         "pa_allocator_set_swap_space": (st, [vp, i32]),
         "pa_seq_swap_out": (st, [vp, i64, pi32, i32, pi32]),
         "pa_seq_swap_in": (st, [vp, i64, pi32, i32, pi32]),
@@ -517,6 +526,38 @@ class Allocator:
         _check(_lib.pa_seq_create_prefix(self._h, seq_id, _i32p(t) if len(t) else None, len(t),
                                          mc, ctypes.byref(n)))
         return n.value
+
+    def create_prefix_ex(self, seq_id: int, tokens, max_cached_tokens=None):
+        """create_prefix that also brings the prompt's host-tier hits back;
+        returns (positions covered, pairs int32 [k][2] (host block, device
+        block) to copy host -> device before decoding)."""
+        np = self._np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        mc = len(t) if max_cached_tokens is None else int(max_cached_tokens)
+        cap = max(len(t) // self.block_size, 1)
+        pairs = np.zeros((cap, 2), dtype=np.int32)
+        n, k = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(_lib.pa_seq_create_prefix_ex(self._h, seq_id, t.ctypes.data if len(t) else None,
+                                            len(t), mc, ctypes.byref(n), pairs.ctypes.data,
+                                            cap, ctypes.byref(k)))
+        return n.value, pairs[:k.value].copy()
+
+    def offload(self, max_blocks: int):
+        """Move up to max_blocks of the oldest released prefix-cache blocks
+        to the host tier; returns pairs int32 [k][2] (device block, host
+        block) to copy device -> host before the device pool is written."""
+        np = self._np
+        cap = max(int(max_blocks), 1)
+        pairs = np.zeros((cap, 2), dtype=np.int32)
+        k = ctypes.c_int32(0)
+        _check(_lib.pa_prefix_cache_offload(self._h, int(max_blocks), pairs.ctypes.data, cap,
+                                            ctypes.byref(k)))
+        return pairs[:k.value].copy()
+
+    def host_stats(self) -> dict:
+        st = PrefixHostStats()
+        _check(_lib.pa_prefix_host_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in PrefixHostStats._fields_}
 
     def append_tokens(self, seq_id: int, tokens):
         """Append positions with their token ids (full blocks get registered).

@@ -35,7 +35,19 @@
 // releases its device blocks as pa_seq_free does; swapping in takes fresh
 // device blocks and returns the host ones.  A swapped sequence's table holds
 // host block ids.
+//
+// Host tier of the prefix cache.  Registered entries are named by node ids:
+// device block b is node b, host block h is node num_blocks + h, and a key's
+// parent is a node id.  pa_prefix_cache_offload moves the oldest queued
+// registered blocks to free host blocks (their device blocks become free);
+// an entry keeps its key across the move, and its children's keys follow
+// it.  Queued descendants are older than their ancestors, so a host entry's
+// registered descendants are all on the host too.  pa_seq_create_prefix_ex
+// brings host entries that a prompt hits back into fresh device blocks.
+// Evicting a device entry drops its subtree, host entries included, whose
+// host blocks go back to the host stack lowest id on top.
 #include <algorithm>
+#include <functional>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -108,20 +120,42 @@ struct pa_allocator {
     std::vector<int32_t> host_stack;  // top = back
     int32_t num_swapped = 0;
     int64_t swap_out_blocks = 0, swap_in_blocks = 0;
+    // host tier of the prefix cache
+    int32_t num_host_cached = 0;
+    int64_t offloaded_blocks = 0, reloaded_blocks = 0;
+    std::vector<int32_t> dropped_host;  // scratch of unregister_tree
 
     bool cache_ready() const { return !registered.empty(); }
-    // Per-block prefix-cache arrays, sized on first use.
+    int32_t num_nodes() const { return num_blocks + num_host_blocks; }
+    // Per-node prefix-cache arrays (device and host blocks) and per-block
+    // queue arrays, sized on first use.
     void init_cache() {
         if (cache_ready()) return;
-        registered.assign(num_blocks, 0);
-        key_parent.assign(num_blocks, -1);
-        key_tokens.assign((size_t)num_blocks * block_size, 0);
-        key_hashes.assign(num_blocks, 0);
-        children.resize(num_blocks);
+        const size_t nn = (size_t)num_nodes();
+        registered.assign(nn, 0);
+        key_parent.assign(nn, -1);
+        key_tokens.assign(nn * block_size, 0);
+        key_hashes.assign(nn, 0);
+        children.resize(nn);
+        key_map.reserve(nn);  // re-keying never rehashes
+        dropped_host.reserve(num_host_blocks);
         lru_prev.assign(num_blocks, -1);
         lru_next.assign(num_blocks, -1);
         in_lru.assign(num_blocks, 0);
     }
+    // The node arrays after the host pool changes size (no host entries).
+    void resize_nodes() {
+        if (!cache_ready()) return;
+        const size_t nn = (size_t)num_nodes();
+        registered.resize(nn, 0);
+        key_parent.resize(nn, -1);
+        key_tokens.resize(nn * block_size, 0);
+        key_hashes.resize(nn, 0);
+        children.resize(nn);
+        key_map.reserve(nn);
+        dropped_host.reserve(num_host_blocks);
+    }
+    bool on_host(int32_t node) const { return node >= num_blocks; }
     size_t num_free() const { return free_stack.size() + lru_size; }
     void lru_push_back(int32_t b) {
         lru_prev[b] = lru_tail;
@@ -152,13 +186,15 @@ struct pa_allocator {
         return -1;
     }
     // Drops the key of b and of every registered descendant (all of them are
-    // queued: whoever holds a block holds its parent).
+    // queued or on the host: whoever holds a block holds its parent).  Host
+    // entries among them free their host blocks, lowest id on top.
     void unregister_tree(int32_t top) {
         const int32_t p = key_parent[top];
         if (p >= 0) {
             auto &sib = children[p];
             sib.erase(std::find(sib.begin(), sib.end(), top));
         }
+        dropped_host.clear();
         std::vector<int32_t> todo{top};
         while (!todo.empty()) {
             const int32_t b = todo.back();
@@ -174,7 +210,47 @@ struct pa_allocator {
             registered[b] = 0;
             key_parent[b] = -1;
             --num_registered;
+            if (on_host(b)) dropped_host.push_back(b - num_blocks);
         }
+        std::sort(dropped_host.begin(), dropped_host.end(), std::greater<int32_t>());
+        for (int32_t h : dropped_host) host_stack.push_back(h);  // capacity: the pool
+        num_host_cached -= (int32_t)dropped_host.size();
+    }
+    // Moves entry `from` to node `to` (unregistered): its key, its place in
+    // its parent's children and the map, and its children's keys (whose
+    // parent is now `to`).  Allocates nothing: the map has room for every
+    // node and map nodes are re-keyed in place.
+    void move_node(int32_t from, int32_t to) {
+        const int32_t p = key_parent[from];
+        registered[to] = 1;
+        key_parent[to] = p;
+        key_hashes[to] = key_hashes[from];
+        std::copy(key_tokens.begin() + (size_t)from * block_size,
+                  key_tokens.begin() + (size_t)(from + 1) * block_size,
+                  key_tokens.begin() + (size_t)to * block_size);
+        auto range = key_map.equal_range(key_hashes[from]);
+        for (auto it = range.first; it != range.second; ++it)
+            if (it->second == from) {
+                it->second = to;
+                break;
+            }
+        if (p >= 0) *std::find(children[p].begin(), children[p].end(), from) = to;
+        children[to].swap(children[from]);
+        for (int32_t c : children[to]) {
+            auto r = key_map.equal_range(key_hashes[c]);
+            for (auto it = r.first; it != r.second; ++it)
+                if (it->second == c) {
+                    auto nh = key_map.extract(it);
+                    key_parent[c] = to;
+                    key_hashes[c] = key_hash(to, key_tokens.data() + (size_t)c * block_size,
+                                             block_size);
+                    nh.key() = key_hashes[c];
+                    key_map.insert(std::move(nh));
+                    break;
+                }
+        }
+        registered[from] = 0;
+        key_parent[from] = -1;
     }
     // Registers the just-filled block b of s under (s.parent, s.pending);
     // a key already present, or no memory, ends the sequence's chain.
@@ -475,10 +551,19 @@ pa_status pa_batch_append_tokens(pa_allocator *a, int32_t num_seqs, const int64_
                         cow_cap, n_cow);
 }
 
-pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
-                               int32_t n_tokens, int32_t max_cached_tokens, int32_t *n_cached) {
-    const char *fn = "pa_seq_create_prefix";
-    if (!a || !n_cached || n_tokens < 0 || (n_tokens > 0 && !tokens))
+}  // extern "C"
+
+namespace {
+
+// Shared body of pa_seq_create_prefix (host == false: a host entry ends the
+// chain) and pa_seq_create_prefix_ex (host entries are brought back into
+// fresh device blocks, pairs (host block, device block) out).
+pa_status create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                        int32_t n_tokens, int32_t max_cached_tokens, int32_t *n_cached,
+                        bool host, int32_t *pairs_out, int32_t cap, int32_t *n_pairs) {
+    const char *fn = host ? "pa_seq_create_prefix_ex" : "pa_seq_create_prefix";
+    if (!a || !n_cached || n_tokens < 0 || (n_tokens > 0 && !tokens) ||
+        (host && (!n_pairs || cap < 0 || (cap > 0 && !pairs_out))))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
     if (a->seqs.count(seq_id))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: sequence %lld exists", fn, (long long)seq_id);
@@ -486,25 +571,41 @@ pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *t
     const int32_t full = n_tokens / bs;
     const int32_t limit = std::min(n_tokens, std::max(max_cached_tokens, 0)) / bs;
     std::vector<int32_t> hits;
+    int32_t n_dev = 0, n_host = 0;
     try {
         a->init_cache();
+        // The chain: device entries first; once an entry is on the host, so
+        // are all the rest (a host entry's descendants are on the host).
         int32_t parent = -1;
         for (int32_t j = 0; j < limit; ++j) {
             const int32_t b = a->lookup(parent, tokens + (int64_t)j * bs);
-            if (b < 0) break;
+            if (b < 0 || (a->on_host(b) && !host)) break;
             hits.push_back(b);
             parent = b;
         }
+        // Device hits with no holder leave the free count once reused; each
+        // host hit then needs a free device block (and a pair slot).
+        int64_t avail = (int64_t)a->num_free();
+        for (int32_t b : hits) {
+            if (a->on_host(b)) break;
+            ++n_dev;
+            if (a->refcount[b] == 0) --avail;
+        }
+        n_host = (int32_t)std::min<int64_t>({(int64_t)hits.size() - n_dev, std::max<int64_t>(avail, 0),
+                                             (int64_t)cap});
+        if (!host) n_host = 0;
+        hits.resize(n_dev + n_host);
         Sequence s;
         s.table = hits;
         s.length = (int32_t)hits.size() * bs;
-        s.parent = parent;
         s.pending.reserve(bs);
         a->seqs.emplace(seq_id, std::move(s));
     } catch (...) {
         return pa::fail(PA_ERR_INVALID_ARG, "%s: out of host memory", fn);
     }
-    for (int32_t b : hits) {
+    Sequence &s = a->seqs.find(seq_id)->second;
+    for (int32_t j = 0; j < n_dev; ++j) {
+        const int32_t b = hits[j];
         if (a->refcount[b] == 0) {
             a->lru_remove(b);
             a->refcount[b] = 1;
@@ -512,9 +613,78 @@ pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *t
             a->add_ref(b);
         }
     }
+    // Every device hit is held now, so taking a block cannot evict one of
+    // them or an ancestor of the host hits.
+    for (int32_t j = n_dev; j < n_dev + n_host; ++j) {
+        const int32_t node = hits[j];
+        const int32_t d = a->take();
+        a->move_node(node, d);
+        a->host_stack.push_back(node - a->num_blocks);  // capacity: the pool
+        pairs_out[2 * (j - n_dev)] = node - a->num_blocks;
+        pairs_out[2 * (j - n_dev) + 1] = d;
+        s.table[j] = d;
+    }
+    a->num_host_cached -= n_host;
+    a->reloaded_blocks += n_host;
+    s.parent = s.table.empty() ? -1 : s.table.back();
     a->queried_blocks += full;
-    a->hit_blocks += (int64_t)hits.size();
-    *n_cached = (int32_t)hits.size() * bs;
+    a->hit_blocks += (int64_t)s.table.size();
+    *n_cached = (int32_t)s.table.size() * bs;
+    if (host) *n_pairs = n_host;
+    return pa::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_seq_create_prefix(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                               int32_t n_tokens, int32_t max_cached_tokens, int32_t *n_cached) {
+    return create_prefix(a, seq_id, tokens, n_tokens, max_cached_tokens, n_cached, false,
+                         nullptr, 0, nullptr);
+}
+
+pa_status pa_seq_create_prefix_ex(pa_allocator *a, int64_t seq_id, const int32_t *tokens,
+                                  int32_t n_tokens, int32_t max_cached_tokens, int32_t *n_cached,
+                                  int32_t *pairs_out, int32_t cap, int32_t *n_pairs) {
+    return create_prefix(a, seq_id, tokens, n_tokens, max_cached_tokens, n_cached, true,
+                         pairs_out, cap, n_pairs);
+}
+
+pa_status pa_prefix_cache_offload(pa_allocator *a, int32_t max_blocks, int32_t *pairs_out,
+                                  int32_t cap, int32_t *n_pairs) {
+    const char *fn = "pa_prefix_cache_offload";
+    if (!a || !n_pairs || max_blocks < 0 || cap < 0 || (cap > 0 && !pairs_out))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    int32_t n = 0;
+    const int32_t limit = std::min(max_blocks, cap);
+    if (a->cache_ready()) {
+        for (int32_t b = a->lru_head; b >= 0 && n < limit && !a->host_stack.empty();) {
+            const int32_t next = a->lru_next[b];
+            if (a->registered[b]) {
+                const int32_t h = a->host_stack.back();
+                a->host_stack.pop_back();
+                a->move_node(b, a->num_blocks + h);
+                a->lru_remove(b);
+                a->free_stack.push_back(b);  // capacity is num_blocks
+                pairs_out[2 * n] = b;
+                pairs_out[2 * n + 1] = h;
+                ++n;
+            }
+            b = next;
+        }
+    }
+    a->num_host_cached += n;
+    a->offloaded_blocks += n;
+    *n_pairs = n;
+    return pa::ok();
+}
+
+pa_status pa_prefix_host_stats(const pa_allocator *a, pa_prefix_host_stats_t *out) {
+    if (!a || !out) return pa::fail(PA_ERR_INVALID_ARG, "pa_prefix_host_stats: NULL argument");
+    out->host_cached_blocks = a->num_host_cached;
+    out->offloaded_blocks = a->offloaded_blocks;
+    out->reloaded_blocks = a->reloaded_blocks;
     return pa::ok();
 }
 
@@ -658,14 +828,20 @@ pa_status pa_allocator_set_swap_space(pa_allocator *a, int32_t num_host_blocks) 
     if (a->num_swapped > 0)
         return pa::fail(PA_ERR_INVALID_ARG, "%s: %d sequences are swapped out", fn,
                         a->num_swapped);
+    if (a->num_host_cached > 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: %d prefix-cache blocks are on the host", fn,
+                        a->num_host_cached);
+    const int32_t old_n = a->num_host_blocks;
     try {
         std::vector<int32_t> st(num_host_blocks);
         for (int32_t i = 0; i < num_host_blocks; ++i) st[i] = num_host_blocks - 1 - i;
+        a->num_host_blocks = num_host_blocks;
+        a->resize_nodes();
         a->host_stack.swap(st);
     } catch (...) {
+        a->num_host_blocks = old_n;
         return pa::fail(PA_ERR_INVALID_ARG, "%s: out of host memory", fn);
     }
-    a->num_host_blocks = num_host_blocks;
     return pa::ok();
 }
 

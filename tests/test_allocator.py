@@ -265,6 +265,7 @@ def same_swap_state(a: pa.Allocator, m: AllocatorModel):
     assert a.stats() == m.stats()
     assert a.prefix_stats() == m.prefix_stats()
     assert a.swap_stats() == m.swap_stats()
+    assert a.host_stats() == m.host_stats()
     for b in range(m.num_blocks):
         assert a.refcount(b) == m.refcount[b]
     for sid, table in m.tables.items():
@@ -379,3 +380,111 @@ def test_swap_space_cannot_shrink_under_swapped_sequences():
     a.swap_in(1)
     a.set_swap_space(8)
     assert a.swap_stats()["num_host_free"] == 8
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_host_tier_operations_match_model(seed):
+    """The prefix cache's host tier: prompts drawn from a few shared stems
+    admitted with and without reuse of host entries, token appends, frees,
+    offloads of released cached blocks (the queue's oldest first) and, now
+    and then, swap-outs and swap-ins competing for the host pool, on small
+    pools so that offloaded entries are evicted with their ancestors: every
+    pair, slot, table, refcount and counter agrees with the model."""
+    rng = np.random.default_rng(300 + seed)
+    nb, bs, nh = int(rng.choice([12, 24])), int(rng.choice([1, 2, 4])), int(rng.choice([6, 16]))
+    order = rng.permutation(nb)
+    a = pa.Allocator(nb, bs, free_order=order)
+    m = AllocatorModel(nb, bs, free_order=order)
+    a.set_swap_space(nh)
+    m.set_swap_space(nh)
+    stems = [list(rng.integers(0, 3, int(rng.integers(bs, 4 * bs + 2)))) for _ in range(3)]
+    live, next_id = [], 1
+    for step in range(600):
+        op = int(rng.integers(9))
+        resident = [s for s in live if s not in m.swapped]
+        swapped = [s for s in live if s in m.swapped]
+        if op <= 2 or not live:
+            toks = [int(x) for x in stems[int(rng.integers(3))]]
+            toks += [int(x) for x in rng.integers(0, 3, int(rng.integers(1, bs + 2)))]
+            mc = len(toks) - 1
+            if op == 0:
+                assert a.create_prefix(next_id, toks, mc) == m.create_prefix(next_id, toks, mc)
+            else:
+                n_a, p_a = a.create_prefix_ex(next_id, toks, mc)
+                n_m, p_m = m.create_prefix_ex(next_id, toks, mc)
+                assert n_a == n_m and [tuple(x) for x in p_a] == p_m
+            live.append(next_id)
+            rest = toks[m.lengths[next_id]:]
+            try:
+                want = m.append(next_id, len(rest), tokens=rest)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append_tokens(next_id, rest)
+            else:
+                s_, p_ = a.append_tokens(next_id, rest)
+                assert list(s_) == want[0] and [tuple(x) for x in p_] == want[1]
+            next_id += 1
+        elif op in (3, 4):
+            k = int(rng.integers(0, 5))
+            assert [tuple(x) for x in a.offload(k)] == m.offload(k)
+        elif op == 5 and resident:
+            sid = resident[int(rng.integers(len(resident)))]
+            try:
+                want = m.swap_out(sid)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.swap_out(sid)
+            else:
+                assert [tuple(x) for x in a.swap_out(sid)] == want
+        elif op == 6 and swapped:
+            sid = swapped[int(rng.integers(len(swapped)))]
+            try:
+                want = m.swap_in(sid)
+            except OutOfBlocks:
+                want = None
+            if want is None:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.swap_in(sid)
+            else:
+                assert [tuple(x) for x in a.swap_in(sid)] == want
+        elif live:
+            sid = live.pop(int(rng.integers(len(live))))
+            a.free(sid)
+            m.free(sid)
+        if step % 20 == 0:
+            same_swap_state(a, m)
+    same_swap_state(a, m)
+    assert m.offloaded_blocks > 0 and m.reloaded_blocks > 0
+
+
+def test_host_tier_by_hand():
+    """Block size 2, two-block prompt [1 2 | 3 4 | 5]: released, its blocks
+    wait in the queue (the deeper first); one offload moves that deeper
+    block to host block 0 and frees its device block.  A plain create_prefix
+    stops at the host entry; create_prefix_ex brings it back into a fresh
+    device block with the pair (host 0, that block); swap space cannot be
+    resized while an entry is on the host."""
+    a = pa.Allocator(6, 2)  # hands out blocks 0, 1, 2, ...
+    a.set_swap_space(4)
+    toks = [1, 2, 3, 4, 5]
+    assert a.create_prefix(1, toks, 4) == 0
+    a.append_tokens(1, toks)
+    assert list(a.block_table(1)) == [0, 1, 2]
+    a.free(1)  # 2 (unregistered) -> free stack; 1 then 0 -> queue
+    assert a.prefix_stats()["cached_free_blocks"] == 2
+    assert [tuple(x) for x in a.offload(1)] == [(1, 0)]
+    assert a.host_stats() == {"host_cached_blocks": 1, "offloaded_blocks": 1,
+                              "reloaded_blocks": 0}
+    with pytest.raises(pa.PAError):
+        a.set_swap_space(8)
+    assert a.create_prefix(2, toks, 4) == 2  # block 0 only: the chain stops at the host
+    n, pairs = a.create_prefix_ex(3, toks, 4)
+    d = int(pairs[0][1])
+    assert n == 4 and [tuple(x) for x in pairs] == [(0, d)]
+    assert list(a.block_table(3)) == [0, d] and a.refcount(0) == 2
+    assert a.host_stats()["host_cached_blocks"] == 0 and a.swap_stats()["num_host_free"] == 4
+    a.set_swap_space(8)

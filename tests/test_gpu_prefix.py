@@ -473,3 +473,79 @@ def test_grouped_decode_malformed_groups_decode_alone(pa, bad):
     say(f"case grouped decode, malformed groups: {bad}")
     ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), ps, 4)
     assert torch.isfinite(ref).all() and torch.equal(got, ref)
+
+
+def test_prefix_cache_host_tier_round_trip(pa):
+    """Released prompt blocks are offloaded to the host tier (pa_swap_blocks
+    device -> host with the allocator's pairs), their device blocks are
+    reused and overwritten by another request, then a new request with the
+    same prompt reloads them (pa_seq_create_prefix_ex, host -> device
+    copies) and decodes bit for bit like the same prompt written afresh; its
+    rows match the fp64 oracle."""
+    sh = wl.DecodeShape("host_tier", 2, 8, 4, 64, 16, 96, "bf16", 78)
+    dev = "cuda"
+    hkv, d, bs, nb, nh = sh.num_kv_heads, sh.head_dim, sh.block_size, sh.num_blocks, 48
+    gen = wl.make_generator(sh.seed, dev)
+    rng = np.random.default_rng(sh.seed)
+    prompt = rng.integers(0, 1000, 40 * bs + 7).astype(np.int32)
+    kp = wl.randn((len(prompt), hkv, d), torch.bfloat16, gen, dev)
+    vp = wl.randn((len(prompt), hkv, d), torch.bfloat16, gen, dev)
+    kshape, vshape = pa.kv_cache_shapes(nb, hkv, bs, d)
+    k_pool = torch.full(kshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(vshape, float("nan"), dtype=torch.bfloat16, device=dev)
+    hk, hv = pa.kv_cache_shapes(nh, hkv, bs, d)
+    k_host = torch.empty(hk, dtype=torch.bfloat16, pin_memory=True)
+    v_host = torch.empty(hv, dtype=torch.bfloat16, pin_memory=True)
+    alloc = pa.Allocator(nb, bs, free_order=rng.permutation(nb))
+    alloc.set_swap_space(nh)
+
+    def write(seq, lo):
+        slots, pairs = alloc.append_tokens(seq, prompt[lo:])
+        assert len(pairs) == 0
+        pa.pa_cache_write(kp[lo:].contiguous(), vp[lo:].contiguous(), k_pool, v_pool,
+                          torch.as_tensor(slots, device=dev))
+
+    assert alloc.create_prefix(1, prompt, len(prompt) - 1) == 0
+    write(1, 0)
+    alloc.free(1)
+    out_pairs = alloc.offload(64)
+    assert len(out_pairs) == len(prompt) // bs  # every full block of the prompt
+    pa.pa_swap_blocks(k_pool, v_pool, k_host, v_host, torch.as_tensor(out_pairs, device=dev))
+    # another request takes the freed blocks and overwrites them
+    alloc.create(2)
+    slots, _ = alloc.append(2, nb * bs - 8 * bs)
+    junk = torch.full((len(slots), hkv, d), 3.0, dtype=torch.bfloat16, device=dev)
+    pa.pa_cache_write(junk, junk, k_pool, v_pool, torch.as_tensor(slots, device=dev))
+    alloc.free(2)
+    # the prompt again: every full block comes back from the host
+    n, in_pairs = alloc.create_prefix_ex(3, prompt, len(prompt) - 1)
+    assert n == len(prompt) // bs * bs and len(in_pairs) == len(prompt) // bs
+    pa.pa_swap_blocks(k_host, v_host, k_pool, v_pool, torch.as_tensor(in_pairs, device=dev))
+    write(3, n)
+    st = alloc.host_stats()
+    say(f"case prefix host tier: offloaded {st['offloaded_blocks']}, reloaded "
+        f"{st['reloaded_blocks']} blocks")
+    assert st["reloaded_blocks"] == len(in_pairs) and st["host_cached_blocks"] == 0
+    # the same prompt written in full into a second pool
+    k2 = torch.full_like(k_pool, float("nan"))
+    v2 = torch.full_like(v_pool, float("nan"))
+    fresh = pa.Allocator(nb, bs)
+    fresh.create(3)
+    fs, _ = fresh.append(3, len(prompt))
+    pa.pa_cache_write(kp, vp, k2, v2, torch.as_tensor(fs, device=dev))
+    q = wl.randn((1, sh.num_q_heads, d), torch.bfloat16, gen, dev)
+    outs = []
+    for al, kk, vv in ((alloc, k_pool, v_pool), (fresh, k2, v2)):
+        t, lens = al.batch_tables([3], 48, nb - 1)
+        o = torch.empty((1, sh.num_q_heads, d), device=dev)
+        ws = pa.decode_workspace(1, sh.num_q_heads, hkv, d, bs, int(lens[0]), 64, dev)
+        pa.pa_decode(o, q, kk, vv, torch.as_tensor(t, device=dev),
+                     torch.as_tensor(lens, device=dev), sh.scale, int(lens[0]), 64, ws)
+        outs.append((o, t, lens))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0][0]).all() and torch.equal(outs[0][0], outs[1][0])
+    ref = oracle_decode_all(q, k_pool, v_pool, outs[0][1], outs[0][2], bs, sh.scale, pa.K_AXES,
+                            pa.V_AXES)
+    err = float(np.abs(outs[0][0].double().cpu().numpy() - ref).max())
+    say(f"  reloaded == fresh bit for bit; oracle err {err:.3e}")
+    assert err <= TOL
