@@ -659,7 +659,20 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_block
  * The step writing a prompt's last chunk yields the request's first token,
  * each decode one more; at max_new tokens the request finishes and its
  * blocks are freed (pa_sched_complete).  Request ids are the allocator's
- * sequence ids.  Host memory only; not thread-safe. */
+ * sequence ids.  Host memory only; not thread-safe.
+ *
+ * Parallel sampling ([VE] §3.1: the outputs drawn from one prompt share its
+ * KV blocks, copy-on-write where they diverge): a request added with
+ * pa_sched_add_samples asks for n samples.  It runs as one sequence (its own
+ * id) until its prompt is written; pa_sched_complete of that step forks
+ * samples 2..n from it (pa_seq_fork), each of which already holds its first
+ * token.  From then on the request's n sequences decode in the same steps,
+ * adjacent in decode_ids (the request's id first, then its sample ids in the
+ * order given), and are preempted, swapped back and finished together;
+ * their first appends into the shared partial block come with copy-on-write
+ * pairs.  max_num_seqs counts sequences, and a request holds n of them from
+ * admission on.  Such a decode batch is grouped for pa_decode_grouped by
+ * giving each request's run one group id (pa_decode_groups). */
 
 typedef struct pa_sched pa_sched;
 
@@ -671,12 +684,14 @@ typedef struct pa_sched pa_sched;
  * decode entry, then each prefill chunk's positions in order), then run the
  * prefill chunks and the decode batch. */
 typedef struct {
-    int64_t *decode_ids;      /* [cap_seqs] requests decoding this step */
+    int64_t *decode_ids;      /* [cap_seqs] sequences decoding this step */
     int32_t *decode_lens;     /* [cap_seqs] their context length after the append */
     int64_t *prefill_ids;     /* [cap_seqs] requests writing a prompt chunk */
     int32_t *prefill_starts;  /* [cap_seqs] first position of the chunk */
     int32_t *prefill_lens;    /* [cap_seqs] positions in the chunk */
-    int64_t *preempted_ids;   /* [cap_seqs] sent back to start over */
+    int64_t *preempted_ids;   /* [cap_seqs] requests sent back to start over (with
+                                 samples: all of them are dropped, to be forked
+                                 again) */
     int32_t cap_seqs;         /* >= max_num_seqs */
     int64_t *slots;           /* [cap_slots] slots of the step's new positions */
     int32_t cap_slots;        /* >= max_batched_tokens */
@@ -684,17 +699,23 @@ typedef struct {
     int32_t cap_cow;          /* >= max_num_seqs */
     int32_t *swap_out_pairs;  /* [cap_swap_pairs][2] (device block, host block) */
     int32_t *swap_in_pairs;   /* [cap_swap_pairs][2] (host block, device block) */
-    int32_t cap_swap_pairs;   /* >= the allocator's num_blocks */
+    int32_t cap_swap_pairs;   /* >= the allocator's num_blocks and its number of
+                                 host blocks (forked samples swap out a private
+                                 copy each of the blocks they share) */
     int32_t n_decode, n_prefill, n_preempted, n_slots, n_cow, n_swap_out, n_swap_in;
 } pa_sched_plan_t;
 
 typedef struct {
-    int32_t waiting, running, swapped;
-    int64_t finished, swap_preemptions, recompute_preemptions;
+    int32_t waiting, running, swapped;  /* requests */
+    int32_t running_seqs;               /* sequences the running requests hold */
+    int64_t finished, swap_preemptions, recompute_preemptions;  /* requests */
+    int64_t forked_samples;             /* sample sequences forked so far */
 } pa_sched_stats_t;
 
 /* The scheduler borrows the allocator (which must outlive it, and whose swap
- * space, if any, enables preemption by swap). */
+ * space, if any, enables preemption by swap).  INVALID_ARG unless all three
+ * sizes are >= 1 and max_batched_tokens >= max_num_seqs (a step may decode
+ * one position for each of max_num_seqs sequences). */
 pa_status pa_sched_create(pa_allocator *a, int32_t max_num_seqs, int32_t max_batched_tokens,
                           int32_t max_prefill_chunk, pa_sched **out);
 void pa_sched_destroy(pa_sched *s);
@@ -702,11 +723,24 @@ void pa_sched_destroy(pa_sched *s);
  * generate; tokens [n_prompt] (host) or NULL (no prefix-cache reuse). */
 pa_status pa_sched_add(pa_sched *s, int64_t id, int32_t n_prompt, int32_t max_new,
                        const int32_t *tokens);
+/* Queue a request for num_samples >= 1 parallel samples (see above), each
+ * generating max_new tokens; sample_ids [num_samples - 1] (host, NULL when
+ * num_samples is 1) are the sequence ids of samples 2..n.  INVALID_ARG if
+ * num_samples > max_num_seqs (it could never be admitted) or an id repeats
+ * or is taken by an earlier request or sample of this scheduler.
+ * pa_sched_add is this call with one sample. */
+pa_status pa_sched_add_samples(pa_sched *s, int64_t id, int32_t n_prompt, int32_t max_new,
+                               const int32_t *tokens, const int64_t *sample_ids,
+                               int32_t num_samples);
 /* Plan the next step (see above).  INVALID_ARG if the previous plan was not
  * completed or the plan arrays are short; the allocator then is unchanged. */
 pa_status pa_sched_step(pa_sched *s, pa_sched_plan_t *plan);
-/* The planned step ran: count its tokens and free finished requests, whose
- * ids go to finished_ids [cap >= running requests]. */
+/* The planned step ran: fork the samples of requests whose prompt it wrote,
+ * count its tokens and free finished requests, whose sequence ids (the
+ * request's, then its samples') go to finished_ids [cap >= running_seqs].
+ * A failed fork (a sample id the caller created in the allocator, host
+ * memory) undoes this call's forks, returns its status and leaves the plan
+ * pending. */
 pa_status pa_sched_complete(pa_sched *s, int64_t *finished_ids, int32_t cap,
                             int32_t *n_finished);
 pa_status pa_sched_stats(const pa_sched *s, pa_sched_stats_t *out);

@@ -57,7 +57,7 @@ EXPORTED = (
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
     "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
-    "pa_prefix_host_stats",
+    "pa_prefix_host_stats", "pa_sched_add_samples",
 )
 
 
@@ -98,8 +98,9 @@ class SchedPlan(ctypes.Structure):
 
 class SchedStats(ctypes.Structure):
     _fields_ = [("waiting", ctypes.c_int32), ("running", ctypes.c_int32),
-                ("swapped", ctypes.c_int32), ("finished", ctypes.c_int64),
-                ("swap_preemptions", ctypes.c_int64), ("recompute_preemptions", ctypes.c_int64)]
+                ("swapped", ctypes.c_int32), ("running_seqs", ctypes.c_int32),
+                ("finished", ctypes.c_int64), ("swap_preemptions", ctypes.c_int64),
+                ("recompute_preemptions", ctypes.c_int64), ("forked_samples", ctypes.c_int64)]
 
 
 class PrefixHostStats(ctypes.Structure):
@@ -162,6 +163,7 @@ def _declare(lib):
         "pa_sched_create": (st, [vp, i32, i32, i32, ctypes.POINTER(vp)]),
         "pa_sched_destroy": (None, [vp]),
         "pa_sched_add": (st, [vp, i64, i32, i32, pi32]),
+        "pa_sched_add_samples": (st, [vp, i64, i32, i32, pi32, pi64, i32]),
         "pa_sched_step": (st, [vp, ctypes.POINTER(SchedPlan)]),
         "pa_sched_complete": (st, [vp, pi64, i32, pi32]),
         "pa_sched_stats": (st, [vp, ctypes.POINTER(SchedStats)]),
@@ -460,6 +462,7 @@ class Allocator:
         self._np = np
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
+        self.num_host_blocks = 0
         h = ctypes.c_void_p()
         fo = None
         if free_order is not None:
@@ -591,6 +594,7 @@ class Allocator:
 
     def set_swap_space(self, num_host_blocks: int):
         _check(_lib.pa_allocator_set_swap_space(self._h, num_host_blocks))
+        self.num_host_blocks = int(num_host_blocks)
 
     def _swap(self, fn, seq_id):
         np = self._np
@@ -686,8 +690,17 @@ class Scheduler:
             ptype = ctypes.c_int64 if v.dtype == np.int64 else ctypes.c_int32
             setattr(self._plan, k, v.ctypes.data_as(ctypes.POINTER(ptype)))
         self._plan.cap_seqs, self._plan.cap_slots, self._plan.cap_cow = n, t, n
-        self._plan.cap_swap_pairs = nb
+        self._swap_cap(max(nb, alloc.num_host_blocks))
         self._fin = np.zeros(n, np.int64)
+
+    def _swap_cap(self, cap):
+        """(Re)size the swap pair arrays: a step needs room for the larger of
+        the device and host pool sizes."""
+        np = self._np
+        for k in ("swap_out_pairs", "swap_in_pairs"):
+            self._a[k] = np.zeros((cap, 2), np.int32)
+            setattr(self._plan, k, self._a[k].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        self._plan.cap_swap_pairs = cap
 
     def close(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -697,16 +710,22 @@ class Scheduler:
     def __del__(self):
         self.close()
 
-    def add(self, rid: int, n_prompt: int, max_new: int, tokens=None):
+    def add(self, rid: int, n_prompt: int, max_new: int, tokens=None, samples=()):
+        """Queue a request; samples lists the sequence ids of its parallel
+        samples 2..n (pa_sched_add_samples), none for one sample."""
         np = self._np
         t = None
         if tokens is not None:
             self._tok = np.ascontiguousarray(tokens, dtype=np.int32)
             t = _i32p(self._tok)
-        _check(_lib.pa_sched_add(self._h, rid, n_prompt, max_new, t))
+        ids = np.ascontiguousarray(list(samples), dtype=np.int64)
+        _check(_lib.pa_sched_add_samples(self._h, rid, n_prompt, max_new, t,
+                                         _i64p(ids) if len(ids) else None, 1 + len(ids)))
 
     def step(self) -> dict:
         """Plan one step; returns copies of the filled plan arrays."""
+        if self._plan.cap_swap_pairs < self.alloc.num_host_blocks:
+            self._swap_cap(self.alloc.num_host_blocks)
         _check(_lib.pa_sched_step(self._h, ctypes.byref(self._plan)))
         p, a = self._plan, self._a
         return {"decode": list(zip(a["decode_ids"][:p.n_decode].tolist(),

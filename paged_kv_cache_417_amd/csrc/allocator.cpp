@@ -361,6 +361,8 @@ struct pa_allocator {
     }
 };
 
+int32_t pa::block_size(const pa_allocator *a) { return a->block_size; }
+
 extern "C" {
 
 pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,

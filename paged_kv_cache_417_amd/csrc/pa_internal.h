@@ -13,4 +13,7 @@ pa_status fail(pa_status st, const char *fmt, ...) __attribute__((format(printf,
 // Clear this thread's message and return PA_OK.
 pa_status ok();
 
+// The allocator's positions per block.
+int32_t block_size(const pa_allocator *a);
+
 }  // namespace pa

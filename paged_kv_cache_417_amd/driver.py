@@ -7,18 +7,27 @@ requires: swap-out copies, swap-in copies, copy-on-write copies, the cache
 write of the step's new positions, the prompt chunks (pa_prefill_chunk) and
 the decode batch (pa_decode).  There is no model: the caller supplies the K/V
 rows of every new position and the q rows of every query (``rows_fn``,
-``q_fn``, each called once per batch with a list of (request id, positions)
+``q_fn``, each called once per batch with a list of (sequence id, positions)
 and returning the rows of all entries back to back), so the loop exercises
 the whole library end to end on synthetic data.
+
+Parallel sampling (《加速 LLM 推理：深入了解 vLLM 引擎》 §3.1: the samples drawn
+from one prompt share its KV blocks): a request added with sample ids is
+forked by the scheduler once its prompt is written, and its samples decode
+side by side.  A decode batch holding such runs goes through
+pa_decode_grouped, each request's run one group (pa_decode_groups derives the
+blocks its members share), so the shared prompt blocks are read once per
+group; the result is the same as pa_decode's, bit for bit.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (Allocator, Scheduler, decode_workspace, kv_cache_shapes, pa_cache_write,
-               pa_cache_write_fp8, pa_copy_blocks, pa_decode, pa_decode_fp8, pa_prefill_chunk,
-               pa_prefill_chunk_fp8, pa_swap_blocks)
+from . import (Allocator, Scheduler, decode_groups, decode_workspace, kv_cache_shapes,
+               pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode, pa_decode_fp8,
+               pa_decode_grouped, pa_decode_grouped_fp8, pa_prefill_chunk, pa_prefill_chunk_fp8,
+               pa_swap_blocks)
 
 
 class ServingLoop:
@@ -50,11 +59,35 @@ class ServingLoop:
         self.ws = decode_workspace(max_num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                    self.max_ctx, 0, device)
         self.scale = head_dim ** -0.5
+        self.request_of = {}  # sample sequence id -> its request id
+        self.grouped_steps = 0       # decode steps that ran grouped
+        self.shared_block_reads = 0  # group-shared blocks, summed over those steps
 
-    def add(self, rid, n_prompt, max_new, tokens=None):
+    def add(self, rid, n_prompt, max_new, tokens=None, samples=()):
+        """Queue a request; samples: sequence ids of its parallel samples
+        2..n."""
         if n_prompt + max_new > self.max_ctx:
             raise ValueError("request longer than max_context_len")
-        self.sched.add(rid, n_prompt, max_new, tokens)
+        self.sched.add(rid, n_prompt, max_new, tokens, samples=samples)
+        for x in samples:
+            self.request_of[int(x)] = rid
+
+    def decode_grouping(self, seq_ids):
+        """seq_group for pa_decode_groups: each run of two or more sequences
+        of one request (the scheduler keeps them adjacent) is a group, every
+        other sequence -1; None when there is no group."""
+        owner = [self.request_of.get(x, x) for x in seq_ids]
+        seq_group = np.full(len(seq_ids), -1, dtype=np.int32)
+        g, i = 0, 0
+        while i < len(owner):
+            j = i + 1
+            while j < len(owner) and owner[j] == owner[i]:
+                j += 1
+            if j - i > 1:
+                seq_group[i:j] = g
+                g += 1
+            i = j
+        return seq_group if g else None
 
     def step(self, rows_fn, q_fn):
         """One scheduler step on the GPU.  rows_fn(entries) -> (k, v)
@@ -101,8 +134,22 @@ class ServingLoop:
             t, lens = self.alloc.batch_tables(ids, self.stride, self.pad)
             q = q_fn(dec_entries)
             dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
+            seq_group = self.decode_grouping(ids)
+            groups = None
+            if seq_group is not None:
+                off, sg, shared, largest = decode_groups(t, lens, seq_group, self.bs)
+                groups = (torch.as_tensor(off, device=dev), torch.as_tensor(sg, device=dev),
+                          torch.as_tensor(shared, device=dev), largest)
+                self.grouped_steps += 1
+                self.shared_block_reads += int(shared.sum())
             t, lens = torch.as_tensor(t, device=dev), torch.as_tensor(lens, device=dev)
-            if self.fp8:
+            if groups and self.fp8:
+                pa_decode_grouped_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
+                                      self.max_ctx, *groups, 0, self.ws, kv_reuse=True)
+            elif groups:
+                pa_decode_grouped(dec_out, q, self.k, self.v, t, lens, self.scale, self.max_ctx,
+                                  *groups, 0, self.ws, kv_reuse=True)
+            elif self.fp8:
                 pa_decode_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
                               self.max_ctx, 0, self.ws)
             else:

@@ -1,8 +1,8 @@
 """The C++ continuous-batching scheduler (behind the C ABI) against the
 Python reference model: identical plans (decode set, prompt chunks, slots,
 copy-on-write pairs, swap pairs, preemptions) and finished lists at every
-step of randomised request streams, with and without swap space and prefix
-reuse."""
+step of randomised request streams, with and without swap space, prefix
+reuse and parallel samples; a hand-worked parallel-sampling case."""
 import numpy as np
 import pytest
 
@@ -21,9 +21,23 @@ def same_plan(got: dict, want):
     assert [tuple(x) for x in got["swap_in"].tolist()] == want.swap_in
 
 
-@pytest.mark.parametrize("seed,pressure", [(k, False) for k in range(6)] +
-                         [(k, True) for k in range(6, 14)])
-def test_random_streams_plan_like_the_model(seed, pressure):
+def check_samples_adjacent(plan, model):
+    """Each request's decoding sequences form one run, its own id first and
+    its samples in order."""
+    ids = [x for x, _ in plan.decode]
+    i = 0
+    while i < len(ids):
+        r = model.reqs[ids[i]]
+        assert ids[i:i + 1 + len(r.samples)] == r.seqs()
+        i += len(r.seqs())
+
+
+@pytest.mark.parametrize("seed,pressure,samples",
+                         [(k, False, False) for k in range(6)] +
+                         [(k, True, False) for k in range(6, 14)] +
+                         [(k, False, True) for k in range(14, 20)] +
+                         [(k, True, True) for k in range(20, 28)])
+def test_random_streams_plan_like_the_model(seed, pressure, samples):
     rng = np.random.default_rng(300 + seed)
     nb, bs = int(rng.choice([24, 48, 96])), int(rng.choice([2, 4, 16]))
     host = int(rng.choice([0, 16, 64]))
@@ -53,12 +67,22 @@ def test_random_streams_plan_like_the_model(seed, pressure):
                     toks = (stems[int(rng.integers(3))] + list(rng.integers(0, 5, n)))[:max(n, 1)]
                     n = len(toks)
                 new = int(rng.integers(1, 40 if pressure else 20))
-                s.add(next_id, n, new, toks)
-                ms.add(next_id, n, new, toks)
+                extra = []
+                if samples and rng.random() < 0.5:
+                    # k samples, max_new cut so that k * ceil((n + new - 1) / bs) + 1
+                    # blocks fit the pool (the scheduler refuses more)
+                    k = int(rng.integers(2, min(4, seqs) + 1))
+                    room = (nb - 1) // k * bs - n + 1
+                    if room >= 1:
+                        new = min(new, room)
+                        extra = [10_000 + 8 * next_id + j for j in range(k - 1)]
+                s.add(next_id, n, new, toks, samples=extra)
+                ms.add(next_id, n, new, toks, samples=extra)
                 next_id += 1
         got = s.step()
         want = ms.step()
         same_plan(got, want)
+        check_samples_adjacent(want, ms)
         assert s.complete() == ms.complete(want)
         assert s.stats() == ms.stats()
         assert a.stats() == m.stats()
@@ -66,11 +90,13 @@ def test_random_streams_plan_like_the_model(seed, pressure):
             break
     assert ms.stats()["finished"] == n_req
     assert a.stats()["num_free"] == nb
+    st = ms.stats()
     if pressure:
-        st = ms.stats()
         assert st["swap_preemptions"] + st["recompute_preemptions"] > 0
         if host:
             assert st["swap_preemptions"] > 0
+    if samples:
+        assert st["forked_samples"] > 0
 
 
 def test_step_needs_complete_and_room():
@@ -85,3 +111,96 @@ def test_step_needs_complete_and_room():
         s.add(1, 3, 1)  # id exists
     with pytest.raises(pa.PAError):
         s.add(2, 0, 1)
+
+
+def test_parallel_samples_by_hand():
+    """One request, prompt of 6 positions in blocks of 4, three samples, three
+    tokens each.  Worked by hand: the prompt takes blocks 5 and 2 (the free
+    order); completing the prompt step forks samples 101 and 102, so all three
+    hold [5, 2] with block 2 half full; the first decode step appends position
+    6 for 1, 101, 102 in that order: 1 and 101 copy block 2 into the next
+    free blocks (7, then 0), 102 is then its only holder and writes in place;
+    the second decode step appends position 7 with no copy; the request's
+    three sequences then finish together."""
+    order = [5, 2, 7, 0, 1, 3, 4, 6]
+    a = pa.Allocator(8, 4, free_order=order)
+    s = pa.Scheduler(a, 4, 16, 16)
+    s.add(1, 6, 3, samples=[101, 102])
+    p = s.step()
+    assert p["prefill"] == [(1, 0, 6)] and p["decode"] == []
+    assert p["slots"].tolist() == [20, 21, 22, 23, 8, 9]
+    assert s.complete() == []
+    st = s.stats()
+    assert (st["running"], st["running_seqs"], st["forked_samples"]) == (1, 3, 2)
+    for x in (1, 101, 102):
+        assert list(a.block_table(x)) == [5, 2]
+    assert a.refcount(2) == 3
+    p = s.step()
+    assert p["decode"] == [(1, 7), (101, 7), (102, 7)]
+    assert [tuple(x) for x in p["cow"].tolist()] == [(2, 7), (2, 0)]
+    assert p["slots"].tolist() == [7 * 4 + 2, 0 * 4 + 2, 2 * 4 + 2]
+    assert [list(a.block_table(x)) for x in (1, 101, 102)] == [[5, 7], [5, 0], [5, 2]]
+    assert a.refcount(5) == 3
+    assert s.complete() == []
+    p = s.step()
+    assert p["decode"] == [(1, 8), (101, 8), (102, 8)]
+    assert p["cow"].tolist() == [] and p["slots"].tolist() == [31, 3, 11]
+    assert s.complete() == [1, 101, 102]
+    assert a.stats()["num_free"] == 8 and s.stats()["finished"] == 1
+
+
+def test_parallel_samples_count_against_max_num_seqs():
+    """A request holds all its sequences from admission: with room for 4, a
+    3-sample request leaves one place, so a second 2-sample request waits
+    while a single-sample one is admitted."""
+    a = pa.Allocator(64, 4)
+    s = pa.Scheduler(a, 4, 64, 64)
+    s.add(1, 4, 5, samples=[11, 12])
+    s.add(2, 4, 5, samples=[21])
+    s.add(3, 4, 5)
+    p = s.step()
+    assert [x[0] for x in p["prefill"]] == [1]  # 2 blocks the queue: FCFS
+    s.complete()
+    assert s.stats()["running_seqs"] == 3
+    m = AllocatorModel(64, 4)
+    ms = SchedulerModel(m, 4, 64, 64)
+    ms.add(1, 4, 5, samples=[11, 12])
+    ms.add(2, 4, 5, samples=[21])
+    ms.add(3, 4, 5)
+    assert [x[0] for x in ms.step().prefill] == [1]
+
+
+def test_parallel_sample_ids_are_checked():
+    a = pa.Allocator(16, 4)
+    s = pa.Scheduler(a, 4, 16, 16)
+    s.add(1, 4, 2, samples=[2, 3])
+    for rid, extra in [(4, [5, 5]), (4, [4]), (4, [2]), (2, []), (6, [1]), (7, [8, 9, 10, 11])]:
+        with pytest.raises(pa.PAError):
+            s.add(rid, 4, 2, samples=extra)
+    s.add(4, 4, 2, samples=[5, 6, 7])  # 4 sequences: max_num_seqs exactly
+    with pytest.raises(pa.PAError):
+        pa.Scheduler(a, 8, 4, 4)  # fewer batched tokens than sequences
+    # a request that alone might not fit the 16 blocks: 3 x ceil(21/4) + 1
+    with pytest.raises(pa.PAError):
+        s.add(8, 16, 6, samples=[9, 10])
+    s.add(8, 16, 5, samples=[9, 10])  # 3 x ceil(20/4) + 1 = 16
+    with pytest.raises(pa.PAError):
+        s.add(11, 60, 6)  # one sequence of 17 blocks
+    s.add(11, 60, 5)
+
+
+def test_fork_failure_leaves_the_plan_pending():
+    """A sample id the caller took in the allocator makes the fork fail:
+    complete() raises, undoes its forks and may be called again once the id
+    is free."""
+    a = pa.Allocator(16, 4)
+    s = pa.Scheduler(a, 4, 16, 16)
+    s.add(1, 5, 2, samples=[2, 3])
+    s.step()
+    a.create(3)
+    with pytest.raises(pa.PAError):
+        s.complete()
+    assert a.refcount(a.block_table(1)[0]) == 1  # sample 2's fork was undone
+    a.free(3)
+    assert s.complete() == []
+    assert s.stats()["forked_samples"] == 2
