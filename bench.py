@@ -476,6 +476,87 @@ def row_serving(pa, wl, torch, np, cpu_budget):
     return out
 
 
+def row_serving_samples(pa, wl, torch, np):
+    """Parallel sampling through the serving loop: 64 requests, each drawing 4
+    samples from its prompt (prompts U{1024..2048}, outputs U{64..256} per
+    sample), 7B-shaped attention (32/32 heads, head_dim 128, block 16, bf16),
+    a 16,384-block pool, at most 128 sequences (32 requests), 4,096 tokens and
+    1,024-token prompt chunks per step.  The scheduler forks each request's
+    samples once its prompt is written.  The same request stream runs twice:
+    decode batches grouped by request (pa_decode_grouped: the shared prompt
+    blocks read once per group), then one sequence at a time (pa_decode with
+    the cache-keeping policy).  Plans, and so all other work, are identical;
+    every decode call is event-timed.  A short untimed pass warms up first."""
+    from paged_kv_cache_417_amd.driver import ServingLoop
+    dev = "cuda"
+    hq = hkv = 32
+    d, bs, nb, k = 128, 16, 16384, 4
+    rng = np.random.default_rng(wl.SEED_BASE + 9)
+    n_req = 64
+    prompts = rng.integers(1024, 2048, n_req, endpoint=True)
+    outs = rng.integers(64, 256, n_req, endpoint=True)
+    order = rng.permutation(nb)
+    out = {}
+    # (False, True, False): the first pass warms up (first calls, allocator growth)
+    for n_pass, grouped in enumerate((False, True, False)):
+        n_run = 8 if n_pass == 0 else n_req
+        loop = ServingLoop(num_blocks=nb, block_size=bs, num_q_heads=hq, num_kv_heads=hkv,
+                           head_dim=d, max_num_seqs=128, max_batched_tokens=4096,
+                           max_prefill_chunk=1024, max_context_len=2048 + 256,
+                           free_order=order, group_samples=grouped)
+        loop.time_decode = True
+        gen = wl.make_generator(wl.SEED_BASE + 9, dev)
+
+        def rows(entries):
+            n = sum(len(p) for _, p in entries)
+            return (wl.randn((n, hkv, d), torch.bfloat16, gen, dev),
+                    wl.randn((n, hkv, d), torch.bfloat16, gen, dev))
+
+        def qs(entries):
+            return wl.randn((sum(len(p) for _, p in entries), hq, d), torch.bfloat16, gen, dev)
+
+        for r in range(n_run):
+            loop.add(r, int(prompts[r]), int(outs[r]),
+                     samples=[100_000 + k * r + j for j in range(k - 1)])
+        steps, dec_rows = 0, 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while loop.sched.stats()["finished"] < n_run and steps < 5000:
+            plan, _, _, _ = loop.step(rows, qs)
+            steps += 1
+            dec_rows += len(plan["decode"])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dec_ms = loop.decode_ms()
+        st = loop.sched.stats()
+        if n_pass == 0:
+            del loop
+            continue
+        key = "grouped" if grouped else "per_sequence"
+        out[key] = {"wall_s": wall, "steps": steps, "ms_per_step": wall * 1e3 / steps,
+                    "generated_tokens_per_s": k * int(outs.sum()) / wall,
+                    "decode_ms_total": dec_ms, "decode_us_per_step": dec_ms * 1e3 / steps,
+                    "mean_decode_batch": dec_rows / max(steps, 1),
+                    "forked_samples": st["forked_samples"],
+                    "swap_preemptions": st["swap_preemptions"],
+                    "recompute_preemptions": st["recompute_preemptions"]}
+        if grouped:
+            out[key]["grouped_steps"] = loop.grouped_steps
+            out[key]["mean_shared_blocks_per_step"] = loop.shared_block_reads / max(
+                loop.grouped_steps, 1)
+        del loop
+        torch.cuda.empty_cache()
+    out["speedup_wall"] = out["per_sequence"]["wall_s"] / out["grouped"]["wall_s"]
+    out["speedup_decode"] = (out["per_sequence"]["decode_ms_total"] /
+                             out["grouped"]["decode_ms_total"])
+    out["workload"] = ("parallel sampling in the serving loop: 64 requests x 4 samples, prompts "
+                       "U[1024,2048], outputs U[64,256] per sample, 7B-shaped attention (32/32 "
+                       "heads, D 128, block 16, bf16), 16384-block pool, 128 seqs / 4096 tokens / "
+                       "1024-token chunks per step; grouped (pa_decode_grouped per request) vs "
+                       "per sequence (pa_decode, cache-keeping policy)")
+    return out
+
+
 PCIE_GBPS = 64.0  # PCIe 5.0 x16, per direction, nominal
 
 
@@ -1533,7 +1614,8 @@ PHASES = ("headline decode step (7B-shaped)", "gqa decode", "prefix-shared decod
           "long-context split-K decode",
           "mixed step (cache write + decode + prefill)",
           "fp8 prompt chunks (quantizing write + prefill)",
-          "swap out / in (pinned host pool)", "serving loop (continuous batching)")
+          "swap out / in (pinned host pool)", "serving loop (continuous batching)",
+          "serving loop with parallel samples (grouped, then per sequence)")
 
 
 def mark_phase(torch):
@@ -1794,6 +1876,10 @@ def main():
         log("bench: row serving loop")
         mark_phase(torch)
         rows["serving"] = row_serving(pa, wl, torch, np, args.row_cpu_budget)
+        torch.cuda.empty_cache()
+        log("bench: row serving loop with parallel samples")
+        mark_phase(torch)
+        rows["serving_samples"] = row_serving_samples(pa, wl, torch, np)
         torch.cuda.empty_cache()
         result["rows"] = rows
         for k, v in rows.items():

@@ -34,9 +34,14 @@ class ServingLoop:
     def __init__(self, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
                  max_num_seqs, max_batched_tokens, max_prefill_chunk, max_context_len,
                  host_blocks=0, free_order=None, device="cuda", dtype=torch.bfloat16,
-                 fp8_scales=None):
+                 fp8_scales=None, group_samples=True):
         """fp8_scales=(k_scale, v_scale): keep the cache as OCP E4M3 codes
-        (uint8 pools) and use the fp8 calls; new rows are still bf16."""
+        (uint8 pools) and use the fp8 calls; new rows are still bf16.
+        group_samples=False decodes sample runs one sequence at a time
+        (pa_decode with the cache-keeping policy) instead of grouped."""
+        self.group_samples = group_samples
+        self.time_decode = False  # True: event-time every decode call (decode_ms())
+        self._dec_events = []
         self.bs, self.hq, self.hkv, self.d = block_size, num_q_heads, num_kv_heads, head_dim
         self.max_ctx = int(max_context_len)
         self.dev, self.dtype = device, dtype
@@ -136,13 +141,18 @@ class ServingLoop:
             dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
             seq_group = self.decode_grouping(ids)
             groups = None
-            if seq_group is not None:
+            if seq_group is not None and self.group_samples:
                 off, sg, shared, largest = decode_groups(t, lens, seq_group, self.bs)
-                groups = (torch.as_tensor(off, device=dev), torch.as_tensor(sg, device=dev),
-                          torch.as_tensor(shared, device=dev), largest)
+                # one upload for the three group arrays
+                g = torch.as_tensor(np.concatenate([off, sg, shared]), device=dev)
+                n0, n1 = len(off), len(off) + len(sg)
+                groups = (g[:n0], g[n0:n1], g[n1:], largest)
                 self.grouped_steps += 1
                 self.shared_block_reads += int(shared.sum())
             t, lens = torch.as_tensor(t, device=dev), torch.as_tensor(lens, device=dev)
+            if self.time_decode:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record()
             if groups and self.fp8:
                 pa_decode_grouped_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
                                       self.max_ctx, *groups, 0, self.ws, kv_reuse=True)
@@ -151,9 +161,17 @@ class ServingLoop:
                                   *groups, 0, self.ws, kv_reuse=True)
             elif self.fp8:
                 pa_decode_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
-                              self.max_ctx, 0, self.ws)
+                              self.max_ctx, 0, self.ws, kv_reuse=seq_group is not None)
             else:
                 pa_decode(dec_out, q, self.k, self.v, t, lens, self.scale, self.max_ctx, 0,
-                          self.ws)
+                          self.ws, kv_reuse=seq_group is not None)
+            if self.time_decode:
+                ev[1].record()
+                self._dec_events.append(ev)
         fin = self.sched.complete()
         return p, dec_out, pre_out, fin
+
+    def decode_ms(self):
+        """Total event time of the decode calls timed so far (synchronizes)."""
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self._dec_events)
