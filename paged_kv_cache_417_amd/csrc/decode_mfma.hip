@@ -224,24 +224,24 @@ __device__ __forceinline__ int32_t shared_parts(const DecodeParams &p, int s, in
     return (int32_t)max((int64_t)0, min(parts, (int64_t)np - 1));
 }
 
-// One per-sequence work item: (kv head, sequence, partition slot) of the
-// 1-D grid index.
+// Whether a context length can be walked: 0 <= L <= max_context_len and its
+// blocks fit the table row.
+__device__ __forceinline__ bool bad_length(const DecodeParams &p, int32_t L, int block_size) {
+    const int32_t nb = (L + block_size - 1) / block_size;
+    return L < 0 || L > p.max_context_len || nb > p.table_stride;
+}
+__device__ __forceinline__ int32_t num_parts(const DecodeParams &p, int32_t L, bool bad) {
+    return bad ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
+}
+
+// The walk over partition `part` of sequence s (context of L tokens in np
+// partitions) for kv head kvh, or its NaN rows when the length is bad.
 template <int D, int BS, bool NT, bool FP8>
-__device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t index) {
+__device__ __forceinline__ void decode_part(const DecodeParams &p, int kvh, int s, int part,
+                                            int32_t L, int32_t np, bool bad_len) {
     using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
-    const DecodeItem item = decode_item(index, p.num_kv_heads, p.num_seqs);
-    const int kvh = item.kvh;
-    const int s = item.seq;
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;
-
-    const int32_t L = p.context_lens[s];
-    const int32_t nb = (L + BS - 1) / BS;
-    const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
-    const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-    const int part = decode_partition(item.slot, np, p.np_max);
-    if (part < 0 || part < shared_parts(p, s, np)) return;  // shared: the group kernel's
-
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h = kvh * G + n;  // this lane's query head (live when n < G)
     const bool live = n < G;
@@ -383,6 +383,20 @@ __device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t 
             p.ws_ml[2 * slot + 1] = bad_block ? qnan : lsum;
         }
     }
+}
+
+
+// One per-sequence work item of the slot grid: (kv head, sequence,
+// partition slot) of the 1-D grid index.
+template <int D, int BS, bool NT, bool FP8>
+__device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t index) {
+    const DecodeItem item = decode_item(index, p.num_kv_heads, p.num_seqs);
+    const int32_t L = p.context_lens[item.seq];
+    const bool bad_len = bad_length(p, L, BS);
+    const int32_t np = num_parts(p, L, bad_len);
+    const int part = decode_partition(item.slot, np, p.np_max);
+    if (part < 0 || part < shared_parts(p, item.seq, np)) return;  // shared: the group kernel's
+    decode_part<D, BS, NT, FP8>(p, item.kvh, item.seq, part, L, np, bad_len);
 }
 
 // Shared partitions of a group of sequences, one wave per (kv head, group,
@@ -559,6 +573,145 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         decode_seq_item<D, BS, NT, FP8>(p, blockIdx.x - group_items);
 }
 
+// ---------------------------------------------------------------------------
+// Longest-first decode for batches of up to kScanMaxSeqs sequences.  The
+// slot grid above dispatches (kv head, sequence, slot) in slot order and
+// launches a wave for every slot up to the longest sequence's partition
+// count, so a batch of mixed lengths launches many waves that find no
+// partition, and its last partitions (of every length) drain in sequence
+// order.  Here each wave loads all the context lengths (one vector load per
+// 64 sequences, in place of the slot grid's single length load) and finds
+// its work item among the batch's partitions taken in this order: the bad
+// lengths (a NaN row), then the full partitions (every sequence's first,
+// then every second, ...), then the last, partial partitions from the
+// longest to the shortest (ties in sequence order).  Waves past the last
+// item exit at once, after every item's wave has been dispatched, and the
+// grid drains with its shortest partitions.  Every partition is computed
+// exactly as in the slot grid.
+constexpr int kScanMaxSeqs = 256;
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__builtin_popcountll(m); }
+// the lane holding the r-th set bit of m (r < popcount(m))
+__device__ __forceinline__ int nth_set_lane(uint64_t m, uint32_t r, int lane) {
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const bool mine = ((m >> lane) & 1ull) != 0 && below == r;
+    return __builtin_ctzll(__ballot(mine));
+}
+
+// C: chunks of 64 sequences (num_seqs <= 64 C).
+template <int D, int BS, bool NT, bool FP8, int C>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_scan_kernel(
+    DecodeParams p) {
+    const int lane = threadIdx.x;
+    const uint32_t hkv = (uint32_t)p.num_kv_heads;
+    const uint32_t e0 = blockIdx.x / hkv;
+    const int kvh = (int)(blockIdx.x - e0 * hkv);
+    const int32_t ps = p.partition_size;
+    // per lane: sequences lane, lane + 64, ...
+    int32_t Lc[C], full[C], tail[C];
+    bool badc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int sq = 64 * c + lane;
+        const bool valid = sq < p.num_seqs;
+        const int32_t L = valid ? p.context_lens[sq] : 0;
+        const bool bad = valid && bad_length(p, L, BS);
+        const int32_t np = num_parts(p, L, bad);
+        const int32_t last = L - (np - 1) * ps;  // tokens of the last partition
+        const bool ok = valid && !bad;
+        Lc[c] = L;
+        badc[c] = bad;
+        full[c] = ok ? np - 1 + (last == ps ? 1 : 0) : 0;
+        tail[c] = ok && last != ps ? (last + 31) / 32 : -1;
+    }
+    uint32_t nbad = 0, ntail = 0;
+    int32_t nfull = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        nbad += popc64(__ballot(badc[c]));
+        ntail += popc64(__ballot(tail[c] >= 0));
+        nfull += wave_sum(full[c]);
+    }
+    uint32_t e = e0;
+    if (e >= nbad + (uint32_t)nfull + ntail) return;  // no item left for this wave
+    // the e-th set bit over the chunks' masks -> sequence, its length
+    int s = 0;
+    int32_t L = 0;
+    auto pick = [&](const uint64_t *m, uint32_t r) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint32_t cnt = popc64(m[c]);
+            if (r < cnt) {
+                const int ln = nth_set_lane(m[c], r, lane);
+                s = 64 * c + ln;
+                L = __builtin_amdgcn_readlane(Lc[c], ln);
+                return;
+            }
+            r -= cnt;
+        }
+    };
+    uint64_t m[C];
+    if (e < nbad) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) m[c] = __ballot(badc[c]);
+        pick(m, e);
+        decode_part<D, BS, NT, FP8>(p, kvh, s, 0, L, 1, true);
+        return;
+    }
+    e -= nbad;
+    int part = 0;
+    bool found = false;
+    if (e < (uint32_t)nfull) {
+        // full partitions, partition-major (k < np_max always finds it: the
+        // counts of the k sum to nfull)
+        for (int32_t k = 0; k < p.np_max; ++k) {
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                m[c] = __ballot(full[c] > k);
+                cnt += popc64(m[c]);
+            }
+            if (e < cnt) {
+                pick(m, e);
+                part = k;
+                found = true;
+                break;
+            }
+            e -= cnt;
+        }
+    } else {
+        // last partial partitions, most steps first
+        e -= (uint32_t)nfull;
+        for (int32_t v = ps / 32; v >= 0; --v) {
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                m[c] = __ballot(tail[c] == v);
+                cnt += popc64(m[c]);
+            }
+            if (e < cnt) {
+                pick(m, e);
+                part = num_parts(p, L, false) - 1;
+                found = true;
+                break;
+            }
+            e -= cnt;
+        }
+    }
+    if (!found) return;
+    // wave-uniform by construction; say so, so that they stay in scalar registers
+    s = __builtin_amdgcn_readfirstlane(s);
+    part = __builtin_amdgcn_readfirstlane(part);
+    L = __builtin_amdgcn_readfirstlane(L);
+    decode_part<D, BS, NT, FP8>(p, kvh, s, part, L, num_parts(p, L, false), false);
+}
+
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
     const int64_t seq_items = (int64_t)p.np_max * p.num_kv_heads * p.num_seqs;
@@ -579,6 +732,24 @@ void launch_one(const DecodeParams &p, hipStream_t s) {
         return;
     }
     const dim3 grid((unsigned)seq_items);
+    if (p.np_max > 1 && p.num_seqs <= kScanMaxSeqs) {
+#define PA_SCAN(NTv, FP8v, Cv) \
+    hipLaunchKernelGGL((decode_scan_kernel<D, BS, NTv, FP8v, Cv>), grid, dim3(64), 0, s, p)
+#define PA_SCAN_C(NTv, FP8v)                           \
+    do {                                               \
+        if (p.num_seqs <= 64) PA_SCAN(NTv, FP8v, 1);   \
+        else if (p.num_seqs <= 128) PA_SCAN(NTv, FP8v, 2); \
+        else PA_SCAN(NTv, FP8v, 4);                    \
+    } while (0)
+        if (p.kv_fp8) {
+            if (p.kv_reuse) PA_SCAN_C(false, true); else PA_SCAN_C(true, true);
+        } else {
+            if (p.kv_reuse) PA_SCAN_C(false, false); else PA_SCAN_C(true, false);
+        }
+#undef PA_SCAN_C
+#undef PA_SCAN
+        return;
+    }
     if (p.kv_fp8) {
         if (p.kv_reuse)
             hipLaunchKernelGGL((decode_mfma_kernel<D, BS, false, true>), grid, dim3(64), 0, s, p);
