@@ -59,6 +59,14 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_
         ps /= 2;
     if (pairs <= 256)
         while (ps < 4096 && pairs * ceil_div(max_len, 2 * ps) >= 1024) ps *= 2;
+    // Then at most 16 partitions for the longest context, while the grid
+    // keeps at least 512 waves: each partition's wave starts with a chain of
+    // dependent loads that a longer partition amortises (on one box: the GQA
+    // batch of up to 8192 tokens 184.5 -> 178.9 us at 1024, 8 x 32768 196.4
+    // -> 189.0 us at 4096; batches of up to 4096 tokens keep 512, where 1024
+    // is no faster).
+    while (ps < 4096 && max_len >= 16 * (int64_t)ps && pairs * ceil_div(max_len, 2 * ps) >= 512)
+        ps *= 2;
     return ps;
 }
 

@@ -88,10 +88,13 @@ def test_default_partition_is_a_multiple_of_step_and_block():
             ps = pa.pa_decode_default_partition(s, hkv, bs, maxlen)
             assert ps % 32 == 0 and ps % bs == 0 and 32 <= ps <= 4096
     # Many (sequence, kv head) pairs keep 512; a few long contexts grow the
-    # partition while the grid keeps >= 1024 waves; short ones shrink it.
+    # partition while the grid keeps >= 1024 waves; short ones shrink it; a
+    # longest context of 16 partitions or more grows it (to 4096 at most)
+    # while the grid keeps >= 512 waves.
     assert pa.pa_decode_default_partition(64, 32, 16, 4096) == 512
-    assert pa.pa_decode_default_partition(128, 8, 16, 8192) == 512
-    assert pa.pa_decode_default_partition(8, 8, 128, 32768) == 2048  # 64 pairs x 16 partitions
+    assert pa.pa_decode_default_partition(128, 8, 16, 8192) == 1024  # at most 16 partitions
+    assert pa.pa_decode_default_partition(8, 8, 128, 32768) == 4096  # 64 pairs x 8 partitions
+    assert pa.pa_decode_default_partition(1, 32, 16, 32768) == 2048  # keeps 512 waves
     assert pa.pa_decode_default_partition(4, 8, 16, 201) == 32
     assert pa.pa_decode_default_partition(4, 8, 128, 201) == 128
 
