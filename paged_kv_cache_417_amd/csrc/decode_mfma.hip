@@ -395,7 +395,9 @@ __device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t 
     const bool bad_len = bad_length(p, L, BS);
     const int32_t np = num_parts(p, L, bad_len);
     const int part = decode_partition(item.slot, np, p.np_max);
-    if (part < 0 || part < shared_parts(p, item.seq, np)) return;  // shared: the group kernel's
+    // shared partitions are the group kernel's; a last partition never is
+    // (no group lookups for it)
+    if (part < 0 || (part < np - 1 && part < shared_parts(p, item.seq, np))) return;
     decode_part<D, BS, NT, FP8>(p, item.kvh, item.seq, part, L, np, bad_len);
 }
 
@@ -420,35 +422,22 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;
 
-    const int32_t lo = p.grp_offsets[grp];
+    // The group's run and shared partitions (scalar loads, issued together).
+    // A wave starts streaming after only these and one round of vector
+    // loads: every load that decides which columns are live, and the
+    // members' table slices, go out in that one round.
+    const int32_t lo = p.grp_offsets[grp], hi = p.grp_offsets[grp + 1];
+    const int64_t grp_parts = (int64_t)p.grp_shared[grp] * p.block_size / p.partition_size;
     if (lo < 0 || lo >= p.num_seqs) return;
     const int G = p.num_q_heads / p.num_kv_heads;
     const int mpw = 16 / G;  // members per wave
+    // No member is live unless the group shares this partition and the
+    // chunk's first member lies in the group's run (shared_parts() below).
+    if (part >= grp_parts || lo + chunk * mpw >= hi) return;
     // this lane's column: member s_n, query head h
     const int32_t s_n = lo + chunk * mpw + n / G;
     const int h = kvh * G + n % G;
-    // a column past the group's run may hold the next group's sequence: only
-    // this group's members are served here
-    bool live = n < mpw * G && s_n < p.num_seqs && p.seq_group[s_n] == grp;
-    if (live) {
-        const int32_t L = p.context_lens[s_n];
-        const int32_t nb = (L + BS - 1) / BS;
-        const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
-        const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-        live = part < shared_parts(p, s_n, np);
-    }
-    if (!__any(live)) return;
-
-    // q as the B operand: column n = (member, head)
-    bf16x8 qb[D / 32];
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
-                           ((int64_t)(live ? s_n : 0) * p.num_q_heads + (live ? h : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-        u32x4 v = ld16(qrow + kslot_dim(ks, g));
-        if (!live) v = u32x4{0u, 0u, 0u, 0u};
-        qb[ks] = as_bf16x8(v);
-    }
+    const bool in_range = n < mpw * G && s_n < p.num_seqs;
 
     const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
     const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
@@ -460,17 +449,57 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     const int32_t nsteps = p.partition_size / 32;
     const int32_t b_first = t_begin / BS, b_last = (t_end - 1) / BS;
 
-    // Each live member's table must equal the leader's over the partition:
-    // lanes compare 64 entries at a time, member by member.
-    bool bad_table = false;
-    for (int k = 0; k < mpw; ++k) {
+    // one round of loads: the member's group and length, q, the leader's
+    // first table window, the members' first table windows
+    const int32_t s_col = in_range ? s_n : lo;
+    const int32_t grp_of = p.seq_group[s_col];
+    const int32_t L_n = p.context_lens[s_col];
+    bf16x8 qb[D / 32];
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(p.q) +
+                           ((int64_t)s_col * p.num_q_heads + (in_range ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qb[ks] = as_bf16x8(ld16(qrow + kslot_dim(ks, g)));
+    // (these loads precede the liveness check, which is what bounds b_last
+    // by a member's table for a well-formed group: clamp to the row too)
+    const int32_t jw = b_first + lane;  // this lane's entry of the first window
+    const bool jw_in = jw <= b_last && jw < p.table_stride;
+    int32_t tbl = jw_in ? table[jw] : 0;
+    int32_t mt[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
         const int32_t s_k = lo + chunk * mpw + k;
-        if (!__shfl(live ? 1 : 0, k * G, 64)) continue;  // column k * G is member k
-        const int32_t *mt = p.block_tables + (int64_t)s_k * p.table_stride;
-        bool diff = false;
-        for (int32_t b = b_first; b <= b_last; b += 64) {
-            const int32_t j = b + lane;
-            diff = diff || (j <= b_last && mt[j] != table[j]);
+        mt[k] = (k < mpw && s_k < p.num_seqs && jw_in)
+                    ? p.block_tables[(int64_t)s_k * p.table_stride + jw]
+                    : 0;
+    }
+
+    // a column is live when its sequence belongs to this group's run and the
+    // group computes this partition for it: shared_parts() for g = grp
+    bool live = false;
+    if (in_range && grp_of == grp && s_n < hi && s_n - lo < p.grp_cover) {
+        const int32_t nb = (L_n + BS - 1) / BS;
+        const bool bad_len = L_n < 0 || L_n > p.max_context_len || nb > p.table_stride;
+        const int32_t np = bad_len ? 1 : max(1, (L_n + p.partition_size - 1) / p.partition_size);
+        live = part < max((int64_t)0, min(grp_parts, (int64_t)np - 1));
+    }
+    if (!__any(live)) return;
+    if (!live) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) qb[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+
+    // Each live member's table must equal the leader's over the partition:
+    // the first 64 entries from the loads above, any further ones 64 at a
+    // time, member by member.
+    bool bad_table = false;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k >= mpw || !__shfl(live ? 1 : 0, k * G, 64)) continue;  // column k * G is member k
+        bool diff = jw_in && mt[k] != tbl;
+        const int32_t *mtk = p.block_tables + (int64_t)(lo + chunk * mpw + k) * p.table_stride;
+        for (int32_t b = b_first + 64; b <= b_last; b += 64) {
+            const int32_t jj = b + lane;
+            diff = diff || (jj <= b_last && mtk[jj] != table[jj]);
         }
         if (__any(diff) && n / G == k) bad_table = true;
     }
@@ -481,7 +510,6 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     int32_t win = b_first;
-    int32_t tbl = (win + lane <= b_last) ? table[win + lane] : 0;
     bool bad_block = false;
     auto block_id = [&](int32_t j) -> int32_t {
         if (j - win >= 64) {
