@@ -45,7 +45,7 @@ METRIC = "paged decode tokens/s and achieved KV HBM GB/s (% of MI355X peak), 1 G
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mha_7b_traffic.json")
-DECODE_KERNEL = "decode_mfma_kernel"
+DECODE_KERNEL = "decode_scan_kernel"
 KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip", "device_common.h", "launch.h")
 CALIB_PAIRS = 4096
 HOST_WARM = 4  # untimed steps before the host-inclusive loop's timed ones
@@ -1734,7 +1734,7 @@ def main():
         head = summary.get(DECODE_PHASES[0])
         if head and head["read"] > 0 and head["write"] > 0:
             with open(TRAFFIC_FILE, "w") as fh:
-                json.dump({"kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+                json.dump({"kernel": "pa_decode (decode_scan_kernel + decode_reduce_kernel)",
                            "kernel_source_sha256": kernel_source_hash(),
                            "workload": DECODE_PHASES[0],
                            "hbm_read_bytes_per_call": head["read"],
@@ -1800,7 +1800,7 @@ def main():
         "hbm_frac": h["achieved"] / PEAK_HBM_GBPS,
         "decode_us": h["dec_avg_ms"] * 1e3,
         "roofline": {
-            "kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+            "kernel": "pa_decode (decode_scan_kernel + decode_reduce_kernel)",
             "bound": "hbm",
             "achieved": h["achieved"],
             "peak": PEAK_HBM_GBPS,
