@@ -45,7 +45,9 @@ METRIC = "paged decode tokens/s and achieved KV HBM GB/s (% of MI355X peak), 1 G
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mha_7b_traffic.json")
-DECODE_KERNEL = "decode_scan_kernel"
+# the decode partition kernel: the longest-first scan grid (batches of up to
+# 256 sequences, as every bench workload) or the slot grid
+DECODE_KERNEL = ("decode_scan_kernel", "decode_mfma_kernel")
 KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip", "device_common.h", "launch.h")
 CALIB_PAIRS = 4096
 HOST_WARM = 4  # untimed steps before the host-inclusive loop's timed ones
@@ -1295,9 +1297,13 @@ def _read_counters(d):
 
 
 def _per_dispatch(rows, counter, kernel_substr):
+    """Counter totals per dispatch of the kernels whose names contain
+    kernel_substr (a string, or a tuple of alternatives)."""
+    subs = (kernel_substr,) if isinstance(kernel_substr, str) else tuple(kernel_substr)
     acc = {}
     for r in rows:
-        if r.get("Counter_Name") != counter or kernel_substr not in r.get("Kernel_Name", ""):
+        name = r.get("Kernel_Name", "")
+        if r.get("Counter_Name") != counter or not any(k in name for k in subs):
             continue
         key = r.get("Dispatch_Id") or r.get("Correlation_Id")
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
@@ -1310,7 +1316,7 @@ def pmc_summary(fetch_dir, write_dir, block_bytes):
     calibration copy (CALIB_PAIRS blocks of block_bytes per K and V region,
     read once and written once)."""
     expect = CALIB_PAIRS * 2 * block_bytes
-    out = {"kernel": DECODE_KERNEL, "kernel_source_sha256": kernel_source_hash(),
+    out = {"kernel": " or ".join(DECODE_KERNEL), "kernel_source_sha256": kernel_source_hash(),
            "calibration": f"pa_copy_blocks over {CALIB_PAIRS} blocks: {expect} B read, "
                           f"{expect} B written"}
     total = 0.0
