@@ -473,3 +473,42 @@ def test_copy_blocks_bit_exact(pa):
     oracle.copy_blocks(k_host, v_host, pairs[:2], pa.K_AXES, pa.V_AXES)
     assert (host_bits(case.k_pool) == k_host).all()
     assert (host_bits(case.v_pool) == v_host).all()
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 128, 129, 256, 257])
+def test_longest_first_grid_edges(pa, S):
+    """Batch sizes on both sides of the longest-first grid's 64-sequence chunks
+    and of its 256-sequence limit (past which the slot grid runs), lengths
+    mixing empty contexts, exactly full partitions, one-token tails and long
+    ones, plus two bad lengths: every good row against the oracle, every bad
+    row NaN, at the default partition and at 64-token partitions."""
+    rng = np.random.default_rng(500 + S)
+    maxlen = 700
+    lengths = rng.integers(1, maxlen, S)
+    for i, v in enumerate([0, 64, 128, 65, 1, maxlen - 1, 512]):
+        if i < S:
+            lengths[(i * 7) % S] = v
+    lengths = [int(x) for x in lengths]
+    case = small_case(pa, "bf16", 4, 2, 64, 16, lengths, seed=S)
+    sh = case.shape
+    dev = "cuda"
+    call_lens = list(lengths)
+    bad = sorted({S // 3, (2 * S) // 3}) if S >= 3 else []
+    if bad:
+        call_lens[bad[0]] = -1
+        call_lens[bad[-1]] = maxlen + 1
+    good = [i for i in range(S) if i not in bad]
+    t_dev = torch.as_tensor(case.tables, dtype=torch.int32, device=dev)
+    l_dev = torch.as_tensor(call_lens, dtype=torch.int32, device=dev)
+    for ps in (0, 64):
+        say(f"case longest-first grid S={S} ps={ps}")
+        out = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
+        ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
+                                 sh.block_size, maxlen, ps, dev)
+        pa.pa_decode(out, case.q, case.k_pool, case.v_pool, t_dev, l_dev, sh.scale, maxlen, ps,
+                     ws)
+        torch.cuda.synchronize()
+        err = check_rows(pa, case, out, good)
+        for b in bad:
+            assert torch.isnan(out[b]).all()
+        say(f"  {len(good)} rows max err {err:.3e}, {len(bad)} NaN rows")
