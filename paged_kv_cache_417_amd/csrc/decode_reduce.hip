@@ -32,18 +32,20 @@ void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int
 
 namespace {
 
-constexpr int kReduceThreads = 256;
+constexpr int kReduceWaves = 4;  // (sequence, query head) items per workgroup, one per wave
 
-// One workgroup of 256 threads per (sequence, query head).  Thread (slice
-// sl, dim d) merges partitions sl, sl + slices, ... (slices = 256 / D) with
-// the same online rescaling the partition kernel uses, so its loads do not
-// wait on any reduction; the slices are then merged by the first D threads.
-// Every merge runs in partition-index order: the result is deterministic.
-__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
-    __shared__ float part_m[kReduceThreads], part_l[kReduceThreads], part_o[kReduceThreads];
-    const int s = blockIdx.x / p.num_q_heads;
-    const int h = blockIdx.x % p.num_q_heads;
-    const int tid = threadIdx.x;
+// One wave per (sequence, query head): lane l holds dims l*D/64 .. of the
+// output and merges the partitions 0 .. np-1 in order with the same online
+// rescaling the partition kernel uses (the (m, l) pair of a partition is the
+// same for every lane: scalar loads).  Deterministic: one fixed order.
+template <int D>
+__global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(DecodeParams p) {
+    constexpr int kDpl = D / 64;  // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kReduceWaves + (threadIdx.x >> 6);
+    if (item >= (int64_t)p.num_seqs * p.num_q_heads) return;
+    const int s = (int)(item / p.num_q_heads);
+    const int h = (int)(item - (int64_t)s * p.num_q_heads);
     const int32_t L = p.context_lens[s];
     const int32_t nb = (L + p.block_size - 1) / p.block_size;
     if (L < 0 || L > p.max_context_len || nb > p.table_stride) return;  // row already NaN
@@ -51,44 +53,47 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
     if (np <= 1) return;  // written directly by the partition kernel
     const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.np_max;
     const float *ml = p.ws_ml + 2 * base;
-    const int D = p.head_dim;
-    const int slices = kReduceThreads / D;
-    const int d = tid % D, sl = tid / D;
-    const float *op = p.ws_o + base * D + d;
+    const float *op = p.ws_o + base * D + kDpl * lane;
 
-    float m = kNegInf, l = 0.f, o = 0.f;
+    float m = kNegInf, l = 0.f, o[kDpl];
+#pragma unroll
+    for (int k = 0; k < kDpl; ++k) o[k] = 0.f;
 #pragma unroll 4
-    for (int32_t i = sl; i < np; i += slices) {
-        const float mi = ml[2 * i], li = ml[2 * i + 1], oi = op[(int64_t)i * D];
+    for (int32_t i = 0; i < np; ++i) {
+        const float mi = ml[2 * i], li = ml[2 * i + 1];
+        float oi[kDpl];
+        if constexpr (kDpl == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(op + (int64_t)i * D);
+            oi[0] = v.x;
+            oi[1] = v.y;
+        } else {
+            oi[0] = op[(int64_t)i * D];
+        }
         const float mn = fmaxf(m, mi);
         const float a = fast_exp2(m - mn), b = fast_exp2(mi - mn);
         l = l * a + li * b;
-        o = o * a + oi * b;
+#pragma unroll
+        for (int k = 0; k < kDpl; ++k) o[k] = o[k] * a + oi[k] * b;
         m = mn;
     }
-    part_m[tid] = m;
-    part_l[tid] = l;
-    part_o[tid] = o;
-    __syncthreads();
-    if (tid < D) {
-        float M = part_m[tid];
-        for (int k = 1; k < slices; ++k) M = fmaxf(M, part_m[k * D + tid]);
-        float lt = 0.f, ot = 0.f;
-        for (int k = 0; k < slices; ++k) {
-            const float w = fast_exp2(part_m[k * D + tid] - M);
-            lt += w * part_l[k * D + tid];
-            ot += w * part_o[k * D + tid];
-        }
-        p.out[((int64_t)s * p.num_q_heads + h) * D + tid] = ot / lt;
-    }
+    float *orow = p.out + ((int64_t)s * p.num_q_heads + h) * D + kDpl * lane;
+    if constexpr (kDpl == 2)
+        *reinterpret_cast<float2 *>(orow) = float2{o[0] / l, o[1] / l};
+    else
+        orow[0] = o[0] / l;
 }
 
 }  // namespace
 
 int launch_decode_reduce(const DecodeParams &p, void *stream) {
     if (p.np_max <= 1 || p.num_seqs == 0) return 0;
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(p.num_seqs * p.num_q_heads)),
-                       dim3(kReduceThreads), 0, reinterpret_cast<hipStream_t>(stream), p);
+    const int64_t items = (int64_t)p.num_seqs * p.num_q_heads;
+    const dim3 grid((unsigned)((items + kReduceWaves - 1) / kReduceWaves)), block(64 * kReduceWaves);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.head_dim == 128)
+        hipLaunchKernelGGL(decode_reduce_kernel<128>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(decode_reduce_kernel<64>, grid, block, 0, s, p);
     return (int)hipGetLastError();
 }
 
