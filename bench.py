@@ -773,12 +773,14 @@ def headline(args, pa, wl, torch, np):
     if args.calibrate:
         calibrate_copy(pa, torch, np, case, alloc)
     copy_ref = copy_reference(pa, torch, np, case, alloc, args.reps)
+    read_ref = read_reference(pa, torch, case, args.reps)
+    read_ref["decode_frac_of_read_stream"] = achieved / read_ref["GBps"]
 
     res = {
         "S": S, "replicas": R, "ms_step": ms_step, "dec_avg_ms": dec_avg_ms, "dec_ms": dec_ms,
         "bytes_avg": bytes_avg, "achieved": achieved, "ps": ps_used,
         "seq_len": float(h_lens[W:].mean()), "alloc_us": alloc_us, "host_rate": host_rate,
-        "copy_ref": copy_ref,
+        "copy_ref": copy_ref, "read_ref": read_ref,
     }
     # the first replica as a batch of its own, for the CPU baseline
     first = wl.DecodeCase(sh, case.lengths[:S].copy(), case.perm, case.tables[:S].copy(),
@@ -878,6 +880,34 @@ def copy_reference(pa, torch, np, case, alloc, reps):
             "GBps_read_plus_write": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
             "workload": f"pa_copy_blocks of {CALIB_PAIRS} unused block pairs of the headline pool "
                         f"(K and V, {block_bytes // 1024} KiB each)"}
+
+
+READ_REF_BYTES = 8 << 30  # 32 times the MALL
+
+
+def read_reference(pa, torch, case, reps):
+    """The plain streaming read of the same GPU, as the practical ceiling
+    beside the 8 TB/s peak: pa_read_stream over READ_REF_BYTES of the headline
+    K pool (contiguous, 16-byte non-temporal loads, one XOR fold per
+    workgroup), event-timed."""
+    flat = case.k_pool.view(-1)
+    n = min(flat.numel(), READ_REF_BYTES // flat.element_size())
+    src = flat[:n]
+    sink = torch.empty(pa.READ_STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.pa_read_stream(src, sink)
+
+    for _ in range(3):
+        call()
+    med, ms = events_time(torch, call, reps, stream)
+    nbytes = n * flat.element_size()
+    gbps = nbytes / (med * 1e-3) / 1e9
+    return {"us": med * 1e3, **spread(ms), "bytes_read": nbytes, "GBps": gbps,
+            "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
+            "workload": f"pa_read_stream over {nbytes >> 30} GiB of the headline K pool "
+                        "(contiguous, 16-byte non-temporal loads)"}
 
 
 # ---------------------------------------------------------------------------
@@ -1818,6 +1848,7 @@ def main():
         "host_allocator_us_per_step": h["alloc_us"],
         "host_inclusive_tokens_per_s": h["host_rate"],
         "copy_reference": h["copy_ref"],
+        "read_reference": h["read_ref"],
     }
     if args.cpu_budget > 0:
         log("bench: CPU baseline (oracle)")

@@ -101,6 +101,21 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache,
                          int32_t block_size, int32_t num_blocks,
                          pa_dtype dtype, void *stream);
 
+/* Reference read stream, for measurement only (no part of attention): reads
+ * the `bytes` bytes at `src` once, in 16-byte non-temporal loads spread over
+ * a fixed grid, the plain streaming-read rate beside which the decode
+ * kernels' HBM rates are reported.  The loads are folded with XOR into one
+ * 32-bit word per workgroup, written to sink[0 .. PA_READ_STREAM_SINK_WORDS);
+ * the XOR of those words equals the XOR of all 32-bit words of the buffer.
+ *   src    device, 16-byte aligned, not written
+ *   bytes  a multiple of 16 (0 allowed: the sink words become 0)
+ *   sink   device, PA_READ_STREAM_SINK_WORDS words, 4-byte aligned, written
+ * Asynchronous on `stream`.  PA_ERR_INVALID_ARG on NULL or misaligned
+ * pointers or a size that is not a multiple of 16. */
+#define PA_READ_STREAM_SINK_WORDS 8192
+pa_status pa_read_stream(const void *src, size_t bytes, uint32_t *sink,
+                         void *stream);
+
 /* Partition size (tokens) pa_decode uses when called with partition_size 0:
  * sequences longer than one partition are split and their parts processed
  * independently, then merged ([VF] §1.1: segments of a sequence can be

@@ -45,7 +45,7 @@ V_AXES = "bhdr"
 
 # Every symbol the header declares; the CPU tests check the library exports them.
 EXPORTED = (
-    "pa_last_error", "pa_cache_write", "pa_copy_blocks", "pa_decode_default_partition",
+    "pa_last_error", "pa_cache_write", "pa_copy_blocks", "pa_read_stream", "pa_decode_default_partition",
     "pa_decode_workspace_size", "pa_decode", "pa_decode_ex", "pa_prefill_chunk",
     "pa_allocator_create",
     "pa_allocator_destroy", "pa_seq_create", "pa_seq_fork", "pa_seq_append", "pa_seq_free",
@@ -124,6 +124,7 @@ def _declare(lib):
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_cache_write": (st, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]),
         "pa_copy_blocks": (st, [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]),
+        "pa_read_stream": (st, [vp, ctypes.c_size_t, vp, vp]),
         "pa_decode_default_partition": (i32, [i32, i32, i32, i32]),
         "pa_decode_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -260,6 +261,20 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     n = src_dst.numel() // 2
     _check(_lib.pa_copy_blocks(_p(k_cache), _p(v_cache), _p(src_dst), n, hkv, d, bs, nb,
                                _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
+
+
+READ_STREAM_SINK_WORDS = 8192
+
+
+def pa_read_stream(src, sink, stream=None) -> None:
+    """Read every byte of the device tensor ``src`` once (the plain streaming
+    read the decode rates are compared with); ``sink`` is a device int32 or
+    uint32 tensor of READ_STREAM_SINK_WORDS words that receives one XOR fold
+    per workgroup."""
+    if sink.numel() * sink.element_size() < 4 * READ_STREAM_SINK_WORDS:
+        raise PAError(PA_ERR_INVALID_ARG, "pa_read_stream: sink smaller than 8192 words")
+    _check(_lib.pa_read_stream(_p(src), src.numel() * src.element_size(), _p(sink),
+                               ctypes.c_void_p(_stream(stream))))
 
 
 def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst, stream=None) -> None:

@@ -155,6 +155,19 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, i
     return pa::ok();
 }
 
+pa_status pa_read_stream(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    const char *fn = "pa_read_stream";
+    static_assert(PA_READ_STREAM_SINK_WORDS == pa::kReadStreamBlocks, "one sink word per workgroup");
+    if (!src || !sink) return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (bytes % 16 != 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "%s: %zu bytes is not a multiple of 16", fn, bytes);
+    int rc = pa::launch_read_stream(src, bytes, sink, stream);
+    if (rc) return pa::fail(PA_ERR_DEVICE, "%s: launch failed (hip error %d)", fn, rc);
+    return pa::ok();
+}
+
 pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_blocks, void *dst_k,
                          void *dst_v, int32_t dst_blocks, const int32_t *src_dst,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,

@@ -98,6 +98,11 @@ int launch_cache_write_fp8(const void *k_new, const void *v_new, pa_dtype in_dty
                            int32_t block_size, int32_t num_blocks, float k_scale,
                            float v_scale, void *stream);
 
+// Plain read stream (bandwidth.hip): one sink word per workgroup of a fixed
+// grid of kReadStreamBlocks.
+constexpr int kReadStreamBlocks = 8192;
+int launch_read_stream(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst, int32_t num_pairs,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, pa_dtype dtype, void *stream);

@@ -118,6 +118,16 @@ def test_cache_write_and_copy_reject():
     assert cb(FAKE, FAKE, NULL, 0, 8, 128, 16, 64, 1, STREAM) == pa.PA_OK
 
 
+def test_read_stream_rejects():
+    rs = lib.pa_read_stream
+    assert rs(NULL, 64, FAKE, STREAM) == pa.PA_ERR_INVALID_ARG
+    assert rs(FAKE, 64, NULL, STREAM) == pa.PA_ERR_INVALID_ARG
+    assert rs(MISALIGNED, 64, FAKE, STREAM) == pa.PA_ERR_INVALID_ARG
+    assert rs(FAKE, 64, ctypes.c_void_p((1 << 20) + 2), STREAM) == \
+        pa.PA_ERR_INVALID_ARG
+    assert rs(FAKE, 24, FAKE, STREAM) == pa.PA_ERR_INVALID_ARG
+
+
 def test_prefill_rejects():
     pf = lib.pa_prefill_chunk
 

@@ -1,0 +1,48 @@
+"""The reference read stream (pa_read_stream): every 32-bit word of the
+buffer is read, so the XOR of the per-workgroup sink words equals the XOR of
+the buffer's words, whatever the grid order."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_417_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+SINK = pa.READ_STREAM_SINK_WORDS
+
+
+def host_xor(words):
+    return int(np.bitwise_xor.reduce(words.view(np.uint32))) if words.size else 0
+
+
+# 16 bytes (one load, most workgroups idle), a ragged size below one pass of
+# the grid, one grid pass of four loads per thread plus a ragged tail, 64 MiB
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 8192 * 256 * 64 + 16 * 7, 64 << 20])
+def test_read_stream_folds_every_word(nbytes):
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.full((SINK,), 0x5a5a5a5a, dtype=torch.int32, device="cuda")
+    pa.pa_read_stream(src, sink)
+    torch.cuda.synchronize()
+    assert host_xor(sink.cpu().numpy()) == host_xor(words)
+
+
+def test_read_stream_zero_bytes_clears_the_sink():
+    src = torch.ones(4, dtype=torch.int32, device="cuda")
+    sink = torch.full((SINK,), 7, dtype=torch.int32, device="cuda")
+    lib = pa.lib()
+    rc = lib.pa_read_stream(ctypes.c_void_p(src.data_ptr()), 0, ctypes.c_void_p(sink.data_ptr()),
+                            None)
+    assert rc == pa.PA_OK
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+
+
+def test_read_stream_binding_checks_the_sink_size():
+    src = torch.ones(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PAError):
+        pa.pa_read_stream(src, torch.zeros(SINK - 1, dtype=torch.int32, device="cuda"))
