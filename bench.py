@@ -1918,6 +1918,13 @@ def main():
         mark_phase(torch)
         rows["serving_samples"] = row_serving_samples(pa, wl, torch, np)
         torch.cuda.empty_cache()
+        # each HBM-bound row beside the same run's plain read stream as well
+        read_gbps = h["read_ref"]["GBps"]
+        for v in rows.values():
+            if isinstance(v, dict) and v.get("bound") == "hbm":
+                gb = v.get("GBps", v.get("GBps_unique"))
+                if gb is not None:
+                    v["frac_of_read_stream"] = gb / read_gbps
         result["rows"] = rows
         for k, v in rows.items():
             log(f"bench: {k}: " + ", ".join(
