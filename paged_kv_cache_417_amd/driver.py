@@ -30,6 +30,65 @@ from . import (Allocator, Scheduler, decode_groups, decode_workspace, kv_cache_s
                pa_swap_blocks)
 
 
+class _Staging:
+    """A step's small integer arrays (slots, tables, lengths, prefix sums,
+    group arrays, block pairs) go to the device together: they are packed
+    into one pinned buffer and sent with one asynchronous copy, instead of
+    one synchronous upload from pageable memory each.  Two buffers alternate;
+    a buffer is refilled only once its previous copy has completed, and its
+    device twin is overwritten only by a later copy on the same stream, after
+    the kernels that read it."""
+
+    def __init__(self, device, nbytes=1 << 20):
+        self.dev = device
+        self.i = 0
+        self.host = [None, None]
+        self.devbuf = [None, None]
+        self.done = [None, None]
+        self.cap = [0, 0]
+        self.want = nbytes
+
+    def begin(self):
+        b = self.i
+        if self.done[b] is not None:
+            self.done[b].synchronize()
+        self.parts = []
+        self.off = 0
+
+    def put(self, arr):
+        """Queue a numpy array; returns its index for ``send``'s list."""
+        arr = np.ascontiguousarray(arr)
+        self.parts.append((self.off, arr))
+        self.off += -(-arr.nbytes // 16) * 16  # keep every part 16-byte aligned
+        return len(self.parts) - 1
+
+    def send(self):
+        """One host-to-device copy of everything queued; device tensors in
+        ``put`` order, each with its array's dtype and shape."""
+        b = self.i
+        self.i ^= 1
+        need = max(self.off, 16)
+        if self.cap[b] < need:
+            self.cap[b] = max(need, self.want, 2 * self.cap[b])
+            self.host[b] = torch.empty(self.cap[b], dtype=torch.uint8, pin_memory=True)
+            self.devbuf[b] = torch.empty(self.cap[b], dtype=torch.uint8, device=self.dev)
+        hb = self.host[b].numpy()
+        for off, arr in self.parts:
+            hb[off:off + arr.nbytes] = arr.view(np.uint8).reshape(-1)
+        self.devbuf[b][:self.off].copy_(self.host[b][:self.off], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream())
+        self.done[b] = ev
+        out = []
+        for off, arr in self.parts:
+            t = self.devbuf[b][off:off + arr.nbytes].view(_TORCH_OF[arr.dtype.str[1:]])
+            out.append(t.view(arr.shape))
+        return out
+
+
+_TORCH_OF = {"i4": torch.int32, "i8": torch.int64}
+
+
 class ServingLoop:
     def __init__(self, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
                  max_num_seqs, max_batched_tokens, max_prefill_chunk, max_context_len,
@@ -65,6 +124,7 @@ class ServingLoop:
                                    self.max_ctx, 0, device)
         self.scale = head_dim ** -0.5
         self.request_of = {}  # sample sequence id -> its request id
+        self.staging = _Staging(device)
         self.grouped_steps = 0       # decode steps that ran grouped
         self.shared_block_reads = 0  # group-shared blocks, summed over those steps
 
@@ -101,33 +161,52 @@ class ServingLoop:
         prefill output or None, finished ids)."""
         dev = self.dev
         p = self.sched.step()
-        if len(p["swap_out"]):
-            pa_swap_blocks(self.k, self.v, self.hk, self.hv, torch.as_tensor(p["swap_out"], device=dev))
-        if len(p["swap_in"]):
-            pa_swap_blocks(self.hk, self.hv, self.k, self.v, torch.as_tensor(p["swap_in"], device=dev))
-        if len(p["cow"]):
-            pa_copy_blocks(self.k, self.v, torch.as_tensor(p["cow"], device=dev))
+        # every integer array of the step goes up in one pinned copy
+        st = self.staging
+        st.begin()
+        i_out = st.put(np.asarray(p["swap_out"], np.int32)) if len(p["swap_out"]) else None
+        i_in = st.put(np.asarray(p["swap_in"], np.int32)) if len(p["swap_in"]) else None
+        i_cow = st.put(np.asarray(p["cow"], np.int32)) if len(p["cow"]) else None
         # new positions: decode positions first, then each chunk's
         dec_entries = [(rid, np.array([ctx - 1])) for rid, ctx in p["decode"]]
         pre_entries = [(rid, np.arange(start, start + n)) for rid, start, n in p["prefill"]]
-        if dec_entries or pre_entries:
-            k, v = rows_fn(dec_entries + pre_entries)
-            slots = torch.as_tensor(p["slots"], device=dev)
-            if self.fp8:
-                pa_cache_write_fp8(k, v, self.k, self.v, slots, *self.fp8)
-            else:
-                pa_cache_write(k, v, self.k, self.v, slots)
-        pre_out = dec_out = None
+        i_slots = st.put(np.asarray(p["slots"], np.int64)) if dec_entries or pre_entries else None
         if p["prefill"]:
             ids = [x[0] for x in p["prefill"]]
-            t, ctx = self.alloc.batch_tables(ids, self.stride, self.pad)
+            t, _ = self.alloc.batch_tables(ids, self.stride, self.pad)
             qlens = np.array([x[2] for x in p["prefill"]], dtype=np.int32)
             # the chunk's context ends at its last new position
             ctx = np.array([x[1] + x[2] for x in p["prefill"]], dtype=np.int32)
             cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+            i_pre = (st.put(t), st.put(cu), st.put(ctx))
+        groups = None
+        if p["decode"]:
+            ids = [x[0] for x in p["decode"]]
+            t, lens = self.alloc.batch_tables(ids, self.stride, self.pad)
+            seq_group = self.decode_grouping(ids)
+            if seq_group is not None and self.group_samples:
+                off, sg, shared, largest = decode_groups(t, lens, seq_group, self.bs)
+                groups = (st.put(off), st.put(sg), st.put(shared), largest)
+                self.grouped_steps += 1
+                self.shared_block_reads += int(shared.sum())
+            i_dec = (st.put(t), st.put(lens))
+        d = st.send()
+        if i_out is not None:
+            pa_swap_blocks(self.k, self.v, self.hk, self.hv, d[i_out])
+        if i_in is not None:
+            pa_swap_blocks(self.hk, self.hv, self.k, self.v, d[i_in])
+        if i_cow is not None:
+            pa_copy_blocks(self.k, self.v, d[i_cow])
+        if i_slots is not None:
+            k, v = rows_fn(dec_entries + pre_entries)
+            if self.fp8:
+                pa_cache_write_fp8(k, v, self.k, self.v, d[i_slots], *self.fp8)
+            else:
+                pa_cache_write(k, v, self.k, self.v, d[i_slots])
+        pre_out = dec_out = None
+        if p["prefill"]:
             pre_out = torch.empty((int(cu[-1]), self.hq, self.d), device=dev)
-            args = (torch.as_tensor(t, device=dev), torch.as_tensor(cu, device=dev),
-                    torch.as_tensor(ctx, device=dev), self.scale)
+            args = (d[i_pre[0]], d[i_pre[1]], d[i_pre[2]], self.scale)
             if self.fp8:
                 pa_prefill_chunk_fp8(pre_out, q_fn(pre_entries), self.k, self.v, *args, *self.fp8,
                                      int(qlens.max()), self.max_ctx)
@@ -135,21 +214,11 @@ class ServingLoop:
                 pa_prefill_chunk(pre_out, q_fn(pre_entries), self.k, self.v, *args,
                                  int(qlens.max()), self.max_ctx)
         if p["decode"]:
-            ids = [x[0] for x in p["decode"]]
-            t, lens = self.alloc.batch_tables(ids, self.stride, self.pad)
             q = q_fn(dec_entries)
             dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
-            seq_group = self.decode_grouping(ids)
-            groups = None
-            if seq_group is not None and self.group_samples:
-                off, sg, shared, largest = decode_groups(t, lens, seq_group, self.bs)
-                # one upload for the three group arrays
-                g = torch.as_tensor(np.concatenate([off, sg, shared]), device=dev)
-                n0, n1 = len(off), len(off) + len(sg)
-                groups = (g[:n0], g[n0:n1], g[n1:], largest)
-                self.grouped_steps += 1
-                self.shared_block_reads += int(shared.sum())
-            t, lens = torch.as_tensor(t, device=dev), torch.as_tensor(lens, device=dev)
+            t, lens = d[i_dec[0]], d[i_dec[1]]
+            if groups:
+                groups = (d[groups[0]], d[groups[1]], d[groups[2]], groups[3])
             if self.time_decode:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record()
