@@ -141,18 +141,22 @@ class ServingLoop:
         """seq_group for pa_decode_groups: each run of two or more sequences
         of one request (the scheduler keeps them adjacent) is a group, every
         other sequence -1; None when there is no group."""
-        owner = [self.request_of.get(x, x) for x in seq_ids]
-        seq_group = np.full(len(seq_ids), -1, dtype=np.int32)
-        g, i = 0, 0
-        while i < len(owner):
-            j = i + 1
-            while j < len(owner) and owner[j] == owner[i]:
-                j += 1
-            if j - i > 1:
-                seq_group[i:j] = g
-                g += 1
-            i = j
-        return seq_group if g else None
+        n = len(seq_ids)
+        ro = self.request_of
+        owner = np.fromiter((ro.get(x, x) for x in seq_ids), dtype=np.int64, count=n)
+        if n < 2:
+            return None
+        # runs of equal owners: start index and length of each
+        starts = np.flatnonzero(np.concatenate(([True], owner[1:] != owner[:-1])))
+        lengths = np.diff(np.append(starts, n))
+        multi = lengths > 1
+        if not multi.any():
+            return None
+        seq_group = np.full(n, -1, dtype=np.int32)
+        run_group = np.cumsum(multi) - 1  # group id of each multi-member run
+        member = np.repeat(multi, lengths)
+        seq_group[member] = np.repeat(run_group[multi], lengths[multi]).astype(np.int32)
+        return seq_group
 
     def step(self, rows_fn, q_fn):
         """One scheduler step on the GPU.  rows_fn(entries) -> (k, v)
@@ -168,7 +172,9 @@ class ServingLoop:
         i_in = st.put(np.asarray(p["swap_in"], np.int32)) if len(p["swap_in"]) else None
         i_cow = st.put(np.asarray(p["cow"], np.int32)) if len(p["cow"]) else None
         # new positions: decode positions first, then each chunk's
-        dec_entries = [(rid, np.array([ctx - 1])) for rid, ctx in p["decode"]]
+        dpos = np.fromiter((ctx - 1 for _, ctx in p["decode"]), dtype=np.int64,
+                           count=len(p["decode"]))
+        dec_entries = [(x[0], dpos[i:i + 1]) for i, x in enumerate(p["decode"])]
         pre_entries = [(rid, np.arange(start, start + n)) for rid, start, n in p["prefill"]]
         i_slots = st.put(np.asarray(p["slots"], np.int64)) if dec_entries or pre_entries else None
         if p["prefill"]:
