@@ -1010,7 +1010,7 @@ def decode_row(pa, torch, case, reps, ps=0, tables=None, lengths=None, kv_reuse=
     q_rep = [case.q[r * S:(r + 1) * S] for r in range(replicas)]
     out = torch.empty((S, sh.num_q_heads, sh.head_dim), device=dev)
     ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                             maxlen, ps, dev)
+                             maxlen, ps, dev, grouped=groups is not None)
     stream = torch.cuda.current_stream()
 
     if groups is not None:
@@ -1116,17 +1116,25 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     tables, lens, ids = case.tables, case.lengths, range(len(case.lengths))
     # The allocator reports shared blocks: the batch is decoded with the
     # samples of each prompt as one group (pa_decode_grouped: the shared
-    # partitions are read once per group) and the cache-keeping load policy.
-    # Per-sequence decode with that policy and with the streaming one are
-    # timed beside it.
+    # region is read once per group) at the partition size
+    # pa_decode_grouped_partition picks, with the streaming load policy (no
+    # block is read twice).  The grouped call at the plain default size and
+    # the per-sequence decode with the cache-keeping policy (the sharers'
+    # re-reads hit the caches) and the streaming one are timed beside it.
     assert alloc.stats()["num_shared"] > 0
-    ps = pa.pa_decode_default_partition(len(ids), sh.num_kv_heads, sh.block_size,
-                                        int(lens.max()))
-    groups = pa.decode_groups(tables, lens, np.arange(len(ids)) // samples, sh.block_size)[:3]
-    r = decode_row(pa, torch, case, reps, kv_reuse=True, groups=groups, max_group=samples)
+    maxlen = int(lens.max())
+    ps0 = pa.pa_decode_default_partition(len(ids), sh.num_kv_heads, sh.block_size, maxlen)
+    groups = pa.decode_groups(tables, lens, np.arange(len(ids)) // samples, sh.block_size)
+    ps = pa.decode_grouped_partition(lens, *groups, sh.num_q_heads, sh.num_kv_heads,
+                                     sh.block_size, maxlen)
+    groups = groups[:3]
+    r = decode_row(pa, torch, case, reps, ps=ps, groups=groups, max_group=samples)
+    r["partition_size"] = ps
+    r["us_grouped_default_partition"] = decode_row(pa, torch, case, reps, ps=ps0, groups=groups,
+                                                   max_group=samples)["us"]
     r["us_per_sequence"] = decode_row(pa, torch, case, reps, kv_reuse=True)["us"]
     r["us_streaming_policy"] = decode_row(pa, torch, case, reps)["us"]
-    r["shared_partitions_per_group"] = int(groups[2][0]) * sh.block_size // ps
+    r["shared_partitions_per_group"] = -(-int(groups[2][0]) * sh.block_size // ps)
     # unique bytes: each physical block's valid rows once
     unique_tokens = 0
     seen = set()
@@ -1149,8 +1157,9 @@ def row_prefix_shared(pa, wl, torch, np, reps, cpu_budget):
     r["logical_bytes"] = r.pop("algorithmic_bytes")
     r["workload"] = ("prefix-shared decode: 16 prompts of 2048+j tokens x 8 samples sharing "
                      "them, tails U[1,512], 32/32 heads, head_dim 128, block 16, bf16; us: "
-                     "pa_decode_grouped (one group per prompt), us_per_sequence: pa_decode_ex "
-                     "with the cache-keeping policy")
+                     "pa_decode_grouped (one group per prompt, pa_decode_grouped_partition's "
+                     "size, streaming policy), us_per_sequence: pa_decode_ex with the "
+                     "cache-keeping policy")
     if cpu_budget > 0:
         r["cpu_oracle"] = cpu_decode_row(case, cpu_budget)
     cow = {"us": copy_med * 1e3, "pairs": int(len(pairs)), "bytes_moved": copy_bytes,
@@ -1501,9 +1510,12 @@ def decode_only(pa, wl, torch, np, reps, out_json):
     # the batch's set-up kernels (cache writes, copy-on-write copies) run
     # before the next marker: the summary counts only decode kernels there
     case, alloc, _, _, samples = prefix_shared_batch(pa, wl, torch, np)
+    psh = wl.PREFIX_SHARED
     groups = pa.decode_groups(case.tables, case.lengths, np.arange(len(case.lengths)) // samples,
-                              wl.PREFIX_SHARED.block_size)[:3]
-    r = run(DECODE_PHASES[5], case, replicas=1, kv_reuse=True, groups=groups, max_group=samples)
+                              psh.block_size)
+    gps = pa.decode_grouped_partition(case.lengths, *groups, psh.num_q_heads, psh.num_kv_heads,
+                                      psh.block_size, int(case.lengths.max()))
+    r = run(DECODE_PHASES[5], case, replicas=1, ps=gps, groups=groups[:3], max_group=samples)
     phases[-1]["algorithmic_bytes"] = None  # unique bytes: see the bench row
     mark_phase(torch)
     calibrate_copy(pa, torch, np, case, alloc)

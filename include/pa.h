@@ -259,10 +259,20 @@ pa_status pa_prefill_chunk(float *out, const void *q,
 
 /* Paged decode of a batch whose sequences share leading blocks (parallel
  * sampling, forked prompts: [VE] §3.1 KV sharing; [VI] §1 shared prompt
- * prefixes).  Same result as pa_decode_ex with the same arguments, bit for
- * bit, but a partition that every member of a group holds in the same
- * physical blocks is read once for the whole group: one wave computes it
- * for up to 16 / (num_q_heads / num_kv_heads) members at once.
+ * prefixes).  The result of pa_decode_ex, but the blocks every member of a
+ * group holds in common are read once for the whole group: one wave
+ * computes a piece of them for up to 16 / (num_q_heads / num_kv_heads)
+ * members at once.
+ * Split ([VF] §1.1: segments are processed independently, then merged).
+ * Group g's shared region is its first group_shared[g] blocks, T tokens.  A
+ * member whose context (L tokens) extends past it, 0 < T < L, is split at
+ * T: the region in partitions [i ps, min((i + 1) ps, T)), computed for the
+ * group, then the member's own tokens in partitions [T + j ps, min(T + (j +
+ * 1) ps, L)).  No member reads a shared block itself, whatever T is.  Other
+ * sequences are split as in pa_decode_ex.  With T a multiple of the
+ * partition size ps the partitions are pa_decode_ex's and so is the result,
+ * bit for bit; otherwise the merge adds the same terms split at other
+ * points, and the result differs from pa_decode_ex's by that rounding.
  *   group_offsets  [num_groups + 1] int32 device: group g is the run of
  *                  sequences group_offsets[g] .. group_offsets[g + 1] - 1;
  *                  the first is its leader, whose table is read.
@@ -272,16 +282,14 @@ pa_status pa_prefill_chunk(float *out, const void *q,
  *                  max_group_size members); otherwise it is decoded alone.
  *   group_shared   [num_groups] int32 device: leading block-table entries
  *                  (blocks) that every member holds equal to the leader's
- *                  (pa_decode_groups derives them).  The library shares the
- *                  whole partitions they cover at the partition size it runs
- *                  with, so the count does not depend on partition_size;
- *                  each member shares at most its partition count - 1.  A
- *                  member whose own entries differ from the leader's over a
- *                  shared partition gets a NaN row.
+ *                  (pa_decode_groups derives them).  A member whose own
+ *                  entries differ from the leader's over a shared partition
+ *                  gets a NaN row.
  *   num_groups     >= 0 (0: pa_decode_ex).
  *   max_group_size host bound of the group sizes (>= 1 when num_groups > 0).
+ *   workspace      at least pa_decode_grouped_workspace_size(...) bytes.
  * dtype must be BF16 (the fp32 path has no grouped kernel: UNSUPPORTED).
- * Workspace, flags and errors as pa_decode_ex. */
+ * Flags and errors as pa_decode_ex. */
 pa_status pa_decode_grouped(float *out, const void *q,
                             const void *k_cache, const void *v_cache,
                             const int32_t *block_tables,
@@ -297,6 +305,33 @@ pa_status pa_decode_grouped(float *out, const void *q,
                             int32_t max_group_size, void *workspace,
                             size_t workspace_bytes, pa_dtype dtype,
                             uint32_t flags, void *stream);
+
+/* Bytes of device workspace pa_decode_grouped (and pa_decode_grouped_fp8)
+ * need: the partials of ceil(max_context_len / partition_size) + 1
+ * partitions per (sequence, query head) -- one more than pa_decode_ex's, for
+ * a member split at its group's shared region -- so never 0 for a batch;
+ * (size_t)-1 on invalid sizes. */
+size_t pa_decode_grouped_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len,
+                                        int32_t partition_size);
+
+/* Partition size for pa_decode_grouped on this batch, from host copies of
+ * its lengths and group arrays (the arguments of pa_decode_grouped).  The
+ * grouped grid holds a wave per (kv head, group chunk, shared partition)
+ * and per (kv head, sequence, own partition), each of which pays a start-up
+ * before it streams ([VE] §3.3: decode is bound by memory bandwidth).
+ * Starting from pa_decode_default_partition, the size doubles while that
+ * grid keeps at least 2048 waves, up to 4096 tokens; with no group sharing
+ * anything it is pa_decode_default_partition.  Always a multiple of 32 and
+ * of block_size.  0 on invalid arguments (pa_last_error says which). */
+int32_t pa_decode_grouped_partition(const int32_t *context_lens,
+                                    const int32_t *group_offsets,
+                                    const int32_t *seq_group,
+                                    const int32_t *group_shared, int32_t num_seqs,
+                                    int32_t num_groups, int32_t max_group_size,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t block_size, int32_t max_context_len);
 
 /* Group arrays for pa_decode_grouped from host block tables ([VE] §3.1:
  * sequences forked from one prompt hold its physical blocks).  Host memory
@@ -358,7 +393,7 @@ pa_status pa_decode_fp8(float *out, const void *q, const void *k_cache, const vo
                         size_t workspace_bytes, uint32_t flags, void *stream);
 
 /* pa_decode_grouped over fp8 (E4M3) caches with their scales, as
- * pa_decode_fp8; group arguments as pa_decode_grouped. */
+ * pa_decode_fp8; group arguments and workspace as pa_decode_grouped. */
 pa_status pa_decode_grouped_fp8(float *out, const void *q,
                                 const void *k_cache, const void *v_cache,
                                 const int32_t *block_tables,

@@ -56,7 +56,7 @@ EXPORTED = (
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
-    "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
+    "pa_decode_grouped_workspace_size", "pa_decode_grouped_partition", "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
     "pa_prefix_host_stats", "pa_sched_add_samples",
 )
 
@@ -127,6 +127,7 @@ def _declare(lib):
         "pa_read_stream": (st, [vp, ctypes.c_size_t, vp, vp]),
         "pa_decode_default_partition": (i32, [i32, i32, i32, i32]),
         "pa_decode_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "pa_decode_grouped_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                            i32, vp, sz, ctypes.c_int, vp]),
         "pa_decode_ex": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -180,6 +181,8 @@ def _declare(lib):
         "pa_decode_noalloc": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                    f32, i32, i32, ctypes.c_int, ctypes.c_uint32, vp]),
         "pa_decode_groups": (st, [pi32, i32, pi32, pi32, i32, i32, i32, pi32, pi32, pi32]),
+        "pa_decode_grouped_partition": (i32, [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32,
+                                              i32, i32]),
         "pa_decode_grouped_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, i32, i32, vp, vp, vp, i32, i32, vp, sz,
                                        ctypes.c_uint32, vp]),
@@ -306,11 +309,22 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
     return int(n)
 
 
+def pa_decode_grouped_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, partition_size=0) -> int:
+    n = _lib.pa_decode_grouped_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(PA_ERR_INVALID_ARG, "pa_decode_grouped_workspace_size: invalid sizes")
+    return int(n)
+
+
 def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                     partition_size=0, device="cuda"):
-    """A device buffer large enough for pa_decode's split-K partials (or None)."""
-    n = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                 max_context_len, partition_size)
+                     partition_size=0, device="cuda", grouped=False):
+    """A device buffer large enough for the split-K partials of pa_decode
+    (grouped: of pa_decode_grouped, which needs more), or None."""
+    size = pa_decode_grouped_workspace_size if grouped else pa_decode_workspace_size
+    n = size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+             partition_size)
     return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -388,6 +402,24 @@ def decode_groups(tables, lens, seq_group, block_size):
         raise ValueError(_lib.pa_last_error().decode(errors="replace"))
     _check(st)
     return offsets, seq_group, shared[:G], largest.value
+
+
+def decode_grouped_partition(lens, group_offsets, seq_group, group_shared, max_group_size,
+                             num_q_heads, num_kv_heads, block_size, max_context_len) -> int:
+    """pa_decode_grouped_partition on host arrays (those decode_groups
+    returns): the partition size for a grouped decode of this batch."""
+    import numpy as np
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    offsets = np.ascontiguousarray(group_offsets, dtype=np.int32)
+    seq_group = np.ascontiguousarray(seq_group, dtype=np.int32)
+    shared = np.ascontiguousarray(group_shared, dtype=np.int32)
+    ps = _lib.pa_decode_grouped_partition(_i32p(lens), _i32p(offsets), _i32p(seq_group),
+                                          _i32p(shared), len(lens), len(shared),
+                                          int(max_group_size), num_q_heads, num_kv_heads,
+                                          block_size, int(max_context_len))
+    if ps <= 0:
+        raise PAError(PA_ERR_INVALID_ARG, _lib.pa_last_error().decode(errors="replace"))
+    return int(ps)
 
 
 def pa_decode_grouped_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,

@@ -42,34 +42,6 @@ pa_status check_geometry(const char *fn, int32_t num_kv_heads, int32_t head_dim,
     return PA_OK;
 }
 
-// Partition size in tokens: a multiple of 32 (the decode step) and of the
-// block size.  Start at 512 and halve while the grid would leave the 256
-// compute units short of work (about 8 waves each).  With few (sequence,
-// kv head) pairs -- a handful of long contexts -- every wave streams a full
-// partition, and longer partitions amortise each wave's start-up (length,
-// table slice, first loads) and shrink the merge: grow up to 4096 tokens
-// while the grid keeps at least 1024 waves (4 per compute unit).
-int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                          int32_t max_context_len) {
-    const int32_t unit = block_size > 32 ? block_size : 32;
-    const int64_t max_len = max_context_len > 0 ? max_context_len : 1;
-    int32_t ps = 512;
-    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-    while (ps / 2 >= unit && (ps / 2) % unit == 0 && pairs * ceil_div(max_len, ps) < 2048)
-        ps /= 2;
-    if (pairs <= 256)
-        while (ps < 4096 && pairs * ceil_div(max_len, 2 * ps) >= 1024) ps *= 2;
-    // Then at most 16 partitions for the longest context, while the grid
-    // keeps at least 512 waves: each partition's wave starts with a chain of
-    // dependent loads that a longer partition amortises (on one box: the GQA
-    // batch of up to 8192 tokens 184.5 -> 178.9 us at 1024, 8 x 32768 196.4
-    // -> 189.0 us at 4096; batches of up to 4096 tokens keep 512, where 1024
-    // is no faster).
-    while (ps < 4096 && max_len >= 16 * (int64_t)ps && pairs * ceil_div(max_len, 2 * ps) >= 512)
-        ps *= 2;
-    return ps;
-}
-
 // Address at which the GPU reaches memory p: p itself for device memory, the
 // mapped address for pinned host memory; nullptr for anything else
 // (pageable host memory, which a kernel must never touch).
@@ -201,22 +173,42 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_block
     return pa::ok();
 }
 
-int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                                    int32_t max_context_len) {
-    return default_partition(num_seqs, num_kv_heads, block_size, max_context_len);
-}
+}  // extern "C"
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
-                                int32_t partition_size) {
+namespace {
+
+// Workspace bytes of a decode call; grouped: one partition more per row.
+size_t workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                      int32_t partition_size, bool grouped) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || max_context_len < 0 || partition_size < 0)
         return (size_t)-1;
     const int32_t ps = partition_size ? partition_size
-                                      : default_partition(num_seqs, num_kv_heads, block_size,
+                                      : pa::default_partition(num_seqs, num_kv_heads, block_size,
                                                           max_context_len);
     const int64_t np_max = ceil_div(max_context_len > 0 ? max_context_len : 1, ps);
-    return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_max);
+    const int64_t np_slots = grouped ? np_max + 1 : np_max;
+    return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_slots);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size) {
+    return workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, partition_size, false);
+}
+
+size_t pa_decode_grouped_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len,
+                                        int32_t partition_size) {
+    return workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, partition_size, true);
 }
 
 pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *v_cache,
@@ -297,16 +289,20 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 16))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     const int32_t ps = partition_size ? partition_size
-                                      : default_partition(num_seqs, num_kv_heads, block_size,
+                                      : pa::default_partition(num_seqs, num_kv_heads, block_size,
                                                           max_context_len);
     const int64_t np_max = ceil_div(max_context_len > 0 ? max_context_len : 1, ps);
-    const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_max);
+    // a grouped call's members may split at their shared region's end: one
+    // partition more per sequence at most
+    const bool grouped = grp && grp->num_groups > 0;
+    const int64_t np_slots = grouped ? np_max + 1 : np_max;
+    const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np_slots);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return pa::fail(PA_ERR_INVALID_ARG, "%s: workspace %zu bytes, need %zu", fn,
                         workspace ? workspace_bytes : (size_t)0, need);
-    if (np_max * num_kv_heads * (int64_t)num_seqs > kMaxDecodeItems)
+    if (np_slots * num_kv_heads * (int64_t)num_seqs > kMaxDecodeItems)
         return pa::fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions x kv heads x sequences > %lld",
-                        fn, (long long)(np_max * num_kv_heads * (int64_t)num_seqs),
+                        fn, (long long)(np_slots * num_kv_heads * (int64_t)num_seqs),
                         (long long)kMaxDecodeItems);
     if (num_seqs == 0) return pa::ok();
 
@@ -327,19 +323,22 @@ pa_status decode_impl(const char *fn, float *out, const void *q, const void *k_c
     p.max_context_len = max_context_len;
     p.partition_size = ps;
     p.np_max = (int32_t)np_max;
+    p.np_slots = (int32_t)np_slots;
     p.scale_log2 = fp8 ? scale * k_scale * kLog2e : scale * kLog2e;
     p.kv_reuse = (flags & PA_DECODE_KV_REUSE) != 0;
     p.kv_fp8 = fp8;
     p.v_scale = fp8 ? v_scale : 1.f;
-    if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_max, &p.ws_ml,
+    if (need > 0) pa::decode_workspace_split(workspace, num_seqs, num_q_heads, np_slots, &p.ws_ml,
                                              &p.ws_o);
-    if (grp && grp->num_groups > 0 && np_max > 1) {
+    if (grouped) {
         // one wave serves 16 / G members; chunks cover max_group_size members
         const int64_t mpw = kMaxGroup / (num_q_heads / num_kv_heads);
         const int64_t chunks = (grp->max_group_size + mpw - 1) / mpw;
-        if ((np_max - 1) * chunks * grp->num_groups * num_kv_heads > kMaxDecodeItems)
-            return pa::fail(PA_ERR_UNSUPPORTED, "%s: %lld group work items > %lld", fn,
-                            (long long)((np_max - 1) * chunks * grp->num_groups * num_kv_heads),
+        const int64_t group_items = np_max * chunks * grp->num_groups * num_kv_heads;
+        const int64_t seq_items = np_slots * num_kv_heads * (int64_t)num_seqs;
+        if (group_items + seq_items > kMaxDecodeItems)
+            return pa::fail(PA_ERR_UNSUPPORTED, "%s: %lld group + %lld sequence work items > %lld",
+                            fn, (long long)group_items, (long long)seq_items,
                             (long long)kMaxDecodeItems);
         p.seq_group = grp->seq_group;
         p.grp_offsets = grp->offsets;

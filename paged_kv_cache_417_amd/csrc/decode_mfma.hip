@@ -43,6 +43,7 @@
 // score scale and the V scale into the output, both in fp32.
 #include <type_traits>
 
+#include "decode_split.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -207,38 +208,14 @@ __device__ __forceinline__ void compute_step(const StepRegs<D> &r, const bf16x8 
     }
 }
 
-// Leading partitions of sequence s (np partitions in all) that its group
-// computes; 0 when s is in no group.  The group's shared count is in blocks;
-// the partitions it covers wholly are shared.  The per-sequence kernel and
-// the group kernel both decide membership with this one function, so every
-// partition is computed by exactly one of them.  The last partition is never
-// shared, so the merge always sees at least two partitions or none is
-// shared.
-__device__ __forceinline__ int32_t shared_parts(const DecodeParams &p, int s, int32_t np) {
-    if (!p.seq_group) return 0;
-    const int32_t g = p.seq_group[s];
-    if (g < 0 || g >= p.num_groups) return 0;
-    const int32_t lo = p.grp_offsets[g], hi = p.grp_offsets[g + 1];
-    if (lo < 0 || s < lo || s >= hi || s - lo >= p.grp_cover) return 0;
-    const int64_t parts = (int64_t)p.grp_shared[g] * p.block_size / p.partition_size;
-    return (int32_t)max((int64_t)0, min(parts, (int64_t)np - 1));
-}
-
-// Whether a context length can be walked: 0 <= L <= max_context_len and its
-// blocks fit the table row.
-__device__ __forceinline__ bool bad_length(const DecodeParams &p, int32_t L, int block_size) {
-    const int32_t nb = (L + block_size - 1) / block_size;
-    return L < 0 || L > p.max_context_len || nb > p.table_stride;
-}
-__device__ __forceinline__ int32_t num_parts(const DecodeParams &p, int32_t L, bool bad) {
-    return bad ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-}
-
-// The walk over partition `part` of sequence s (context of L tokens in np
-// partitions) for kv head kvh, or its NaN rows when the length is bad.
+// The walk over partition `part` of sequence s (np partitions in all),
+// tokens [t_begin, t_end), for kv head kvh, or its NaN rows when the length
+// is bad.  Only the sequence's last partition may end off a 32-token step,
+// at its context length t_end.
 template <int D, int BS, bool NT, bool FP8>
 __device__ __forceinline__ void decode_part(const DecodeParams &p, int kvh, int s, int part,
-                                            int32_t L, int32_t np, bool bad_len) {
+                                            int32_t t_begin, int32_t t_end, int32_t np,
+                                            bool bad_len) {
     using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;
@@ -272,8 +249,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams &p, int kvh, int 
     const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
     const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
     const int32_t *table = p.block_tables + (int64_t)s * p.table_stride;
-    const int32_t t_begin = part * p.partition_size;
-    const int32_t t_end = min(L, t_begin + p.partition_size);
+    const int32_t L = t_end;  // tokens at or past it are masked (last step only)
     const int32_t nsteps = (t_end - t_begin + 31) / 32;
     const bool has_tail = ((t_end - t_begin) & 31) != 0;
 
@@ -370,7 +346,7 @@ __device__ __forceinline__ void decode_part(const DecodeParams &p, int kvh, int 
             *reinterpret_cast<floatx4 *>(out_row + 16 * j + 4 * g) = o;
         }
     } else {
-        const int64_t slot = ((int64_t)s * p.num_q_heads + h) * p.np_max + part;
+        const int64_t slot = ((int64_t)s * p.num_q_heads + h) * p.np_slots + part;
         float *o_part = p.ws_o + slot * D;
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
@@ -387,29 +363,35 @@ __device__ __forceinline__ void decode_part(const DecodeParams &p, int kvh, int 
 
 
 // One per-sequence work item of the slot grid: (kv head, sequence,
-// partition slot) of the 1-D grid index.
-template <int D, int BS, bool NT, bool FP8>
+// partition slot) of the 1-D grid index.  GROUPED: a grouped call, whose
+// shared partitions are the group kernel's and whose members' private
+// partitions start at the end of their group's shared region.
+template <int D, int BS, bool NT, bool FP8, bool GROUPED>
 __device__ __forceinline__ void decode_seq_item(const DecodeParams &p, uint32_t index) {
     const DecodeItem item = decode_item(index, p.num_kv_heads, p.num_seqs);
     const int32_t L = p.context_lens[item.seq];
+    const int32_t gid = GROUPED ? p.seq_group[item.seq] : -1;  // loaded beside L
     const bool bad_len = bad_length(p, L, BS);
-    const int32_t np = num_parts(p, L, bad_len);
-    const int part = decode_partition(item.slot, np, p.np_max);
-    // shared partitions are the group kernel's; a last partition never is
-    // (no group lookups for it)
-    if (part < 0 || (part < np - 1 && part < shared_parts(p, item.seq, np))) return;
-    decode_part<D, BS, NT, FP8>(p, item.kvh, item.seq, part, L, np, bad_len);
+    const SeqSplit sp = GROUPED ? seq_split(p, item.seq, gid, L, bad_len)
+                                : SeqSplit{num_parts(p, L, bad_len), 0, 0};
+    const int part = decode_partition(item.slot, sp.np, p.np_slots);
+    if (part < sp.shared) return;  // no partition in this slot, or the group's
+    const int32_t t_begin = sp.t_shared + (part - sp.shared) * p.partition_size;
+    const int32_t t_end = bad_len ? t_begin : min(L, t_begin + p.partition_size);
+    decode_part<D, BS, NT, FP8>(p, item.kvh, item.seq, part, t_begin, t_end, sp.np, bad_len);
 }
 
 // Shared partitions of a group of sequences, one wave per (kv head, group,
-// member chunk, partition).  The wave reads the partition's K/V once, through
+// member chunk, partition).  Partition i of the group's shared region (T
+// tokens) is [i ps, min((i + 1) ps, T)); the wave reads its K/V once, through
 // the leader's block table, and serves 16 / G members at once: MFMA column n
 // is member n / G of the chunk, query head n % G of the kv head (the same
 // layout the per-sequence kernel gives the G heads of one sequence), so each
-// member's partial is computed exactly as the per-sequence kernel would.
-// A member whose own table differs from the leader's over the partition gets
-// NaN partials (its row comes out NaN); a bad block id makes every member's
-// partials NaN.
+// member's partial is the one the per-sequence walk of that token range
+// gives.  Members whose context ends at or before T are not served (they
+// are decoded alone, member_shares()).  A member whose own table differs
+// from the leader's over the partition gets NaN partials (its row comes out
+// NaN); a bad block id makes every member's partials NaN.
 template <int D, int BS, bool NT, bool FP8>
 __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_t item) {
     using Regs = std::conditional_t<FP8, StepRaw8<D>, StepRegs<D>>;
@@ -427,13 +409,13 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     // loads: every load that decides which columns are live, and the
     // members' table slices, go out in that one round.
     const int32_t lo = p.grp_offsets[grp], hi = p.grp_offsets[grp + 1];
-    const int64_t grp_parts = (int64_t)p.grp_shared[grp] * p.block_size / p.partition_size;
+    const int64_t T = shared_tokens(p, p.grp_shared[grp]);
     if (lo < 0 || lo >= p.num_seqs) return;
     const int G = p.num_q_heads / p.num_kv_heads;
     const int mpw = 16 / G;  // members per wave
-    // No member is live unless the group shares this partition and the
-    // chunk's first member lies in the group's run (shared_parts() below).
-    if (part >= grp_parts || lo + chunk * mpw >= hi) return;
+    // No member is live unless the partition starts inside the shared region
+    // and the chunk's first member lies in the group's run.
+    if ((int64_t)part * p.partition_size >= T || lo + chunk * mpw >= hi) return;
     // this lane's column: member s_n, query head h
     const int32_t s_n = lo + chunk * mpw + n / G;
     const int h = kvh * G + n % G;
@@ -442,11 +424,13 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     const uint16_t *kc = reinterpret_cast<const uint16_t *>(p.k_cache);
     const uint16_t *vc = reinterpret_cast<const uint16_t *>(p.v_cache);
     const int32_t *table = p.block_tables + (int64_t)lo * p.table_stride;
-    // A shared partition lies wholly inside every live member's context.
+    // A shared partition lies wholly inside every live member's context
+    // (T < L_n); only the region's last one may end off a 32-token step.
     const int32_t t_begin = part * p.partition_size;
-    const int32_t t_end = t_begin + p.partition_size;
-    const int32_t L = t_end;  // no token of the partition is masked
-    const int32_t nsteps = p.partition_size / 32;
+    const int32_t t_end = (int32_t)min((int64_t)t_begin + p.partition_size, T);
+    const int32_t L = t_end;  // tokens at or past it are masked
+    const int32_t nsteps = (t_end - t_begin + 31) / 32;
+    const bool has_tail = ((t_end - t_begin) & 31) != 0;
     const int32_t b_first = t_begin / BS, b_last = (t_end - 1) / BS;
 
     // one round of loads: the member's group and length, q, the leader's
@@ -473,15 +457,11 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
                     : 0;
     }
 
-    // a column is live when its sequence belongs to this group's run and the
-    // group computes this partition for it: shared_parts() for g = grp
-    bool live = false;
-    if (in_range && grp_of == grp && s_n < hi && s_n - lo < p.grp_cover) {
-        const int32_t nb = (L_n + BS - 1) / BS;
-        const bool bad_len = L_n < 0 || L_n > p.max_context_len || nb > p.table_stride;
-        const int32_t np = bad_len ? 1 : max(1, (L_n + p.partition_size - 1) / p.partition_size);
-        live = part < max((int64_t)0, min(grp_parts, (int64_t)np - 1));
-    }
+    // a column is live when its sequence belongs to this group's run and
+    // its context extends past the shared region: member_shares(), the test
+    // the per-sequence items and the merge apply
+    const bool live = in_range && grp_of == grp &&
+                      member_shares(p, s_n, grp_of, lo, hi, T, L_n, bad_length(p, L_n, BS));
     if (!__any(live)) return;
     if (!live) {
 #pragma unroll
@@ -545,9 +525,12 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
         } else {
             rp = &raw;
         }
-        compute_step<D, false>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        if (has_tail && st == nsteps - 1)
+            compute_step<D, true>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
+        else
+            compute_step<D, false>(*rp, qb, t0, L, p.scale_log2, m, lsum, acc, lane);
     };
-    // the same ping-pong as the per-sequence kernel (the partition is whole)
+    // the same ping-pong as the per-sequence kernel
     {
         Regs ra, rb;
         issue(ra, 0);
@@ -566,7 +549,7 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
     const float qnan = __builtin_nanf("");
     const float vs = FP8 ? p.v_scale : 1.f;
     const bool bad = bad_block || bad_table;
-    const int64_t slot = ((int64_t)s_n * p.num_q_heads + h) * p.np_max + part;
+    const int64_t slot = ((int64_t)s_n * p.num_q_heads + h) * p.np_slots + part;
     float *o_part = p.ws_o + slot * D;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
@@ -585,7 +568,7 @@ __device__ __forceinline__ void decode_group_item(const DecodeParams &p, uint32_
 template <int D, int BS, bool NT, bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(
     DecodeParams p) {
-    decode_seq_item<D, BS, NT, FP8>(p, blockIdx.x);
+    decode_seq_item<D, BS, NT, FP8, false>(p, blockIdx.x);
 }
 
 // Grouped decode in one grid: the first group_items workgroups compute the
@@ -598,7 +581,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     if (blockIdx.x < group_items)
         decode_group_item<D, BS, NT, FP8>(p, blockIdx.x);
     else
-        decode_seq_item<D, BS, NT, FP8>(p, blockIdx.x - group_items);
+        decode_seq_item<D, BS, NT, FP8, true>(p, blockIdx.x - group_items);
 }
 
 // ---------------------------------------------------------------------------
@@ -689,7 +672,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
         for (int c = 0; c < C; ++c) m[c] = __ballot(badc[c]);
         pick(m, e);
-        decode_part<D, BS, NT, FP8>(p, kvh, s, 0, L, 1, true);
+        decode_part<D, BS, NT, FP8>(p, kvh, s, 0, 0, 0, 1, true);
         return;
     }
     e -= nbad;
@@ -737,16 +720,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     s = __builtin_amdgcn_readfirstlane(s);
     part = __builtin_amdgcn_readfirstlane(part);
     L = __builtin_amdgcn_readfirstlane(L);
-    decode_part<D, BS, NT, FP8>(p, kvh, s, part, L, num_parts(p, L, false), false);
+    const int32_t t_begin = part * p.partition_size;
+    decode_part<D, BS, NT, FP8>(p, kvh, s, part, t_begin, min(L, t_begin + p.partition_size),
+                                num_parts(p, L, false), false);
 }
 
 template <int D, int BS>
 void launch_one(const DecodeParams &p, hipStream_t s) {
-    const int64_t seq_items = (int64_t)p.np_max * p.num_kv_heads * p.num_seqs;
-    if (p.seq_group && p.num_groups > 0 && p.np_max > 1) {
-        // shared partitions: all but a sequence's last
+    const int64_t seq_items = (int64_t)p.np_slots * p.num_kv_heads * p.num_seqs;
+    if (p.seq_group && p.num_groups > 0) {
+        // shared partitions: ceil(T / ps) <= np_max for a region T shorter
+        // than a member's context
         const int64_t group_items =
-            (int64_t)(p.np_max - 1) * p.grp_chunks * p.num_groups * p.num_kv_heads;
+            (int64_t)p.np_max * p.grp_chunks * p.num_groups * p.num_kv_heads;
         const dim3 grid((unsigned)(group_items + seq_items));
 #define PA_GROUPED(NTv, FP8v)                                                                     \
     hipLaunchKernelGGL((decode_grouped_kernel<D, BS, NTv, FP8v>), grid, dim3(64), 0, s, p,      \

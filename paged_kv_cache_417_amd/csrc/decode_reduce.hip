@@ -8,23 +8,26 @@
 // the sum of 2^(z - m_p) over its tokens, and the matching unnormalised
 // weighted sum of V rows.  With M = max_p m_p and w_p = 2^(m_p - M):
 //   out = sum_p w_p o_p / sum_p w_p l_p.
-// Partitions are visited in index order, so the result is deterministic.
+// Partitions are visited in index order (token order), so the result is
+// deterministic.  A grouped call's members split at their group's shared
+// region (decode_split.h), so the merge looks their split up the same way.
+#include "decode_split.h"
 #include "device_common.h"
 #include "launch.h"
 
 namespace pa {
 
 size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                              int64_t np_max) {
-    if (np_max <= 1) return 0;
-    const int64_t rows = num_seqs * num_q_heads * np_max;
+                              int64_t np_slots) {
+    if (np_slots <= 1) return 0;
+    const int64_t rows = num_seqs * num_q_heads * np_slots;
     const int64_t ml = (rows * 2 * 4 + 255) / 256 * 256;
     return (size_t)(ml + rows * head_dim * 4);
 }
 
-void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int64_t np_max,
+void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int64_t np_slots,
                             float **ml, float **o) {
-    const int64_t rows = num_seqs * num_q_heads * np_max;
+    const int64_t rows = num_seqs * num_q_heads * np_slots;
     const int64_t ml_bytes = (rows * 2 * 4 + 255) / 256 * 256;
     *ml = reinterpret_cast<float *>(ws);
     *o = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + ml_bytes);
@@ -47,11 +50,12 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(Decode
     const int s = (int)(item / p.num_q_heads);
     const int h = (int)(item - (int64_t)s * p.num_q_heads);
     const int32_t L = p.context_lens[s];
-    const int32_t nb = (L + p.block_size - 1) / p.block_size;
-    if (L < 0 || L > p.max_context_len || nb > p.table_stride) return;  // row already NaN
-    const int32_t np = max(1, (L + p.partition_size - 1) / p.partition_size);
+    const int32_t gid = p.seq_group ? p.seq_group[s] : -1;
+    const bool bad_len = bad_length(p, L, p.block_size);
+    if (bad_len) return;  // row already NaN
+    const int32_t np = seq_split(p, s, gid, L, false).np;
     if (np <= 1) return;  // written directly by the partition kernel
-    const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.np_max;
+    const int64_t base = ((int64_t)s * p.num_q_heads + h) * p.np_slots;
     const float *ml = p.ws_ml + 2 * base;
     const float *op = p.ws_o + base * D + kDpl * lane;
 
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(Decode
 }  // namespace
 
 int launch_decode_reduce(const DecodeParams &p, void *stream) {
-    if (p.np_max <= 1 || p.num_seqs == 0) return 0;
+    if (p.np_slots <= 1 || p.num_seqs == 0) return 0;
     const int64_t items = (int64_t)p.num_seqs * p.num_q_heads;
     const dim3 grid((unsigned)((items + kReduceWaves - 1) / kReduceWaves)), block(64 * kReduceWaves);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

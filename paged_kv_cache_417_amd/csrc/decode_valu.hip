@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     const int32_t nb = (L + BS - 1) / BS;
     const bool bad_len = L < 0 || L > p.max_context_len || nb > p.table_stride;
     const int32_t np = bad_len ? 1 : max(1, (L + p.partition_size - 1) / p.partition_size);
-    const int part = decode_partition(item.slot, np, p.np_max);
+    const int part = decode_partition(item.slot, np, p.np_slots);
     if (part < 0) return;
     const int G = p.num_q_heads / p.num_kv_heads;
     const int h0 = kvh * G;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
                 p.out[((int64_t)s * p.num_q_heads + h) * D + lane + 64 * e] =
                     bad_block ? qnan : acc[gi][e] * inv;
         } else {
-            const int64_t slot = ((int64_t)s * p.num_q_heads + h) * p.np_max + part;
+            const int64_t slot = ((int64_t)s * p.num_q_heads + h) * p.np_slots + part;
 #pragma unroll
             for (int e = 0; e < DPL; ++e)
                 p.ws_o[slot * D + lane + 64 * e] = bad_block ? qnan : acc[gi][e];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 int launch_decode_valu(const DecodeParams &p, pa_dtype dtype, void *stream) {
     if (p.num_seqs == 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)((int64_t)p.np_max * p.num_kv_heads * p.num_seqs));
+    const dim3 grid((unsigned)((int64_t)p.np_slots * p.num_kv_heads * p.num_seqs));
     if (dtype == PA_DTYPE_F32) {
         if (p.head_dim == 64)
             hipLaunchKernelGGL((decode_valu_kernel<uint32_t, 64>), grid, dim3(64), 0, s, p);

@@ -9,8 +9,10 @@
 // A group is a run of consecutive sequences of the decode batch.  What the
 // members share is read off their block tables: the leading entries that
 // every member's table holds equal to the leader's (its first member's),
-// counted over the blocks every member fills completely.  The kernel turns
-// that count into whole partitions of the partition size it runs with.
+// counted over the blocks every member fills completely.  The decode splits
+// that region into partitions of the size it runs with, the last one ending
+// where the region ends, and each member's own tokens after it.
+
 #include <cstdint>
 
 #include "pa_internal.h"

@@ -26,8 +26,8 @@ struct DecodeParams {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
-    float *ws_ml;      // [S][Hq][np_max][2] (running max in log2 units, sum)
-    float *ws_o;       // [S][Hq][np_max][D] unnormalised partial outputs
+    float *ws_ml;      // [S][Hq][np_slots][2] (running max in log2 units, sum)
+    float *ws_o;       // [S][Hq][np_slots][D] unnormalised partial outputs
     int32_t table_stride;
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -38,6 +38,8 @@ struct DecodeParams {
     int32_t max_context_len;
     int32_t partition_size;
     int32_t np_max;    // ceil(max_context_len / partition_size), >= 1
+    int32_t np_slots;  // partitions per sequence the grid and workspace hold:
+                       // np_max, one more in a grouped call (decode_split.h)
     float scale_log2;  // scale * log2(e) (times the K scale for an fp8 cache)
     bool kv_reuse;     // keep K/V cached (shared blocks) instead of streaming them
     bool kv_fp8;       // K/V hold OCP E4M3 codes (q stays bf16)
@@ -45,9 +47,11 @@ struct DecodeParams {
     // Groups of sequences that share leading blocks (null seq_group: none).
     // Sequence s belongs to group g = seq_group[s] when 0 <= g < num_groups,
     // grp_offsets[g] <= s < grp_offsets[g + 1] and s - grp_offsets[g] <
-    // grp_cover; its first min(grp_shared[g], np(s) - 1) partitions are then
-    // computed once for the whole group, through the table of sequence
-    // grp_offsets[g] (the leader).
+    // grp_cover.  When its context extends past the group's shared region
+    // (the first grp_shared[g] blocks) that region's partitions are computed
+    // once for the whole group, through the table of sequence grp_offsets[g]
+    // (the leader), and its own partitions start where the region ends
+    // (decode_split.h).
     const int32_t *seq_group;
     const int32_t *grp_offsets;
     const int32_t *grp_shared;
@@ -79,10 +83,11 @@ struct PrefillParams {
     float v_scale;     // value of a V code = code * v_scale (1 for bf16)
 };
 
-// Workspace layout shared by the decode kernels and the split-K reduce.
+// Workspace layout shared by the decode kernels and the split-K reduce:
+// np_slots partials per (sequence, query head) row (0 bytes when <= 1).
 size_t decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                              int64_t np_max);
-void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int64_t np_max,
+                              int64_t np_slots);
+void decode_workspace_split(void *ws, int64_t num_seqs, int64_t num_q_heads, int64_t np_slots,
                             float **ml, float **o);
 
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,

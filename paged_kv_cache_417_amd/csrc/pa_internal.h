@@ -16,4 +16,8 @@ pa_status ok();
 // The allocator's positions per block.
 int32_t block_size(const pa_allocator *a);
 
+// Default decode partition size (pa_decode_default_partition).
+int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                          int32_t max_context_len);
+
 }  // namespace pa

@@ -17,14 +17,18 @@ forked by the scheduler once its prompt is written, and its samples decode
 side by side.  A decode batch holding such runs goes through
 pa_decode_grouped, each request's run one group (pa_decode_groups derives the
 blocks its members share), so the shared prompt blocks are read once per
-group; the result is the same as pa_decode's, bit for bit.
+group, at the partition size pa_decode_grouped_partition picks for the batch
+and with the streaming load policy (no block is read twice).  The result is
+pa_decode's up to the merge's rounding (bit for bit where the shared region
+ends on a partition boundary).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (Allocator, Scheduler, decode_groups, decode_workspace, kv_cache_shapes,
+from . import (Allocator, Scheduler, decode_grouped_partition, decode_groups, decode_workspace,
+               kv_cache_shapes,
                pa_cache_write, pa_cache_write_fp8, pa_copy_blocks, pa_decode, pa_decode_fp8,
                pa_decode_grouped, pa_decode_grouped_fp8, pa_prefill_chunk, pa_prefill_chunk_fp8,
                pa_swap_blocks)
@@ -120,8 +124,9 @@ class ServingLoop:
         self.sched = Scheduler(self.alloc, max_num_seqs, max_batched_tokens, max_prefill_chunk)
         self.stride = -(-self.max_ctx // block_size) + 1
         self.pad = num_blocks - 1
+        # sized for pa_decode_grouped, which needs more than pa_decode
         self.ws = decode_workspace(max_num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                   self.max_ctx, 0, device)
+                                   self.max_ctx, 0, device, grouped=True)
         self.scale = head_dim ** -0.5
         self.request_of = {}  # sample sequence id -> its request id
         self.staging = _Staging(device)
@@ -192,7 +197,9 @@ class ServingLoop:
             seq_group = self.decode_grouping(ids)
             if seq_group is not None and self.group_samples:
                 off, sg, shared, largest = decode_groups(t, lens, seq_group, self.bs)
-                groups = (st.put(off), st.put(sg), st.put(shared), largest)
+                gps = decode_grouped_partition(lens, off, sg, shared, largest, self.hq,
+                                               self.hkv, self.bs, self.max_ctx)
+                groups = (st.put(off), st.put(sg), st.put(shared), largest, gps)
                 self.grouped_steps += 1
                 self.shared_block_reads += int(shared.sum())
             i_dec = (st.put(t), st.put(lens))
@@ -224,16 +231,17 @@ class ServingLoop:
             dec_out = torch.empty((len(ids), self.hq, self.d), device=dev)
             t, lens = d[i_dec[0]], d[i_dec[1]]
             if groups:
+                gps = groups[4]
                 groups = (d[groups[0]], d[groups[1]], d[groups[2]], groups[3])
             if self.time_decode:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record()
             if groups and self.fp8:
                 pa_decode_grouped_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
-                                      self.max_ctx, *groups, 0, self.ws, kv_reuse=True)
+                                      self.max_ctx, *groups, gps, self.ws)
             elif groups:
                 pa_decode_grouped(dec_out, q, self.k, self.v, t, lens, self.scale, self.max_ctx,
-                                  *groups, 0, self.ws, kv_reuse=True)
+                                  *groups, gps, self.ws)
             elif self.fp8:
                 pa_decode_fp8(dec_out, q, self.k, self.v, t, lens, self.scale, *self.fp8,
                               self.max_ctx, 0, self.ws, kv_reuse=seq_group is not None)

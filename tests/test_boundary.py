@@ -178,6 +178,25 @@ def test_decode_grouped_rejects(kw, status):
     assert lib.pa_last_error()
 
 
+def test_decode_grouped_workspace_holds_one_more_partition():
+    """A grouped call may split a member at its group's shared region: one
+    partition more per (sequence, head) row than pa_decode's; a workspace
+    sized for pa_decode is refused (nothing is launched on that path)."""
+    plain = pa.pa_decode_workspace_size(2, 8, 8, 128, 16, 5000, 512)
+    need = pa.pa_decode_grouped_workspace_size(2, 8, 8, 128, 16, 5000, 512)
+    rows = 2 * 8 * 11  # ceil(5000 / 512) + 1 partitions
+    assert need == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4 and need > plain
+    rows = 2 * 8 * 2  # one partition, and one for a split member
+    assert pa.pa_decode_grouped_workspace_size(2, 8, 8, 128, 16, 512, 512) == \
+        (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert pa.pa_decode_grouped_workspace_size(0, 8, 8, 128, 16, 512, 512) == 0
+    with pytest.raises(pa.PAError):
+        pa.pa_decode_grouped_workspace_size(2, 8, 8, 128, 16, -1, 512)
+    assert lib.pa_decode_grouped(*grouped_args(maxlen=5000, ps=512, ws=FAKE, wsb=plain)) == \
+        pa.PA_ERR_INVALID_ARG
+    assert b"workspace" in lib.pa_last_error()
+
+
 def test_decode_grouped_empty_batch_and_no_groups_are_ok():
     none = dict(S=0, out=NULL, q=NULL, tables=NULL, lens=NULL)
     assert lib.pa_decode_grouped(*grouped_args(**none)) == pa.PA_OK

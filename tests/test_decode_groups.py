@@ -60,3 +60,87 @@ def test_no_groups():
     off, sg, shd, largest = pa.decode_groups(np.zeros((3, 2), np.int32),
                                              np.full(3, 16, np.int32), np.full(3, -1), 16)
     assert list(off) == [0] and shd.size == 0 and largest == 0
+
+
+def _grid_waves(lens, off, sg, shd, max_group, hq, hkv, bs, ps):
+    """Waves of a grouped grid at partition size ps, counted from the
+    membership rule stated for pa_decode_grouped: a member shares when its
+    context extends past its group's region of shd blocks."""
+    mpw = 16 // (hq // hkv)
+    cover = -(-max_group // mpw) * mpw
+    n = 0
+    sharing = set()
+    for s, L in enumerate(lens):
+        g = sg[s]
+        own = L
+        if g >= 0:
+            T = int(shd[g]) * bs
+            if off[g] <= s < off[g + 1] and s - off[g] < cover and 0 < T < L:
+                own = L - T
+                sharing.add(g)
+        n += max(1, -(-own // ps))
+    for g in sharing:
+        members = min(off[g + 1] - off[g], cover)
+        n += -(-members // mpw) * -(-(int(shd[g]) * bs) // ps)
+    return n * hkv, bool(sharing)
+
+
+@pytest.mark.parametrize("case", ["prefix_shared", "gqa_random", "long_shared", "few_seqs"])
+def test_grouped_partition_doubles_while_the_grid_stays_full(case):
+    """pa_decode_grouped_partition: the plain default, doubled while the
+    grouped grid keeps >= 2048 waves (at most 4096 tokens)."""
+    rng = np.random.default_rng(5)
+    bs, hq, hkv = 16, 32, 32
+    if case == "prefix_shared":  # 16 prompts of 2048 + j tokens x 8 samples
+        n_groups, per = 16, 8
+        T = np.full(n_groups, 2048)
+        lens = np.concatenate([2048 + 1 + i % 15 + rng.integers(1, 513, per)
+                               for i in range(n_groups)])
+    elif case == "gqa_random":
+        hkv, n_groups, per = 8, 32, 4
+        T = rng.integers(512, 4097, n_groups) // bs * bs
+        lens = np.concatenate([t + rng.integers(1, 513, per) for t in T])
+    elif case == "long_shared":
+        n_groups, per = 4, 8
+        T = np.full(n_groups, 16384)
+        lens = np.concatenate([16384 + 5 + rng.integers(1, 513, per) for _ in range(n_groups)])
+    else:
+        n_groups, per = 2, 3
+        T = np.array([320, 96])
+        lens = np.concatenate([t + rng.integers(1, 40, per) for t in T])
+    lens = lens.astype(np.int32)
+    S = len(lens)
+    off = np.arange(0, S + 1, per, dtype=np.int32)
+    sg = (np.arange(S) // per).astype(np.int32)
+    shd = (T // bs).astype(np.int32)
+    maxlen = int(lens.max())
+    ps = pa.decode_grouped_partition(lens, off, sg, shd, per, hq, hkv, bs, maxlen)
+    base = pa.pa_decode_default_partition(S, hkv, bs, maxlen)
+    want = base
+    while want < 4096 and _grid_waves(lens, off, sg, shd, per, hq, hkv, bs, 2 * want)[0] >= 2048:
+        want *= 2
+    assert ps == want and ps % 32 == 0 and ps % bs == 0 and base <= ps <= 4096
+    if case == "prefix_shared":
+        assert ps == 4096  # one shared and one own partition per sample: 4608 waves
+    if case == "few_seqs":
+        assert ps == base  # six sequences: the grid is never full
+
+
+def test_grouped_partition_without_sharing_is_the_plain_default():
+    lens = np.array([900, 950, 1000, 40], np.int32)
+    off = np.array([0, 3, 4], np.int32)
+    sg = np.array([0, 0, 0, 1], np.int32)
+    for shd in (np.array([0, 0], np.int32), np.array([70, 2], np.int32)):  # none, or past L
+        ps = pa.decode_grouped_partition(lens, off, sg, shd, 3, 8, 8, 16, 1000)
+        assert ps == pa.pa_decode_default_partition(4, 8, 16, 1000)
+
+
+def test_grouped_partition_rejects_bad_sizes():
+    lens = np.array([100], np.int32)
+    args = (lens, np.array([0, 1], np.int32), np.zeros(1, np.int32), np.array([2], np.int32))
+    with pytest.raises(pa.PAError):
+        pa.decode_grouped_partition(*args, 0, 8, 8, 16, 100)  # max_group_size 0 with a group
+    with pytest.raises(pa.PAError):
+        pa.decode_grouped_partition(*args, 1, 6, 4, 16, 100)  # heads
+    with pytest.raises(pa.PAError):
+        pa.decode_grouped_partition(*args, 1, 8, 8, 16, -1)

@@ -309,7 +309,7 @@ def _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups, ps, max_group)
     t_dev = torch.as_tensor(tables, device=dev)
     l_dev = torch.as_tensor(lens, device=dev)
     ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                             maxlen, ps, dev)
+                             maxlen, ps, dev, grouped=True)
     ref = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
     pa.pa_decode(ref, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, ps, ws, kv_reuse=True)
     off, sg, shd = (torch.as_tensor(a, device=dev) for a in groups)
@@ -363,10 +363,12 @@ def test_grouped_decode_matches_per_sequence(pa):
 
 
 def test_grouped_decode_chunks_caps_and_loners(pa):
-    """GQA heads (4 members per wave, groups of 6 in two chunks), 64-token
-    partitions, a group left ungrouped, a group whose shared count is far
-    too large (the leader keeps its own table and stays exact, members whose
-    tables diverge get NaN rows), and an empty group run."""
+    """GQA heads (4 members per wave, groups of 6 in two chunks), a group
+    left ungrouped, a group whose shared count is far too large, and an
+    empty group run.  The prompt's 18 common blocks (288 tokens) end on a
+    partition boundary at 32-token partitions (bit-identical to pa_decode)
+    and inside one at 64 (the region's last partition is partial: equal to
+    pa_decode up to the merge's rounding, every row against the oracle)."""
     sh = wl.DecodeShape("grp", 18, 32, 8, 128, 16, 4096, "bf16", wl.SEED_BASE + 44)
     dev = "cuda"
     plan = wl.prefix_plan(num_prompts=3, samples=6, prompt_len=300, seed=sh.seed, max_tail=200)
@@ -375,27 +377,40 @@ def test_grouped_decode_chunks_caps_and_loners(pa):
     S = len(ids)
     stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
     tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
-    ps = 64
     seq_group = np.array([0] * 6 + [1] * 6 + [-1] * 6, np.int32)
     off, sg, shd, _ = pa.decode_groups(tables, lens, seq_group, sh.block_size)
     assert list(shd) == [300 // 16] * 2  # the prompt's full blocks
     gen = wl.make_generator(sh.seed + 1, dev)
     q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
     say("case grouped decode: GQA chunks, loners")
-    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), ps, 6)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), 32, 6)
     assert torch.isfinite(ref).all() and torch.equal(got, ref)
+    want = oracle_decode_all(q, k_pool, v_pool, tables, lens, sh.block_size, sh.scale,
+                             pa.K_AXES, pa.V_AXES)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd), 64, 6)
+    assert torch.isfinite(got).all() and torch.equal(got[12:], ref[12:])  # the loners
+    assert (got - ref).abs().max().item() <= 1e-5
+    err = float(np.abs(got.double().cpu().numpy() - want).max())
+    say(f"  288 shared tokens at 64-token partitions: all rows vs oracle {err:.3e}")
+    assert err <= TOL
 
-    # group 1 claims 100 shared blocks (25 partitions of 64): capped per
-    # member at its own count - 1; past the prompt the members' tables differ
-    # from the leader's
+    # group 1 claims 100 shared blocks (1600 tokens), more than any member's
+    # context: no member shares, each is decoded alone and exactly
     shd_big = shd.copy()
     shd_big[1] = 100
-    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd_big), ps, 6)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd_big), 32, 6)
+    assert torch.equal(got[6:], ref[6:])
+    # a claim of 25 blocks (400 tokens) reaches past the prompt: members whose
+    # context goes past it share it through the leader's table, and their own
+    # tables differ from the leader's there (NaN rows); the leader and the
+    # members whose context ends inside it are exact
+    shd_mid = shd.copy()
+    shd_mid[1] = 25
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off, sg, shd_mid), 32, 6)
     assert torch.equal(got[:6], ref[:6]) and torch.equal(got[12:], ref[12:])
-    assert torch.equal(got[6], ref[6])  # the leader reads its own table
+    assert (got[6] - ref[6]).abs().max().item() <= 1e-5
     for s in range(7, 12):
-        np_s = -(-int(lens[s]) // ps)
-        if np_s - 1 > int(shd[1]) * sh.block_size // ps:  # one past the common prefix
+        if int(lens[s]) > 400:
             assert torch.isnan(got[s]).all(), s
         else:
             assert torch.equal(got[s], ref[s]), s
@@ -405,8 +420,51 @@ def test_grouped_decode_chunks_caps_and_loners(pa):
     off2 = np.array([0, 6, 6, 12], np.int32)
     sg2 = np.array([0] * 6 + [2] * 6 + [-1] * 6, np.int32)
     shd2 = np.array([shd[0], 7, shd[1]], np.int32)
-    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off2, sg2, shd2), ps, 3)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, (off2, sg2, shd2), 32, 3)
     assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("g,bs,ps", [(1, 16, 64), (4, 16, 128), (8, 32, 256), (1, 128, 512)])
+def test_grouped_decode_shared_region_inside_partitions(pa, g, bs, ps):
+    """Prompts of random lengths: each group's shared region ends at an
+    arbitrary block, mostly inside a partition (with 16-token blocks also
+    inside a 32-token step).  Every row against the fp64 oracle and against
+    pa_decode (the same terms merged at other split points); a member whose
+    context ends exactly at the region's end is decoded alone, exactly."""
+    hkv = 2
+    sh = wl.DecodeShape("grp_split", 40, hkv * g, hkv, 128, bs, 2400, "bf16",
+                        wl.SEED_BASE + 47 + g)
+    dev = "cuda"
+    rng = np.random.default_rng(sh.seed)
+    n_prompts, samples = 10, 4
+    plan = wl.PrefixPlan(rng.integers(bs + 1, 1500, n_prompts).astype(np.int32),
+                         rng.integers(1, 300, (n_prompts, samples)).astype(np.int32))
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), bs) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, bs)
+    shd = groups[2]
+    assert (shd == plan.shared_lens // bs).all()
+    # member 2 of prompt 0 decodes only up to the region's end
+    lens = lens.copy()
+    lens[2] = int(shd[0]) * bs
+    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, bs)
+    assert (groups[2] == shd).all()
+    off_ps = [(int(t) * bs) % ps for t in shd]
+    say(f"case grouped split: G {g}, block {bs}, ps {ps}, region ends {off_ps} into a partition")
+    assert sum(o != 0 for o in off_ps) >= n_prompts // 2
+    gen = wl.make_generator(sh.seed + 1, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    ref, got = _decode_pair(pa, sh, q, k_pool, v_pool, tables, lens, groups[:3], ps, samples)
+    assert torch.isfinite(got).all()
+    assert torch.equal(got[2], ref[2])
+    diff = (got - ref).abs().max().item()
+    want = oracle_decode_all(q, k_pool, v_pool, tables, lens, bs, sh.scale, pa.K_AXES, pa.V_AXES)
+    err = float(np.abs(got.double().cpu().numpy() - want).max())
+    say(f"  all {S} rows: vs pa_decode {diff:.2e}, vs oracle {err:.3e}")
+    assert diff <= 1e-5 and err <= TOL
 
 
 def test_grouped_decode_fp8_matches_per_sequence(pa):
@@ -431,7 +489,7 @@ def test_grouped_decode_fp8_matches_per_sequence(pa):
     maxlen = int(lens.max())
     t_dev, l_dev = torch.as_tensor(tables, device=dev), torch.as_tensor(lens, device=dev)
     ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                             maxlen, ps, dev)
+                             maxlen, ps, dev, grouped=True)
     ref = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
     got = torch.full_like(ref, 7.0)
     say("case grouped decode fp8")

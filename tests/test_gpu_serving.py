@@ -142,8 +142,9 @@ def test_serving_loop_parallel_samples(pa, fp8):
     each request's samples as one group (pa_decode_grouped).  Checks: every
     running sequence's cache holds the prompt rows of its request and its own
     rows past the prompt, bit for bit; each grouped decode equals pa_decode
-    on the same batch bit for bit; every decode row against the oracle on
-    every fourth step."""
+    on the same batch up to the merge's rounding (a member's partitions split
+    at the end of its prompt's full blocks); every decode row against the
+    oracle on every fourth step."""
     from paged_kv_cache_417_amd.driver import ServingLoop
     dev = "cuda"
     # a 50-block pool under up to 12 sequences: forked requests are swapped
@@ -214,7 +215,8 @@ def test_serving_loop_parallel_samples(pa, fp8):
                 pa.pa_decode(ref, q, loop.k, loop.v, t, lens, loop.scale, loop.max_ctx, 0, loop.ws,
                              kv_reuse=True)
             torch.cuda.synchronize()
-            assert torch.equal(ref.view(torch.int32), dec.view(torch.int32))
+            assert torch.isfinite(dec).all()
+            assert (ref - dec).abs().max().item() <= 1e-5
             same_checks += 1
         if live and step % 4 == 0:
             torch.cuda.synchronize()
@@ -244,7 +246,7 @@ def test_serving_loop_parallel_samples(pa, fp8):
     st = loop.sched.stats()
     say(f"case serving loop with samples (fp8 {fp8}): {step + 1} steps, stats {st}, "
         f"{loop.grouped_steps} grouped steps ({loop.shared_block_reads} shared blocks), "
-        f"{same_checks} bit-identity, {cache_checks} cache and {oracle_checks} oracle checks")
+        f"{same_checks} grouped-vs-pa_decode, {cache_checks} cache and {oracle_checks} oracle checks")
     assert st["finished"] == n_req and st["forked_samples"] > 0
     assert st["swap_preemptions"] > 0 and st["recompute_preemptions"] > 0
     assert loop.alloc.stats()["num_free"] == nb

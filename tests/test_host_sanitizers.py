@@ -1,7 +1,7 @@
 """The library's host code and the C oracle under AddressSanitizer and
 UndefinedBehaviorSanitizer, on the CPU.
 
-allocator.cpp, scheduler.cpp, groups.cpp and status.cpp (everything in
+allocator.cpp, scheduler.cpp, groups.cpp, partition.cpp and status.cpp (everything in
 libpa that is not a kernel or a launch) are built with g++
 -fsanitize=address,undefined into a CPU-only library, oracle.c likewise with
 gcc; then the CPU suites that drive them -- random operation streams against
@@ -18,7 +18,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "paged_kv_cache_417_amd", "csrc")
-HOST_SOURCES = ("allocator.cpp", "scheduler.cpp", "groups.cpp", "status.cpp")
+HOST_SOURCES = ("allocator.cpp", "scheduler.cpp", "groups.cpp", "partition.cpp",
+                "status.cpp")
 SUITES = ("tests/test_allocator.py", "tests/test_scheduler.py", "tests/test_decode_groups.py",
           "tests/test_oracle_pins.py")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
