@@ -48,7 +48,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mha_7b_traffic.json")
 # the decode partition kernel: the longest-first scan grid (batches of up to
 # 256 sequences, as every bench workload) or the slot grid
 DECODE_KERNEL = ("decode_scan_kernel", "decode_mfma_kernel")
-KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip", "device_common.h", "launch.h")
+KERNEL_SOURCES = ("decode_mfma.hip", "decode_reduce.hip", "decode_split.h", "device_common.h", "launch.h")
 CALIB_PAIRS = 4096
 HOST_WARM = 4  # untimed steps before the host-inclusive loop's timed ones
 
