@@ -39,16 +39,18 @@ struct SeqSplit {
     int32_t np, shared, t_shared;
 };
 
-// Group extent of a shared region of `blocks` blocks, in tokens (clamped:
-// a malformed count cannot overflow).
+// A shared region of `blocks` blocks, in tokens (64-bit, so a malformed
+// count cannot overflow; any region that is not shorter than a member's
+// context shares nothing with it).
 __device__ __forceinline__ int64_t shared_tokens(const DecodeParams &p, int32_t blocks) {
     return (int64_t)blocks * p.block_size;
 }
 
-// Sequence s (length L, bad_len from bad_length(), group id gid =
-// seq_group[s] already loaded): whether it shares, and its partitions.
-// The group kernel decides a member's column with the same test
-// (member_shares), so every partition is computed exactly once.
+// Whether sequence s (length L, bad_len from bad_length(), group id gid =
+// seq_group[s]; lo, hi the group's run, T its region in tokens) shares the
+// region.  The group kernel decides a member's column, the per-sequence
+// items their partitions and the merge its partition count with this one
+// test, so every partition is computed exactly once.
 __device__ __forceinline__ bool member_shares(const DecodeParams &p, int s, int32_t gid,
                                               int32_t lo, int32_t hi, int64_t T, int32_t L,
                                               bool bad_len) {
