@@ -362,6 +362,59 @@ def test_grouped_decode_matches_per_sequence(pa):
     assert torch.equal(got2[keep], ref2[keep])
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_grouped_decode_at_the_rule_partition(pa, fp8):
+    """The prefix-shared batch at the partition size pa_decode_grouped_partition
+    picks for it (4096 tokens: every context fits one partition, so each
+    member is split only at its group's 2048-token region), with the
+    streaming policy, the workspace sized by pa_decode_grouped_workspace_size:
+    every row against the fp64 oracle and within 1e-5 of per-sequence decode."""
+    sh = wl.PREFIX_SHARED
+    dev = "cuda"
+    plan = wl.prefix_plan()
+    alloc, ids, k_pool, v_pool, order, pairs = build_shared_batch(pa, sh, plan, dev,
+                                                                  sh.num_blocks)
+    n_prompts, samples = plan.tail_lens.shape
+    S = len(ids)
+    stride = max(wl.blocks_needed(alloc.length(s), sh.block_size) for s in ids) + 1
+    tables, lens = alloc.batch_tables(ids, stride, sh.num_blocks - 1)
+    maxlen = int(lens.max())
+    groups = pa.decode_groups(tables, lens, np.arange(S) // samples, sh.block_size)
+    ps = pa.decode_grouped_partition(lens, *groups, sh.num_q_heads, sh.num_kv_heads,
+                                     sh.block_size, maxlen)
+    assert ps == 4096 and maxlen <= ps
+    gen = wl.make_generator(sh.seed + 11, dev)
+    q = wl.randn((S, sh.num_q_heads, sh.head_dim), torch.bfloat16, gen, dev)
+    t_dev, l_dev = torch.as_tensor(tables, device=dev), torch.as_tensor(lens, device=dev)
+    off, sg, shd = (torch.as_tensor(a, device=dev) for a in groups[:3])
+    ws = pa.decode_workspace(S, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                             maxlen, ps, dev, grouped=True)
+    got = torch.full((S, sh.num_q_heads, sh.head_dim), 7.0, device=dev)
+    ref = torch.full_like(got, 7.0)
+    say(f"case grouped decode at the rule's partition ({ps} tokens), fp8 {fp8}")
+    if fp8:
+        sc = wl.FP8_SCALE
+        k8 = (k_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        v8 = (v_pool.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        pa.pa_decode_grouped_fp8(got, q, k8, v8, t_dev, l_dev, sh.scale, sc, sc, maxlen, off, sg,
+                                 shd, samples, ps, ws)
+        pa.pa_decode_fp8(ref, q, k8, v8, t_dev, l_dev, sh.scale, sc, sc, maxlen, ps, ws)
+        kk, vv, scales = k8, v8, (sc, sc)
+    else:
+        pa.pa_decode_grouped(got, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, off, sg,
+                             shd, samples, ps, ws)
+        pa.pa_decode(ref, q, k_pool, v_pool, t_dev, l_dev, sh.scale, maxlen, ps, ws)
+        kk, vv, scales = k_pool, v_pool, ()
+    torch.cuda.synchronize()
+    assert torch.isfinite(got).all()
+    diff = (got - ref).abs().max().item()
+    want = oracle_decode_all(q, kk, vv, tables, lens, sh.block_size, sh.scale, pa.K_AXES,
+                             pa.V_AXES, *scales)
+    err = float(np.abs(got.double().cpu().numpy() - want).max())
+    say(f"  all {S} rows: vs per-sequence {diff:.2e}, vs oracle {err:.3e}")
+    assert diff <= 1e-5 and err <= TOL
+
+
 def test_grouped_decode_chunks_caps_and_loners(pa):
     """GQA heads (4 members per wave, groups of 6 in two chunks), a group
     left ungrouped, a group whose shared count is far too large, and an
