@@ -112,7 +112,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache,
  *   sink   device, PA_READ_STREAM_SINK_WORDS words, 4-byte aligned, written
  * Asynchronous on `stream`.  PA_ERR_INVALID_ARG on NULL or misaligned
  * pointers or a size that is not a multiple of 16. */
-#define PA_READ_STREAM_SINK_WORDS 8192
+#define PA_READ_STREAM_SINK_WORDS 32768
 pa_status pa_read_stream(const void *src, size_t bytes, uint32_t *sink,
                          void *stream);
 

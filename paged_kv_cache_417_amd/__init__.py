@@ -266,7 +266,7 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
                                _dtype_code(k_cache), ctypes.c_void_p(_stream(stream))))
 
 
-READ_STREAM_SINK_WORDS = 8192
+READ_STREAM_SINK_WORDS = 32768
 
 
 def pa_read_stream(src, sink, stream=None) -> None:

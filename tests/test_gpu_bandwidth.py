@@ -20,7 +20,7 @@ def host_xor(words):
 
 # 16 bytes (one load, most workgroups idle), a ragged size below one pass of
 # the grid, one grid pass of four loads per thread plus a ragged tail, 64 MiB
-@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 8192 * 256 * 64 + 16 * 7, 64 << 20])
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, SINK * 256 * 64 + 16 * 7, 64 << 20])
 def test_read_stream_folds_every_word(nbytes):
     rng = np.random.default_rng(nbytes)
     words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
