@@ -287,6 +287,10 @@ pa_status pa_prefill_chunk(float *out, const void *q,
  *                  gets a NaN row.
  *   num_groups     >= 0 (0: pa_decode_ex).
  *   max_group_size host bound of the group sizes (>= 1 when num_groups > 0).
+ *   partition_size 0: pa_decode_default_partition's size; the size
+ *                  pa_decode_grouped_partition picks from host copies of the
+ *                  group arrays suits a grouped batch better (fewer, longer
+ *                  partitions when the groups carry most of the tokens).
  *   workspace      at least pa_decode_grouped_workspace_size(...) bytes.
  * dtype must be BF16 (the fp32 path has no grouped kernel: UNSUPPORTED).
  * Flags and errors as pa_decode_ex. */

@@ -364,8 +364,10 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
                       max_context_len, group_offsets, seq_group, group_shared, max_group_size,
                       partition_size=0, workspace=None, stream=None, kv_reuse=False) -> None:
     """Paged decode with groups of sequences that share leading blocks: each
-    group's shared partitions are read once (int32 device tensors:
-    group_offsets [G+1], seq_group [S], group_shared [G])."""
+    group's shared region is read once (int32 device tensors: group_offsets
+    [G+1], seq_group [S], group_shared [G]).  decode_grouped_partition gives
+    the partition size for such a batch, decode_workspace(..., grouped=True)
+    a workspace large enough."""
     nb, hkv, bs, d = _geometry(k_cache)
     s, hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
