@@ -920,13 +920,22 @@ ROTATE = 4  # disjoint copies of a decode batch visited in turn by the timed cal
 def row_gqa(pa, wl, torch, np, reps, cpu_budget):
     sh = wl.GQA
     case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES, replicas=ROTATE)
-    r = decode_row(pa, torch, case, reps, replicas=ROTATE)
+    # the partition size the library picks from the batch's lengths (a
+    # serving loop knows them on the host); the size-only default beside it
+    S = sh.num_seqs
+    ps = pa.decode_partition_for_lengths(case.lengths[:S], sh.num_kv_heads, sh.block_size,
+                                         int(max(case.lengths)))
+    r = decode_row(pa, torch, case, reps, ps=ps, replicas=ROTATE)
+    r["partition_size"] = ps
+    r["us_default_partition"] = decode_row(pa, torch, case, reps, replicas=ROTATE)["us"]
     if cpu_budget > 0:
         S = sh.num_seqs
         r["cpu_oracle"] = cpu_decode_row(case, cpu_budget, tables=case.tables[:S],
                                          lengths=case.lengths[:S])
     r["workload"] = ("gqa decode: 128 seqs, ctx round(lognormal(ln 1024, 1)) clipped "
-                     "[16, 8192], 32 q / 8 kv heads, head_dim 128, block 16, bf16")
+                     "[16, 8192], 32 q / 8 kv heads, head_dim 128, block 16, bf16; "
+                     "partitions of pa_decode_partition_for_lengths (us_default_partition: "
+                     "pa_decode_default_partition's)")
     return r
 
 
@@ -1489,8 +1498,11 @@ def decode_only(pa, wl, torch, np, reps, out_json):
     run(DECODE_PHASES[0], wl.make_decode_case(wl.MHA_7B, dev, pa.K_AXES, pa.V_AXES,
                                               replicas=ROTATE))
     torch.cuda.empty_cache()
-    run(DECODE_PHASES[1], wl.make_decode_case(wl.GQA, dev, pa.K_AXES, pa.V_AXES,
-                                              replicas=ROTATE))
+    gcase = wl.make_decode_case(wl.GQA, dev, pa.K_AXES, pa.V_AXES, replicas=ROTATE)
+    run(DECODE_PHASES[1], gcase, ps=pa.decode_partition_for_lengths(
+        gcase.lengths[:wl.GQA.num_seqs], wl.GQA.num_kv_heads, wl.GQA.block_size,
+        int(max(gcase.lengths))))
+    del gcase
     torch.cuda.empty_cache()
     sh8 = wl.DecodeShape("mha_7b", 64, 32, 32, 128, 16, 200_000, "fp8", wl.MHA_7B.seed)
 

@@ -123,6 +123,19 @@ pa_status pa_read_stream(const void *src, size_t bytes, uint32_t *sink,
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
                                     int32_t block_size, int32_t max_context_len);
 
+/* Partition size for pa_decode from host copies of the batch's context
+ * lengths ([VF] §1.1: any split into independent segments; [VE] §3.3: decode
+ * is bound by memory bandwidth, so the split should keep every wave slot
+ * streaming).  With 257 .. 1024 (sequence, kv head) pairs the batch runs in
+ * about one round of the chip's 2048 wave slots, and the size is 1.2 times
+ * the average tokens per slot (the valid lengths' sum times num_kv_heads /
+ * 2048), rounded to a multiple of max(128, block_size), at most 4096;
+ * otherwise it is pa_decode_default_partition's.  0 on invalid arguments
+ * (pa_last_error says which). */
+int32_t pa_decode_partition_for_lengths(const int32_t *context_lens, int32_t num_seqs,
+                                        int32_t num_kv_heads, int32_t block_size,
+                                        int32_t max_context_len);
+
 /* Bytes of device workspace pa_decode needs for the split-K partials with
  * these sizes (partition_size 0 = the default above).  0 when no sequence
  * can span more than one partition; (size_t)-1 on invalid sizes. */

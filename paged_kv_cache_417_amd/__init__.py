@@ -56,7 +56,8 @@ EXPORTED = (
     "pa_cache_write_fp8", "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_seq_blocks_needed", "pa_seq_num_blocks",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_add", "pa_sched_step", "pa_sched_complete",
     "pa_sched_stats", "pa_decode_grouped", "pa_decode_grouped_fp8", "pa_decode_groups",
-    "pa_decode_grouped_workspace_size", "pa_decode_grouped_partition", "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
+    "pa_decode_grouped_workspace_size", "pa_decode_grouped_partition",
+    "pa_decode_partition_for_lengths", "pa_decode_noalloc", "pa_seq_create_prefix_ex", "pa_prefix_cache_offload",
     "pa_prefix_host_stats", "pa_sched_add_samples",
 )
 
@@ -183,6 +184,7 @@ def _declare(lib):
         "pa_decode_groups": (st, [pi32, i32, pi32, pi32, i32, i32, i32, pi32, pi32, pi32]),
         "pa_decode_grouped_partition": (i32, [pi32, pi32, pi32, pi32, i32, i32, i32, i32, i32,
                                               i32, i32]),
+        "pa_decode_partition_for_lengths": (i32, [pi32, i32, i32, i32, i32]),
         "pa_decode_grouped_fp8": (st, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, i32, i32, vp, vp, vp, i32, i32, vp, sz,
                                        ctypes.c_uint32, vp]),
@@ -307,6 +309,18 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
     if n == ctypes.c_size_t(-1).value:
         raise PAError(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: invalid sizes")
     return int(n)
+
+
+def decode_partition_for_lengths(lens, num_kv_heads, block_size, max_context_len) -> int:
+    """pa_decode_partition_for_lengths on a host array of context lengths:
+    the partition size for pa_decode of this batch."""
+    import numpy as np
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    ps = _lib.pa_decode_partition_for_lengths(_i32p(lens), len(lens), num_kv_heads, block_size,
+                                              int(max_context_len))
+    if ps <= 0:
+        raise PAError(PA_ERR_INVALID_ARG, _lib.pa_last_error().decode(errors="replace"))
+    return int(ps)
 
 
 def pa_decode_grouped_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

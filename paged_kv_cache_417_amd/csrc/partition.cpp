@@ -51,6 +51,46 @@ int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int3
     return pa::default_partition(num_seqs, num_kv_heads, block_size, max_context_len);
 }
 
+// From the lengths themselves.  With 257 .. 1024 (sequence, kv head) pairs
+// the longest-first grid runs the batch in about one round of the 2048 wave
+// slots, and a round ends when its fullest slot does: the partitions should
+// be a little longer than the average load of a slot, so that full
+// partitions and the tails that follow them pack the slots evenly.  A sweep
+// of ten lognormal-length batches of 128 sequences x 8 kv heads (partitions
+// of 768 .. 1536 tokens) found the fastest size at 1.2 times the average
+// tokens per slot, rounded to 128, on eight of them and within 0.5% on the
+// other two.  Other batches keep pa_decode_default_partition: with many
+// pairs the grid runs several rounds of short partitions, with few the
+// default already grows the partitions.
+int32_t pa_decode_partition_for_lengths(const int32_t *context_lens, int32_t num_seqs,
+                                        int32_t num_kv_heads, int32_t block_size,
+                                        int32_t max_context_len) {
+    const char *fn = "pa_decode_partition_for_lengths";
+    if (num_seqs < 0 || num_kv_heads <= 0 || block_size <= 0 || max_context_len < 0 ||
+        (num_seqs > 0 && !context_lens)) {
+        pa::fail(PA_ERR_INVALID_ARG, "%s: num_seqs %d num_kv_heads %d block_size %d "
+                 "max_context_len %d%s", fn, num_seqs, num_kv_heads, block_size,
+                 max_context_len, num_seqs > 0 && !context_lens ? ", NULL lengths" : "");
+        return 0;
+    }
+    const int32_t ps0 = pa::default_partition(num_seqs, num_kv_heads, block_size,
+                                              max_context_len);
+    pa::ok();
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    if (pairs <= 256 || pairs > 1024) return ps0;
+    int64_t tokens = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t L = context_lens[s];
+        if (L > 0 && L <= max_context_len) tokens += L;
+    }
+    const int64_t unit = block_size > 128 ? block_size : 128;  // a multiple of 32 and of BS
+    const double target = 1.2 * (double)(tokens * num_kv_heads) / 2048.0;
+    int64_t ps = (int64_t)(target / (double)unit + 0.5) * unit;
+    if (ps < unit) ps = unit;
+    if (ps > 4096) ps = 4096;
+    return (int32_t)ps;
+}
+
 // Grouped calls (pa_decode_grouped): the grid holds one wave per (kv head,
 // group chunk, shared partition) and per (kv head, sequence, own partition),
 // and each wave pays a start-up (lengths, group arrays, table slice, first

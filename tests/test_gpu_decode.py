@@ -351,19 +351,24 @@ def test_bad_block_inside_a_split_sequence_gives_nan_row(pa, ps):
 
 
 @pytest.mark.parametrize("name,ps,valu", [("mha_7b", 0, False), ("gqa", 0, False),
-                                          ("mixed", 0, False), ("mixed", 512, False),
-                                          ("mha_7b", 0, True)])
+                                          ("gqa", -1, False), ("mixed", 0, False),
+                                          ("mixed", 512, False), ("mha_7b", 0, True)])
 def test_full_size_batches(pa, name, ps, valu):
     """The 7B-shaped (64 sequences), grouped-query (128) and long-context
     (8 x 32768) batches at full size, in the launch configuration the
-    benchmark times (the library's default partitions; the long-context
-    batch also at 512-token partitions): every row of every sequence
-    against the fp64 oracle, run on the host threads.  The 7B-shaped batch
-    also on the vector-ALU kernel (PA_DECODE_VALU)."""
+    benchmark times (the library's default partitions; the grouped-query
+    batch also at the size pa_decode_partition_for_lengths picks from its
+    lengths, ps=-1 here; the long-context batch also at 512-token
+    partitions): every row of every sequence against the fp64 oracle, run
+    on the host threads.  The 7B-shaped batch also on the vector-ALU kernel
+    (PA_DECODE_VALU)."""
     sh = wl.SHAPES[name]
+    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
+    if ps < 0:
+        ps = pa.decode_partition_for_lengths(case.lengths, sh.num_kv_heads, sh.block_size,
+                                             int(max(case.lengths)))
     say(f"case full-size {name}: S={sh.num_seqs} Hq={sh.num_q_heads} Hkv={sh.num_kv_heads} "
         f"BS={sh.block_size} NB={sh.num_blocks} ps={ps} valu={valu}")
-    case = wl.make_decode_case(sh, "cuda", pa.K_AXES, pa.V_AXES)
     out = run_decode(pa, case, ps=ps, valu=valu)
     assert torch.isfinite(out).all()
     ref = oracle_decode_all(case.q, case.k_pool, case.v_pool, case.tables, case.lengths,
